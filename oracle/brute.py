@@ -1,0 +1,99 @@
+"""Exact pure-Python forms of the operators, for tiny inputs -- TEST INFRASTRUCTURE.
+
+Independent of ``oracle.c``: Python integers (no width, no wrap until asked),
+``fractions.Fraction`` for exact real arithmetic, and fp32 rounding emulated
+through ``struct`` (a double-to-single store rounds to nearest even).  Used
+only to pin the C oracle on small cases.
+"""
+import struct
+from fractions import Fraction
+
+
+def f32(x):
+    """Round a Python float (double) to the nearest fp32 value, ties to even."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def wrap32(v):
+    """Two's-complement wrap of an integer into int32."""
+    v &= 0xFFFFFFFF
+    return v - (1 << 32) if v >= (1 << 31) else v
+
+
+def matmul_integer(A, B, za, zb):
+    """Exact sum_k (A[m][k]-za)(B[k][n]-zb[n]) as Python ints (no wrap).
+
+    A: list of M rows of K ints; B: list of K rows of N ints; zb: list of N.
+    """
+    M, K, N = len(A), len(B), len(B[0])
+    return [[sum((A[m][k] - za) * (B[k][n] - zb[n]) for k in range(K))
+             for n in range(N)] for m in range(M)]
+
+
+def a8w8(A, W, act_scale, weight_scale):
+    """A8W8 with each fp32 step emulated exactly: int -> fp32, *as, *ws.
+
+    The integer sum is exact; an int32 value converts to double exactly and
+    the double -> fp32 store is the single RNE rounding of the cast.  A
+    product of two fp32 values is exact in double (48 significant bits), so
+    rounding it to fp32 is the fp32 multiply.
+    """
+    M, K, N = len(A), len(W), len(W[0])
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = wrap32(sum(A[m][k] * W[k][n] for k in range(K)))
+            f = f32(float(acc))
+            f = f32(f * act_scale[m])
+            f = f32(f * weight_scale[n])
+            row.append((acc, f))
+        out.append(row)
+    return out
+
+
+def w8a32_exact(A, W, scale, zp):
+    """Exact sum_k a (b - zp) scale, and sum_k |a| |b - zp| |scale|, as Fractions."""
+    M, K, N = len(A), len(W), len(W[0])
+    s = Fraction(scale)
+    R, Bd = [], []
+    for m in range(M):
+        r, b = [], []
+        for n in range(N):
+            r.append(sum(Fraction(A[m][k]) * (W[k][n] - zp) for k in range(K)) * s)
+            b.append(sum(abs(Fraction(A[m][k])) * abs(W[k][n] - zp) for k in range(K)) * abs(s))
+        R.append(r)
+        Bd.append(b)
+    return R, Bd
+
+
+def bf16_bits(x):
+    """bfloat16 bits of a finite fp32 value by exact rational rounding.
+
+    Finds the two bfloat16 neighbours of x by exact arithmetic on Fractions and
+    keeps the nearer one, the even one on a tie.  Written independently of
+    the bit trick in the C oracle.
+    """
+    bits = struct.unpack("<I", struct.pack("<f", x))[0]
+    sign = bits >> 31
+    mag = abs(Fraction(x))
+    lo_bits = (bits & 0x7FFFFFFF) & 0xFFFF0000  # truncation toward zero
+    hi_bits = lo_bits + 0x10000
+
+    def val(b):
+        return abs(Fraction(struct.unpack("<f", struct.pack("<I", b))[0])) \
+            if (b & 0x7F800000) != 0x7F800000 else None
+
+    lo = val(lo_bits)
+    hi = val(hi_bits)
+    if hi is None:  # rounding up would reach infinity: compare with the halfway point
+        # largest finite bf16 is lo; the overflow threshold is lo + half an ulp
+        ulp = lo - val(lo_bits - 0x10000)
+        pick = hi_bits if mag >= lo + ulp / 2 else lo_bits
+    elif mag - lo < hi - mag:
+        pick = lo_bits
+    elif mag - lo > hi - mag:
+        pick = hi_bits
+    else:
+        pick = lo_bits if ((lo_bits >> 16) & 1) == 0 else hi_bits
+    return (sign << 15) | (pick >> 16)

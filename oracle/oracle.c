@@ -1,0 +1,245 @@
+/*
+ * CPU oracle for the quantised matrix multiplies -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The product path (the HIP library and its Python
+ * binding) never links, imports or calls it.  It shares no source, header,
+ * table or helper with the HIP path.
+ *
+ * Everything here is the plain definition written out as loops: integer sums
+ * in int64, floating-point references in double, each epilogue step in the
+ * order the pages give.  No blocking, no fusion, no reordering of
+ * floating-point work beyond the loop nest shown (integer sums are exact in
+ * any order).  Compile with -ffp-contract=off so that no multiply is fused
+ * into an add behind our back.
+ *
+ * Sources (page titles; sections named as on the page):
+ *  [P1] "feat(PULPOpen): matmul that dequantises an int8 weight in-kernel",
+ *       intro paragraph and section "The kernel" (the identity
+ *       sum_k a_k (b_k - zp) scale = scale (sum a_k b_k - zp sum a_k)).
+ *  [P2] "Feature/a8w8 matmul dequant fusion", the walkthrough's sequence
+ *       diagram (int8 matmul -> int32 accumulator -> cast to FP32 -> row scale
+ *       by act_scale -> column scale by weight_scale -> cast to out_dtype),
+ *       the Codex review (rank-1 [M]/[N] scales mean rows/columns) and the
+ *       "What Changed" list (INT32 accumulator, FP32/BF16 outputs).
+ *  [P5] "feat(onnx-to-hip): lower quantized integer conv and matmul",
+ *       section "What", MatMulInteger paragraph (ranks 2-4, zero points,
+ *       shared B) and the accumulator paragraph (f32 accumulation only while
+ *       65025*K fits the 24-bit mantissa, otherwise int64 accumulation stored
+ *       as a wrapping int32).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* Helpers that are part of the definition                                 */
+/* ---------------------------------------------------------------------- */
+
+/* int64 -> int32 by two's-complement wrap ([P5] "What": "storing a wrapping
+ * int32").  Done through uint32 so the conversion is defined C. */
+static int32_t wrap_i32(int64_t v) {
+    uint32_t u = (uint32_t)((uint64_t)v & 0xffffffffu);
+    int32_t r;
+    memcpy(&r, &u, sizeof r);
+    return r;
+}
+
+/* IEEE-754 binary32 -> bfloat16, round to nearest, ties to even, written
+ * from the definition on the bit pattern: keep the top 16 bits, add half an
+ * ulp of the kept part, with ties going to the even kept value.  NaN stays a
+ * quiet NaN of the same sign.  ([P2] out_dtype BF16 "cast".) */
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x007fffffu) != 0)
+        return (uint16_t)((b >> 16) | 0x0040u);
+    uint32_t kept_lsb = (b >> 16) & 1u;
+    uint32_t rounded = b + 0x7fffu + kept_lsb;
+    return (uint16_t)(rounded >> 16);
+}
+
+/* ---------------------------------------------------------------------- */
+/* W8A32 ([P1]): naive dequantise-then-matmul                              */
+/* ---------------------------------------------------------------------- */
+
+/* The Dequant node of [P1]'s intro, materialised: Wd = (W - zp) * scale,
+ * then the fp32 matmul A @ Wd -- here carried out in double so that R is the
+ * exact result up to double rounding.  `bound` receives
+ * |scale| * sum_k |A[m,k]| * |W[k,n] - zp|, the scale of the tolerance.
+ * A: [M,K] (lda), W: [K,N] (ldw), R and bound: [M,N] dense. */
+void oracle_w8a32(int64_t M, int64_t N, int64_t K,
+                  const float* A, int64_t lda,
+                  const int8_t* W, int64_t ldw,
+                  float scale, int32_t zero_point,
+                  double* R, double* bound) {
+    double* Wd = (double*)malloc(sizeof(double) * (size_t)(K * N));
+    double* Wabs = (double*)malloc(sizeof(double) * (size_t)(K * N));
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            double centred = (double)W[k * ldw + n] - (double)zero_point;
+            Wd[k * N + n] = centred * (double)scale;
+            Wabs[k * N + n] = fabs(centred) * fabs((double)scale);
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, b = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = (double)A[m * lda + k];
+                s += a * Wd[k * N + n];
+                b += fabs(a) * Wabs[k * N + n];
+            }
+            R[m * N + n] = s;
+            if (bound) bound[m * N + n] = b;
+        }
+    }
+    free(Wd);
+    free(Wabs);
+}
+
+/* ---------------------------------------------------------------------- */
+/* A8W8 ([P2]): int8 x int8 -> int32 -> fp32 -> *act_scale -> *weight_scale */
+/* ---------------------------------------------------------------------- */
+
+static float a8w8_epilogue(int32_t acc, float as, float ws) {
+    float f = (float)acc;    /* cast: int32 -> fp32, round to nearest even */
+    f = f * as;              /* row scale, rounded to fp32                 */
+    f = f * ws;              /* column scale, rounded to fp32              */
+    return f;
+}
+
+/* W is [K,N] (ldw) when b_trans == 0 and [N,K] (ldw) when b_trans == 1.
+ * act_scale has length 1 or M, weight_scale length 1 or N.
+ * Outputs ([M,N] dense) may each be NULL. */
+void oracle_a8w8(int64_t M, int64_t N, int64_t K,
+                 const int8_t* A, int64_t lda,
+                 const int8_t* W, int64_t ldw, int b_trans,
+                 const float* act_scale, int64_t as_len,
+                 const float* weight_scale, int64_t ws_len,
+                 int32_t* acc_out, float* out_f32, uint16_t* out_bf16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t a = A[m * lda + k];
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t b = b_trans ? W[n * ldw + k] : W[k * ldw + n];
+                row[n] += a * b;
+            }
+        }
+        float as = act_scale[as_len == 1 ? 0 : m];
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t acc = wrap_i32(row[n]);
+            float f = a8w8_epilogue(acc, as, weight_scale[ws_len == 1 ? 0 : n]);
+            if (acc_out) acc_out[m * N + n] = acc;
+            if (out_f32) out_f32[m * N + n] = f;
+            if (out_bf16) out_bf16[m * N + n] = oracle_f32_to_bf16(f);
+        }
+        free(row);
+    }
+}
+
+/* Same as oracle_a8w8 at `count` chosen output positions (rows[i], cols[i]);
+ * results go to index i of each (nullable) output. */
+void oracle_a8w8_at(int64_t M, int64_t N, int64_t K,
+                    const int8_t* A, int64_t lda,
+                    const int8_t* W, int64_t ldw, int b_trans,
+                    const float* act_scale, int64_t as_len,
+                    const float* weight_scale, int64_t ws_len,
+                    int64_t count, const int64_t* rows, const int64_t* cols,
+                    int32_t* acc_out, float* out_f32, uint16_t* out_bf16) {
+    (void)M; (void)N;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = rows[i], n = cols[i];
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t b = b_trans ? W[n * ldw + k] : W[k * ldw + n];
+            s += (int64_t)A[m * lda + k] * b;
+        }
+        int32_t acc = wrap_i32(s);
+        float f = a8w8_epilogue(acc, act_scale[as_len == 1 ? 0 : m],
+                                weight_scale[ws_len == 1 ? 0 : n]);
+        if (acc_out) acc_out[i] = acc;
+        if (out_f32) out_f32[i] = f;
+        if (out_bf16) out_bf16[i] = oracle_f32_to_bf16(f);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* MatMulInteger ([P5])                                                    */
+/* ---------------------------------------------------------------------- */
+
+static int64_t load_8bit(const void* base, int is_u8, int64_t idx) {
+    return is_u8 ? (int64_t)((const uint8_t*)base)[idx]
+                 : (int64_t)((const int8_t*)base)[idx];
+}
+
+/* Y[b,m,n] = wrap32( sum_k (A[b,m,k] - a_zp) * (B[b,k,n] - b_zp[n or 0]) ).
+ * A: batch x [M,K] with row stride lda and batch stride a_bstride (0 means
+ * one A shared by every batch); B: batch x [K,N] with ldb and b_bstride
+ * (0 = one shared matrix); zero points already widened to int32; b_zp may be
+ * NULL (absent = 0) or hold 1 or N values.  Y: batch x [M,N] (ldy,
+ * y_bstride). */
+void oracle_matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void* A, int a_is_u8, int64_t lda, int64_t a_bstride,
+                           const void* B, int b_is_u8, int64_t ldb, int64_t b_bstride,
+                           int32_t a_zp, const int32_t* b_zp, int64_t b_zp_len,
+                           int32_t* Y, int64_t ldy, int64_t y_bstride) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bt = 0; bt < batch; ++bt) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t a = load_8bit(A, a_is_u8, bt * a_bstride + m * lda + k) - a_zp;
+                for (int64_t n = 0; n < N; ++n) {
+                    int64_t zb = b_zp ? b_zp[b_zp_len == 1 ? 0 : n] : 0;
+                    int64_t b = load_8bit(B, b_is_u8, bt * b_bstride + k * ldb + n) - zb;
+                    row[n] += a * b;
+                }
+            }
+            for (int64_t n = 0; n < N; ++n)
+                Y[bt * y_bstride + m * ldy + n] = wrap_i32(row[n]);
+            free(row);
+        }
+    }
+}
+
+/* Same sum at `count` positions (bts[i], rows[i], cols[i]) -> Y[i]. */
+void oracle_matmul_integer_at(int64_t K,
+                              const void* A, int a_is_u8, int64_t lda, int64_t a_bstride,
+                              const void* B, int b_is_u8, int64_t ldb, int64_t b_bstride,
+                              int32_t a_zp, const int32_t* b_zp, int64_t b_zp_len,
+                              int64_t count, const int64_t* bts, const int64_t* rows,
+                              const int64_t* cols, int32_t* Y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t bt = bts[i], m = rows[i], n = cols[i];
+        int64_t zb = b_zp ? b_zp[b_zp_len == 1 ? 0 : n] : 0;
+        int64_t s = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t a = load_8bit(A, a_is_u8, bt * a_bstride + m * lda + k) - a_zp;
+            int64_t b = load_8bit(B, b_is_u8, bt * b_bstride + k * ldb + n) - zb;
+            s += a * b;
+        }
+        Y[i] = wrap_i32(s);
+    }
+}
+
+/* The f32-accumulator form [P5] selects while 65025*K fits the 24-bit
+ * mantissa: the same centred products, summed one after another in fp32,
+ * the total converted to int32.  Used only to check the accumulator bound;
+ * one dot product of length K (a: stride 1, b: stride ldb). */
+int32_t oracle_dot_f32acc(int64_t K, const void* a, int a_is_u8,
+                          const void* b, int b_is_u8, int64_t ldb,
+                          int32_t a_zp, int32_t b_zp) {
+    float s = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float p = (float)((load_8bit(a, a_is_u8, k) - a_zp) *
+                          (load_8bit(b, b_is_u8, k * ldb) - b_zp));
+        s = s + p;
+    }
+    return (int32_t)s;
+}

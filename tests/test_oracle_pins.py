@@ -1,0 +1,355 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, brute force,
+library routines on special cases.  CPU only; no HIP involved."""
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+import seeded_inputs as si
+from golden_io import load
+
+
+
+# ---------------------------------------------------------------------------
+# MatMulInteger: accumulator bound and wrap (worked values on the hip-ep page)
+# ---------------------------------------------------------------------------
+
+def test_k259_worked_value_from_page():
+    g = load("matmul_integer_accumulator.txt")
+    a = np.full((1, 259), 255, np.uint8)
+    b = np.full((259, 1), 255, np.uint8)
+    assert oracle.matmul_integer(a, b, 0, None)[0, 0] == int(g["u8_all_255_k259"])
+    assert 65025 * 259 == int(g["u8_all_255_k259"])
+
+
+def test_f32_accumulator_exact_up_to_258_and_not_beyond():
+    g = load("matmul_integer_accumulator.txt")
+    kmax = int(g["f32_max_exact_k"])
+    assert 65025 * kmax <= 2 ** 24 < 65025 * (kmax + 1)
+    a = np.full(kmax, 255, np.uint8)
+    assert oracle.dot_f32acc(a, a) == int(g["u8_all_255_k258"])
+    a = np.full(kmax + 1, 255, np.uint8)
+    exact = int(g["u8_all_255_k259"])
+    f32_sum = oracle.dot_f32acc(a, a)
+    # an independent sequential fp32 sum (numpy's cumsum is a running sum)
+    running = np.cumsum(np.full(kmax + 1, 65025, np.float32), dtype=np.float32)[-1]
+    assert f32_sum == int(running) == exact + 1
+
+
+def test_f32_accumulator_agrees_with_int_when_k_at_most_258():
+    g = si.rng(7)
+    for K in (1, 17, 200, 258):
+        for a_dt, b_dt, za, zb in ((np.uint8, np.uint8, 0, 255), (np.uint8, np.int8, 255, -128),
+                                   (np.int8, np.int8, -128, 127), (np.int8, np.uint8, 127, 0)):
+            a = si.randint(g, (K,), 0 if a_dt == np.uint8 else -128, 255 if a_dt == np.uint8 else 127, a_dt)
+            b = si.randint(g, (K,), 0 if b_dt == np.uint8 else -128, 255 if b_dt == np.uint8 else 127, b_dt)
+            y = oracle.matmul_integer(a.reshape(1, K), b.reshape(K, 1), za, zb)[0, 0]
+            assert oracle.dot_f32acc(a, b, za, zb) == y
+
+
+def test_wrap_to_int32():
+    g = load("matmul_integer_accumulator.txt")
+    K = 40000
+    a = np.full((1, K), 255, np.uint8)
+    b = np.full((K, 1), 255, np.uint8)
+    assert oracle.matmul_integer(a, b)[0, 0] == int(g["u8_all_255_k40000_wrapped"])
+    assert brute.wrap32(65025 * K) == int(g["u8_all_255_k40000_wrapped"])
+
+
+# ---------------------------------------------------------------------------
+# MatMulInteger: closed forms and brute force
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("a_dt,b_dt", [(np.uint8, np.uint8), (np.uint8, np.int8),
+                                       (np.int8, np.int8), (np.int8, np.uint8)])
+@pytest.mark.parametrize("za,zb", [(0, 0), (1, 127), (128, 255), (-128, -8), (127, 8)])
+def test_product_table_k1(a_dt, b_dt, za, zb):
+    """K = 1 with every 8-bit value on each side: Y is the outer product."""
+    if a_dt == np.uint8 and za < 0 or a_dt == np.int8 and za > 127:
+        pytest.skip("zero point outside the operand's range")
+    if b_dt == np.uint8 and zb < 0 or b_dt == np.int8 and zb > 127:
+        pytest.skip("zero point outside the operand's range")
+    av = np.arange(256).astype(a_dt) if a_dt == np.uint8 else np.arange(-128, 128).astype(a_dt)
+    bv = np.arange(256).astype(b_dt) if b_dt == np.uint8 else np.arange(-128, 128).astype(b_dt)
+    Y = oracle.matmul_integer(av.reshape(256, 1), bv.reshape(1, 256), za, zb)
+    expect = np.outer(av.astype(np.int64) - za, bv.astype(np.int64) - zb)
+    np.testing.assert_array_equal(Y, expect)
+
+
+def test_constant_fill_closed_form():
+    for (av, za, bv, zb, K) in ((200, 3, -100, 7, 2048), (0, 255, 255, 0, 1000), (-128, 127, -128, 127, 333)):
+        a_dt = np.uint8 if av >= 0 and za >= 0 and av <= 255 and za <= 255 and (av > 127 or za > 127) else np.int8
+        b_dt = np.uint8 if bv >= 0 and bv > 127 else np.int8
+        A = np.full((3, K), av).astype(a_dt)
+        B = np.full((K, 5), bv).astype(b_dt)
+        Y = oracle.matmul_integer(A, B, za, zb)
+        assert (Y == brute.wrap32(K * (av - za) * (bv - zb))).all()
+
+
+def test_one_hot_row_selects_centred_row_of_b():
+    A, B, zb = si.matmul_integer_inputs(1, 1, 37, 53, seed=11)
+    B = B.astype(np.int8)
+    for j in (0, 9, 52):
+        a = np.zeros((1, 53), np.uint8)
+        a[0, j] = 1
+        Y = oracle.matmul_integer(a, B, 0, zb)
+        np.testing.assert_array_equal(Y[0], B[j].astype(np.int64) - zb.astype(np.int64))
+
+
+def _rand8(g, shape, dt):
+    return si.randint(g, shape, 0, 255, dt) if dt == np.uint8 else si.randint(g, shape, -128, 127, dt)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_matmul_integer_brute_force(seed):
+    g = si.rng(1000 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 10, size=3))
+    a_dt = (np.uint8, np.int8)[seed % 2]
+    b_dt = (np.uint8, np.int8)[(seed // 2) % 2]
+    A = _rand8(g, (M, K), a_dt)
+    B = _rand8(g, (K, N), b_dt)
+    za = int(_rand8(g, (), a_dt))
+    per_col = seed % 3 != 0
+    zb = _rand8(g, (N,), b_dt) if per_col else np.array(int(_rand8(g, (), b_dt)))
+    Y = oracle.matmul_integer(A, B, za, zb)
+    zbl = [int(x) for x in np.broadcast_to(zb, (N,))]
+    exact = brute.matmul_integer(A.astype(int).tolist(), B.astype(int).tolist(), za, zbl)
+    assert Y.tolist() == [[brute.wrap32(v) for v in r] for r in exact]
+
+
+def test_zero_point_identity_used_by_the_kernels():
+    """sum (a-za)(b-zb) = sum a'b' + cb*sum a' + ca*sum b' + K*ca*cb with
+    a' = a - 128 (u8) or a (i8), ca = 128 - za (u8) or -za (i8); same for b.
+    Checked in exact integers against the oracle; this is the form the HIP
+    kernels evaluate, so the oracle itself never uses it."""
+    g = si.rng(99)
+    for trial in range(40):
+        M, N, K = (int(x) for x in g.integers(1, 12, size=3))
+        a_dt = (np.uint8, np.int8)[trial % 2]
+        b_dt = (np.uint8, np.int8)[(trial // 2) % 2]
+        A = _rand8(g, (M, K), a_dt).astype(np.int64)
+        B = _rand8(g, (K, N), b_dt).astype(np.int64)
+        za = int(_rand8(g, (), a_dt))
+        zb = _rand8(g, (N,), b_dt).astype(np.int64)
+        sa = 128 if a_dt == np.uint8 else 0
+        sb = 128 if b_dt == np.uint8 else 0
+        A1, B1 = A - sa, B - sb
+        ca, cb = sa - za, sb - zb
+        ident = A1 @ B1 + np.outer(A1.sum(1), cb) + ca * B1.sum(0)[None, :] + K * ca * cb[None, :]
+        Y = oracle.matmul_integer(A.astype(a_dt), B.astype(b_dt), za, zb.astype(b_dt))
+        np.testing.assert_array_equal(Y, ident)
+
+
+def test_shared_b_and_size1_batch_broadcast():
+    g = si.rng(5)
+    A = _rand8(g, (3, 4, 6, 9), np.uint8)
+    B = _rand8(g, (9, 7), np.int8)
+    zb = _rand8(g, (7,), np.int8)
+    Y = oracle.matmul_integer(A, B, 100, zb)
+    assert Y.shape == (3, 4, 6, 7)
+    for i in range(3):
+        for j in range(4):
+            np.testing.assert_array_equal(Y[i, j], oracle.matmul_integer(A[i, j], B, 100, zb))
+    # B whose batch dimensions are all 1 is the same shared matrix
+    np.testing.assert_array_equal(oracle.matmul_integer(A, B.reshape(1, 1, 9, 7), 100, zb), Y)
+    # a size-1 batch on A is repeated against a batched B
+    A1 = _rand8(g, (1, 6, 9), np.int8)
+    B3 = _rand8(g, (4, 9, 7), np.int8)
+    Y3 = oracle.matmul_integer(A1, B3, -3, None)
+    for i in range(4):
+        np.testing.assert_array_equal(Y3[i], oracle.matmul_integer(A1[0], B3[i], -3, None))
+
+
+def test_zero_point_zero_is_library_matmul():
+    """With both zero points 0 the operator is the plain integer matmul."""
+    A, B, _ = si.matmul_integer_inputs(2, 33, 45, 77, seed=3)
+    Y = oracle.matmul_integer(A, B, 0, None)
+    ref = np.matmul(A.astype(np.int64), B.astype(np.int64))
+    np.testing.assert_array_equal(Y, ref)
+
+
+def test_matmul_integer_at_matches_full():
+    A, B, zb = si.matmul_integer_inputs(3, 20, 30, 70, seed=8)
+    Y = oracle.matmul_integer(A, B, 128, zb)
+    g = si.rng(1)
+    bts, rows, cols = g.integers(0, 3, 50), g.integers(0, 20, 50), g.integers(0, 30, 50)
+    y = oracle.matmul_integer_at(A, B, 128, zb, bts, rows, cols, b_shared=True)
+    np.testing.assert_array_equal(y, Y[bts, rows, cols])
+
+
+# ---------------------------------------------------------------------------
+# A8W8 (pypto page): epilogue order, scale forms, torch expression
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_a8w8_brute_force(seed):
+    g = si.rng(2000 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 9, size=3))
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=seed, lo=-128, hi=127)
+    r = oracle.a8w8(A, W, s_a, s_w)
+    ref = brute.a8w8(A.astype(int).tolist(), W.astype(int).tolist(),
+                     [float(x) for x in s_a], [float(x) for x in s_w])
+    assert r["acc"].tolist() == [[c[0] for c in row] for row in ref]
+    assert r["f32"].tolist() == [[c[1] for c in row] for row in ref]
+
+
+def test_a8w8_unit_scales_give_the_rounded_accumulator():
+    A, W, _, _ = si.a8w8_inputs(40, 50, 3000, seed=4, lo=-128, hi=127)
+    r = oracle.a8w8(A, W, np.ones(1, np.float32), np.ones(1, np.float32))
+    acc = np.matmul(A.astype(np.int64), W.astype(np.int64))
+    np.testing.assert_array_equal(r["acc"], acc)
+    np.testing.assert_array_equal(r["f32"], acc.astype(np.float32))
+
+
+def test_a8w8_power_of_two_scales_are_exact():
+    A, W, _, _ = si.a8w8_inputs(16, 24, 500, seed=6)
+    s_a = np.array([2.0 ** -(i % 7) for i in range(16)], np.float32)
+    s_w = np.array([2.0 ** (i % 5 - 2) for i in range(24)], np.float32)
+    r = oracle.a8w8(A, W, s_a, s_w)
+    acc = np.matmul(A.astype(np.int64), W.astype(np.int64)).astype(np.float64)
+    np.testing.assert_array_equal(r["f32"].astype(np.float64), acc * s_a[:, None] * s_w[None, :])
+
+
+def test_a8w8_rank1_act_scale_scales_rows_when_square():
+    """With M == N a rank-1 act_scale must scale rows, not columns."""
+    M = N = 12
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, 64, seed=12)
+    s_a = np.arange(1, M + 1, dtype=np.float32)
+    s_w = np.ones(N, np.float32)
+    r = oracle.a8w8(A, W, s_a, s_w)
+    acc = np.matmul(A.astype(np.int64), W.astype(np.int64)).astype(np.float32)
+    np.testing.assert_array_equal(r["f32"], acc * s_a[:, None])
+    assert not np.array_equal(r["f32"], acc * s_a[None, :])
+
+
+def test_a8w8_scalar_scales_equal_broadcast_vectors():
+    A, W, s_a, s_w = si.a8w8_inputs(9, 11, 100, seed=13)
+    r1 = oracle.a8w8(A, W, s_a[:1], s_w[:1])
+    r2 = oracle.a8w8(A, W, np.full(9, s_a[0]), np.full(11, s_w[0]))
+    for k in ("acc", "f32", "bf16"):
+        np.testing.assert_array_equal(r1[k], r2[k])
+
+
+def test_a8w8_torch_expression_on_256x1024x1024():
+    """The pypto page's torch reference, fp32 matmul then * act_scale[:, None]
+    * weight_scale[None, :], is exact at K = 1024 with values in [-127, 127]
+    (every partial sum is an integer below 2^24), so on the CPU it must equal
+    the oracle bit for bit."""
+    A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
+    r = oracle.a8w8(A, W, s_a, s_w)
+    t = torch.matmul(torch.from_numpy(A).float(), torch.from_numpy(W).float())
+    t = t * torch.from_numpy(s_a)[:, None] * torch.from_numpy(s_w)[None, :]
+    np.testing.assert_array_equal(r["f32"], t.numpy())
+    np.testing.assert_array_equal(
+        r["bf16"], t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_a8w8_b_trans_equals_transposed_weight():
+    A, W, s_a, s_w = si.a8w8_inputs(13, 29, 70, seed=14)
+    r1 = oracle.a8w8(A, W, s_a, s_w)
+    r2 = oracle.a8w8(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True)
+    np.testing.assert_array_equal(r1["f32"], r2["f32"])
+
+
+def test_a8w8_at_matches_full():
+    A, W, s_a, s_w = si.a8w8_inputs(30, 40, 200, seed=15)
+    r = oracle.a8w8(A, W, s_a, s_w)
+    g = si.rng(2)
+    rows, cols = g.integers(0, 30, 64), g.integers(0, 40, 64)
+    s = oracle.a8w8_at(A, W, s_a, s_w, rows, cols)
+    for k in ("acc", "f32", "bf16"):
+        np.testing.assert_array_equal(s[k], r[k][rows, cols])
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding
+# ---------------------------------------------------------------------------
+
+def test_bf16_matches_torch_and_exact_rounding():
+    g = si.rng(21)
+    x = np.concatenate([
+        g.standard_normal(2000).astype(np.float32) * 1e3,
+        g.uniform(-1e-3, 1e-3, 500).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38, 1e-40], np.float32),
+    ])
+    # exact ties: low 16 bits 0x8000 with even and odd kept parts
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0xC0418000, 0x47FF8000], np.uint32).view(np.float32)
+    x = np.concatenate([x, ties])
+    bits = oracle.f32_to_bf16(x)
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, t)
+    for v, b in zip(x[::17].tolist() + ties.tolist(), bits[::17].tolist() + bits[-5:].tolist()):
+        assert brute.bf16_bits(v) == b
+    assert bits[-5:].tolist() == [0x3F80, 0x3F82, 0xBF80, 0xC042, 0x4800]
+
+
+# ---------------------------------------------------------------------------
+# W8A32 (PULP page): dequantise-then-matmul in double
+# ---------------------------------------------------------------------------
+
+def test_w8a32_worked_example():
+    gv = load("w8a32_identity.txt")
+    a = np.array([[float(x) for x in gv["a"].split()]], np.float32)
+    b = np.array([[int(x)] for x in gv["b"].split()], np.int8)
+    R, B = oracle.w8a32(a, b, float(gv["scale"]), int(gv["zp"]))
+    assert R[0, 0] == float(gv["result"])
+    assert B[0, 0] == 0.5 * (1 * 1 + 2 * 2 + 3 * 9)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_w8a32_brute_force_exact(seed):
+    g = si.rng(3000 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 8, size=3))
+    A, W = si.w8a32_inputs(M, N, K, seed=seed)
+    scale, zp = float(np.float32(0.02)), int(g.integers(-9, 10))
+    R, B = oracle.w8a32(A, W, scale, zp)
+    Rx, Bx = brute.w8a32_exact(A.tolist(), W.astype(int).tolist(), scale, zp)
+    for m in range(M):
+        for n in range(N):
+            assert abs(R[m, n] - float(Rx[m][n])) <= 1e-13 * float(Bx[m][n]) + 1e-300
+            assert abs(B[m, n] - float(Bx[m][n])) <= 1e-13 * float(Bx[m][n])
+
+
+def test_w8a32_integer_activations_are_exact():
+    """Integer-valued A: every sum is an exact integer, so R must equal
+    scale * (integer matmul of A with W - zp) exactly, and the factorised form
+    scale * (S1 - zp * S2) gives the same number."""
+    g = si.rng(31)
+    A = g.integers(-3, 4, size=(64, 128)).astype(np.float32)
+    W = si.randint(g, (128, 64), -128, 127, np.int8)
+    scale = np.float32(0.02)
+    for zp in (3, 0, -5):
+        R, _ = oracle.w8a32(A, W, scale, zp)
+        Ai = A.astype(np.int64)
+        centred = Ai @ (W.astype(np.int64) - zp)
+        np.testing.assert_array_equal(R, centred.astype(np.float64) * np.float64(scale))
+        S1 = Ai @ W.astype(np.int64)
+        S2 = Ai.sum(1)
+        np.testing.assert_array_equal(centred, S1 - zp * S2[:, None])
+
+
+def test_w8a32_zero_point_zero_is_the_plain_loop():
+    """zp == 0 and scale == 1: the operator is A @ float(W)."""
+    A, W = si.w8a32_inputs(64, 64, 128, seed=101)
+    R, B = oracle.w8a32(A, W, 1.0, 0)
+    ref = A.astype(np.float64) @ W.astype(np.float64)
+    assert np.all(np.abs(R - ref) <= 1e-14 * B)
+
+
+def test_w8a32_weight_equal_to_zero_point_gives_zero():
+    A, _ = si.w8a32_inputs(8, 8, 50, seed=5)
+    W = np.full((50, 8), -5, np.int8)
+    R, B = oracle.w8a32(A, W, 0.01, -5)
+    assert (R == 0).all() and (B == 0).all()
+
+
+def test_w8a32_factorised_form_within_double_rounding():
+    A, W = si.w8a32_inputs(64, 64, 128, seed=101)
+    for zp in (3, 0):
+        R, B = oracle.w8a32(A, W, 0.02, zp)
+        A64 = A.astype(np.float64)
+        fact = np.float64(np.float32(0.02)) * (A64 @ W.astype(np.float64) - zp * A64.sum(1)[:, None])
+        assert np.all(np.abs(R - fact) <= 1e-12 * B)

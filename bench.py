@@ -1,0 +1,199 @@
+"""Benchmark of the quantised matmul hot path on one MI355X.
+
+Headline: A8W8 8192 x 8192 x 8192 (int8 x int8 -> int32 -> fp32 scales ->
+bf16), throughput in tera int8 ops per second, with inputs resident in HBM.
+One step is one call of the operator on that batch.  The same run also times
+the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
+K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
+4096^3, and the two small parity shapes) and reports them under "rows".
+Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
+that no call finds its inputs in the 256 MB Infinity Cache.
+
+Prints one JSON line.  Options: --gpus N (only 1 is supported: this build
+runs on one GPU), --steps K, --warmup W, --no-cpu-baseline, --only NAME.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # dense int8 matrix-core peak, tera-ops/s
+PEAK_FP32_TFLOPS = 157.3     # dense fp32 matrix-core peak
+PEAK_HBM_GBS = 8000.0        # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="time one row only (prefill, decode, mmi, w8a32, small)")
+    return ap.parse_args()
+
+
+def time_calls(fn, sets, steps, warmup, stream):
+    """Average milliseconds per call over `steps` calls, cycling `sets`."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels run on one GPU's share; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_int8_gemm_amd as q
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    steps, warmup = args.steps, args.warmup
+    rows = {}
+
+    def to(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def want(name):
+        return args.only is None or args.only == name
+
+    # ---- headline: A8W8 8192^3, bf16 out --------------------------------
+    M = N = K = 8192
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=505)
+    tA, tW, ta, tw = to(A), to(W), to(s_a), to(s_w)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    head_ms = None
+    if want("prefill"):
+        call = lambda s: q.qgemm_a8w8(tA, tW, ta, tw, out_dtype=torch.bfloat16, out=out)
+        head_ms = time_calls(call, [None], steps, warmup, stream)
+        kernel = q.last_kernel()
+        ops = 2.0 * M * N * K
+        tops = ops / (head_ms * 1e-3) / 1e12
+        rows["a8w8_prefill_8192_bf16"] = {"kernel": kernel, "us": head_ms * 1e3, "TOPS": tops,
+                                          "frac_int8_peak": tops / PEAK_INT8_TOPS}
+        outf = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ms = time_calls(lambda s: q.qgemm_a8w8(tA, tW, ta, tw, out=outf), [None], steps, warmup, stream)
+        rows["a8w8_prefill_8192_fp32"] = {"us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
+                                          "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+        del outf
+    del A, W
+
+    # ---- decode: M in {1, 4, 16}, K = N = 8192, bf16 out ---------------
+    if want("decode"):
+        for m in (1, 4, 16):
+            A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
+            base_w = to(W)
+            sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),
+                     torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)) for r in range(9)]
+            call = lambda s: q.qgemm_a8w8(s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4])
+            ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+            nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rows[f"a8w8_decode_m{m}_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
+                                                   "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+            del sets, base_w
+
+    # ---- MatMulInteger 8 x 512 x 2048 x 2048, shared B -------------------
+    if want("mmi"):
+        A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+        tB, tzb = to(B), to(zb)
+        sets = [(to(A), torch.empty((8, 512, 2048), dtype=torch.int32, device=dev)) for _ in range(13)]
+        call = lambda s: q.matmul_integer(s[0], tB, 128, tzb, out=s[1])
+        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        ops = 2.0 * 8 * 512 * 2048 * 2048
+        nbytes = 8 * 512 * 2048 + 2048 * 2048 + 2048 + 4 * 8 * 512 * 2048
+        rows["matmul_integer_8x512x2048x2048"] = {
+            "kernel": q.last_kernel(), "us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
+            "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del sets
+
+    # ---- W8A32 4096^3 -----------------------------------------------------
+    if want("w8a32"):
+        A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
+        tA, tW = to(A), to(W)
+        outc = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+        ms = time_calls(lambda s: q.qgemm_w8a32(tA, tW, 0.01, -5, out=outc), [None], steps, warmup, stream)
+        fl = 2.0 * 4096 ** 3
+        rows["w8a32_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "TFLOPS": fl / (ms * 1e-3) / 1e12,
+                              "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
+        del A, W, tA, tW, outc
+
+    # ---- the small parity shapes (launch-latency bound) ------------------
+    if want("small"):
+        A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
+        sA, sW, sa, sw = to(A), to(W), to(s_a), to(s_w)
+        o = torch.empty((256, 1024), dtype=torch.float32, device=dev)
+        ms = time_calls(lambda s: q.qgemm_a8w8(sA, sW, sa, sw, out=o), [None], 100, 10, stream)
+        rows["a8w8_256x1024x1024_fp32"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
+        A, W = si.w8a32_inputs(64, 64, 128, seed=101)
+        wA, wW = to(A), to(W)
+        o = torch.empty((64, 64), dtype=torch.float32, device=dev)
+        ms = time_calls(lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o), [None], 100, 10, stream)
+        rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the headline ----
+    cpu = None
+    if not args.no_cpu_baseline and want("prefill"):
+        import oracle
+        A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
+        rows_probe = 2
+        t0 = time.perf_counter()
+        oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)
+        dt = time.perf_counter() - t0
+        nrows = int(max(rows_probe, min(512, rows_probe * 12.0 / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        oracle.a8w8(A[:nrows], W, s_a[:nrows], s_w)
+        dt = time.perf_counter() - t0
+        cpu = {"value": 2.0 * nrows * N * K / dt / 1e12, "unit": "TOPS", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"first {nrows} rows of the 8192x8192x8192 A8W8 workload ({dt:.1f} s)"}
+
+    line = {
+        "metric": "int8 GEMM TOPS and skinny-M GB/s; % of MI355X int8 MFMA / HBM peak",
+        "value": rows.get("a8w8_prefill_8192_bf16", {}).get("TOPS"),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": head_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "a8w8_prefill_8192x8192x8192_bf16", "M": 8192, "N": 8192, "K": 8192,
+                   "out_dtype": "bf16", "parallelism": "single_gpu"},
+    }
+    if head_ms is not None:
+        tops = rows["a8w8_prefill_8192_bf16"]["TOPS"]
+        line["roofline"] = {"kernel": rows["a8w8_prefill_8192_bf16"]["kernel"], "bound": "mfma",
+                            "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                            "frac": tops / PEAK_INT8_TOPS, "traffic": None}
+    line["cpu_baseline"] = cpu
+    line["rows"] = rows
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * qgemm: quantised matrix multiplies for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor pointer is a DEVICE pointer owned by the caller; the
+ * library allocates no memory and keeps no state apart from a per-thread
+ * record of the last kernel it launched.  Matrices are row-major with an
+ * explicit leading dimension (elements between consecutive rows).  Every
+ * compute call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ * stream): it validates its arguments on the host, clears any pending HIP
+ * error, launches, and reports the launch status.  Failures during execution
+ * surface at the caller's next synchronisation.  Outputs must not overlap
+ * inputs.  Calls on different streams may run concurrently from several host
+ * threads, provided they do not share a workspace.
+ *
+ * Errors (qg_status):
+ *   QG_ERR_INVALID_ARGUMENT  a bad size, leading dimension, pointer, dtype,
+ *                            scale length or zero point; nothing launched.
+ *   QG_ERR_UNSUPPORTED       a well-formed form this library does not
+ *                            implement (listed per call); nothing launched.
+ *   QG_ERR_WORKSPACE         a workspace smaller than qgemm_workspace_bytes()
+ *                            was passed; nothing launched.
+ *   QG_ERR_HIP               the kernel launch itself failed.
+ * Following the launch convention of "feat(onnx-to-hip): lower quantized
+ * integer conv and matmul" ("What", last paragraph), a HIP error already
+ * pending before the call is cleared and does not fail the call.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_INVALID_ARGUMENT = 1,
+    QG_ERR_UNSUPPORTED = 2,
+    QG_ERR_WORKSPACE = 3,
+    QG_ERR_HIP = 4
+} qg_status;
+
+typedef enum {
+    QG_FP32 = 0,
+    QG_BF16 = 1,
+    QG_INT32 = 2,
+    QG_INT8 = 3,
+    QG_UINT8 = 4
+} qg_dtype;
+
+/* Operation ids for qgemm_workspace_bytes. */
+enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2 };
+
+/*
+ * W8A32: fp32 activations times an int8 weight with a per-tensor scale and
+ * zero point ("feat(PULPOpen): matmul that dequantises an int8 weight
+ * in-kernel", section "The kernel"):
+ *
+ *   C[m,n] = sum_k A[m,k] * (W[k,n] - zero_point) * scale
+ *          = scale * (sum_k A[m,k] W[k,n] - zero_point * sum_k A[m,k])
+ *
+ * evaluated in the second (factorised) form with fp32 arithmetic; the
+ * dequantised weight is never formed.  zero_point == 0 drops the correction.
+ *   A: fp32 [M,K], row stride lda >= K.    W: int8 [K,N], row stride ldw >= N.
+ *   C: fp32 [M,N], row stride ldc >= N.    scale: finite fp32 (host value).
+ *   zero_point: any int32 (host value).
+ * Requires M, N, K >= 1.  QG_ERR_UNSUPPORTED if K*ldw or M*lda*4 reaches 2^31
+ * bytes.  The result is not bit-defined (summation order is the kernel's);
+ * it is within 1e-5 * |scale| * sum_k |A[m,k]| * |W[k,n] - zp| of the exact
+ * value for the library's workloads.
+ */
+qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
+                      const float* A, int64_t lda,
+                      const int8_t* W, int64_t ldw,
+                      float scale, int32_t zero_point,
+                      float* C, int64_t ldc,
+                      void* stream);
+
+/*
+ * A8W8 matmul with fused dequantisation ("Feature/a8w8 matmul dequant
+ * fusion": sequence diagram and "What Changed"):
+ *
+ *   acc[m,n] = sum_k A[m,k] * W[k,n]          exact, int32 (wraps mod 2^32)
+ *   out[m,n] = cast_out( (((float)acc) * act_scale[m]) * weight_scale[n] )
+ *
+ * with each fp32 step rounded to nearest even in exactly this order, and the
+ * bf16 cast rounding to nearest even.  Results are bit-exact.
+ *   A: int8 [M,K], row stride lda >= K.
+ *   W: int8 [K,N] with row stride ldw >= N (b_trans == 0), or
+ *      int8 [N,K] with row stride ldw >= K (b_trans == 1).
+ *   act_scale: fp32, act_scale_len == M (one per row) or 1 (one for all).
+ *     A rank-1 [M] scale always scales ROWS, also when M == N.
+ *   weight_scale: fp32, weight_scale_len == N (per column) or 1.
+ *   out: out_dtype QG_FP32 or QG_BF16, [M,N], row stride ldo >= N.
+ *   workspace: NULL, or device memory of at least
+ *     qgemm_workspace_bytes(QG_OP_A8W8, 1, M, N, K) bytes, zero-filled
+ *     before its first use.  Decode shapes split K across workgroups: the
+ *     front of the workspace holds one ticket counter per 256 columns, the
+ *     rest the exact int32 partial sums.  Every call returns the tickets to
+ *     zero when it completes, so the same workspace serves the next call on
+ *     the same stream without clearing; calls that overlap in time must not
+ *     share one.  With NULL, decode shapes use a single-pass kernel.
+ * Decode shapes (M <= 16, b_trans == 0) run a bandwidth-bound kernel that
+ * streams W once; all other shapes run the tiled matrix-core kernel.
+ * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
+ */
+qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
+                     const int8_t* A, int64_t lda,
+                     const int8_t* W, int64_t ldw, int b_trans,
+                     const float* act_scale, int64_t act_scale_len,
+                     const float* weight_scale, int64_t weight_scale_len,
+                     void* out, qg_dtype out_dtype, int64_t ldo,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * MatMulInteger ("feat(onnx-to-hip): lower quantized integer conv and
+ * matmul", section "What", MatMulInteger and accumulator paragraphs):
+ *
+ *   Y[b,m,n] = wrap32( sum_k (A[b,m,k] - a_zero_point) * (B[b,k,n] - zb[n]) )
+ *
+ * summed exactly and stored as a wrapping (two's-complement) int32, the
+ * result the page's int64 accumulation gives for any K.  Bit-exact.
+ *   A: a_dtype QG_UINT8 or QG_INT8, `batch` matrices [M,K], row stride
+ *      lda >= K, batch stride a_batch_stride (0: one A used by every batch,
+ *      the page's size-1 batch expanded without a copy).
+ *   B: b_dtype QG_UINT8 or QG_INT8, [K,N], row stride ldb >= N, batch stride
+ *      b_batch_stride (0: one shared matrix, never copied per batch).
+ *   a_zero_point: scalar, within a_dtype's range.
+ *   b_zero_point: device pointer to b_dtype values, NULL (all zero), or
+ *      b_zero_point_len == 1 (scalar) or N (one per column).
+ *   Y: int32, `batch` matrices [M,N], row stride ldy >= N, batch stride
+ *      y_batch_stride >= (M-1)*ldy + N when batch > 1.
+ *   workspace: reserved; pass NULL / 0.
+ * Requires batch, M, N, K >= 1.  QG_ERR_UNSUPPORTED: an operand byte span
+ * that reaches 2^31.  (Per-row activation zero points and ranks outside 2-4
+ * are rejected by the Python binding, which maps ONNX ranks to batch.)
+ */
+qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K,
+                         const void* A, qg_dtype a_dtype, int64_t lda, int64_t a_batch_stride,
+                         const void* B, qg_dtype b_dtype, int64_t ldb, int64_t b_batch_stride,
+                         int32_t a_zero_point,
+                         const void* b_zero_point, int64_t b_zero_point_len,
+                         int32_t* Y, int64_t ldy, int64_t y_batch_stride,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes the fastest kernel for this shape wants (0: none). */
+size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K);
+
+/* Static text for a status code. */
+const char* qgemm_status_string(qg_status s);
+
+/* Name of the kernel the calling thread's last successful call launched
+ * (static text; "" before the first launch). */
+const char* qgemm_last_kernel(void);
+
+/* Library version string. */
+const char* qgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

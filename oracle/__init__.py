@@ -68,8 +68,15 @@ def _load():
     lib.oracle_matmul_integer_at.restype = None
     lib.oracle_dot_f32acc.argtypes = [_i64, _p, _int, _p, _int, _i64, _i32, _i32]
     lib.oracle_dot_f32acc.restype = _i32
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = _int
     _lib = lib
     return lib
+
+
+def threads():
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().oracle_threads())
 
 
 def _ptr(a):

@@ -29,9 +29,13 @@
  *       as a wrapping int32).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* Helpers that are part of the definition                                 */

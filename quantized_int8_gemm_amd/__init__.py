@@ -1,0 +1,27 @@
+"""MI355X-native quantised matrix multiplies.
+
+The C-ABI library ``libqgemm.so`` (HIP kernels for gfx950) does the work;
+this package is its thin Python binding, with the same call names:
+
+* ``qgemm_w8a32(A, W, scale, zero_point=0)``: fp32 x int8 weight with a
+  per-tensor scale and zero point, dequantisation folded into the epilogue.
+* ``qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32)``:
+  int8 x int8 with int32 accumulation, per-row and per-column fp32 scales,
+  fp32 or bf16 output.
+* ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
+  MatMulInteger, int32 output, shared weight never copied.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    QG_OP_A8W8,
+    QG_OP_MATMUL_INTEGER,
+    QG_OP_W8A32,
+    QGemmError,
+    last_kernel,
+    matmul_integer,
+    qgemm_a8w8,
+    qgemm_w8a32,
+    status_string,
+    version,
+    workspace_bytes,
+)

@@ -1,0 +1,308 @@
+"""ctypes binding of libqgemm.so: argument marshalling only.
+
+Each function checks dtypes (TypeError) and shapes (ValueError), maps the
+tensors to pointers, leading dimensions and batch strides, allocates the
+output with torch on the tensors' device, and calls the C entry point of the
+same name on torch's current stream.  All arithmetic runs in the HIP
+kernels; there is no fallback.  If the library is missing, importing this
+module raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_UNSUPPORTED, QG_ERR_WORKSPACE, QG_ERR_HIP = range(5)
+QG_FP32, QG_BF16, QG_INT32, QG_INT8, QG_UINT8 = range(5)
+QG_OP_W8A32, QG_OP_A8W8, QG_OP_MATMUL_INTEGER = range(3)
+
+_p, _i64, _i32, _int, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_size_t)
+
+# C prototypes, in the order of include/qgemm.h.
+PROTOTYPES = {
+    "qgemm_w8a32": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p], _int),
+    "qgemm_a8w8": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64,
+                    _p, _int, _i64, _p, _sz, _p], _int),
+    "matmul_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
+                        _i32, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
+    "qgemm_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
+    "qgemm_status_string": ([_int], ctypes.c_char_p),
+    "qgemm_last_kernel": ([], ctypes.c_char_p),
+    "qgemm_version": ([], ctypes.c_char_p),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (args, res) in PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {lib.qgemm_status_string(status).decode()} (status {status})")
+
+
+def _check(status, where):
+    if status == QG_OK:
+        return
+    if status == QG_ERR_INVALID_ARGUMENT:
+        raise ValueError(f"{where}: invalid argument")
+    if status == QG_ERR_UNSUPPORTED:
+        raise NotImplementedError(f"{where}: unsupported form")
+    raise QGemmError(status, where)
+
+
+def status_string(status):
+    return lib.qgemm_status_string(int(status)).decode()
+
+
+def last_kernel():
+    """Name of the kernel the calling thread's last successful call launched."""
+    return lib.qgemm_last_kernel().decode()
+
+
+def version():
+    return lib.qgemm_version().decode()
+
+
+def workspace_bytes(op, batch, M, N, K):
+    return int(lib.qgemm_workspace_bytes(int(op), batch, M, N, K))
+
+
+def _need(t, dtypes, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+
+
+def _on_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must be on a GPU device")
+        if t.device != dev:
+            raise ValueError("tensors must be on the same device")
+    return dev
+
+
+def _rows(t, name):
+    """Leading dimension of a row-major 2-D view with unit column stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0), t.size(1)) if t.size(0) > 1 else t.size(1)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+# ---------------------------------------------------------------------------
+# W8A32
+# ---------------------------------------------------------------------------
+
+def qgemm_w8a32(A, W, scale, zero_point=0, out=None):
+    """C = A @ ((W - zero_point) * scale) with the dequantisation folded in.
+
+    A: fp32 [M, K]; W: int8 [K, N]; scale: Python float (per tensor);
+    zero_point: Python int (per tensor, default 0).  Returns fp32 [M, N].
+    """
+    _need(A, (torch.float32,), "A")
+    _need(W, (torch.int8,), "W")
+    if A.dim() != 2 or W.dim() != 2:
+        raise ValueError("A and W must be 2-D")
+    M, K = A.shape
+    K2, N = W.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, W is {tuple(W.shape)}")
+    dev = _on_gpu(A, W)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    else:
+        _need(out, (torch.float32,), "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    st = lib.qgemm_w8a32(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"),
+                         float(scale), int(zero_point), _ptr(out), _rows(out, "out"), _stream(dev))
+    _check(st, "qgemm_w8a32")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# A8W8
+# ---------------------------------------------------------------------------
+
+_workspaces = {}
+
+
+def _workspace(dev, nbytes):
+    """A zero-filled workspace per (device, stream); the library leaves it zeroed."""
+    if nbytes == 0:
+        return None
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def _act_scale(s, M):
+    """act_scale as [M] / [M,1] / [1] / scalar -> (contiguous fp32, length).
+
+    A rank-1 [M] act_scale scales rows, never columns (also when M == N)."""
+    _need(s, (torch.float32,), "act_scale")
+    if s.dim() == 0 or (s.dim() == 1 and s.numel() in (1, M)) or (s.dim() == 2 and s.shape[1] == 1
+                                                                   and s.shape[0] in (1, M)):
+        flat = s.reshape(-1).contiguous()
+        return flat, flat.numel()
+    raise ValueError(f"act_scale of shape {tuple(s.shape)} is not [M], [M,1] or scalar (M={M})")
+
+
+def _weight_scale(s, N):
+    _need(s, (torch.float32,), "weight_scale")
+    if s.dim() == 0 or (s.dim() == 1 and s.numel() in (1, N)) or (s.dim() == 2 and s.shape[0] == 1
+                                                                   and s.shape[1] in (1, N)):
+        flat = s.reshape(-1).contiguous()
+        return flat, flat.numel()
+    raise ValueError(f"weight_scale of shape {tuple(s.shape)} is not [N], [1,N] or scalar (N={N})")
+
+
+def qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=False, out=None,
+               workspace=None):
+    """out = cast(((float)(A @ W)_int32 * act_scale[m]) * weight_scale[n]).
+
+    A: int8 [M, K]; W: int8 [K, N] (or [N, K] with b_trans=True);
+    act_scale: fp32 [M], [M, 1] or scalar; weight_scale: fp32 [N], [1, N] or
+    scalar; out_dtype: torch.float32 (default) or torch.bfloat16.
+    """
+    _need(A, (torch.int8,), "A")
+    _need(W, (torch.int8,), "W")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if A.dim() != 2 or W.dim() != 2:
+        raise ValueError("A and W must be 2-D")
+    M, K = A.shape
+    N, K2 = (W.shape[0], W.shape[1]) if b_trans else (W.shape[1], W.shape[0])
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, W is {tuple(W.shape)}")
+    s_a, n_a = _act_scale(act_scale, M)
+    s_w, n_w = _weight_scale(weight_scale, N)
+    dev = _on_gpu(A, W, s_a, s_w)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _need(out, (out_dtype,), "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    if workspace is None:
+        ws = _workspace(dev, workspace_bytes(QG_OP_A8W8, 1, M, N, K))
+    else:
+        ws = workspace
+    st = lib.qgemm_a8w8(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),
+                        _ptr(s_a), n_a, _ptr(s_w), n_w,
+                        _ptr(out), QG_FP32 if out_dtype == torch.float32 else QG_BF16, _rows(out, "out"),
+                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, "qgemm_a8w8")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# MatMulInteger
+# ---------------------------------------------------------------------------
+
+_QG_OF = {torch.uint8: QG_UINT8, torch.int8: QG_INT8}
+
+
+def _batch_view(t, name, batch_shape):
+    """(batch stride, leading dim) of t broadcast to batch_shape + t.shape[-2:]."""
+    lead = t.shape[:-2]
+    if all(d == 1 for d in lead):
+        return 0
+    if tuple(lead) != tuple(batch_shape):
+        # a size-1 batch broadcast against a larger one is covered above; any
+        # other mismatch would need a per-dimension stride the ABI lacks
+        raise ValueError(f"{name} batch dimensions {tuple(lead)} do not match {tuple(batch_shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous when batched")
+    return t.shape[-2] * t.shape[-1]
+
+
+def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
+    """ONNX MatMulInteger: int32 wrap(sum_k (A - a_zp) * (B - b_zp)).
+
+    A: uint8/int8 of rank 2-4, [..., M, K]; B: uint8/int8 of rank 2-4,
+    [..., K, N].  A rank-2 B, or one whose batch dimensions are all 1, is
+    shared by every batch without a copy; a size-1 batch of A is likewise
+    reused.  a_zero_point: scalar of A's range (per-row zero points are not
+    supported); b_zero_point: None, scalar, [N] or [..., 1, N] per-column
+    values of B's dtype.  Returns int32 [*batch, M, N].
+    """
+    _need(A, (torch.uint8, torch.int8), "A")
+    _need(B, (torch.uint8, torch.int8), "B")
+    if not (2 <= A.dim() <= 4 and 2 <= B.dim() <= 4):
+        raise ValueError("MatMulInteger operands must have rank 2 to 4")
+    M, K = A.shape[-2:]
+    K2, N = B.shape[-2:]
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if isinstance(a_zero_point, torch.Tensor):
+        if a_zero_point.numel() != 1:
+            raise NotImplementedError("per-row activation zero points are not supported")
+        _need(a_zero_point, (A.dtype,), "a_zero_point")
+        a_zero_point = int(a_zero_point.item())
+    zb, zb_len = None, 0
+    if b_zero_point is not None:
+        if isinstance(b_zero_point, torch.Tensor):
+            _need(b_zero_point, (B.dtype,), "b_zero_point")
+            if b_zero_point.numel() not in (1, N):
+                raise ValueError(f"b_zero_point has {b_zero_point.numel()} values; expected 1 or N={N}")
+            if b_zero_point.dim() >= 2 and b_zero_point.shape[-2] != 1:
+                raise ValueError("a per-column b_zero_point must have shape [..., 1, N]")
+            zb = b_zero_point.reshape(-1).contiguous()
+        else:
+            zb = torch.tensor([int(b_zero_point)], dtype=B.dtype, device=B.device)
+        zb_len = zb.numel()
+    batch_shape = torch.broadcast_shapes(A.shape[:-2], B.shape[:-2])
+    batch = 1
+    for d in batch_shape:
+        batch *= d
+    a_bs = _batch_view(A, "A", batch_shape)
+    b_bs = _batch_view(B, "B", batch_shape)
+    A2 = A.reshape(-1, A.shape[-1]) if a_bs else A.reshape(A.shape[-2:])
+    B2 = B.reshape(-1, B.shape[-1]) if b_bs else B.reshape(B.shape[-2:])
+    dev = _on_gpu(*([A, B] + ([zb] if zb is not None else [])))
+    if out is None:
+        out = torch.empty(tuple(batch_shape) + (M, N), dtype=torch.int32, device=dev)
+    else:
+        _need(out, (torch.int32,), "out")
+        if tuple(out.shape) != tuple(batch_shape) + (M, N) or not out.is_contiguous():
+            raise ValueError("out has the wrong shape or is not contiguous")
+    st = lib.matmul_integer(batch, M, N, K,
+                            _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
+                            _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
+                            int(a_zero_point), _ptr(zb), zb_len,
+                            _ptr(out), N, M * N, None, 0, _stream(dev))
+    _check(st, "matmul_integer")
+    return out

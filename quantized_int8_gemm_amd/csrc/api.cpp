@@ -1,0 +1,248 @@
+// C-ABI entry points: argument validation (before any HIP call), kernel
+// selection, launch, and the launch-status convention of
+// "feat(onnx-to-hip): lower quantized integer conv and matmul" ("What", last
+// paragraph): clear the pending HIP error, launch, return hipGetLastError().
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qgemm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local const char* g_last_kernel = "";
+
+constexpr int64_t SPAN_LIMIT = (int64_t)1 << 31;  // 32-bit buffer offsets
+constexpr int SKINNY_MAX_M = 16;
+
+bool env_is(const char* name, const char* value) {
+    const char* v = std::getenv(name);
+    return v != nullptr && std::strcmp(v, value) == 0;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    return v != nullptr && *v ? std::atoi(v) : dflt;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void log_dispatch(const char* op, const char* kernel, int64_t batch, int64_t M, int64_t N, int64_t K,
+                  int extra) {
+    if (env_is("QGEMM_LOG_DISPATCH", "1"))
+        std::fprintf(stderr, "[qgemm] %s -> %s batch=%lld M=%lld N=%lld K=%lld splits=%d\n", op, kernel,
+                     (long long)batch, (long long)M, (long long)N, (long long)K, extra);
+}
+
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    const int64_t lim = (int64_t)1 << 30;
+    return M >= 1 && N >= 1 && K >= 1 && M < lim && N < lim && K < lim;
+}
+
+// Tile shape of the int8 tiled kernel for an (effective) problem shape:
+// the largest tile that still gives every compute unit work.
+int pick_tile(int64_t batch, int64_t M, int64_t N) {
+    const int forced = env_int("QGEMM_TILE", -1);
+    if (forced >= 0 && forced < qg::NUM_TILE_CFGS) return forced;
+    const int64_t t256 = batch * ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t256x128 = batch * ((M + 255) / 256) * ((N + 127) / 128);
+    if (t256 >= 512) return qg::TILE_256x256;
+    if (t256x128 >= 256) return qg::TILE_256x128;
+    return qg::TILE_128x128;
+}
+
+qg_status finish_launch(hipError_t e, const char* name) {
+    if (e != hipSuccess) return QG_ERR_HIP;
+    g_last_kernel = name;
+    return QG_OK;
+}
+
+hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, int epi, int zp,
+                        hipStream_t s, const char** name) {
+    static const char* names[] = {"int8_tiled_256x256", "int8_tiled_256x128", "int8_tiled_128x128"};
+    // The byte-wise (any alignment) variants exist for the 128x128 tile only.
+    if (!vec) cfg = qg::TILE_128x128;
+    *name = names[cfg];
+    switch (cfg) {
+        case qg::TILE_256x256: return qg::launch_tiled_256x256(a, bkm, vec, epi, zp, s);
+        case qg::TILE_256x128: return qg::launch_tiled_256x128(a, bkm, vec, epi, zp, s);
+        default: return qg::launch_tiled_128x128(a, bkm, vec, epi, zp, s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qgemm_version(void) { return "qgemm 0.1 (gfx950)"; }
+
+const char* qgemm_last_kernel(void) { return g_last_kernel; }
+
+const char* qgemm_status_string(qg_status s) {
+    switch (s) {
+        case QG_OK: return "ok";
+        case QG_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case QG_ERR_UNSUPPORTED: return "unsupported";
+        case QG_ERR_WORKSPACE: return "workspace too small";
+        case QG_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+static int a8w8_skinny_splits(int64_t M, int64_t N, int64_t K) {
+    const int forced = env_int("QGEMM_SPLITS", 0);
+    if (forced > 0) return forced;
+    return qg::skinny_splits((int)M, (int)N, (int)K);
+}
+
+static bool a8w8_is_skinny(int64_t M, int b_trans) {
+    if (env_is("QGEMM_FORCE_KERNEL", "tiled")) return false;
+    if (env_is("QGEMM_FORCE_KERNEL", "skinny")) return !b_trans && M <= SKINNY_MAX_M;
+    return !b_trans && M <= SKINNY_MAX_M;
+}
+
+size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
+    (void)batch;
+    if (op != QG_OP_A8W8 || !dims_ok(M, N, K) || !a8w8_is_skinny(M, 0)) return 0;
+    const int splits = a8w8_skinny_splits(M, N, K);
+    return qg::skinny_workspace_bytes((int)M, (int)N, splits);
+}
+
+qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
+                      int64_t ldw, float scale, int32_t zero_point, float* C, int64_t ldc, void* stream) {
+    if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
+    if (A == nullptr || W == nullptr || C == nullptr) return QG_ERR_INVALID_ARGUMENT;
+    if (lda < K || ldw < N || ldc < N) return QG_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale)) return QG_ERR_INVALID_ARGUMENT;
+    if ((K + 64) * ldw >= SPAN_LIMIT || (128 * lda + K + 64) * 4 >= SPAN_LIMIT) return QG_ERR_UNSUPPORTED;
+
+    qg::W8A32Args a{};
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.A = A; a.lda = lda; a.W = W; a.ldw = ldw;
+    a.scale = scale; a.zp = zero_point; a.C = C; a.ldc = ldc;
+    const bool vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+    const bool vec_w = (reinterpret_cast<uintptr_t>(W) & 3u) == 0 && ldw % 4 == 0 && N % 4 == 0;
+    const char* name = "";
+    (void)hipGetLastError();
+    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, (hipStream_t)stream, &name);
+    log_dispatch("w8a32", name, 1, M, N, K, 1);
+    return finish_launch(e, name);
+}
+
+qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                     int64_t ldw, int b_trans, const float* act_scale, int64_t act_scale_len,
+                     const float* weight_scale, int64_t weight_scale_len, void* out, qg_dtype out_dtype,
+                     int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
+    if (A == nullptr || W == nullptr || act_scale == nullptr || weight_scale == nullptr || out == nullptr)
+        return QG_ERR_INVALID_ARGUMENT;
+    if (b_trans != 0 && b_trans != 1) return QG_ERR_INVALID_ARGUMENT;
+    if (lda < K || ldo < N || ldw < (b_trans ? K : N)) return QG_ERR_INVALID_ARGUMENT;
+    if (act_scale_len != 1 && act_scale_len != M) return QG_ERR_INVALID_ARGUMENT;
+    if (weight_scale_len != 1 && weight_scale_len != N) return QG_ERR_INVALID_ARGUMENT;
+    if (out_dtype != QG_FP32 && out_dtype != QG_BF16) return QG_ERR_INVALID_ARGUMENT;
+    if (256 * lda + K + 256 >= SPAN_LIMIT || (b_trans ? 256 * ldw + K + 256 : (K + 256) * ldw) >= SPAN_LIMIT)
+        return QG_ERR_UNSUPPORTED;
+
+    qg::Int8GemmArgs a{};
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = 1;
+    a.A = A; a.lda = lda; a.a_bstride = 0;
+    a.B = W; a.ldb = ldw; a.b_bstride = 0;
+    a.a_flip = 0; a.b_flip = 0;
+    a.out = out; a.ldo = ldo; a.o_bstride = 0;
+    a.act_scale = act_scale; a.as_stride = act_scale_len == 1 ? 0 : 1;
+    a.weight_scale = weight_scale; a.ws_stride = weight_scale_len == 1 ? 0 : 1;
+    const int epi = out_dtype == QG_FP32 ? qg::EPI_F32 : qg::EPI_BF16;
+    const bool vec = aligned16(A) && aligned16(W) && lda % 16 == 0 && ldw % 16 == 0 && K % 16 == 0 &&
+                     (b_trans || N % 16 == 0);
+
+    const char* name = "";
+    hipError_t e;
+    if (a8w8_is_skinny(M, b_trans)) {
+        int splits = a8w8_skinny_splits(M, N, K);
+        const size_t need = qg::skinny_workspace_bytes((int)M, (int)N, splits);
+        if (need > 0 && workspace == nullptr) {
+            splits = 1;
+        } else if (need > workspace_bytes) {
+            return QG_ERR_WORKSPACE;
+        }
+        a.workspace = workspace;
+        a.splits = splits;
+        (void)hipGetLastError();
+        e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name);
+        log_dispatch("a8w8", name, 1, M, N, K, splits);
+    } else {
+        const int cfg = pick_tile(1, M, N);
+        (void)hipGetLastError();
+        e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
+        log_dispatch("a8w8", name, 1, M, N, K, 1);
+    }
+    return finish_launch(e, name);
+}
+
+qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, qg_dtype a_dtype,
+                         int64_t lda, int64_t a_batch_stride, const void* B, qg_dtype b_dtype, int64_t ldb,
+                         int64_t b_batch_stride, int32_t a_zero_point, const void* b_zero_point,
+                         int64_t b_zero_point_len, int32_t* Y, int64_t ldy, int64_t y_batch_stride,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!dims_ok(M, N, K) || batch < 1 || batch >= 65536) return QG_ERR_INVALID_ARGUMENT;
+    if (A == nullptr || B == nullptr || Y == nullptr) return QG_ERR_INVALID_ARGUMENT;
+    if ((a_dtype != QG_UINT8 && a_dtype != QG_INT8) || (b_dtype != QG_UINT8 && b_dtype != QG_INT8))
+        return QG_ERR_INVALID_ARGUMENT;
+    if (lda < K || ldb < N || ldy < N) return QG_ERR_INVALID_ARGUMENT;
+    if (a_batch_stride < 0 || b_batch_stride < 0 || y_batch_stride < 0) return QG_ERR_INVALID_ARGUMENT;
+    if (batch > 1) {
+        if (a_batch_stride != 0 && a_batch_stride < (M - 1) * lda + K) return QG_ERR_INVALID_ARGUMENT;
+        if (b_batch_stride != 0 && b_batch_stride < (K - 1) * ldb + N) return QG_ERR_INVALID_ARGUMENT;
+        if (y_batch_stride < (M - 1) * ldy + N) return QG_ERR_INVALID_ARGUMENT;
+    }
+    const bool a_u8 = a_dtype == QG_UINT8, b_u8 = b_dtype == QG_UINT8;
+    if (a_u8 ? (a_zero_point < 0 || a_zero_point > 255) : (a_zero_point < -128 || a_zero_point > 127))
+        return QG_ERR_INVALID_ARGUMENT;
+    if (b_zero_point != nullptr && b_zero_point_len != 1 && b_zero_point_len != N)
+        return QG_ERR_INVALID_ARGUMENT;
+    if (b_zero_point == nullptr && b_zero_point_len != 0 && b_zero_point_len != 1 && b_zero_point_len != N)
+        return QG_ERR_INVALID_ARGUMENT;
+    if (256 * lda + K + 256 >= SPAN_LIMIT || (K + 256) * ldb >= SPAN_LIMIT) return QG_ERR_UNSUPPORTED;
+
+    qg::Int8GemmArgs a{};
+    a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = (int)batch;
+    a.A = reinterpret_cast<const int8_t*>(A); a.lda = lda; a.a_bstride = a_batch_stride;
+    a.B = reinterpret_cast<const int8_t*>(B); a.ldb = ldb; a.b_bstride = b_batch_stride;
+    a.a_flip = a_u8 ? 0x80808080u : 0u;
+    a.b_flip = b_u8 ? 0x80808080u : 0u;
+    a.out = Y; a.ldo = ldy; a.o_bstride = y_batch_stride;
+    a.b_zp = b_zero_point;
+    a.b_zp_stride = (b_zero_point != nullptr && b_zero_point_len == N && N > 1) ? 1 : 0;
+    a.b_zp_u8 = b_u8 ? 1 : 0;
+    a.ca = (a_u8 ? 128 : 0) - a_zero_point;
+    a.sb = b_u8 ? 128 : 0;
+    // Fold the batch into M when B is shared and A / Y batches are contiguous
+    // row blocks: one [batch*M, K] x [K, N] product with the same B.
+    if (batch > 1 && b_batch_stride == 0 && a_batch_stride == M * lda && y_batch_stride == M * ldy &&
+        batch * M < ((int64_t)1 << 30)) {
+        a.M = (int)(batch * M);
+        a.batch = 1;
+    }
+    // Row sums of A are needed when some cb[n] = sb - zb[n] may be non-zero;
+    // column sums of B when ca != 0.
+    const bool need_rowsum = b_zero_point != nullptr || b_u8;
+    const bool need_colsum = a.ca != 0;
+    const int zp = (need_rowsum ? 1 : 0) | (need_colsum ? 2 : 0);
+    const bool vec = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
+                     N % 16 == 0 && (a.batch == 1 || (a_batch_stride % 16 == 0 && b_batch_stride % 16 == 0));
+    const int cfg = pick_tile(a.batch, a.M, N);
+    const char* name = "";
+    (void)hipGetLastError();
+    const hipError_t e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
+    log_dispatch("matmul_integer", name, a.batch, a.M, N, K, 1);
+    return finish_launch(e, name);
+}
+
+}  // extern "C"

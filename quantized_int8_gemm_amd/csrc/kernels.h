@@ -1,0 +1,61 @@
+// Launchers for the gfx950 kernels and the argument blocks they take.
+// Host code (the C-ABI entry points) fills these blocks after validation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+// Epilogue selector of the int8 tiled kernel.
+enum Int8Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_I32 = 2 };
+
+// Arguments of the int8 x int8 -> int32 tiled matrix-core kernel and of the
+// skinny (decode) kernel.  One block describes one problem of `batch`
+// independent [M,K] x [K,N] products (batch strides may be 0 for a shared
+// operand).
+struct Int8GemmArgs {
+    int M, N, K, batch;
+    const int8_t* A; int64_t lda; int64_t a_bstride;
+    const int8_t* B; int64_t ldb; int64_t b_bstride;  // [K,N] rows, or [N,K] if k-major
+    uint32_t a_flip, b_flip;                          // 0x80808080 turns uint8 into int8 - 128
+    void* out; int64_t ldo; int64_t o_bstride;
+    // A8W8 epilogue: scales indexed by row / column (stride 0 = one value)
+    const float* act_scale; int as_stride;
+    const float* weight_scale; int ws_stride;
+    // MatMulInteger epilogue: Y = acc + cb[n]*rowsum + ca*colsum + K*ca*cb[n]
+    const void* b_zp; int b_zp_stride; int b_zp_u8;  // NULL means zero
+    int32_t ca;   // (128 if A is uint8 else 0) - a_zero_point
+    int32_t sb;   // 128 if B is uint8 else 0; cb[n] = sb - b_zp[n]
+    // split-K workspace (skinny kernel): counters then int32 partials
+    void* workspace;
+    int splits;
+};
+
+// Tile shapes of the tiled kernel (four waves each).
+enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, NUM_TILE_CFGS = 3 };
+
+// Tiled kernel, one launcher per tile shape.  bkm: B is [N,K]; vec: 16-byte
+// vector loads allowed (only the 128x128 shape has byte-wise variants);
+// epi: Int8Epilogue; zp bit 0: row sums of A needed, bit 1: column sums of B.
+hipError_t launch_tiled_256x256(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
+hipError_t launch_tiled_256x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
+hipError_t launch_tiled_128x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
+
+// Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
+hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,
+                              const char** name);
+size_t skinny_workspace_bytes(int M, int N, int splits);
+int skinny_splits(int M, int N, int K);
+
+// W8A32: C = scale * (A @ W - zp * rowsum(A)) with fp32 matrix cores.
+struct W8A32Args {
+    int M, N, K;
+    const float* A; int64_t lda;
+    const int8_t* W; int64_t ldw;
+    float scale; int32_t zp;
+    float* C; int64_t ldc;
+};
+hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, hipStream_t s,
+                        const char** name);
+
+}  // namespace qg

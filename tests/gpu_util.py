@@ -1,0 +1,60 @@
+"""Helpers for the GPU parity tests: device transfer and comparisons."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+
+
+def bf16_bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def case(msg):
+    """Name the case on stderr before touching the GPU (survives a crash)."""
+    sys.stderr.write(f"[case] {msg}\n")
+    sys.stderr.flush()
+
+
+def ulp_diff_f32(a, b):
+    """|a - b| in units in the last place, via the ordered integer map."""
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, np.int64(-2 ** 31) - ai, ai)
+    bi = np.where(bi < 0, np.int64(-2 ** 31) - bi, bi)
+    return np.abs(ai - bi)
+
+
+def ulp_diff_bf16(a, b):
+    return ulp_diff_f32((np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32),
+                        (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)) >> 16
+
+
+class env:
+    """Temporarily set environment variables (read by the library per call)."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kw}
+        for k, v in self.kw.items():
+            os.environ[k] = str(v)
+
+    def __exit__(self, *a):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v

@@ -1,0 +1,178 @@
+"""A8W8 on the GPU against the oracle: bit-exact fp32 and bf16 outputs
+(the spec bar is 1 ulp; the fixed epilogue order makes them exact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_int8_gemm_amd as q
+import seeded_inputs as si
+from gpu_util import bf16_bits, case, dev, env, to_dev, ulp_diff_bf16, ulp_diff_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def run(A, W, s_a, s_w, out_dtype, b_trans=False, **kw):
+    return q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(s_a), to_dev(s_w), out_dtype=out_dtype,
+                        b_trans=b_trans, **kw)
+
+
+def check(A, W, s_a, s_w, b_trans=False, expect_kernel=None):
+    ref = oracle.a8w8(A, W, s_a, s_w, b_trans=b_trans)
+    f = run(A, W, s_a, s_w, torch.float32, b_trans).cpu().numpy()
+    if expect_kernel:
+        assert q.last_kernel().startswith(expect_kernel), q.last_kernel()
+    h = bf16_bits(run(A, W, s_a, s_w, torch.bfloat16, b_trans))
+    assert ulp_diff_f32(f, ref["f32"]).max() <= 1
+    assert ulp_diff_bf16(h, ref["bf16"]).max() <= 1
+    # the epilogue order is fixed, so the results are in fact identical
+    np.testing.assert_array_equal(f, ref["f32"])
+    np.testing.assert_array_equal(h, ref["bf16"])
+
+
+def test_a8w8_256x1024x1024_all_scale_forms():
+    case("a8w8 256x1024x1024 seed 202")
+    A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
+    check(A, W, s_a, s_w, expect_kernel="int8_tiled")
+    ref = run(A, W, s_a, s_w, torch.float32).cpu().numpy()
+    # [M,1] / [1,N] scales give the same bits as [M] / [N]
+    two_d = q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(s_a).reshape(-1, 1), to_dev(s_w).reshape(1, -1))
+    np.testing.assert_array_equal(two_d.cpu().numpy(), ref)
+    # a scalar scale equals a broadcast vector of that value
+    one = q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(s_a[:1]), to_dev(s_w[:1])).cpu().numpy()
+    vec = q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(np.full(256, s_a[0], np.float32)),
+                       to_dev(np.full(1024, s_w[0], np.float32))).cpu().numpy()
+    np.testing.assert_array_equal(one, vec)
+    np.testing.assert_array_equal(one, oracle.a8w8(A, W, s_a[:1], s_w[:1])["f32"])
+
+
+def test_a8w8_raw_accumulator():
+    """The int32 accumulator itself (MatMulInteger with zero zero-points on
+    int8 operands runs the same matrix-core loop)."""
+    case("a8w8 raw accumulator 256x1024x1024")
+    A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
+    acc = q.matmul_integer(to_dev(A), to_dev(W)).cpu().numpy()
+    np.testing.assert_array_equal(acc, oracle.a8w8(A, W, s_a, s_w)["acc"])
+
+
+def test_a8w8_square_rank1_act_scale_scales_rows():
+    case("a8w8 square 512 rank-1 row scale")
+    A, W, _, _ = si.a8w8_inputs(512, 512, 256, seed=17)
+    s_a = np.linspace(0.5, 2.0, 512).astype(np.float32)
+    s_w = np.ones(512, np.float32)
+    out = run(A, W, s_a, s_w, torch.float32).cpu().numpy()
+    acc = (A.astype(np.int64) @ W.astype(np.int64)).astype(np.float32)
+    np.testing.assert_array_equal(out, acc * s_a[:, None])
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 1), (2, 7, 7), (4, 65, 258), (16, 64, 259), (17, 128, 261), (33, 520, 1100),
+    (300, 130, 129), (257, 255, 512), (64, 1024, 16), (129, 384, 4096),
+])
+@pytest.mark.parametrize("kernel", ["auto", "tiled"])
+def test_a8w8_ragged(M, N, K, kernel):
+    case(f"a8w8 ragged M={M} N={N} K={K} kernel={kernel}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M * 7 + N * 3 + K, lo=-128, hi=127)
+    with env(QGEMM_FORCE_KERNEL=kernel):
+        check(A, W, s_a, s_w, expect_kernel="a8w8_skinny" if (kernel == "auto" and M <= 16) else "int8_tiled")
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 40, 50), (64, 256, 512), (200, 300, 259)])
+def test_a8w8_b_trans(M, N, K):
+    case(f"a8w8 b_trans M={M} N={N} K={K}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=5 + M)
+    check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True, expect_kernel="int8_tiled")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_a8w8_decode_8192(M):
+    """Decode shapes at full size, every output compared."""
+    case(f"a8w8 decode M={M} K=N=8192")
+    A, W, s_a, s_w = si.a8w8_inputs(M, 8192, 8192, seed=404 + M)
+    ref = oracle.a8w8(A, W, s_a, s_w)
+    out = bf16_bits(run(A, W, s_a, s_w, torch.bfloat16))
+    assert q.last_kernel() == "a8w8_skinny"
+    np.testing.assert_array_equal(out, ref["bf16"])
+
+
+def test_a8w8_decode_split_counts_agree():
+    """Integer partial sums: any split of K gives identical bits."""
+    case("a8w8 decode M=16 splits 1/2/7/16/32")
+    A, W, s_a, s_w = si.a8w8_inputs(16, 2048, 8192, seed=9)
+    outs = []
+    for s in (1, 2, 7, 16, 32):
+        with env(QGEMM_SPLITS=s):
+            outs.append(bf16_bits(run(A, W, s_a, s_w, torch.bfloat16)))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    np.testing.assert_array_equal(outs[0], oracle.a8w8(A, W, s_a, s_w)["bf16"])
+
+
+def test_a8w8_decode_without_workspace_and_tickets_reset():
+    case("a8w8 decode M=4 no workspace / workspace reuse")
+    A, W, s_a, s_w = si.a8w8_inputs(4, 4096, 4096, seed=10)
+    d = dev()
+    ref = oracle.a8w8(A, W, s_a, s_w)["f32"]
+    nbytes = q.workspace_bytes(q.QG_OP_A8W8, 1, 4, 4096, 4096)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=d)
+    for _ in range(3):
+        out = run(A, W, s_a, s_w, torch.float32, workspace=ws)
+        np.testing.assert_array_equal(out.cpu().numpy(), ref)
+    # the split tickets at the front of the workspace are back at zero
+    tiles_n = (4096 + 255) // 256
+    assert int(ws[: ((tiles_n * 4 + 255) // 256) * 256].sum().item()) == 0
+    from quantized_int8_gemm_amd import _binding as b
+    # NULL workspace: single-pass kernel, same bits
+    out = torch.empty(4, 4096, dtype=torch.float32, device=d)
+    tA, tW, ta, tw = to_dev(A), to_dev(W), to_dev(s_a), to_dev(s_w)
+    import ctypes
+    st = b.lib.qgemm_a8w8(4, 4096, 4096, b._ptr(tA), 4096, b._ptr(tW), 4096, 0, b._ptr(ta), 4,
+                          b._ptr(tw), 4096, b._ptr(out), b.QG_FP32, 4096, None, 0,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    np.testing.assert_array_equal(out.cpu().numpy(), ref)
+
+
+def test_a8w8_large_8192_sampled():
+    """8192^3 at full size: sampled outputs, plus whole first/last rows."""
+    case("a8w8 8192x8192x8192 sampled")
+    A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
+    tA, tW, ta, tw = to_dev(A), to_dev(W), to_dev(s_a), to_dev(s_w)
+    out16 = bf16_bits(q.qgemm_a8w8(tA, tW, ta, tw, out_dtype=torch.bfloat16))
+    assert q.last_kernel().startswith("int8_tiled")
+    out32 = q.qgemm_a8w8(tA, tW, ta, tw).cpu().numpy()
+    g = si.rng(1)
+    rows = np.concatenate([g.integers(0, 8192, 3000), np.zeros(8192, np.int64), np.full(8192, 8191)])
+    cols = np.concatenate([g.integers(0, 8192, 3000), np.arange(8192), np.arange(8192)])
+    ref = oracle.a8w8_at(A, W, s_a, s_w, rows, cols)
+    np.testing.assert_array_equal(out16[rows, cols], ref["bf16"])
+    np.testing.assert_array_equal(out32[rows, cols], ref["f32"])
+
+
+def test_a8w8_output_guard_band():
+    """Writes stay inside [M, N] of a wider output buffer."""
+    case("a8w8 guard band 70x100x300 ldo=128")
+    A, W, s_a, s_w = si.a8w8_inputs(70, 100, 300, seed=3)
+    d = dev()
+    big = torch.full((70, 128), -7.0, dtype=torch.float32, device=d)
+    view = big[:, :100]
+    q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(s_a), to_dev(s_w), out=view)
+    got = big.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :100], oracle.a8w8(A, W, s_a, s_w)["f32"])
+    assert (got[:, 100:] == -7.0).all()
+
+
+def test_a8w8_repeatable():
+    case("a8w8 repeat 10x")
+    A, W, s_a, s_w = si.a8w8_inputs(300, 640, 1000, seed=4)
+    first = run(A, W, s_a, s_w, torch.float32).cpu().numpy()
+    for _ in range(9):
+        np.testing.assert_array_equal(run(A, W, s_a, s_w, torch.float32).cpu().numpy(), first)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_a8w8_every_tile_shape(tile):
+    case(f"a8w8 tile cfg {tile} 520x700x1000")
+    A, W, s_a, s_w = si.a8w8_inputs(520, 768, 1024, seed=40 + tile)
+    with env(QGEMM_TILE=tile):
+        check(A, W, s_a, s_w, expect_kernel="int8_tiled")

@@ -1,0 +1,98 @@
+"""MatMulInteger on the GPU against the oracle: bit-exact int32."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_int8_gemm_amd as q
+import seeded_inputs as si
+from gpu_util import case, dev, env, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_matmul_integer_batched_shared_b_8x512x2048x2048():
+    """The full batched workload, every output compared."""
+    case("matmul_integer 8x512x2048x2048 shared B")
+    A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+    y = q.matmul_integer(to_dev(A), to_dev(B), 128, to_dev(zb)).cpu().numpy()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, 128, zb))
+
+
+@pytest.mark.parametrize("a_dt,b_dt", [(np.uint8, np.int8), (np.uint8, np.uint8),
+                                       (np.int8, np.int8), (np.int8, np.uint8)])
+@pytest.mark.parametrize("za,zb_kind", [(0, "none"), ("mid", "scalar"), ("mid", "column"), ("edge", "column")])
+@pytest.mark.parametrize("M,N,K", [(3, 5, 259), (40, 130, 261), (130, 256, 512)])
+def test_matmul_integer_dtypes_and_zero_points(a_dt, b_dt, za, zb_kind, M, N, K):
+    case(f"matmul_integer {np.dtype(a_dt)}x{np.dtype(b_dt)} za={za} zb={zb_kind} M={M} N={N} K={K}")
+    g = si.rng(M * 1000 + N + K)
+    A = si.randint(g, (M, K), 0, 255, a_dt) if a_dt == np.uint8 else si.randint(g, (M, K), -128, 127, a_dt)
+    B = si.randint(g, (K, N), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (K, N), -128, 127, b_dt)
+    if za == "mid":
+        za = 128 if a_dt == np.uint8 else -3
+    elif za == "edge":
+        za = 255 if a_dt == np.uint8 else -128
+    if zb_kind == "none":
+        zb = None
+    elif zb_kind == "scalar":
+        zb = np.array([200 if b_dt == np.uint8 else 7], dtype=b_dt)
+    else:
+        zb = (si.randint(g, (N,), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (N,), -128, 127, b_dt))
+    y = q.matmul_integer(to_dev(A), to_dev(B), za, None if zb is None else to_dev(zb)).cpu().numpy()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, za, zb))
+
+
+@pytest.mark.parametrize("a_shape,b_shape", [
+    ((2, 1, 2), (2, 3)),              # rank-3 A with a rank-2 B (batch stride 0)
+    ((3, 70, 259), (259, 33)),        # shared B, contiguous A batches (folded into M)
+    ((3, 70, 259), (1, 259, 33)),     # B with batch dims of 1 is shared too
+    ((1, 40, 100), (4, 100, 50)),     # size-1 batch on A, batched B
+    ((2, 3, 17, 64), (2, 3, 64, 24)), # rank 4, distinct per-batch weights
+    ((4, 17, 259), (4, 259, 9)),      # length-259 reduction, distinct per-batch weights
+])
+def test_matmul_integer_batch_rules(a_shape, b_shape):
+    case(f"matmul_integer batch A{a_shape} B{b_shape}")
+    g = si.rng(sum(a_shape) + sum(b_shape))
+    A = si.randint(g, a_shape, 0, 255, np.uint8)
+    B = si.randint(g, b_shape, -128, 127, np.int8)
+    zb = si.randint(g, (b_shape[-1],), -8, 8, np.int8)
+    y = q.matmul_integer(to_dev(A), to_dev(B), 128, to_dev(zb)).cpu().numpy()
+    ref = oracle.matmul_integer(A, B, 128, zb)
+    assert y.shape == ref.shape
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_matmul_integer_k259_all_255():
+    """The worked value on the hip-ep page: a length-259 uint8 dot of 255s."""
+    case("matmul_integer k259 all-255")
+    A = np.full((4, 259), 255, np.uint8)
+    B = np.full((259, 3), 255, np.uint8)
+    y = q.matmul_integer(to_dev(A), to_dev(B)).cpu().numpy()
+    assert (y == 16841475).all()
+
+
+def test_matmul_integer_wraps_mod_2_32():
+    """int8 x int8 sums past 2^31 store the two's-complement wrap (checks
+    that the matrix-core int32 accumulation wraps rather than saturates)."""
+    case("matmul_integer wrap K=131200 (-128 x -128)")
+    K = 131200
+    A = np.full((16, K), -128, np.int8)
+    B = np.full((K, 16), -128, np.int8)
+    y = q.matmul_integer(to_dev(A), to_dev(B)).cpu().numpy()
+    ref = oracle.matmul_integer(A, B)
+    assert ref[0, 0] == ((16384 * K + 2 ** 31) % 2 ** 32) - 2 ** 31
+    np.testing.assert_array_equal(y, ref)
+    # uint8 with zero point 0 on both sides: 65025 * 40000 wraps
+    A = np.full((2, 40000), 255, np.uint8)
+    B = np.full((40000, 2), 255, np.uint8)
+    y = q.matmul_integer(to_dev(A), to_dev(B)).cpu().numpy()
+    assert (y == -1693967296).all()
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_matmul_integer_every_tile_shape(tile):
+    case(f"matmul_integer tile {tile}")
+    A, B, zb = si.matmul_integer_inputs(2, 300, 512, 640, seed=31 + tile)
+    with env(QGEMM_TILE=tile):
+        y = q.matmul_integer(to_dev(A), to_dev(B), 100, to_dev(zb)).cpu().numpy()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, 100, zb))

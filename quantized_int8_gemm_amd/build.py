@@ -19,6 +19,9 @@ SOURCES = [
     "int8_tiled_256x256.hip",
     "int8_tiled_256x128.hip",
     "int8_tiled_128x128.hip",
+    "int8_dma_256x256.hip",
+    "int8_dma_256x128.hip",
+    "int8_dma_128x128.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
     "api.cpp",

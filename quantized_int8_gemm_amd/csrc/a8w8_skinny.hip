@@ -84,6 +84,24 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
     const uint32_t a_voff = (uint32_t)(l16 * lda + (lane >> 4) * 16);
 
     u32x4 wst[16];
+    u32x4 ast[KC / 64];
+    auto load_a = [&](int k) -> u32x4 {   // 16 bytes of row l16 from k + 16*(lane/16) on
+        if constexpr (VEC) {
+            return buffer_load16(a_rsrc, a_voff + (uint32_t)k, 0u);
+        } else {
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+            if (l16 < p.M) {
+                const int kk = k + (lane >> 4) * 16;
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    if (kk + b < p.K)
+                        d[b >> 2] |= (uint32_t)(uint8_t)p.A[(int64_t)l16 * p.lda + kk + b] << (8 * (b & 3));
+            }
+            return u32x4{d[0], d[1], d[2], d[3]};
+        }
+    };
+    // Issue the loads of chunk c: this thread's 16 x 16 W block and its A
+    // fragments (A is small and L2 resident).
     auto fetch = [&](int c) {
         const int k0 = c * KC;
 #pragma unroll
@@ -103,21 +121,8 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
                 wst[r] = u32x4{d[0], d[1], d[2], d[3]};
             }
         }
-    };
-    auto load_a = [&](int k) -> u32x4 {   // 16 bytes of row l16 from k on
-        if constexpr (VEC) {
-            return buffer_load16(a_rsrc, a_voff + (uint32_t)k, 0u);
-        } else {
-            uint32_t d[4] = {0u, 0u, 0u, 0u};
-            if (l16 < p.M) {
-                const int kk = k + (lane >> 4) * 16;
 #pragma unroll
-                for (int b = 0; b < 16; ++b)
-                    if (kk + b < p.K)
-                        d[b >> 2] |= (uint32_t)(uint8_t)p.A[(int64_t)l16 * p.lda + kk + b] << (8 * (b & 3));
-            }
-            return u32x4{d[0], d[1], d[2], d[3]};
-        }
+        for (int ks = 0; ks < KC / 64; ++ks) ast[ks] = load_a(k0 + ks * 64);
     };
 
     v4i acc[4];
@@ -129,20 +134,21 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
         // registers -> LDS (W^T), then prefetch the next chunk
         u32x4 t[16];
         transpose16x16(wst, t);
+        u32x4 af[KC / 64];
+#pragma unroll
+        for (int ks = 0; ks < KC / 64; ++ks) af[ks] = ast[ks];
         __syncthreads();  // previous chunk's reads are done
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(Ws + sk_off(i * 16 + cb, rg)) = t[i];
         __syncthreads();
         if (c + 1 < c_end) fetch(c + 1);
-        const int k0 = c * KC;
 #pragma unroll
         for (int ks = 0; ks < KC / 64; ++ks) {
-            const u32x4 af = load_a(k0 + ks * 64);
             const int seg = ks * 4 + (lane >> 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4 bf = *reinterpret_cast<const u32x4*>(Ws + sk_off(wave * 64 + j * 16 + l16, seg));
-                acc[j] = mfma_i8_16x16x64(af, bf, acc[j]);
+                acc[j] = mfma_i8_16x16x64(af[ks], bf, acc[j]);
             }
         }
     }
@@ -176,24 +182,33 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
     int32_t* part = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.workspace) +
                                                ((tiles_n * 4 + 255) / 256) * 256) +
                     (int64_t)tn * S * 16 * TN;
+    // Partials and tickets cross workgroups (and XCDs, whose L2s are not
+    // coherent with each other), so every access to them is a device-scope
+    // coherent access: stores and loads that bypass the non-coherent cache
+    // level, and an atomic ticket.  The wait on all outstanding memory
+    // operations orders each thread's partial stores before the barrier,
+    // and the barrier orders them before thread 0's ticket.  No cache-wide
+    // writeback or invalidate is needed.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            part[(split * 16 + row0 + r) * TN + wave * 64 + j * 16 + l16] = acc[j][r];
-    __threadfence();
+            __hip_atomic_store(&part[(split * 16 + row0 + r) * TN + wave * 64 + j * 16 + l16], acc[j][r],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
-    __threadfence();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             uint32_t sum = 0;
             const int idx = (row0 + r) * TN + wave * 64 + j * 16 + l16;
-            for (int s = 0; s < S; ++s) sum += (uint32_t) __builtin_nontemporal_load(&part[s * 16 * TN + idx]);
+            for (int s = 0; s < S; ++s)
+                sum += (uint32_t)__hip_atomic_load(&part[s * 16 * TN + idx], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
             epilogue(j, r, (int32_t)sum);
         }
     }

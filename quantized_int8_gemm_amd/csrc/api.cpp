@@ -61,12 +61,31 @@ qg_status finish_launch(hipError_t e, const char* name) {
     return QG_OK;
 }
 
+// The multi-stage direct-to-LDS kernel takes every 16-byte-aligned shape
+// except those whose bytes past K would reach a sum: uint8 flips, zero-point
+// sums and a k-major B need K % 64 == 0.  Everything else runs the
+// register-staged kernel, which clears bytes past K itself.
+bool dma_ok(const qg::Int8GemmArgs& a, bool bkm, bool vec, int epi) {
+    if (!vec || env_is("QGEMM_FAMILY", "staged")) return false;
+    const bool needs_k64 = bkm || epi == qg::EPI_I32;
+    return !needs_k64 || a.K % 64 == 0;
+}
+
 hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, int epi, int zp,
                         hipStream_t s, const char** name) {
-    static const char* names[] = {"int8_tiled_256x256", "int8_tiled_256x128", "int8_tiled_128x128"};
+    static const char* staged_names[] = {"int8_staged_256x256", "int8_staged_256x128", "int8_staged_128x128"};
+    static const char* dma_names[] = {"int8_dma_256x256", "int8_dma_256x128", "int8_dma_128x128"};
+    if (dma_ok(a, bkm, vec, epi)) {
+        *name = dma_names[cfg];
+        switch (cfg) {
+            case qg::TILE_256x256: return qg::launch_dma_256x256(a, bkm, epi, zp, s);
+            case qg::TILE_256x128: return qg::launch_dma_256x128(a, bkm, epi, zp, s);
+            default: return qg::launch_dma_128x128(a, bkm, epi, zp, s);
+        }
+    }
     // The byte-wise (any alignment) variants exist for the 128x128 tile only.
     if (!vec) cfg = qg::TILE_128x128;
-    *name = names[cfg];
+    *name = staged_names[cfg];
     switch (cfg) {
         case qg::TILE_256x256: return qg::launch_tiled_256x256(a, bkm, vec, epi, zp, s);
         case qg::TILE_256x128: return qg::launch_tiled_256x128(a, bkm, vec, epi, zp, s);

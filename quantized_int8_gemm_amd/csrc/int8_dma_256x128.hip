@@ -1,0 +1,8 @@
+// Tile shape 256 x 128 (four waves of 128 x 64) of the multi-stage int8 kernel.
+#include "int8_dma_impl.h"
+
+namespace qg {
+hipError_t launch_dma_256x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
+    return dma::launch_shape<256, 128, 128, 64>(a, bkm, epi, zp, s);
+}
+}  // namespace qg

@@ -1,0 +1,322 @@
+// Multi-stage int8 x int8 -> int32 matrix-core kernel for gfx950, fed by
+// direct global-to-LDS loads.  Shared by the A8W8 matmul-dequant operator
+// and MatMulInteger; included by one translation unit per tile shape.
+//
+// Operator sources (page titles and sections):
+//  * "Feature/a8w8 matmul dequant fusion": int8 matmul into an INT32
+//    accumulator, cast to FP32, multiply by act_scale per row, then by
+//    weight_scale per column, cast to the output type (sequence diagram,
+//    "What Changed").
+//  * "feat(onnx-to-hip): lower quantized integer conv and matmul", "What":
+//    MatMulInteger, Y = sum_k (A - a_zp)(B - b_zp), int32 result, shared B.
+//
+// One workgroup (four waves) computes a BM x BN output tile, K in chunks of
+// 64 bytes held in a ring of four LDS stages:
+//  * Loads go global -> LDS directly (buffer_load_dwordx4 ... lds), three
+//    chunks ahead of the one being multiplied, so about three chunks of
+//    memory latency are covered and no register holds staged data.  Each
+//    lane's 16 bytes land at consecutive LDS addresses, so the lane picks the
+//    global segment whose swizzled home is that address.  Rows past M (A) or
+//    K (B) read as zero through the buffer range check.
+//  * A fragments (K contiguous) come from ds_read_b128.  B stays as stored,
+//    [K rows][N bytes], and its fragments come from ds_read_b64_tr_b8: within
+//    each 16-lane group, lanes 2j and 2j+1 point at the two 8-byte halves of
+//    k-row j of a 16-column block and lane i receives column i of those eight
+//    rows, which is the matrix core's B layout.  Two such reads give a lane
+//    its 16 k-bytes.  B given as [N,K] is stored and read like A.
+//  * v_mfma_i32_16x16x64_i8 accumulates; uint8 operands are shifted to int8
+//    by flipping bit 7 as fragments are read, and the row / column sums the
+//    MatMulInteger correction needs come from the same fragments.
+//  * Epilogue as in the register-staged kernel.
+// This kernel needs K % 64 == 0 whenever an operand is flipped or a row or
+// column sum is taken (bytes past K are not cleared); the host routes other
+// shapes to the register-staged kernel.
+#pragma once
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qg {
+namespace dma {
+
+constexpr int BK = 64;
+constexpr int STAGES = 4;
+constexpr int GROUP_M = 8;
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Buffer descriptor words for [base, base + bytes); loads past the end give 0.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4i r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane.
+// Written as inline assembly so that the compiler does not wait for these
+// loads before every LDS read; the kernel waits for them explicitly.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(m0) : "memory");
+}
+
+// s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ u32x4 xor4(u32x4 v, uint32_t f) {
+    return u32x4{v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f};
+}
+
+// K-contiguous tile (A, or B as [N,K]): rows of 64 bytes, segment s of row r
+// at slot s ^ ((r >> 1) & 3).
+__device__ __forceinline__ int kc_slot(int r, int s) { return s ^ ((r >> 1) & 3); }
+
+template <int BM, int BN, int WM, int WN, bool B_KMAJOR, int EPI, int ZP, int FLIP>
+__global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
+    constexpr int WAVES_N = BN / WN;
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_ROUNDS = A_BYTES / 4096, B_ROUNDS = B_BYTES / 4096;
+    constexpr int LOADS = A_ROUNDS + B_ROUNDS;      // per thread per chunk
+    constexpr bool ROWSUM = (ZP & 1) != 0, COLSUM = (ZP & 2) != 0;
+    constexpr bool FLIP_A = (FLIP & 1) != 0, FLIP_B = (FLIP & 2) != 0;
+    static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole load rounds");
+    static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int g = lane >> 4, i16 = lane & 15;
+
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, GROUP_M, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN, bz = blockIdx.y;
+    const int rows_a = p.M - m0 < BM ? p.M - m0 : BM;
+    const int cols_b = p.N - n0 < BN ? p.N - n0 : BN;
+    const int lda = (int)p.lda, ldb = (int)p.ldb;
+    const int8_t* A = p.A + (int64_t)bz * p.a_bstride + (int64_t)m0 * p.lda;
+    const int8_t* B = B_KMAJOR ? p.B + (int64_t)bz * p.b_bstride + (int64_t)n0 * p.ldb
+                               : p.B + (int64_t)bz * p.b_bstride + n0;
+    const v4i a_rsrc = rsrc_words(A, (uint32_t)((rows_a - 1) * lda + p.K));
+    const v4i b_rsrc = B_KMAJOR ? rsrc_words(B, (uint32_t)((cols_b - 1) * ldb + p.K))
+                                : rsrc_words(B, (uint32_t)((p.K - 1) * ldb + (p.N - n0)));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // Per-lane global offsets (chunk 0) of each load round.  Round q of a
+    // stage covers LDS bytes [q*4096, q*4096 + 4096); this lane writes the 16
+    // bytes at q*4096 + wave*1024 + lane*16.
+    uint32_t a_off[A_ROUNDS], b_off[B_ROUNDS];
+#pragma unroll
+    for (int q = 0; q < A_ROUNDS; ++q) {
+        const int o = q * 4096 + wave * 1024 + lane * 16;
+        const int r = o / BK, slot = (o % BK) / 16;
+        a_off[q] = (uint32_t)(r * lda + 16 * kc_slot(r, slot));
+    }
+#pragma unroll
+    for (int q = 0; q < B_ROUNDS; ++q) {
+        const int o = q * 4096 + wave * 1024 + lane * 16;
+        if constexpr (B_KMAJOR) {
+            const int r = o / BK, slot = (o % BK) / 16;
+            b_off[q] = (uint32_t)(r * ldb + 16 * kc_slot(r, slot));
+        } else {
+            const int r = o / BN, slot = (o % BN) / 16;
+            b_off[q] = (uint32_t)(r * ldb + 16 * (slot ^ (r & 7)));
+        }
+    }
+
+    auto issue = [&](int kt, int stage) {
+        const uint32_t sbase = lds0 + stage * STAGE + wave * 1024;
+        const uint32_t ka = (uint32_t)(kt * BK);
+#pragma unroll
+        for (int q = 0; q < A_ROUNDS; ++q) dma16(a_rsrc, a_off[q] + ka, sbase + q * 4096);
+        const uint32_t kb = B_KMAJOR ? ka : (uint32_t)(kt * BK * ldb);
+#pragma unroll
+        for (int q = 0; q < B_ROUNDS; ++q) dma16(b_rsrc, b_off[q] + kb, sbase + A_BYTES + q * 4096);
+    };
+
+    v4i acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    int rs[FM], cs[FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a) rs[a] = 0;
+#pragma unroll
+    for (int b = 0; b < FN; ++b) cs[b] = 0;
+
+    // Fragment read offsets within a stage (per lane; the block index adds an
+    // immediate).
+    const int a_rd = (wm * WM + i16) * BK + (kc_slot(i16, g) << 4);
+    int b_rd = 0;
+    if constexpr (B_KMAJOR) {
+        b_rd = A_BYTES + (wn * WN + i16) * BK + (kc_slot(i16, g) << 4);
+    } else {
+        // ds_read_b64_tr_b8: lane (g, i) addresses k-row 16g + 8h + i/2,
+        // bytes 8*(i&1) .. of the fragment's 16-column segment.
+        b_rd = A_BYTES + (16 * g + (i16 >> 1)) * BN + 8 * (i16 & 1);
+    }
+    const int b_x = i16 >> 1;   // row & 7 of this lane's tr rows
+
+    auto compute = [&](int stage) {
+        const uint8_t* S = smem + stage * STAGE;
+        u32x4 bf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (B_KMAJOR) {
+                bf[j] = *reinterpret_cast<const u32x4*>(S + b_rd + j * 16 * BK);
+            } else {
+                const int seg = (wn * WN) / 16 + j;
+                const uint8_t* base = S + b_rd + ((seg ^ b_x) << 4);
+                const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(base));
+                const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(base + 8 * BN));
+                bf[j] = u32x4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
+            }
+            if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
+            if constexpr (COLSUM)
+                cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
+        }
+        // A fragments one block ahead, so each LDS read overlaps the
+        // previous block's matrix-core work.
+        u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd);
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            u32x4 af = af_next;
+            if (a + 1 < FM) af_next = *reinterpret_cast<const u32x4*>(S + a_rd + (a + 1) * 16 * BK);
+            __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
+            if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
+            if constexpr (ROWSUM)
+                rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
+#pragma unroll
+            for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(af, bf[b], acc[a][b]);
+        }
+    };
+
+    const int nk = (p.K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+        // chunk kt has landed once at most the later chunks are outstanding
+        if (kt + STAGES - 2 < nk) wait_vmcnt<LOADS * (STAGES - 2)>();
+        else if (kt + 1 < nk) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+        compute(kt % STAGES);
+    }
+
+    if constexpr (ROWSUM) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            rs[a] += __shfl_xor(rs[a], 16);
+            rs[a] += __shfl_xor(rs[a], 32);
+        }
+    }
+    if constexpr (COLSUM) {
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            cs[b] += __shfl_xor(cs[b], 16);
+            cs[b] += __shfl_xor(cs[b], 32);
+        }
+    }
+
+    const int row_base = m0 + wm * WM + 4 * g;
+    constexpr int OUT_BYTES = EPI == EPI_BF16 ? 2 : 4;
+    char* out = reinterpret_cast<char*>(p.out) + (int64_t)bz * p.o_bstride * OUT_BYTES;
+#pragma unroll
+    for (int b = 0; b < FN; ++b) {
+        const int n = n0 + wn * WN + b * 16 + i16;
+        const bool n_ok = n < p.N;
+        float ws = 0.f;
+        uint32_t cbn = 0, add_n = 0;
+        if constexpr (EPI == EPI_I32) {
+            int32_t zb = 0;
+            if (p.b_zp != nullptr && n_ok) {
+                const int idx = n * p.b_zp_stride;
+                zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
+                               : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
+            }
+            cbn = (uint32_t)(p.sb - zb);
+            add_n = (uint32_t)p.K * (uint32_t)p.ca * cbn;
+            if constexpr (COLSUM) add_n += (uint32_t)p.ca * (uint32_t)cs[b];
+        } else {
+            if (n_ok) ws = p.weight_scale[n * p.ws_stride];
+        }
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = row_base + a * 16 + r;
+                int rsum = 0;
+                if constexpr (ROWSUM) rsum = __shfl(rs[a], 4 * g + r);
+                if (!(n_ok && m < p.M)) continue;
+                const int64_t o = (int64_t)m * p.ldo + n;
+                if constexpr (EPI == EPI_I32) {
+                    uint32_t y = (uint32_t)acc[a][b][r] + add_n;
+                    if constexpr (ROWSUM) y += cbn * (uint32_t)rsum;
+                    reinterpret_cast<int32_t*>(out)[o] = (int32_t)y;
+                } else {
+                    float f = (float)acc[a][b][r];
+                    f = f * p.act_scale[m * p.as_stride];
+                    f = f * ws;
+                    if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(out)[o] = f;
+                    else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(f);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool BKM, int EPI, int ZP, int FLIP>
+hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, BKM, EPI, ZP, FLIP>), dim3(tiles, a.batch), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int ZP>
+hipError_t by_flip(const Int8GemmArgs& a, int flip, hipStream_t s) {
+    switch (flip) {
+        case 0: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 0>(a, s);
+        case 1: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 1>(a, s);
+        case 2: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 2>(a, s);
+        default: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 3>(a, s);
+    }
+}
+
+// Every variant of one tile shape: A8W8 (fp32 / bf16 out, B as [K,N] or
+// [N,K]) and MatMulInteger (B as [K,N], any flips and sums).
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_shape(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
+    const int flip = (a.a_flip ? 1 : 0) | (a.b_flip ? 2 : 0);
+    if (epi == EPI_I32) {
+        switch (zp) {
+            case 0: return by_flip<BM, BN, WM, WN, EPI_I32, 0>(a, flip, s);
+            case 1: return by_flip<BM, BN, WM, WN, EPI_I32, 1>(a, flip, s);
+            case 2: return by_flip<BM, BN, WM, WN, EPI_I32, 2>(a, flip, s);
+            default: return by_flip<BM, BN, WM, WN, EPI_I32, 3>(a, flip, s);
+        }
+    }
+    if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, true, EPI_F32, 0, 0>(a, s)
+                                   : launch_one<BM, BN, WM, WN, true, EPI_BF16, 0, 0>(a, s);
+    return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, false, EPI_F32, 0, 0>(a, s)
+                          : launch_one<BM, BN, WM, WN, false, EPI_BF16, 0, 0>(a, s);
+}
+
+}  // namespace dma
+}  // namespace qg

@@ -41,6 +41,13 @@ hipError_t launch_tiled_256x256(const Int8GemmArgs& a, bool bkm, bool vec, int e
 hipError_t launch_tiled_256x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 hipError_t launch_tiled_128x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 
+// Multi-stage kernel fed by direct global-to-LDS loads, one launcher per
+// tile shape.  Needs 16-byte aligned rows; K % 64 == 0 when an operand is
+// uint8 or a zero-point sum is taken, or when B is [N,K].
+hipError_t launch_dma_256x256(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_128x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,
                               const char** name);

@@ -33,7 +33,7 @@ def check(A, W, s_a, s_w, b_trans=False, expect_kernel=None):
 def test_a8w8_256x1024x1024_all_scale_forms():
     case("a8w8 256x1024x1024 seed 202")
     A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
-    check(A, W, s_a, s_w, expect_kernel="int8_tiled")
+    check(A, W, s_a, s_w, expect_kernel="int8_")
     ref = run(A, W, s_a, s_w, torch.float32).cpu().numpy()
     # [M,1] / [1,N] scales give the same bits as [M] / [N]
     two_d = q.qgemm_a8w8(to_dev(A), to_dev(W), to_dev(s_a).reshape(-1, 1), to_dev(s_w).reshape(1, -1))
@@ -74,14 +74,14 @@ def test_a8w8_ragged(M, N, K, kernel):
     case(f"a8w8 ragged M={M} N={N} K={K} kernel={kernel}")
     A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M * 7 + N * 3 + K, lo=-128, hi=127)
     with env(QGEMM_FORCE_KERNEL=kernel):
-        check(A, W, s_a, s_w, expect_kernel="a8w8_skinny" if (kernel == "auto" and M <= 16) else "int8_tiled")
+        check(A, W, s_a, s_w, expect_kernel="a8w8_skinny" if (kernel == "auto" and M <= 16) else "int8_")
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 40, 50), (64, 256, 512), (200, 300, 259)])
 def test_a8w8_b_trans(M, N, K):
     case(f"a8w8 b_trans M={M} N={N} K={K}")
     A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=5 + M)
-    check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True, expect_kernel="int8_tiled")
+    check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True, expect_kernel="int8_")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
@@ -139,7 +139,7 @@ def test_a8w8_large_8192_sampled():
     A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
     tA, tW, ta, tw = to_dev(A), to_dev(W), to_dev(s_a), to_dev(s_w)
     out16 = bf16_bits(q.qgemm_a8w8(tA, tW, ta, tw, out_dtype=torch.bfloat16))
-    assert q.last_kernel().startswith("int8_tiled")
+    assert q.last_kernel().startswith("int8_")
     out32 = q.qgemm_a8w8(tA, tW, ta, tw).cpu().numpy()
     g = si.rng(1)
     rows = np.concatenate([g.integers(0, 8192, 3000), np.zeros(8192, np.int64), np.full(8192, 8191)])
@@ -175,4 +175,17 @@ def test_a8w8_every_tile_shape(tile):
     case(f"a8w8 tile cfg {tile} 520x700x1000")
     A, W, s_a, s_w = si.a8w8_inputs(520, 768, 1024, seed=40 + tile)
     with env(QGEMM_TILE=tile):
-        check(A, W, s_a, s_w, expect_kernel="int8_tiled")
+        check(A, W, s_a, s_w, expect_kernel="int8_")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 384, 320), (64, 128, 208)])
+@pytest.mark.parametrize("family", ["dma", "staged"])
+def test_a8w8_both_kernel_families(M, N, K, family):
+    """The multi-stage direct-to-LDS kernel and the register-staged kernel
+    give the same bits (K = 208 is not a multiple of 64)."""
+    case(f"a8w8 family={family} M={M} N={N} K={K}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K)
+    with env(QGEMM_FAMILY=family):
+        check(A, W, s_a, s_w, expect_kernel="int8_dma" if family == "dma" else "int8_staged")
+        check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True,
+              expect_kernel="int8_dma" if (family == "dma" and K % 64 == 0) else "int8_staged")

@@ -96,3 +96,17 @@ def test_matmul_integer_every_tile_shape(tile):
     with env(QGEMM_TILE=tile):
         y = q.matmul_integer(to_dev(A), to_dev(B), 100, to_dev(zb)).cpu().numpy()
     np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, 100, zb))
+
+
+@pytest.mark.parametrize("family", ["dma", "staged"])
+@pytest.mark.parametrize("a_dt,b_dt,za", [(np.uint8, np.int8, 128), (np.int8, np.uint8, -7), (np.uint8, np.uint8, 3)])
+def test_matmul_integer_both_kernel_families(family, a_dt, b_dt, za):
+    case(f"matmul_integer family={family} {np.dtype(a_dt)}x{np.dtype(b_dt)} za={za}")
+    g = si.rng(77)
+    A = si.randint(g, (3, 200, 512), 0, 255, a_dt) if a_dt == np.uint8 else si.randint(g, (3, 200, 512), -128, 127, a_dt)
+    B = si.randint(g, (512, 384), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (512, 384), -128, 127, b_dt)
+    zb = si.randint(g, (384,), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (384,), -8, 8, b_dt)
+    with env(QGEMM_FAMILY=family):
+        y = q.matmul_integer(to_dev(A), to_dev(B), za, to_dev(zb)).cpu().numpy()
+        assert q.last_kernel().startswith("int8_dma" if family == "dma" else "int8_staged")
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, za, zb))

@@ -161,7 +161,7 @@ def main():
         t0 = time.perf_counter()
         oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)
         dt = time.perf_counter() - t0
-        nrows = int(max(rows_probe, min(512, rows_probe * 12.0 / max(dt, 1e-3))))
+        nrows = int(max(rows_probe, min(4096, rows_probe * 15.0 / max(dt, 1e-3))))
         t0 = time.perf_counter()
         oracle.a8w8(A[:nrows], W, s_a[:nrows], s_w)
         dt = time.perf_counter() - t0

@@ -7,210 +7,242 @@
 // reading the weight once from HBM.
 //
 // Grid: (N / 256 column tiles) x (S splits of K).  Each workgroup streams a
-// [K/S x 256] slab of W exactly once:
-//  * every thread reads a 16-row x 16-byte block per 256-row chunk (16
-//    consecutive lanes cover 256 contiguous bytes of a row), transposes it in
-//    registers, and writes 16 k-contiguous column segments to LDS, so W^T is
-//    ready for the matrix cores;
-//  * A (at most 16 rows, resident in L2) is loaded straight into matrix-core
-//    fragments; rows past M and bytes past K read as zero or meet zero
-//    weight rows, so they add nothing;
-//  * v_mfma_i32_16x16x64_i8 accumulates the 16 x 256 int32 partial tile.
-// With S == 1 the epilogue runs directly.  With S > 1 each split stores its
-// exact int32 partial in the workspace and takes a ticket; the last split of a
-// column tile adds the S partials (integer addition, so the order does not
-// matter) and runs the epilogue once, then resets the ticket to zero.
+// [K/S x 256] slab of W once; its four waves take 64-row steps round robin.
+//  * A lane (g = lane/16, c = lane%16) loads rows 16g .. 16g+15 of the step
+//    as 16-byte vectors at columns 16c .. 16c+15 (16 lanes cover 256
+//    contiguous bytes of a row), two steps ahead of the one being multiplied.
+//  * The lane's 16 x 16 byte block is transposed in registers; column j of it
+//    is then exactly a matrix-core B fragment (16 k-bytes of column 16c + j),
+//    and row c of A is the matching A fragment, so v_mfma_i32_16x16x64_i8
+//    number j accumulates output columns {16c + j}.  No LDS in the hot loop.
+//  * The four waves' int32 tiles are added through LDS in natural column
+//    order.  With S == 1 the epilogue runs there.  With S > 1 each split
+//    stores its exact int32 partial (rows < M) and takes a ticket; the last
+//    split of a column tile adds the S partials (integer addition: any order
+//    gives the same bits), runs the epilogue once and resets the ticket.
+// Rows past M and bytes past K read as zero through the buffer range checks
+// (or meet zero weight rows), so they add nothing.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace qg {
 namespace {
 
-constexpr int NT = 256;     // threads
+constexpr int NT = 256;     // threads (four waves)
 constexpr int TN = 256;     // columns per workgroup
-constexpr int KC = 256;     // k rows per chunk
-constexpr int ROW = KC;     // LDS row bytes (one column of W^T per row)
+constexpr int KS = 64;      // k rows per wave step
+constexpr int WAVES = 4;
 
-// LDS row of W^T that holds tile column n (16x16 block transposed: column
-// cb*16 + c goes to row c*16 + cb) and the swizzled offset of segment s.
-__device__ __forceinline__ int sk_off(int row, int seg) { return row * ROW + ((seg ^ (row & 15)) << 4); }
-__device__ __forceinline__ int sk_col_of_row(int row) { return (row & 15) * 16 + (row >> 4); }
-
-__device__ __forceinline__ void transpose16x16(const u32x4 in[16], u32x4 out[16]) {
-    // out[c] word q = bytes (rows 4q..4q+3, column c)
+// In-place 16 x 16 byte transpose: on entry v[r] holds row r (16 bytes); on
+// exit v[c] holds column c (16 bytes, rows 0..15 in order).  Block (q, d) of
+// 4 x 4 bytes (rows 4q.., bytes 4d..) moves to block (d, q), so the two are
+// transposed together.
+__device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t x[4], y[4];
+        for (int d = q; d < 4; ++d) {
+            uint32_t x[4], y[4], xs[4], ys[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (&in[q * 4 + i].x)[d];
+            for (int i = 0; i < 4; ++i) x[i] = (&v[4 * q + i].x)[d];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xs[i] = (&v[4 * d + i].x)[q];
             transpose4x4_bytes(x, y);
+            transpose4x4_bytes(xs, ys);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) (&out[d * 4 + c].x)[q] = y[c];
+            for (int c = 0; c < 4; ++c) (&v[4 * d + c].x)[q] = y[c];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) (&v[4 * q + c].x)[d] = ys[c];
         }
     }
 }
 
 template <bool VEC, int EPI>
 __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t Ws[TN * ROW];
+    __shared__ __attribute__((aligned(16))) int32_t red[WAVES][16][TN];
+    __shared__ float ws_tile[TN];
+    __shared__ float as_rows[16];
     __shared__ int ticket;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l16 = lane & 15;
-    const int tn = blockIdx.x;
-    const int split = blockIdx.y;
-    const int S = gridDim.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int tn = blockIdx.x, split = blockIdx.y, S = gridDim.y;
     const int n0 = tn * TN;
     const int cols = p.N - n0;
 
-    // K range of this split, whole chunks except possibly the last split.
-    const int chunks = (p.K + KC - 1) / KC;
-    const int per = (chunks + S - 1) / S;
-    const int c_begin = split * per;
-    int c_end = c_begin + per;
-    if (c_end > chunks) c_end = chunks;
+    // K range of this split: `per` 64-row steps, a multiple of 2*WAVES.
+    const int per = p.split_steps;
+    const int s_begin = split * per;
 
     const int ldb = (int)p.ldb, lda = (int)p.lda;
     const int8_t* Wt = p.B + n0;
     const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wt, (uint32_t)((p.K - 1) * ldb + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)((p.M - 1) * lda + p.K));
+    const uint32_t w_voff = (uint32_t)(16 * g * ldb + 16 * c16);
+    const uint32_t a_voff = (uint32_t)(c16 * lda + 16 * g);
 
-    const int cb = tid & 15, rg = tid >> 4;           // this thread's 16x16 block
-    const uint32_t w_voff = (uint32_t)(rg * 16 * ldb + cb * 16);
-    const uint32_t a_voff = (uint32_t)(l16 * lda + (lane >> 4) * 16);
+    // The epilogue's scales, loaded now so their latency hides behind the
+    // weight stream.
+    if (tid < TN) ws_tile[tid] = (n0 + tid < p.N) ? p.weight_scale[(n0 + tid) * p.ws_stride] : 0.f;
+    if (tid < 16) as_rows[tid] = (tid < p.M) ? p.act_scale[tid * p.as_stride] : 0.f;
 
-    u32x4 wst[16];
-    u32x4 ast[KC / 64];
-    auto load_a = [&](int k) -> u32x4 {   // 16 bytes of row l16 from k + 16*(lane/16) on
+    u32x4 wbuf[2][16];
+    u32x4 abuf[2];
+    // Loads of one step into buffer b.  Unconditional: a step past this
+    // split's range reads rows of the matrix (or zeros past K) that are never
+    // multiplied, so no branch separates the loads and all stay in flight.
+    auto fetch = [&](int step, int b) {
+        const int k0 = step * KS;
         if constexpr (VEC) {
-            return buffer_load16(a_rsrc, a_voff + (uint32_t)k, 0u);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb), 0u);
+            abuf[b] = buffer_load16(a_rsrc, a_voff + (uint32_t)k0, 0u);
         } else {
-            uint32_t d[4] = {0u, 0u, 0u, 0u};
-            if (l16 < p.M) {
-                const int kk = k + (lane >> 4) * 16;
 #pragma unroll
-                for (int b = 0; b < 16; ++b)
-                    if (kk + b < p.K)
-                        d[b >> 2] |= (uint32_t)(uint8_t)p.A[(int64_t)l16 * p.lda + kk + b] << (8 * (b & 3));
-            }
-            return u32x4{d[0], d[1], d[2], d[3]};
-        }
-    };
-    // Issue the loads of chunk c: this thread's 16 x 16 W block and its A
-    // fragments (A is small and L2 resident).
-    auto fetch = [&](int c) {
-        const int k0 = c * KC;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if constexpr (VEC) {
-                wst[r] = buffer_load16(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb), 0u);
-            } else {
-                const int gk = k0 + rg * 16 + r;
+            for (int r = 0; r < 16; ++r) {
+                const int gk = k0 + 16 * g + r;
                 uint32_t d[4] = {0u, 0u, 0u, 0u};
                 if (gk < p.K) {
 #pragma unroll
-                    for (int b = 0; b < 16; ++b) {
-                        const int cc = cb * 16 + b;
-                        if (cc < cols) d[b >> 2] |= (uint32_t)(uint8_t)Wt[(int64_t)gk * p.ldb + cc] << (8 * (b & 3));
+                    for (int e = 0; e < 16; ++e) {
+                        const int cc = 16 * c16 + e;
+                        if (cc < cols) d[e >> 2] |= (uint32_t)(uint8_t)Wt[(int64_t)gk * p.ldb + cc] << (8 * (e & 3));
                     }
                 }
-                wst[r] = u32x4{d[0], d[1], d[2], d[3]};
+                wbuf[b][r] = u32x4{d[0], d[1], d[2], d[3]};
             }
-        }
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+            if (c16 < p.M) {
 #pragma unroll
-        for (int ks = 0; ks < KC / 64; ++ks) ast[ks] = load_a(k0 + ks * 64);
+                for (int e = 0; e < 16; ++e) {
+                    const int kk = k0 + 16 * g + e;
+                    if (kk < p.K) d[e >> 2] |= (uint32_t)(uint8_t)p.A[(int64_t)c16 * p.lda + kk] << (8 * (e & 3));
+                }
+            }
+            abuf[b] = u32x4{d[0], d[1], d[2], d[3]};
+        }
     };
 
-    v4i acc[4];
+    v4i acc[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < 16; ++j) acc[j] = v4i{0, 0, 0, 0};
 
-    if (c_begin < c_end) fetch(c_begin);
-    for (int c = c_begin; c < c_end; ++c) {
-        // registers -> LDS (W^T), then prefetch the next chunk
-        u32x4 t[16];
-        transpose16x16(wst, t);
-        u32x4 af[KC / 64];
+    // This wave's steps: s_begin + wave + WAVES*i, i < n_my.  Every split
+    // spans a multiple of 2*WAVES steps (steps past K read as zeros and add
+    // nothing), so n_my is even and the same for all waves, and no branch
+    // sits between the loads.  Two steps are in flight; the loop is unrolled
+    // by two so both register buffers have fixed homes, and the last pair is
+    // peeled so that nothing is fetched past the wave's range.
+    const int first = s_begin + wave;
+    const int n_my = per / WAVES;
+    auto consume = [&](int b) {
+        transpose16x16_inplace(wbuf[b]);
 #pragma unroll
-        for (int ks = 0; ks < KC / 64; ++ks) af[ks] = ast[ks];
-        __syncthreads();  // previous chunk's reads are done
-#pragma unroll
-        for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(Ws + sk_off(i * 16 + cb, rg)) = t[i];
-        __syncthreads();
-        if (c + 1 < c_end) fetch(c + 1);
-#pragma unroll
-        for (int ks = 0; ks < KC / 64; ++ks) {
-            const int seg = ks * 4 + (lane >> 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4 bf = *reinterpret_cast<const u32x4*>(Ws + sk_off(wave * 64 + j * 16 + l16, seg));
-                acc[j] = mfma_i8_16x16x64(af[ks], bf, acc[j]);
-            }
-        }
+        for (int j = 0; j < 16; ++j) acc[j] = mfma_i8_16x16x64(abuf[b], wbuf[b][j], acc[j]);
+    };
+    // Scheduling barriers keep each fetch's loads together, so that waiting
+    // for one buffer never waits for the other buffer's loads.
+    fetch(first, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(first + WAVES, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i + 2 < n_my; i += 2) {
+        consume(0);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(first + WAVES * (i + 2), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(1);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(first + WAVES * (i + 3), 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    consume(0);
+    consume(1);
 
-    // Row 4*(lane/16)+r, column col_of_row(wave*64 + j*16 + l16) of the tile.
-    const int row0 = 4 * (lane >> 4);
-    auto epilogue = [&](int j, int r, int32_t v) {
-        const int m = row0 + r;
-        const int n = n0 + sk_col_of_row(wave * 64 + j * 16 + l16);
-        if (m >= p.M || n >= p.N) return;
+    // Add the four waves' tiles through LDS in natural column order:
+    // register r of MFMA j holds row 4g + r, column 16*c16 + j.
+    const int M = p.M;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (4 * g + r < M) red[wave][4 * g + r][16 * c16 + j] = acc[j][r];
+    __syncthreads();
+
+    // Items: (row m < M, group of 4 columns); each thread takes some.
+    auto tile_sum = [&](int m, int cg) -> int4 {
+        int4 s = *reinterpret_cast<const int4*>(&red[0][m][cg * 4]);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) {
+            const int4 v = *reinterpret_cast<const int4*>(&red[w][m][cg * 4]);
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        return s;
+    };
+    auto epilogue = [&](int m, int n, int32_t v) {
+        if (n >= p.N) return;
         float f = (float)v;
-        f = f * p.act_scale[m * p.as_stride];
-        f = f * p.weight_scale[n * p.ws_stride];
+        f = f * as_rows[m];
+        f = f * ws_tile[n - n0];
         const int64_t o = (int64_t)m * p.ldo + n;
         if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(p.out)[o] = f;
         else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(f);
     };
+    const int items = M * (TN / 4);
 
     if (S == 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) epilogue(j, r, acc[j][r]);
+        for (int it = tid; it < items; it += NT) {
+            const int m = it / (TN / 4), cg = it % (TN / 4);
+            const int4 s = tile_sum(m, cg);
+            epilogue(m, n0 + cg * 4 + 0, s.x);
+            epilogue(m, n0 + cg * 4 + 1, s.y);
+            epilogue(m, n0 + cg * 4 + 2, s.z);
+            epilogue(m, n0 + cg * 4 + 3, s.w);
+        }
         return;
     }
 
     // Split-K: workspace = [tickets: one int per column tile, padded to 256 B]
-    //                      [partials: S x 16 x TN int32 per column tile]
+    //                      [partials: per column tile, S x 16 x TN int32]
+    // Partials and tickets cross workgroups (and XCDs, whose L2s are not
+    // coherent with each other), so every access to them is device-coherent:
+    // stores and loads with the device-scope cache policy (they bypass the
+    // XCD-private cache level) and an atomic ticket.  Waiting for all
+    // outstanding memory operations orders each thread's partial stores
+    // before the barrier, and the barrier orders them before thread 0's
+    // ticket; no cache-wide writeback or invalidate is needed.
     const int tiles_n = gridDim.x;
     int* tickets = reinterpret_cast<int*>(p.workspace);
-    int32_t* part = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.workspace) +
-                                               ((tiles_n * 4 + 255) / 256) * 256) +
-                    (int64_t)tn * S * 16 * TN;
-    // Partials and tickets cross workgroups (and XCDs, whose L2s are not
-    // coherent with each other), so every access to them is a device-scope
-    // coherent access: stores and loads that bypass the non-coherent cache
-    // level, and an atomic ticket.  The wait on all outstanding memory
-    // operations orders each thread's partial stores before the barrier,
-    // and the barrier orders them before thread 0's ticket.  No cache-wide
-    // writeback or invalidate is needed.
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            __hip_atomic_store(&part[(split * 16 + row0 + r) * TN + wave * 64 + j * 16 + l16], acc[j][r],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    char* part = reinterpret_cast<char*>(p.workspace) + ((tiles_n * 4 + 255) / 256) * 256 +
+                 (size_t)tn * S * 16 * TN * 4;
+    // Partial tile of split s: rows m < M of [16][TN] int32, as 16-byte
+    // vectors through a buffer resource with device-coherent cache policy.
+    const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * 16 * TN * 4));
+    constexpr int COHERENT = 16;  // sc1: device scope, bypass the XCD-private cache level
+    for (int it = tid; it < items; it += NT) {
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        const int4 s4 = tile_sum(m, cg);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, s4), p_rsrc,
+                                               ((split * 16 + m) * TN + cg * 4) * 4, 0, COHERENT);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            uint32_t sum = 0;
-            const int idx = (row0 + r) * TN + wave * 64 + j * 16 + l16;
-            for (int s = 0; s < S; ++s)
-                sum += (uint32_t)__hip_atomic_load(&part[s * 16 * TN + idx], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            epilogue(j, r, (int32_t)sum);
+    for (int it = tid; it < items; it += NT) {
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        v4i sum = v4i{0, 0, 0, 0};
+        for (int s = 0; s < S; ++s) {
+            const v4i v = __builtin_bit_cast(
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, ((s * 16 + m) * TN + cg * 4) * 4, 0, COHERENT));
+            sum = v4i{(int)((uint32_t)sum.x + (uint32_t)v.x), (int)((uint32_t)sum.y + (uint32_t)v.y),
+                      (int)((uint32_t)sum.z + (uint32_t)v.z), (int)((uint32_t)sum.w + (uint32_t)v.w)};
         }
+        epilogue(m, n0 + cg * 4 + 0, sum.x);
+        epilogue(m, n0 + cg * 4 + 1, sum.y);
+        epilogue(m, n0 + cg * 4 + 2, sum.z);
+        epilogue(m, n0 + cg * 4 + 3, sum.w);
     }
     if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -224,23 +256,31 @@ size_t skinny_workspace_bytes(int M, int N, int splits) {
     return ((tiles_n * 4 + 255) / 256) * 256 + tiles_n * (size_t)splits * 16 * TN * 4;
 }
 
+// Steps (64 k-rows) per split: a multiple of 2*WAVES, chosen so that about
+// one workgroup runs per compute unit (256 CUs).
+int skinny_split_steps(int N, int K) {
+    const int tiles_n = (N + TN - 1) / TN;
+    const int steps = (K + KS - 1) / KS;
+    const int want = (256 + tiles_n - 1) / tiles_n;        // splits wanted
+    int per = (steps + want - 1) / want;
+    per = ((per + 2 * WAVES - 1) / (2 * WAVES)) * (2 * WAVES);
+    return per;
+}
+
+int skinny_splits_for(int N, int K, int per) {
+    const int steps = (K + KS - 1) / KS;
+    return (steps + per - 1) / per;
+}
+
 int skinny_splits(int M, int N, int K) {
     (void)M;
-    const int tiles_n = (N + TN - 1) / TN;
-    const int chunks = (K + KC - 1) / KC;
-    // aim at about two workgroups per compute unit (256 CUs)
-    int s = (512 + tiles_n - 1) / tiles_n;
-    if (s > chunks) s = chunks;
-    if (s < 1) s = 1;
-    // every split must own at least one chunk
-    const int per = (chunks + s - 1) / s;
-    s = (chunks + per - 1) / per;
-    return s;
+    return skinny_splits_for(N, K, skinny_split_steps(N, K));
 }
 
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s, const char** name) {
     dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
     *name = "a8w8_skinny";
+    if (a.split_steps % (2 * WAVES) != 0 || (int64_t)a.split_steps * grid.y * KS < a.K) return hipErrorInvalidValue;
     if (vec) {
         if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32>), grid, dim3(NT), 0, s, a);
         else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16>), grid, dim3(NT), 0, s, a);

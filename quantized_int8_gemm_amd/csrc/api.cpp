@@ -112,10 +112,25 @@ const char* qgemm_status_string(qg_status s) {
     return "unknown status";
 }
 
-static int a8w8_skinny_splits(int64_t M, int64_t N, int64_t K) {
+// Splits of K for the decode kernel, and the steps each split covers.
+// QGEMM_SPLITS asks for a split count (tests and tuning).
+static void a8w8_skinny_plan(int64_t M, int64_t N, int64_t K, int* splits, int* steps) {
+    (void)M;
     const int forced = env_int("QGEMM_SPLITS", 0);
-    if (forced > 0) return forced;
-    return qg::skinny_splits((int)M, (int)N, (int)K);
+    int per = qg::skinny_split_steps((int)N, (int)K);
+    if (forced > 0) {
+        const int total = (int)((K + 63) / 64);
+        per = (total + forced - 1) / forced;
+        per = ((per + 7) / 8) * 8;
+    }
+    *steps = per;
+    *splits = qg::skinny_splits_for((int)N, (int)K, per);
+}
+
+static int a8w8_skinny_splits(int64_t M, int64_t N, int64_t K) {
+    int s, per;
+    a8w8_skinny_plan(M, N, K, &s, &per);
+    return s;
 }
 
 static bool a8w8_is_skinny(int64_t M, int b_trans) {
@@ -182,15 +197,19 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t l
     const char* name = "";
     hipError_t e;
     if (a8w8_is_skinny(M, b_trans)) {
-        int splits = a8w8_skinny_splits(M, N, K);
+        int splits, per;
+        a8w8_skinny_plan(M, N, K, &splits, &per);
         const size_t need = qg::skinny_workspace_bytes((int)M, (int)N, splits);
         if (need > 0 && workspace == nullptr) {
+            // no workspace: one split covering all of K
+            per = (int)(((K + 63) / 64 + 7) / 8) * 8;
             splits = 1;
         } else if (need > workspace_bytes) {
             return QG_ERR_WORKSPACE;
         }
         a.workspace = workspace;
         a.splits = splits;
+        a.split_steps = per;
         (void)hipGetLastError();
         e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name);
         log_dispatch("a8w8", name, 1, M, N, K, splits);

@@ -75,9 +75,25 @@ __device__ __forceinline__ u32x4 xor4(u32x4 v, uint32_t f) {
     return u32x4{v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f};
 }
 
-// K-contiguous tile (A, or B as [N,K]): rows of 64 bytes, segment s of row r
-// at slot s ^ ((r >> 1) & 3).
-__device__ __forceinline__ int kc_slot(int r, int s) { return s ^ ((r >> 1) & 3); }
+// K-contiguous tile (A, or B as [N,K]): rows of 64 bytes (4 segments of
+// 16), segment s of row r at slot s ^ f(r) with f(r) = bits (r1 ^ r3, r2).
+// Rows r, r+2, r+4, r+6 then take four distinct slots, and so do rows r,
+// r+4, r+8, r+12, so a fragment read (16 consecutive rows, one segment) is
+// conflict-free whether the LDS serves 8 lanes over 32 banks or 16 lanes over
+// 64 banks per cycle.
+__device__ __forceinline__ int kc_slot(int r, int s) {
+    return s ^ ((((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2));
+}
+
+// [K,N] tile: rows of BN bytes; segment s of k-row r at slot
+// s ^ (r & 7) ^ t(r), where t flips bit 3 (BN >= 256) or bit 0 (BN = 128)
+// for rows 16..31 of each 32.  A transposed read touches rows 16g+8h+0..7
+// for two lane groups g at once; the flip keeps those 16 rows apart.
+template <int BN>
+__device__ __forceinline__ int kn_slot(int r, int s) {
+    const int t = (r >> 4) & 1;
+    return s ^ (r & 7) ^ (BN >= 256 ? (t << 3) : t);
+}
 
 template <int BM, int BN, int WM, int WN, bool B_KMAJOR, int EPI, int ZP, int FLIP>
 __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
@@ -131,7 +147,7 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
             b_off[q] = (uint32_t)(r * ldb + 16 * kc_slot(r, slot));
         } else {
             const int r = o / BN, slot = (o % BN) / 16;
-            b_off[q] = (uint32_t)(r * ldb + 16 * (slot ^ (r & 7)));
+            b_off[q] = (uint32_t)(r * ldb + 16 * kn_slot<BN>(r, slot));
         }
     }
 
@@ -167,7 +183,8 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
         // bytes 8*(i&1) .. of the fragment's 16-column segment.
         b_rd = A_BYTES + (16 * g + (i16 >> 1)) * BN + 8 * (i16 & 1);
     }
-    const int b_x = i16 >> 1;   // row & 7 of this lane's tr rows
+    // slot = seg ^ b_x for this lane's transposed-read rows (16g + 8h + i/2)
+    const int b_x = (i16 >> 1) ^ (BN >= 256 ? ((g & 1) << 3) : (g & 1));
 
     auto compute = [&](int stage) {
         const uint8_t* S = smem + stage * STAGE;
@@ -201,9 +218,26 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
             if constexpr (ROWSUM)
                 rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
 #pragma unroll
-            for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(af, bf[b], acc[a][b]);
+            for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(bf[b], af, acc[a][b]);
         }
     };
+
+    // The A8W8 epilogue's scales, loaded now so their latency hides behind
+    // the main loop: rows wm*WM + 16a + i16 and columns wn*WN + 16b + i16
+    // (each lane fetches the column scales its neighbours need).
+    float as_r[EPI == EPI_I32 ? 1 : FM], ws_c[EPI == EPI_I32 ? 1 : FN];
+    if constexpr (EPI != EPI_I32) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            const int m = m0 + wm * WM + a * 16 + i16;
+            as_r[a] = m < p.M ? p.act_scale[m * p.as_stride] : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const int n = n0 + wn * WN + b * 16 + i16;
+            ws_c[b] = n < p.N ? p.weight_scale[n * p.ws_stride] : 0.f;
+        }
+    }
 
     const int nk = (p.K + BK - 1) / BK;
 #pragma unroll
@@ -219,6 +253,7 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
         compute(kt % STAGES);
     }
 
+    // Complete row / column sums: add the four lane groups (k segments).
     if constexpr (ROWSUM) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
@@ -234,47 +269,87 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
         }
     }
 
-    const int row_base = m0 + wm * WM + 4 * g;
+    // With the operands swapped in the MFMA, register r of block (a, b) in
+    // lane (g, i) holds row 16a + i, column 16b + 4g + r of the wave's tile:
+    // four consecutive columns, stored as one vector.
     constexpr int OUT_BYTES = EPI == EPI_BF16 ? 2 : 4;
     char* out = reinterpret_cast<char*>(p.out) + (int64_t)bz * p.o_bstride * OUT_BYTES;
+    const bool vec_out = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
-        const int n = n0 + wn * WN + b * 16 + i16;
-        const bool n_ok = n < p.N;
-        float ws = 0.f;
-        uint32_t cbn = 0, add_n = 0;
+        const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
+        uint32_t add_n[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
+        float ws[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == EPI_I32) {
-            int32_t zb = 0;
-            if (p.b_zp != nullptr && n_ok) {
-                const int idx = n * p.b_zp_stride;
-                zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
-                               : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = nq + r;
+                int32_t zb = 0;
+                if (p.b_zp != nullptr && n < p.N) {
+                    const int idx = n * p.b_zp_stride;
+                    zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
+                                   : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
+                }
+                cbn[r] = (uint32_t)(p.sb - zb);
+                add_n[r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[r];
+                if constexpr (COLSUM) add_n[r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
             }
-            cbn = (uint32_t)(p.sb - zb);
-            add_n = (uint32_t)p.K * (uint32_t)p.ca * cbn;
-            if constexpr (COLSUM) add_n += (uint32_t)p.ca * (uint32_t)cs[b];
         } else {
-            if (n_ok) ws = p.weight_scale[n * p.ws_stride];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ws[r] = __shfl(ws_c[b], 4 * g + r);
         }
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
+            const int m = m0 + wm * WM + a * 16 + i16;
+            if (m >= p.M || nq >= p.N) continue;
+            const int64_t o = (int64_t)m * p.ldo + nq;
+            const bool full = nq + 4 <= p.N && vec_out;
+            if constexpr (EPI == EPI_I32) {
+                uint32_t y[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = row_base + a * 16 + r;
-                int rsum = 0;
-                if constexpr (ROWSUM) rsum = __shfl(rs[a], 4 * g + r);
-                if (!(n_ok && m < p.M)) continue;
-                const int64_t o = (int64_t)m * p.ldo + n;
-                if constexpr (EPI == EPI_I32) {
-                    uint32_t y = (uint32_t)acc[a][b][r] + add_n;
-                    if constexpr (ROWSUM) y += cbn * (uint32_t)rsum;
-                    reinterpret_cast<int32_t*>(out)[o] = (int32_t)y;
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = (uint32_t)acc[a][b][r] + add_n[r];
+                    if constexpr (ROWSUM) y[r] += cbn[r] * (uint32_t)rs[a];
+                }
+                int32_t* dst = reinterpret_cast<int32_t*>(out) + o;
+                if (full) {
+                    *reinterpret_cast<int4*>(dst) = make_int4((int)y[0], (int)y[1], (int)y[2], (int)y[3]);
                 } else {
-                    float f = (float)acc[a][b][r];
-                    f = f * p.act_scale[m * p.as_stride];
-                    f = f * ws;
-                    if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(out)[o] = f;
-                    else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(f);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (nq + r < p.N) dst[r] = (int32_t)y[r];
+                }
+            } else {
+                const float as = as_r[a];
+                float f[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f[r] = (float)acc[a][b][r];
+                    f[r] = f[r] * as;
+                    f[r] = f[r] * ws[r];
+                }
+                if constexpr (EPI == EPI_F32) {
+                    float* dst = reinterpret_cast<float*>(out) + o;
+                    if (full) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nq + r < p.N) dst[r] = f[r];
+                    }
+                } else {
+                    uint16_t h[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(f[r]);
+                    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+                    if (full) {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nq + r < p.N) dst[r] = h[r];
+                    }
                 }
             }
         }

@@ -29,6 +29,7 @@ struct Int8GemmArgs {
     // split-K workspace (skinny kernel): counters then int32 partials
     void* workspace;
     int splits;
+    int split_steps;   // skinny kernel: 64-row steps per split (multiple of 8)
 };
 
 // Tile shapes of the tiled kernel (four waves each).
@@ -53,6 +54,8 @@ hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStrea
                               const char** name);
 size_t skinny_workspace_bytes(int M, int N, int splits);
 int skinny_splits(int M, int N, int K);
+int skinny_split_steps(int N, int K);
+int skinny_splits_for(int N, int K, int split_steps);
 
 // W8A32: C = scale * (A @ W - zp * rowsum(A)) with fp32 matrix cores.
 struct W8A32Args {

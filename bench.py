@@ -11,10 +11,20 @@ that no call finds its inputs in the 256 MB Infinity Cache.
 
 Prints one JSON line.  Options: --gpus N (only 1 is supported: this build
 runs on one GPU), --steps K, --warmup W, --no-cpu-baseline, --only NAME.
+
+HBM traffic of the headline kernel comes from hardware counters taken by
+rocprofv3 (FETCH_SIZE, then WRITE_SIZE, each in its own run), scaled by what
+the same counters read for a plain copy of known size (--copy-calibration
+runs one).  --pmc-summary turns those four rocprofv3 databases into
+profiles/traffic.json, stamped with a hash of the library sources; the
+benchmark reports the traffic only while the sources still match.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
+import sqlite3
 import sys
 import time
 
@@ -26,6 +36,63 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0      # dense int8 matrix-core peak, tera-ops/s
 PEAK_FP32_TFLOPS = 157.3     # dense fp32 matrix-core peak
 PEAK_HBM_GBS = 8000.0        # HBM3E
+COPY_BYTES = 256 << 20       # size of the calibration copy
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash():
+    """sha256 over the library's kernel and host sources."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_int8_gemm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _pmc_avg(db_dir, counter, match):
+    """Average per dispatch of `counter` over kernels whose name contains `match`."""
+    dbs = glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True)
+    vals = []
+    for db in dbs:
+        c = sqlite3.connect(db)
+        for name, v in c.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                                 (counter,)):
+            if match in name:
+                vals.append(float(v))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {match!r} under {db_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(args):
+    """Write profiles/traffic.json from four rocprofv3 --pmc runs."""
+    fetch, nf = _pmc_avg(args.fetch_db, "FETCH_SIZE", args.kernel_match)
+    write, nw = _pmc_avg(args.write_db, "WRITE_SIZE", args.kernel_match)
+    cfetch, _ = _pmc_avg(args.copy_fetch_db, "FETCH_SIZE", "neg_kernel")
+    cwrite, _ = _pmc_avg(args.copy_write_db, "WRITE_SIZE", "neg_kernel")
+    f_scale = COPY_BYTES / (cfetch * 1024.0)
+    w_scale = COPY_BYTES / (cwrite * 1024.0)
+    traffic = fetch * 1024.0 * f_scale + write * 1024.0 * w_scale
+    out = {"kernel_match": args.kernel_match, "source_sha256": source_hash(),
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": [nf, nw],
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+           "fetch_scale": f_scale, "write_scale": w_scale, "traffic_bytes_per_dispatch": traffic,
+           "workload": "a8w8_prefill_8192x8192x8192_bf16"}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic():
+    """HBM bytes per launch from profiles/traffic.json, if the sources match."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    return t["traffic_bytes_per_dispatch"] if t.get("source_sha256") == source_hash() else None
 
 
 def parse():
@@ -35,6 +102,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="time one row only (prefill, decode, mmi, w8a32, small)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="write profiles/traffic.json from rocprofv3 databases")
+    ap.add_argument("--fetch-db")
+    ap.add_argument("--write-db")
+    ap.add_argument("--copy-fetch-db")
+    ap.add_argument("--copy-write-db")
+    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 128, false, 1, 0, 0>")
     return ap.parse_args()
 
 
@@ -56,6 +132,19 @@ def time_calls(fn, sets, steps, warmup, stream):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.copy_calibration:
+        # an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
+        import torch
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the kernels run on one GPU's share; see the sharding notes).", file=sys.stderr)
@@ -189,7 +278,7 @@ def main():
         tops = rows["a8w8_prefill_8192_bf16"]["TOPS"]
         line["roofline"] = {"kernel": rows["a8w8_prefill_8192_bf16"]["kernel"], "bound": "mfma",
                             "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                            "frac": tops / PEAK_INT8_TOPS, "traffic": None}
+                            "frac": tops / PEAK_INT8_TOPS, "traffic": measured_traffic()}
     line["cpu_baseline"] = cpu
     line["rows"] = rows
     print(json.dumps(line))

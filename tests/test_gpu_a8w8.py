@@ -1,5 +1,5 @@
 """A8W8 on the GPU against the oracle: bit-exact fp32 and bf16 outputs
-(the spec bar is 1 ulp; the fixed epilogue order makes them exact)."""
+(the stated bar is 1 ulp; the fixed epilogue order makes them exact)."""
 import numpy as np
 import pytest
 import torch

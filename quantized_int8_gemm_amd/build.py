@@ -20,8 +20,11 @@ SOURCES = [
     "int8_tiled_256x128.hip",
     "int8_tiled_128x128.hip",
     "int8_dma_256x256.hip",
-    "int8_dma_256x128.hip",
+    "int8_dma_256x128s3.hip",
     "int8_dma_128x128.hip",
+    "int8_dma_128x128s3.hip",
+    "int8_dma_256x256w8.hip",
+    "int8_dma_256x128w8.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
     "api.cpp",

@@ -43,15 +43,17 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && N >= 1 && K >= 1 && M < lim && N < lim && K < lim;
 }
 
-// Tile shape of the int8 tiled kernel for an (effective) problem shape:
-// the largest tile that still gives every compute unit work.
+// Tile configuration of the int8 GEMM for an (effective) problem shape:
+// large tiles when there are enough of them to fill the chip, smaller tiles
+// (several workgroups per compute unit) otherwise.  QGEMM_TILE forces one.
 int pick_tile(int64_t batch, int64_t M, int64_t N) {
     const int forced = env_int("QGEMM_TILE", -1);
     if (forced >= 0 && forced < qg::NUM_TILE_CFGS) return forced;
+    // 256x256 tiles (eight waves) once there are at least two full waves of
+    // them; measured best for 8192^3.  Otherwise 128x128 tiles, two
+    // workgroups per compute unit (best for 4096x2048x2048 and smaller).
     const int64_t t256 = batch * ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t256x128 = batch * ((M + 255) / 256) * ((N + 127) / 128);
-    if (t256 >= 512) return qg::TILE_256x256;
-    if (t256x128 >= 256) return qg::TILE_256x128;
+    if (t256 >= 512) return qg::TILE_256x256_W8;
     return qg::TILE_128x128;
 }
 
@@ -73,22 +75,30 @@ bool dma_ok(const qg::Int8GemmArgs& a, bool bkm, bool vec, int epi) {
 
 hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, int epi, int zp,
                         hipStream_t s, const char** name) {
-    static const char* staged_names[] = {"int8_staged_256x256", "int8_staged_256x128", "int8_staged_128x128"};
-    static const char* dma_names[] = {"int8_dma_256x256", "int8_dma_256x128", "int8_dma_128x128"};
+    static const char* dma_names[qg::NUM_TILE_CFGS] = {
+        "int8_dma_256x256", "int8_dma_256x128s3", "int8_dma_128x128",
+        "int8_dma_128x128s3", "int8_dma_256x256w8", "int8_dma_256x128w8"};
     if (dma_ok(a, bkm, vec, epi)) {
         *name = dma_names[cfg];
         switch (cfg) {
             case qg::TILE_256x256: return qg::launch_dma_256x256(a, bkm, epi, zp, s);
-            case qg::TILE_256x128: return qg::launch_dma_256x128(a, bkm, epi, zp, s);
-            default: return qg::launch_dma_128x128(a, bkm, epi, zp, s);
+            case qg::TILE_256x128_S3: return qg::launch_dma_256x128s3(a, bkm, epi, zp, s);
+            case qg::TILE_128x128: return qg::launch_dma_128x128(a, bkm, epi, zp, s);
+            case qg::TILE_128x128_S3: return qg::launch_dma_128x128s3(a, bkm, epi, zp, s);
+            case qg::TILE_256x256_W8: return qg::launch_dma_256x256w8(a, bkm, epi, zp, s);
+            default: return qg::launch_dma_256x128w8(a, bkm, epi, zp, s);
         }
     }
-    // The byte-wise (any alignment) variants exist for the 128x128 tile only.
-    if (!vec) cfg = qg::TILE_128x128;
-    *name = staged_names[cfg];
-    switch (cfg) {
-        case qg::TILE_256x256: return qg::launch_tiled_256x256(a, bkm, vec, epi, zp, s);
-        case qg::TILE_256x128: return qg::launch_tiled_256x128(a, bkm, vec, epi, zp, s);
+    // Register-staged kernel: the byte-wise (any alignment) variants exist
+    // for the 128x128 tile only.
+    int shape = cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 ? 0
+              : cfg == qg::TILE_256x128_S3 || cfg == qg::TILE_256x128_W8 ? 1 : 2;
+    if (!vec) shape = 2;
+    static const char* staged_names[] = {"int8_staged_256x256", "int8_staged_256x128", "int8_staged_128x128"};
+    *name = staged_names[shape];
+    switch (shape) {
+        case 0: return qg::launch_tiled_256x256(a, bkm, vec, epi, zp, s);
+        case 1: return qg::launch_tiled_256x128(a, bkm, vec, epi, zp, s);
         default: return qg::launch_tiled_128x128(a, bkm, vec, epi, zp, s);
     }
 }

@@ -1,0 +1,9 @@
+// Tile configuration 256x256w8 of the multi-stage int8 kernel: 256 x 256 output
+// tile, waves of 128 x 64, 4 LDS stages.
+#include "int8_dma_impl.h"
+
+namespace qg {
+hipError_t launch_dma_256x256w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
+    return dma::launch_shape<256, 256, 128, 64, 4>(a, bkm, epi, zp, s);
+}
+}  // namespace qg

@@ -39,7 +39,6 @@ namespace qg {
 namespace dma {
 
 constexpr int BK = 64;
-constexpr int STAGES = 4;
 constexpr int GROUP_M = 8;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -95,18 +94,20 @@ __device__ __forceinline__ int kn_slot(int r, int s) {
     return s ^ (r & 7) ^ (BN >= 256 ? (t << 3) : t);
 }
 
-template <int BM, int BN, int WM, int WN, bool B_KMAJOR, int EPI, int ZP, int FLIP>
-__global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
+template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(Int8GemmArgs p) {
+    constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    constexpr int ROUND = NT * 16;                  // bytes one load round moves
     constexpr int WAVES_N = BN / WN;
     constexpr int FM = WM / 16, FN = WN / 16;
     constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int A_ROUNDS = A_BYTES / 4096, B_ROUNDS = B_BYTES / 4096;
+    constexpr int A_ROUNDS = A_BYTES / ROUND, B_ROUNDS = B_BYTES / ROUND;
     constexpr int LOADS = A_ROUNDS + B_ROUNDS;      // per thread per chunk
     constexpr bool ROWSUM = (ZP & 1) != 0, COLSUM = (ZP & 2) != 0;
     constexpr bool FLIP_A = (FLIP & 1) != 0, FLIP_B = (FLIP & 2) != 0;
-    static_assert((BM / WM) * (BN / WN) == 4, "four waves");
-    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole load rounds");
+    static_assert(NT == 256 || NT == 512, "four or eight waves");
+    static_assert(A_BYTES % ROUND == 0 && B_BYTES % ROUND == 0, "whole load rounds");
     static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
@@ -130,18 +131,18 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
     // Per-lane global offsets (chunk 0) of each load round.  Round q of a
-    // stage covers LDS bytes [q*4096, q*4096 + 4096); this lane writes the 16
-    // bytes at q*4096 + wave*1024 + lane*16.
+    // stage covers LDS bytes [q*ROUND, (q+1)*ROUND); this lane writes the 16
+    // bytes at q*ROUND + wave*1024 + lane*16.
     uint32_t a_off[A_ROUNDS], b_off[B_ROUNDS];
 #pragma unroll
     for (int q = 0; q < A_ROUNDS; ++q) {
-        const int o = q * 4096 + wave * 1024 + lane * 16;
+        const int o = q * ROUND + wave * 1024 + lane * 16;
         const int r = o / BK, slot = (o % BK) / 16;
         a_off[q] = (uint32_t)(r * lda + 16 * kc_slot(r, slot));
     }
 #pragma unroll
     for (int q = 0; q < B_ROUNDS; ++q) {
-        const int o = q * 4096 + wave * 1024 + lane * 16;
+        const int o = q * ROUND + wave * 1024 + lane * 16;
         if constexpr (B_KMAJOR) {
             const int r = o / BK, slot = (o % BK) / 16;
             b_off[q] = (uint32_t)(r * ldb + 16 * kc_slot(r, slot));
@@ -155,10 +156,10 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
         const uint32_t sbase = lds0 + stage * STAGE + wave * 1024;
         const uint32_t ka = (uint32_t)(kt * BK);
 #pragma unroll
-        for (int q = 0; q < A_ROUNDS; ++q) dma16(a_rsrc, a_off[q] + ka, sbase + q * 4096);
+        for (int q = 0; q < A_ROUNDS; ++q) dma16(a_rsrc, a_off[q] + ka, sbase + q * ROUND);
         const uint32_t kb = B_KMAJOR ? ka : (uint32_t)(kt * BK * ldb);
 #pragma unroll
-        for (int q = 0; q < B_ROUNDS; ++q) dma16(b_rsrc, b_off[q] + kb, sbase + A_BYTES + q * 4096);
+        for (int q = 0; q < B_ROUNDS; ++q) dma16(b_rsrc, b_off[q] + kb, sbase + A_BYTES + q * ROUND);
     };
 
     v4i acc[FM][FN];
@@ -356,41 +357,41 @@ __global__ __launch_bounds__(256) void int8_dma_kernel(Int8GemmArgs p) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool BKM, int EPI, int ZP, int FLIP>
+template <int BM, int BN, int WM, int WN, int ST, bool BKM, int EPI, int ZP, int FLIP>
 hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, BKM, EPI, ZP, FLIP>), dim3(tiles, a.batch), dim3(256),
-                       0, s, a);
+    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, ST, BKM, EPI, ZP, FLIP>), dim3(tiles, a.batch),
+                       dim3((BM / WM) * (BN / WN) * 64), 0, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int ZP>
+template <int BM, int BN, int WM, int WN, int ST, int EPI, int ZP>
 hipError_t by_flip(const Int8GemmArgs& a, int flip, hipStream_t s) {
     switch (flip) {
-        case 0: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 0>(a, s);
-        case 1: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 1>(a, s);
-        case 2: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 2>(a, s);
-        default: return launch_one<BM, BN, WM, WN, false, EPI, ZP, 3>(a, s);
+        case 0: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 0>(a, s);
+        case 1: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 1>(a, s);
+        case 2: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 2>(a, s);
+        default: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 3>(a, s);
     }
 }
 
-// Every variant of one tile shape: A8W8 (fp32 / bf16 out, B as [K,N] or
-// [N,K]) and MatMulInteger (B as [K,N], any flips and sums).
-template <int BM, int BN, int WM, int WN>
+// Every variant of one tile configuration: A8W8 (fp32 / bf16 out, B as
+// [K,N] or [N,K]) and MatMulInteger (B as [K,N], any flips and sums).
+template <int BM, int BN, int WM, int WN, int ST>
 hipError_t launch_shape(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
     const int flip = (a.a_flip ? 1 : 0) | (a.b_flip ? 2 : 0);
     if (epi == EPI_I32) {
         switch (zp) {
-            case 0: return by_flip<BM, BN, WM, WN, EPI_I32, 0>(a, flip, s);
-            case 1: return by_flip<BM, BN, WM, WN, EPI_I32, 1>(a, flip, s);
-            case 2: return by_flip<BM, BN, WM, WN, EPI_I32, 2>(a, flip, s);
-            default: return by_flip<BM, BN, WM, WN, EPI_I32, 3>(a, flip, s);
+            case 0: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 0>(a, flip, s);
+            case 1: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 1>(a, flip, s);
+            case 2: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 2>(a, flip, s);
+            default: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 3>(a, flip, s);
         }
     }
-    if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, true, EPI_F32, 0, 0>(a, s)
-                                   : launch_one<BM, BN, WM, WN, true, EPI_BF16, 0, 0>(a, s);
-    return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, false, EPI_F32, 0, 0>(a, s)
-                          : launch_one<BM, BN, WM, WN, false, EPI_BF16, 0, 0>(a, s);
+    if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32, 0, 0>(a, s)
+                                   : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16, 0, 0>(a, s);
+    return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32, 0, 0>(a, s)
+                          : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16, 0, 0>(a, s);
 }
 
 }  // namespace dma

@@ -32,22 +32,33 @@ struct Int8GemmArgs {
     int split_steps;   // skinny kernel: 64-row steps per split (multiple of 8)
 };
 
-// Tile shapes of the tiled kernel (four waves each).
-enum TileCfg { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, NUM_TILE_CFGS = 3 };
+// Tile configurations of the int8 GEMM kernels.
+enum TileCfg {
+    TILE_256x256 = 0,     // four waves of 128x128, four LDS stages
+    TILE_256x128_S3 = 1,  // four waves of 128x64, three stages (two workgroups per CU)
+    TILE_128x128 = 2,     // four waves of 64x64, four stages (two workgroups per CU)
+    TILE_128x128_S3 = 3,  // four waves of 64x64, three stages (three workgroups per CU)
+    TILE_256x256_W8 = 4,  // eight waves of 128x64, four stages
+    TILE_256x128_W8 = 5,  // eight waves of 64x64, four stages
+    NUM_TILE_CFGS = 6
+};
 
-// Tiled kernel, one launcher per tile shape.  bkm: B is [N,K]; vec: 16-byte
-// vector loads allowed (only the 128x128 shape has byte-wise variants);
-// epi: Int8Epilogue; zp bit 0: row sums of A needed, bit 1: column sums of B.
+// Register-staged kernel, one launcher per tile shape.  bkm: B is [N,K];
+// vec: 16-byte vector loads allowed (only the 128x128 shape has byte-wise
+// variants); epi: Int8Epilogue; zp bit 0: row sums of A, bit 1: column sums.
 hipError_t launch_tiled_256x256(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 hipError_t launch_tiled_256x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 hipError_t launch_tiled_128x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 
 // Multi-stage kernel fed by direct global-to-LDS loads, one launcher per
-// tile shape.  Needs 16-byte aligned rows; K % 64 == 0 when an operand is
+// configuration.  Needs 16-byte aligned rows; K % 64 == 0 when an operand is
 // uint8 or a zero-point sum is taken, or when B is [N,K].
 hipError_t launch_dma_256x256(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
-hipError_t launch_dma_256x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x128s3(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_128x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_128x128s3(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x256w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x128w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,

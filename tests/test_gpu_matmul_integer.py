@@ -89,7 +89,7 @@ def test_matmul_integer_wraps_mod_2_32():
     assert (y == -1693967296).all()
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("tile", range(6))
 def test_matmul_integer_every_tile_shape(tile):
     case(f"matmul_integer tile {tile}")
     A, B, zb = si.matmul_integer_inputs(2, 300, 512, 640, seed=31 + tile)

@@ -110,13 +110,28 @@ def parse():
     ap.add_argument("--write-db")
     ap.add_argument("--copy-fetch-db")
     ap.add_argument("--copy-write-db")
-    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 128, false, 1, 0, 0>")
+    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 4, false, 1, 0, 0>")
     return ap.parse_args()
 
 
+SPIN_UP_S = 0.3
+
+
 def time_calls(fn, sets, steps, warmup, stream):
-    """Average milliseconds per call over `steps` calls, cycling `sets`."""
+    """Average milliseconds per call over `steps` calls, cycling `sets`.
+
+    Before the `warmup` calls the same call repeats, untimed, for SPIN_UP_S
+    seconds: an idle GPU needs a few hundred milliseconds of load before its
+    clocks settle, and a handful of 0.5 ms warm-up calls does not cover that
+    (the first timed block then reads about 20% slow)."""
     import torch
+    t_end = time.perf_counter() + SPIN_UP_S
+    i = 0
+    while time.perf_counter() < t_end:
+        fn(sets[i % len(sets)])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()

@@ -57,6 +57,15 @@ int pick_tile(int64_t batch, int64_t M, int64_t N) {
     return qg::TILE_128x128;
 }
 
+// Whether the multi-stage kernel writes its output tile through LDS in whole
+// rows (fewer, wider stores) or straight from the fragments (less latency).
+// QGEMM_STAGE=0/1 forces the choice.
+bool stage_output(int cfg, int64_t batch, int64_t M, int64_t N) {
+    const int forced = env_int("QGEMM_STAGE", -1);
+    if (forced >= 0) return forced != 0;
+    return cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8;
+}
+
 qg_status finish_launch(hipError_t e, const char* name) {
     if (e != hipSuccess) return QG_ERR_HIP;
     g_last_kernel = name;
@@ -80,13 +89,15 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
         "int8_dma_128x128s3", "int8_dma_256x256w8", "int8_dma_256x128w8"};
     if (dma_ok(a, bkm, vec, epi)) {
         *name = dma_names[cfg];
+        qg::Int8GemmArgs d = a;
+        d.stage_out = stage_output(cfg, a.batch, a.M, a.N) ? 1 : 0;
         switch (cfg) {
-            case qg::TILE_256x256: return qg::launch_dma_256x256(a, bkm, epi, zp, s);
-            case qg::TILE_256x128_S3: return qg::launch_dma_256x128s3(a, bkm, epi, zp, s);
-            case qg::TILE_128x128: return qg::launch_dma_128x128(a, bkm, epi, zp, s);
-            case qg::TILE_128x128_S3: return qg::launch_dma_128x128s3(a, bkm, epi, zp, s);
-            case qg::TILE_256x256_W8: return qg::launch_dma_256x256w8(a, bkm, epi, zp, s);
-            default: return qg::launch_dma_256x128w8(a, bkm, epi, zp, s);
+            case qg::TILE_256x256: return qg::launch_dma_256x256(d, bkm, epi, zp, s);
+            case qg::TILE_256x128_S3: return qg::launch_dma_256x128s3(d, bkm, epi, zp, s);
+            case qg::TILE_128x128: return qg::launch_dma_128x128(d, bkm, epi, zp, s);
+            case qg::TILE_128x128_S3: return qg::launch_dma_128x128s3(d, bkm, epi, zp, s);
+            case qg::TILE_256x256_W8: return qg::launch_dma_256x256w8(d, bkm, epi, zp, s);
+            default: return qg::launch_dma_256x128w8(d, bkm, epi, zp, s);
         }
     }
     // Register-staged kernel: the byte-wise (any alignment) variants exist

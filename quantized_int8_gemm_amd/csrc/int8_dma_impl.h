@@ -10,10 +10,10 @@
 //  * "feat(onnx-to-hip): lower quantized integer conv and matmul", "What":
 //    MatMulInteger, Y = sum_k (A - a_zp)(B - b_zp), int32 result, shared B.
 //
-// One workgroup (four waves) computes a BM x BN output tile, K in chunks of
-// 64 bytes held in a ring of four LDS stages:
-//  * Loads go global -> LDS directly (buffer_load_dwordx4 ... lds), three
-//    chunks ahead of the one being multiplied, so about three chunks of
+// One workgroup (four or eight waves) computes a BM x BN output tile, K in
+// chunks of 64 bytes held in a ring of STAGES LDS stages:
+//  * Loads go global -> LDS directly (buffer_load_dwordx4 ... lds), STAGES-1
+//    chunks ahead of the one being multiplied, so that many chunks of
 //    memory latency are covered and no register holds staged data.  Each
 //    lane's 16 bytes land at consecutive LDS addresses, so the lane picks the
 //    global segment whose swizzled home is that address.  Rows past M (A) or
@@ -27,7 +27,8 @@
 //  * v_mfma_i32_16x16x64_i8 accumulates; uint8 operands are shifted to int8
 //    by flipping bit 7 as fragments are read, and the row / column sums the
 //    MatMulInteger correction needs come from the same fragments.
-//  * Epilogue as in the register-staged kernel.
+//  * Epilogue as in the register-staged kernel, written out through LDS in
+//    whole rows.
 // This kernel needs K % 64 == 0 whenever an operand is flipped or a row or
 // column sum is taken (bytes past K are not cleared); the host routes other
 // shapes to the register-staged kernel.
@@ -272,15 +273,121 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 
     // With the operands swapped in the MFMA, register r of block (a, b) in
     // lane (g, i) holds row 16a + i, column 16b + 4g + r of the wave's tile:
-    // four consecutive columns, stored as one vector.
+    // four consecutive columns.  Stored straight to memory these leave as 32-
+    // or 64-byte pieces of rows; with stage_out set the finished values go
+    // through LDS (free once the last chunk is multiplied) and leave as whole
+    // rows, 16 bytes per lane.  Staging row pitch is BN outputs; the 16-byte chunk c of
+    // staged row r sits at chunk c ^ (r & 15), so the 16 rows one fragment
+    // store touches fall in distinct banks, and so do the chunks of a row read
+    // back.  A tile larger than the stage ring is staged in passes of whole
+    // wave rows.
     constexpr int OUT_BYTES = EPI == EPI_BF16 ? 2 : 4;
+    constexpr int ROW_BYTES = BN * OUT_BYTES;
+    constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
+    constexpr int PER_CHUNK = 16 / OUT_BYTES;        // outputs per chunk
+    constexpr int WAVES_M = BM / WM;
+    constexpr int PASSES = (BM * ROW_BYTES + STAGES * STAGE - 1) / (STAGES * STAGE);
+    static_assert(CPR >= 16, "staging swizzle spans 16 chunks");
+    static_assert(WAVES_M % PASSES == 0, "passes of whole wave rows");
+    constexpr int PASS_ROWS = BM / PASSES, PASS_WAVE_ROWS = WAVES_M / PASSES;
+    static_assert((PASS_ROWS * CPR) % NT == 0, "whole store rounds");
+    constexpr int STORE_ROUNDS = PASS_ROWS * CPR / NT;
+
     char* out = reinterpret_cast<char*>(p.out) + (int64_t)bz * p.o_bstride * OUT_BYTES;
-    const bool vec_out = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+    const bool vec_out = ((p.ldo * OUT_BYTES) % 16 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+
+    if (!p.stage_out) {
+        // Direct stores from the fragments (small grids, where the staging
+        // round trip costs more latency than the wider stores save).
+        const bool vec4 = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
+            uint32_t add_n[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
+            float ws[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI == EPI_I32) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = nq + r;
+                    int32_t zb = 0;
+                    if (p.b_zp != nullptr && n < p.N) {
+                        const int idx = n * p.b_zp_stride;
+                        zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
+                                       : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
+                    }
+                    cbn[r] = (uint32_t)(p.sb - zb);
+                    add_n[r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[r];
+                    if constexpr (COLSUM) add_n[r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ws[r] = __shfl(ws_c[b], 4 * g + r);
+            }
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                const int m = m0 + wm * WM + a * 16 + i16;
+                if (m >= p.M || nq >= p.N) continue;
+                const int64_t o = (int64_t)m * p.ldo + nq;
+                const bool full = nq + 4 <= p.N && vec4;
+                if constexpr (EPI == EPI_I32) {
+                    uint32_t y[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        y[r] = (uint32_t)acc[a][b][r] + add_n[r];
+                        if constexpr (ROWSUM) y[r] += cbn[r] * (uint32_t)rs[a];
+                    }
+                    int32_t* dst = reinterpret_cast<int32_t*>(out) + o;
+                    if (full) {
+                        *reinterpret_cast<int4*>(dst) = make_int4((int)y[0], (int)y[1], (int)y[2], (int)y[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nq + r < p.N) dst[r] = (int32_t)y[r];
+                    }
+                } else {
+                    const float as = as_r[a];
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        f[r] = (float)acc[a][b][r];
+                        f[r] = f[r] * as;
+                        f[r] = f[r] * ws[r];
+                    }
+                    if constexpr (EPI == EPI_F32) {
+                        float* dst = reinterpret_cast<float*>(out) + o;
+                        if (full) {
+                            *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (nq + r < p.N) dst[r] = f[r];
+                        }
+                    } else {
+                        uint16_t h[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(f[r]);
+                        uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+                        if (full) {
+                            *reinterpret_cast<uint2*>(dst) =
+                                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (nq + r < p.N) dst[r] = h[r];
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+
+    // Per-column epilogue terms for fragment column block b.
+    uint32_t add_n[FN][EPI == EPI_I32 ? 4 : 1], cbn[FN][EPI == EPI_I32 ? 4 : 1];
+    float ws[FN][EPI == EPI_I32 ? 1 : 4];
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
         const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
-        uint32_t add_n[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
-        float ws[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == EPI_I32) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -291,66 +398,84 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                     zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
                                    : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
                 }
-                cbn[r] = (uint32_t)(p.sb - zb);
-                add_n[r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[r];
-                if constexpr (COLSUM) add_n[r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
+                cbn[b][r] = (uint32_t)(p.sb - zb);
+                add_n[b][r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[b][r];
+                if constexpr (COLSUM) add_n[b][r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ws[r] = __shfl(ws_c[b], 4 * g + r);
+            for (int r = 0; r < 4; ++r) ws[b][r] = __shfl(ws_c[b], 4 * g + r);
         }
+    }
+
+    __syncthreads();   // every wave is done reading the stage ring
 #pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            const int m = m0 + wm * WM + a * 16 + i16;
-            if (m >= p.M || nq >= p.N) continue;
-            const int64_t o = (int64_t)m * p.ldo + nq;
-            const bool full = nq + 4 <= p.N && vec_out;
-            if constexpr (EPI == EPI_I32) {
-                uint32_t y[4];
+    for (int pass = 0; pass < PASSES; ++pass) {
+        if (pass > 0) __syncthreads();   // previous pass has been read back
+        if (wm / PASS_WAVE_ROWS == pass) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    y[r] = (uint32_t)acc[a][b][r] + add_n[r];
-                    if constexpr (ROWSUM) y[r] += cbn[r] * (uint32_t)rs[a];
+            for (int a = 0; a < FM; ++a) {
+                const int row = (wm % PASS_WAVE_ROWS) * WM + a * 16 + i16;
+                uint8_t* srow = smem + row * ROW_BYTES;
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int col = wn * WN + b * 16 + 4 * g;
+                    if constexpr (EPI == EPI_I32) {
+                        uint32_t y[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            y[r] = (uint32_t)acc[a][b][r] + add_n[b][r];
+                            if constexpr (ROWSUM) y[r] += cbn[b][r] * (uint32_t)rs[a];
+                        }
+                        const int c = col / 4;
+                        *reinterpret_cast<u32x4*>(srow + ((c ^ (row & 15)) << 4)) = u32x4{y[0], y[1], y[2], y[3]};
+                    } else {
+                        const float as = as_r[a];
+                        float f[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            f[r] = (float)acc[a][b][r];
+                            f[r] = f[r] * as;
+                            f[r] = f[r] * ws[b][r];
+                        }
+                        if constexpr (EPI == EPI_F32) {
+                            const int c = col / 4;
+                            *reinterpret_cast<u32x4*>(srow + ((c ^ (row & 15)) << 4)) =
+                                u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                                      __float_as_uint(f[3])};
+                        } else {
+                            const int c = col / 8, half = (col / 4) & 1;
+                            uint16_t h[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(f[r]);
+                            *reinterpret_cast<uint2*>(srow + ((c ^ (row & 15)) << 4) + 8 * half) =
+                                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                           (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                        }
+                    }
                 }
-                int32_t* dst = reinterpret_cast<int32_t*>(out) + o;
-                if (full) {
-                    *reinterpret_cast<int4*>(dst) = make_int4((int)y[0], (int)y[1], (int)y[2], (int)y[3]);
-                } else {
+            }
+        }
+        __syncthreads();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (nq + r < p.N) dst[r] = (int32_t)y[r];
-                }
+        for (int q = 0; q < STORE_ROUNDS; ++q) {
+            const int idx = q * NT + tid;
+            const int row = idx / CPR, c = idx % CPR;
+            const int m = m0 + pass * PASS_ROWS + row, n = n0 + c * PER_CHUNK;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * ROW_BYTES + ((c ^ (row & 15)) << 4));
+            if (m >= p.M || n >= p.N) continue;
+            char* dst = out + ((int64_t)m * p.ldo + n) * OUT_BYTES;
+            if (vec_out && n + PER_CHUNK <= p.N) {
+                *reinterpret_cast<u32x4*>(dst) = v;
             } else {
-                const float as = as_r[a];
-                float f[4];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    f[r] = (float)acc[a][b][r];
-                    f[r] = f[r] * as;
-                    f[r] = f[r] * ws[r];
-                }
-                if constexpr (EPI == EPI_F32) {
-                    float* dst = reinterpret_cast<float*>(out) + o;
-                    if (full) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (nq + r < p.N) dst[r] = f[r];
-                    }
-                } else {
-                    uint16_t h[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(f[r]);
-                    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
-                    if (full) {
-                        *reinterpret_cast<uint2*>(dst) =
-                            make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (nq + r < p.N) dst[r] = h[r];
-                    }
+                for (int e = 0; e < PER_CHUNK; ++e) {
+                    if (n + e >= p.N) break;
+                    if constexpr (OUT_BYTES == 4)
+                        reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+                    else
+                        reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e / 2] >> (16 * (e & 1)));
                 }
             }
         }

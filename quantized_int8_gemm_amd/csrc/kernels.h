@@ -30,6 +30,7 @@ struct Int8GemmArgs {
     void* workspace;
     int splits;
     int split_steps;   // skinny kernel: 64-row steps per split (multiple of 8)
+    int stage_out;     // tiled kernel: write the output tile through LDS in whole rows
 };
 
 // Tile configurations of the int8 GEMM kernels.

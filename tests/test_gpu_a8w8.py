@@ -170,12 +170,19 @@ def test_a8w8_repeatable():
         np.testing.assert_array_equal(run(A, W, s_a, s_w, torch.float32).cpu().numpy(), first)
 
 
+@pytest.mark.parametrize("stage", [0, 1])
 @pytest.mark.parametrize("tile", range(6))
-def test_a8w8_every_tile_shape(tile):
-    case(f"a8w8 tile cfg {tile} 520x700x1000")
-    A, W, s_a, s_w = si.a8w8_inputs(520, 768, 1024, seed=40 + tile)
-    with env(QGEMM_TILE=tile):
-        check(A, W, s_a, s_w, expect_kernel="int8_")
+def test_a8w8_every_tile_shape(tile, stage):
+    """Every tile configuration, with the output written straight from the
+    fragments (stage 0) and through LDS in whole rows (stage 1); ragged M and
+    N edges, and (B as [N,K], N = 700) an output row pitch that rules out
+    16-byte stores."""
+    case(f"a8w8 tile cfg {tile} stage {stage} 520x704x1024 and 300x700x512 b_trans")
+    A, W, s_a, s_w = si.a8w8_inputs(520, 704, 1024, seed=40 + tile)
+    A2, W2, s_a2, s_w2 = si.a8w8_inputs(300, 700, 512, seed=50 + tile)
+    with env(QGEMM_TILE=tile, QGEMM_STAGE=stage):
+        check(A, W, s_a, s_w, expect_kernel="int8_dma")
+        check(A2, np.ascontiguousarray(W2.T), s_a2, s_w2, b_trans=True, expect_kernel="int8_dma")
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 384, 320), (64, 128, 208)])

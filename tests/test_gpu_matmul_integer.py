@@ -89,12 +89,16 @@ def test_matmul_integer_wraps_mod_2_32():
     assert (y == -1693967296).all()
 
 
+@pytest.mark.parametrize("stage", [0, 1])
 @pytest.mark.parametrize("tile", range(6))
-def test_matmul_integer_every_tile_shape(tile):
-    case(f"matmul_integer tile {tile}")
-    A, B, zb = si.matmul_integer_inputs(2, 300, 512, 640, seed=31 + tile)
-    with env(QGEMM_TILE=tile):
+def test_matmul_integer_every_tile_shape(tile, stage):
+    """Every tile configuration, output straight from the fragments (stage 0)
+    or through LDS (stage 1), with ragged M and N edges."""
+    case(f"matmul_integer tile {tile} stage {stage} 2x300x528x640")
+    A, B, zb = si.matmul_integer_inputs(2, 300, 528, 640, seed=31 + tile)
+    with env(QGEMM_TILE=tile, QGEMM_STAGE=stage):
         y = q.matmul_integer(to_dev(A), to_dev(B), 100, to_dev(zb)).cpu().numpy()
+        assert q.last_kernel().startswith("int8_dma"), q.last_kernel()
     np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, 100, zb))
 
 

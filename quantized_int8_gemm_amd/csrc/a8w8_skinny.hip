@@ -159,45 +159,72 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
     consume(0);
     consume(1);
 
-    // Add the four waves' tiles through LDS in natural column order:
-    // register r of MFMA j holds row 4g + r, column 16*c16 + j.
+    // Add the four waves' tiles through LDS.  Register r of MFMA j holds
+    // row 4g + r, column 16*c16 + j, so for each r a lane owns 16 consecutive
+    // columns and writes them as four 16-byte chunks.  Chunk 4*c16 + q of a
+    // staged row sits at 4*c16 + (q ^ ((c16 >> 2) & 3)): the 16 lanes of a
+    // group then hit 16 distinct chunks of a 256-byte bank line.
     const int M = p.M;
+    auto chunk = [](int ch) { return (ch & ~3) | ((ch ^ (ch >> 4)) & 3); };
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int r = 0; r < 4; ++r) {
+        if (4 * g + r >= M) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * g + r < M) red[wave][4 * g + r][16 * c16 + j] = acc[j][r];
+        for (int q = 0; q < 4; ++q) {
+            const v4i v = v4i{acc[4 * q][r], acc[4 * q + 1][r], acc[4 * q + 2][r], acc[4 * q + 3][r]};
+            *reinterpret_cast<v4i*>(&red[wave][4 * g + r][4 * chunk(4 * c16 + q)]) = v;
+        }
+    }
     __syncthreads();
 
     // Items: (row m < M, group of 4 columns); each thread takes some.
     auto tile_sum = [&](int m, int cg) -> int4 {
-        int4 s = *reinterpret_cast<const int4*>(&red[0][m][cg * 4]);
+        const int at = 4 * chunk(cg);
+        int4 s = *reinterpret_cast<const int4*>(&red[0][m][at]);
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) {
-            const int4 v = *reinterpret_cast<const int4*>(&red[w][m][cg * 4]);
+            const int4 v = *reinterpret_cast<const int4*>(&red[w][m][at]);
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
         return s;
     };
-    auto epilogue = [&](int m, int n, int32_t v) {
+    // Output row m, columns n .. n+3 (those < N): scales, then one vector
+    // store when the four are in range and aligned.
+    const bool vec_out = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+    auto epilogue = [&](int m, int n, int4 v) {
         if (n >= p.N) return;
-        float f = (float)v;
-        f = f * as_rows[m];
-        f = f * ws_tile[n - n0];
+        const int32_t vi[4] = {v.x, v.y, v.z, v.w};
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = (float)vi[e];
+            f[e] = f[e] * as_rows[m];
+            f[e] = f[e] * ws_tile[(n - n0 + e) & (TN - 1)];
+        }
         const int64_t o = (int64_t)m * p.ldo + n;
-        if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(p.out)[o] = f;
-        else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(f);
+        if (vec_out && n + 4 <= p.N) {
+            if constexpr (EPI == EPI_F32) {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) = make_float4(f[0], f[1], f[2], f[3]);
+            } else {
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) =
+                    make_uint2((uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16),
+                               (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16));
+            }
+            return;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (n + e >= p.N) break;
+            if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(p.out)[o + e] = f[e];
+            else reinterpret_cast<uint16_t*>(p.out)[o + e] = f32_to_bf16_rne(f[e]);
+        }
     };
     const int items = M * (TN / 4);
 
     if (S == 1) {
         for (int it = tid; it < items; it += NT) {
             const int m = it / (TN / 4), cg = it % (TN / 4);
-            const int4 s = tile_sum(m, cg);
-            epilogue(m, n0 + cg * 4 + 0, s.x);
-            epilogue(m, n0 + cg * 4 + 1, s.y);
-            epilogue(m, n0 + cg * 4 + 2, s.z);
-            epilogue(m, n0 + cg * 4 + 3, s.w);
+            epilogue(m, n0 + cg * 4, tile_sum(m, cg));
         }
         return;
     }
@@ -230,19 +257,43 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
     if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
-    for (int it = tid; it < items; it += NT) {
+    // Each thread owns up to four (row, column group) items and keeps all of
+    // their partial loads in flight at once: SU splits per round, loads past
+    // split S - 1 fall outside the buffer range and read as zero.
+    constexpr int SU = 8, IPT = 16 * (TN / 4) / NT;   // items per thread at M = 16
+    static_assert(IPT * NT == 16 * (TN / 4), "whole items");
+    v4i sum[IPT];
+    uint32_t off[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it = tid + i * NT;
         const int m = it / (TN / 4), cg = it % (TN / 4);
-        v4i sum = v4i{0, 0, 0, 0};
-        for (int s = 0; s < S; ++s) {
-            const v4i v = __builtin_bit_cast(
-                v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, ((s * 16 + m) * TN + cg * 4) * 4, 0, COHERENT));
-            sum = v4i{(int)((uint32_t)sum.x + (uint32_t)v.x), (int)((uint32_t)sum.y + (uint32_t)v.y),
-                      (int)((uint32_t)sum.z + (uint32_t)v.z), (int)((uint32_t)sum.w + (uint32_t)v.w)};
-        }
-        epilogue(m, n0 + cg * 4 + 0, sum.x);
-        epilogue(m, n0 + cg * 4 + 1, sum.y);
-        epilogue(m, n0 + cg * 4 + 2, sum.z);
-        epilogue(m, n0 + cg * 4 + 3, sum.w);
+        sum[i] = v4i{0, 0, 0, 0};
+        // an item past M reads past the buffer (zeros) and is not stored
+        off[i] = it < items ? (uint32_t)((m * TN + cg * 4) * 4) : 0xFFFFFFF0u;
+    }
+    for (int s0 = 0; s0 < S; s0 += SU) {
+        v4i v[IPT][SU];
+#pragma unroll
+        for (int i = 0; i < IPT; ++i)
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const uint32_t o = off[i] == 0xFFFFFFF0u ? off[i] : off[i] + (uint32_t)((s0 + u) * 16 * TN * 4);
+                v[i][u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o, 0, COHERENT));
+            }
+#pragma unroll
+        for (int i = 0; i < IPT; ++i)
+#pragma unroll
+            for (int u = 0; u < SU; ++u)
+                sum[i] = v4i{(int)((uint32_t)sum[i].x + (uint32_t)v[i][u].x), (int)((uint32_t)sum[i].y + (uint32_t)v[i][u].y),
+                             (int)((uint32_t)sum[i].z + (uint32_t)v[i][u].z), (int)((uint32_t)sum[i].w + (uint32_t)v[i][u].w)};
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const int it = tid + i * NT;
+        if (it >= items) continue;
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        epilogue(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w});
     }
     if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

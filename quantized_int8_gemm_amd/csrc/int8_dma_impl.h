@@ -228,6 +228,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // the main loop: rows wm*WM + 16a + i16 and columns wn*WN + 16b + i16
     // (each lane fetches the column scales its neighbours need).
     float as_r[EPI == EPI_I32 ? 1 : FM], ws_c[EPI == EPI_I32 ? 1 : FN];
+    // MatMulInteger: cb for column wn*WN + 16b + i16 (sb - b_zp[n]), likewise.
+    int32_t cb_c[EPI == EPI_I32 ? FN : 1];
+    if constexpr (EPI == EPI_I32) {
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const int n = n0 + wn * WN + b * 16 + i16;
+            int32_t zb = 0;
+            if (p.b_zp != nullptr && n < p.N) {
+                const int idx = n * p.b_zp_stride;
+                zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
+                               : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
+            }
+            cb_c[b] = p.sb - zb;
+        }
+    }
     if constexpr (EPI != EPI_I32) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
@@ -276,7 +291,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // four consecutive columns.  Stored straight to memory these leave as 32-
     // or 64-byte pieces of rows; with stage_out set the finished values go
     // through LDS (free once the last chunk is multiplied) and leave as whole
-    // rows, 16 bytes per lane.  Staging row pitch is BN outputs; the 16-byte chunk c of
+    // rows, 16 bytes per lane.  The direct stores are non-temporal: small
+    // grids finish all their tiles at once, and an output left in L2 would be
+    // written back in one burst when the kernel ends (MatMulInteger
+    // 4096x2048x2048: 32 -> 25 us).  The staged path serves large grids whose
+    // earlier tiles' lines leave L2 long before the end; there plain stores
+    // measured 1% faster.  Staging row pitch is BN outputs; the 16-byte chunk c of
     // staged row r sits at chunk c ^ (r & 15), so the 16 rows one fragment
     // store touches fall in distinct banks, and so do the chunks of a row read
     // back.  A tile larger than the stage ring is staged in passes of whole
@@ -308,14 +328,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             if constexpr (EPI == EPI_I32) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = nq + r;
-                    int32_t zb = 0;
-                    if (p.b_zp != nullptr && n < p.N) {
-                        const int idx = n * p.b_zp_stride;
-                        zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
-                                       : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
-                    }
-                    cbn[r] = (uint32_t)(p.sb - zb);
+                    cbn[r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
                     add_n[r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[r];
                     if constexpr (COLSUM) add_n[r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
                 }
@@ -338,7 +351,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                     }
                     int32_t* dst = reinterpret_cast<int32_t*>(out) + o;
                     if (full) {
-                        *reinterpret_cast<int4*>(dst) = make_int4((int)y[0], (int)y[1], (int)y[2], (int)y[3]);
+                        __builtin_nontemporal_store(v4i{(int)y[0], (int)y[1], (int)y[2], (int)y[3]}, reinterpret_cast<v4i*>(dst));
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
@@ -356,7 +369,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                     if constexpr (EPI == EPI_F32) {
                         float* dst = reinterpret_cast<float*>(out) + o;
                         if (full) {
-                            *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+                            __builtin_nontemporal_store(v4f{f[0], f[1], f[2], f[3]}, reinterpret_cast<v4f*>(dst));
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -368,8 +381,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                         for (int r = 0; r < 4; ++r) h[r] = f32_to_bf16_rne(f[r]);
                         uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
                         if (full) {
-                            *reinterpret_cast<uint2*>(dst) =
-                                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                            __builtin_nontemporal_store(
+                                v2i{(int)((uint32_t)h[0] | ((uint32_t)h[1] << 16)), (int)((uint32_t)h[2] | ((uint32_t)h[3] << 16))},
+                                reinterpret_cast<v2i*>(dst));
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
@@ -387,18 +401,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     float ws[FN][EPI == EPI_I32 ? 1 : 4];
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
-        const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
+        // this lane's four columns are wn*WN + 16b + 4g + r
         if constexpr (EPI == EPI_I32) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int n = nq + r;
-                int32_t zb = 0;
-                if (p.b_zp != nullptr && n < p.N) {
-                    const int idx = n * p.b_zp_stride;
-                    zb = p.b_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.b_zp)[idx]
-                                   : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
-                }
-                cbn[b][r] = (uint32_t)(p.sb - zb);
+                cbn[b][r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
                 add_n[b][r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[b][r];
                 if constexpr (COLSUM) add_n[b][r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
             }

@@ -9,6 +9,11 @@ K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
 that no call finds its inputs in the 256 MB Infinity Cache.
 
+"ceilings" holds what this machine reaches on a streaming read of 1 GiB and
+on an int8 matrix-core loop with random and with all-one operands (the
+library's calibration kernels); each row also reports its fraction of the
+matching measured ceiling beside the fraction of the spec peak.
+
 Prints one JSON line.  Options: --gpus N (only 1 is supported: this build
 runs on one GPU), --steps K, --warmup W, --no-cpu-baseline, --only NAME.
 
@@ -37,6 +42,8 @@ PEAK_INT8_TOPS = 5000.0      # dense int8 matrix-core peak, tera-ops/s
 PEAK_FP32_TFLOPS = 157.3     # dense fp32 matrix-core peak
 PEAK_HBM_GBS = 8000.0        # HBM3E
 COPY_BYTES = 256 << 20       # size of the calibration copy
+CEIL_READ_BYTES = 1 << 30    # streaming-read ceiling: 1 GiB, four times the Infinity Cache
+CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops per launch
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -101,7 +108,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None, help="time one row only (prefill, decode, mmi, w8a32, small)")
+    ap.add_argument("--only", default=None,
+                    help="time one row only (prefill, decode, mmi, w8a32, small, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -256,6 +264,29 @@ def main():
         ms = time_calls(lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o), [None], 100, 10, stream)
         rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
 
+    # ---- measured ceilings: streaming read, int8 matrix-core loop -------
+    ceilings = None
+    if args.only is None or args.only == "ceilings":
+        buf = torch.randint(0, 256, (CEIL_READ_BYTES,), dtype=torch.uint8, device=dev)
+        ms = time_calls(lambda s: q.calib_read(buf), [None], steps, warmup, stream)
+        hbm = CEIL_READ_BYTES / (ms * 1e-3) / 1e9
+        del buf
+        g = si.rng(7)
+        rnd = to(si.randint(g, (4096,), -128, 127, np.int8))
+        ones = torch.ones(4096, dtype=torch.int8, device=dev)
+        mf = {}
+        for name, opnd in (("random", rnd), ("ones", ones)):
+            nops = q.calib_mfma_i8(opnd, CEIL_MFMA_ROUNDS)
+            ms = time_calls(lambda s, o=opnd: q.calib_mfma_i8(o, CEIL_MFMA_ROUNDS), [None], steps, warmup, stream)
+            mf[name] = nops / (ms * 1e-3) / 1e12
+        ceilings = {"hbm_read_GBs": hbm, "mfma_i8_random_TOPS": mf["random"], "mfma_i8_ones_TOPS": mf["ones"],
+                    "note": "streaming read of 1 GiB; int8 matrix-core loop on random / all-one operands"}
+        for name, r in rows.items():
+            if "GB/s" in r and "frac_hbm_peak" in r and name.startswith("a8w8_decode"):
+                r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm
+            if "TOPS" in r:
+                r["frac_mfma_random_ceiling"] = r["TOPS"] / mf["random"]
+
     # ---- CPU baseline: the oracle on a bounded sample of the headline ----
     cpu = None
     if not args.no_cpu_baseline and want("prefill"):
@@ -294,6 +325,10 @@ def main():
         line["roofline"] = {"kernel": rows["a8w8_prefill_8192_bf16"]["kernel"], "bound": "mfma",
                             "achieved": tops, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                             "frac": tops / PEAK_INT8_TOPS, "traffic": measured_traffic()}
+        if ceilings is not None:
+            line["roofline"]["measured_ceiling"] = ceilings["mfma_i8_random_TOPS"]
+            line["roofline"]["frac_measured_ceiling"] = tops / ceilings["mfma_i8_random_TOPS"]
+    line["ceilings"] = ceilings
     line["cpu_baseline"] = cpu
     line["rows"] = rows
     print(json.dumps(line))

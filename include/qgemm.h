@@ -160,6 +160,29 @@ const char* qgemm_last_kernel(void);
 /* Library version string. */
 const char* qgemm_version(void);
 
+/*
+ * Calibration (diagnostics for the roofline figures; no part of the
+ * quantised matmuls).  They measure the ceilings the kernels above are held
+ * to on the machine at hand.  Both write QG_CALIB_SINK_WORDS uint32 words to
+ * the device buffer `sink` (only so that the work is kept) and are
+ * asynchronous on `stream`.
+ *
+ * qgemm_calib_read: reads `bytes` bytes of device memory at `buf` once,
+ *   16-byte vectors with a grid stride.  buf 16-byte aligned, bytes a
+ *   positive multiple of 16; otherwise QG_ERR_INVALID_ARGUMENT.
+ * qgemm_calib_mfma_i8: runs `iters` (1 .. 2^20) rounds of int8 matrix-core
+ *   multiplies (v_mfma_i32_16x16x64_i8, 16 independent per wave per round)
+ *   on operands read once from `operands`, a device buffer of 4096 bytes;
+ *   the operand bytes set how much the data paths toggle and hence the clock
+ *   the chip holds.  *ops_out (host) receives the int8 operations performed
+ *   (2 per multiply-add): QG_CALIB_MFMA_OPS_PER_ROUND * iters.
+ */
+#define QG_CALIB_SINK_WORDS 8192
+#define QG_CALIB_MFMA_OPS_PER_ROUND 4294967296LL
+qg_status qgemm_calib_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, void* stream,
+                              int64_t* ops_out);
+
 #ifdef __cplusplus
 }
 #endif

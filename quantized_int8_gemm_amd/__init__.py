@@ -10,6 +10,9 @@ this package is its thin Python binding, with the same call names:
   fp32 or bf16 output.
 * ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
   MatMulInteger, int32 output, shared weight never copied.
+
+``calib_read`` and ``calib_mfma_i8`` measure the machine's HBM read and int8
+matrix-core ceilings for the roofline figures.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
@@ -17,6 +20,8 @@ from ._binding import (  # noqa: F401
     QG_OP_MATMUL_INTEGER,
     QG_OP_W8A32,
     QGemmError,
+    calib_mfma_i8,
+    calib_read,
     last_kernel,
     matmul_integer,
     qgemm_a8w8,

@@ -33,7 +33,10 @@ PROTOTYPES = {
     "qgemm_status_string": ([_int], ctypes.c_char_p),
     "qgemm_last_kernel": ([], ctypes.c_char_p),
     "qgemm_version": ([], ctypes.c_char_p),
+    "qgemm_calib_read": ([_p, _sz, _p, _p], _int),
+    "qgemm_calib_mfma_i8": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
 }
+QG_CALIB_SINK_WORDS = 8192
 
 
 def _load():
@@ -306,3 +309,43 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
                             _ptr(out), N, M * N, None, 0, _stream(dev))
     _check(st, "matmul_integer")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Calibration (roofline ceilings; no part of the matmuls)
+# ---------------------------------------------------------------------------
+
+def _sink(dev, sink):
+    if sink is None:
+        return torch.empty(QG_CALIB_SINK_WORDS, dtype=torch.int32, device=dev)
+    _need(sink, (torch.int32,), "sink")
+    if sink.numel() < QG_CALIB_SINK_WORDS or not sink.is_contiguous():
+        raise ValueError(f"sink must be a contiguous int32 tensor of >= {QG_CALIB_SINK_WORDS} words")
+    return sink
+
+
+def calib_read(buf, sink=None):
+    """Read every byte of the contiguous GPU tensor `buf` once (a streaming
+    read for the HBM ceiling).  Returns the sink tensor."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor")
+    dev = _on_gpu(buf)
+    sink = _sink(dev, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.qgemm_calib_read(_ptr(buf), nbytes, _ptr(sink), _stream(dev)), "qgemm_calib_read")
+    return sink
+
+
+def calib_mfma_i8(operands, iters, sink=None):
+    """Run `iters` rounds of int8 matrix-core multiplies on the 4096 operand
+    bytes in `operands` (an int8 or uint8 GPU tensor).  Returns the number of
+    int8 operations the launch performs."""
+    _need(operands, (torch.int8, torch.uint8), "operands")
+    if operands.numel() != 4096 or not operands.is_contiguous():
+        raise ValueError("operands must be 4096 contiguous bytes")
+    dev = _on_gpu(operands)
+    sink = _sink(dev, sink)
+    ops = ctypes.c_int64(0)
+    _check(lib.qgemm_calib_mfma_i8(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(ops)),
+           "qgemm_calib_mfma_i8")
+    return int(ops.value)

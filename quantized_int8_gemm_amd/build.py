@@ -27,6 +27,7 @@ SOURCES = [
     "int8_dma_256x128w8.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
+    "calibrate.hip",
     "api.cpp",
 ]
 

@@ -120,6 +120,26 @@ extern "C" {
 
 const char* qgemm_version(void) { return "qgemm 0.1 (gfx950)"; }
 
+qg_status qgemm_calib_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    static_assert(qg::CALIB_READ_BLOCKS * 4 == QG_CALIB_SINK_WORDS, "sink size");
+    if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
+        (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+        return QG_ERR_INVALID_ARGUMENT;
+    (void)hipGetLastError();
+    return finish_launch(qg::launch_calib_read(buf, bytes, sink, (hipStream_t)stream), "calib_read");
+}
+
+qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, void* stream,
+                              int64_t* ops_out) {
+    static_assert(qg::CALIB_MFMA_BLOCKS * 4 == QG_CALIB_SINK_WORDS, "sink size");
+    static_assert((int64_t)qg::CALIB_MFMA_BLOCKS * 4 * 16 * 32768 == QG_CALIB_MFMA_OPS_PER_ROUND, "ops");
+    if (operands == nullptr || sink == nullptr || iters < 1 || iters > (1 << 20) || ops_out == nullptr)
+        return QG_ERR_INVALID_ARGUMENT;
+    *ops_out = QG_CALIB_MFMA_OPS_PER_ROUND * (int64_t)iters;
+    (void)hipGetLastError();
+    return finish_launch(qg::launch_calib_mfma(operands, iters, sink, (hipStream_t)stream), "calib_mfma_i8");
+}
+
 const char* qgemm_last_kernel(void) { return g_last_kernel; }
 
 const char* qgemm_status_string(qg_status s) {

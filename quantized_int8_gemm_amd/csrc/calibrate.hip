@@ -1,0 +1,77 @@
+// Calibration kernels for the roofline figures: a streaming read and a
+// matrix-core loop.  They implement no part of the quantised matmuls; they
+// measure, on the machine at hand, the ceilings those kernels are held to
+// (HBM read bandwidth for the decode kernel, int8 matrix-core rate under
+// data-dependent clocks for the tiled kernel).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qg {
+namespace {
+
+constexpr int CAL_NT = 256;
+
+// Each thread reads 16-byte vectors with a grid stride, four in flight, and
+// xors them; one word per wave goes to `sink` so the reads are kept.
+__global__ __launch_bounds__(CAL_NT) void calib_read_kernel(const u32x4* __restrict__ p, size_t n_vec, uint32_t* sink) {
+    size_t i = (size_t)blockIdx.x * CAL_NT + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * CAL_NT;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n_vec; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n_vec; i += stride) {
+        const u32x4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = acc;
+}
+
+// Each wave runs `iters` rounds of 16 independent v_mfma_i32_16x16x64_i8 on
+// operands taken from `ops` (256 16-byte vectors); no memory traffic in the
+// loop.  The operand bytes decide how much the data paths toggle, and with
+// that the clock the chip can hold.
+__global__ __launch_bounds__(CAL_NT) void calib_mfma_kernel(const u32x4* __restrict__ ops, int iters, uint32_t* sink) {
+    const int l = threadIdx.x & 63;
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = ops[(l + 64 * i) & 255];
+        b[i] = ops[(l + 64 * i + 7) & 255];
+    }
+    v4i acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4i{0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = mfma_i8_16x16x64(a[i & 3], b[i >> 2], acc[i]);
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s ^= (uint32_t)(acc[i].x ^ acc[i].y ^ acc[i].z ^ acc[i].w);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s ^= (uint32_t)__shfl_xor((int)s, o);
+    if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(calib_read_kernel, dim3(CALIB_READ_BLOCKS), dim3(CAL_NT), 0, s,
+                       reinterpret_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_mfma(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(calib_mfma_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
+                       reinterpret_cast<const u32x4*>(ops), iters, sink);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -80,4 +80,11 @@ struct W8A32Args {
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, hipStream_t s,
                         const char** name);
 
+// Calibration kernels (roofline ceilings; no part of the method).  Each
+// writes one word per wave: CALIB_*_BLOCKS * 4 words of sink.
+constexpr int CALIB_READ_BLOCKS = 2048;
+constexpr int CALIB_MFMA_BLOCKS = 2048;
+hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_calib_mfma(const void* ops, int iters, uint32_t* sink, hipStream_t s);
+
 }  // namespace qg

@@ -24,7 +24,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
-                          "qgemm_status_string", "qgemm_last_kernel", "qgemm_version"}
+                          "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
+                          "qgemm_calib_read", "qgemm_calib_mfma_i8"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -171,3 +172,17 @@ def test_binding_requires_gpu_tensors():
     W = torch.zeros(8, 4, dtype=torch.int8)
     with pytest.raises(ValueError):
         q.qgemm_a8w8(A, W, torch.ones(4), torch.ones(4))
+
+
+def test_calibration_rejects_bad_arguments():
+    lib = b.lib
+    ops = ctypes.c_int64(0)
+    assert lib.qgemm_calib_read(None, 4096, FAKE, None) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_read(FAKE, 0, FAKE, None) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_read(FAKE, 4100, FAKE, None) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_read(ctypes.c_void_p(4104), 4096, FAKE, None) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_read(FAKE, 4096, None, None) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_mfma_i8(FAKE, 0, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_mfma_i8(FAKE, (1 << 20) + 1, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_mfma_i8(None, 10, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
+    assert lib.qgemm_calib_mfma_i8(FAKE, 10, FAKE, None, None) == b.QG_ERR_INVALID_ARGUMENT

@@ -1,0 +1,37 @@
+"""The calibration kernels behind the measured ceilings: the streaming read
+touches every byte (the xor of its per-wave words equals the xor of the
+buffer's words), and the matrix-core loop reports the operation count the
+header states."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_int8_gemm_amd as q
+import seeded_inputs as si
+from gpu_util import case, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (3 << 20) + 48])
+def test_calib_read_touches_every_word(nbytes):
+    case(f"calib_read {nbytes} bytes")
+    g = si.rng(nbytes)
+    host = si.randint(g, (nbytes // 4,), 0, 2**31 - 1, np.int64).astype(np.uint32)
+    buf = to_dev(host.view(np.int32))
+    sink = q.calib_read(buf)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
+
+
+def test_calib_mfma_counts_ops():
+    case("calib_mfma_i8 3 rounds")
+    ops = torch.ones(4096, dtype=torch.int8, device=dev())
+    n = q.calib_mfma_i8(ops, 3)
+    torch.cuda.synchronize()
+    assert n == 3 * 4294967296
+
+
+def test_calib_rejects_bad_operands():
+    with pytest.raises(ValueError):
+        q.calib_mfma_i8(torch.ones(100, dtype=torch.int8, device=dev()), 3)

@@ -57,6 +57,14 @@ def _load():
     lib.oracle_a8w8_at.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int,
                                    _p, _i64, _p, _i64, _i64, _p, _p, _p, _p, _p]
     lib.oracle_a8w8_at.restype = None
+    lib.oracle_a8w8_acc.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64,
+                                    _p, _i64, _p, _i64, _p, _p, _p]
+    lib.oracle_a8w8_acc.restype = None
+    lib.oracle_matmul_integer_rows.argtypes = [_i64, _i64, _i64, _i64,
+                                               _p, _int, _i64, _i64,
+                                               _p, _int, _i64, _i64,
+                                               _p, _i64, _p, _i64, _p, _i64, _i64]
+    lib.oracle_matmul_integer_rows.restype = None
     lib.oracle_matmul_integer.argtypes = [_i64, _i64, _i64, _i64,
                                           _p, _int, _i64, _i64,
                                           _p, _int, _i64, _i64,
@@ -182,6 +190,26 @@ def a8w8_at(A, W, act_scale, weight_scale, rows, cols, b_trans=False):
     return {"acc": acc, "f32": f, "bf16": h}
 
 
+def a8w8_acc(acc_in, A, W, act_scale, weight_scale, b_trans=False):
+    """A8W8 with an int32 accumulator input: the int8 product is added to
+    acc_in (int32 [M,N], wrapping) before the cast and the two scales.
+    Returns dict(acc=int32, f32=float32, bf16=uint16 bits), each [M,N]."""
+    lib = _load()
+    A = _c(A, np.int8)
+    W = _c(W, np.int8)
+    M, K = A.shape
+    N = W.shape[0] if b_trans else W.shape[1]
+    acc_in = _c(acc_in, np.int32)
+    assert acc_in.shape == (M, N)
+    a, w = _scales(act_scale, weight_scale, M, N)
+    acc = np.empty((M, N), dtype=np.int32)
+    f = np.empty((M, N), dtype=np.float32)
+    h = np.empty((M, N), dtype=np.uint16)
+    lib.oracle_a8w8_acc(M, N, K, _ptr(A), K, _ptr(W), W.shape[1], int(bool(b_trans)),
+                        _ptr(acc_in), N, _ptr(a), a.size, _ptr(w), w.size, _ptr(acc), _ptr(f), _ptr(h))
+    return {"acc": acc, "f32": f, "bf16": h}
+
+
 # ---------------------------------------------------------------------------
 # MatMulInteger
 # ---------------------------------------------------------------------------
@@ -208,8 +236,9 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None):
     A: uint8/int8 of rank 2-4, [..., M, K]; B: uint8/int8 [..., K, N] of rank
     2-4.  Batch dimensions broadcast as in numpy matmul; a size-1 batch of A
     is repeated, and a rank-2 B (or one whose batch dimensions are all 1) is
-    one matrix shared by every batch.  a_zero_point: scalar; b_zero_point:
-    None, a scalar, or N per-column values ([N] or [1, N]).
+    one matrix shared by every batch.  a_zero_point: a scalar, or M per-row
+    values ([M] or [M, 1]); b_zero_point: None, a scalar, or N per-column
+    values ([N] or [1, N]).
     Returns int32 [*batch, M, N].
     """
     lib = _load()
@@ -233,6 +262,18 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None):
         b_bstride = K * N
     zb, zb_len = _b_zero_points(b_zero_point, N)
     Y = np.empty((nb, M, N), dtype=np.int32)
+    za = np.asarray(a_zero_point)
+    if za.size > 1 or za.ndim > 0:
+        # one zero point per row of A: [M] or [M, 1]
+        za = _c(za.astype(np.int64).reshape(-1), np.int32)
+        if za.size not in (1, M):
+            raise ValueError("a_zero_point has 1 or M values")
+        lib.oracle_matmul_integer_rows(nb, M, N, K,
+                                       _ptr(A3), _is_u8(A3), K, M * K,
+                                       _ptr(B3), _is_u8(B3), N, b_bstride,
+                                       _ptr(za), za.size, _ptr(zb), zb_len,
+                                       _ptr(Y), N, M * N)
+        return Y.reshape(batch_shape + (M, N))
     lib.oracle_matmul_integer(nb, M, N, K,
                               _ptr(A3), _is_u8(A3), K, M * K,
                               _ptr(B3), _is_u8(B3), N, b_bstride,

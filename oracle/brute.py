@@ -30,6 +30,30 @@ def matmul_integer(A, B, za, zb):
              for n in range(N)] for m in range(M)]
 
 
+def matmul_integer_rows(A, B, za, zb):
+    """Exact sum_k (A[m][k]-za[m])(B[k][n]-zb[n]) as Python ints (no wrap)."""
+    M, K, N = len(A), len(B), len(B[0])
+    return [[sum((A[m][k] - za[m]) * (B[k][n] - zb[n]) for k in range(K))
+             for n in range(N)] for m in range(M)]
+
+
+def a8w8_acc(acc_in, A, W, act_scale, weight_scale):
+    """A8W8 with an int32 accumulator input, each step exact or emulated
+    fp32: acc = wrap32(acc_in + sum_k A W), then int -> fp32, *as, *ws."""
+    M, K, N = len(A), len(W), len(W[0])
+    out = []
+    for m in range(M):
+        row = []
+        for n in range(N):
+            acc = wrap32(acc_in[m][n] + sum(A[m][k] * W[k][n] for k in range(K)))
+            f = f32(float(acc))
+            f = f32(f * act_scale[m])
+            f = f32(f * weight_scale[n])
+            row.append((acc, f))
+        out.append(row)
+    return out
+
+
 def a8w8(A, W, act_scale, weight_scale):
     """A8W8 with each fp32 step emulated exactly: int -> fp32, *as, *ws.
 

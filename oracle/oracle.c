@@ -172,6 +172,42 @@ void oracle_a8w8_at(int64_t M, int64_t N, int64_t K,
     }
 }
 
+/* A8W8 with an int32 accumulator input ([P2] "Summary" and "What Changed":
+ * the matmul-dequant-acc op takes an INT32 accumulator input and lowers to
+ * tile.matmul_acc / tile.gemv_acc, which add the int8 product into that
+ * accumulator, followed by the same cast and scale chain):
+ *   acc[m,n] = wrap32(acc_in[m,n] + sum_k A[m,k] W[k,n])
+ * then the a8w8 epilogue.  acc_in is [M,N] with row stride ld_acc. */
+void oracle_a8w8_acc(int64_t M, int64_t N, int64_t K,
+                     const int8_t* A, int64_t lda,
+                     const int8_t* W, int64_t ldw, int b_trans,
+                     const int32_t* acc_in, int64_t ld_acc,
+                     const float* act_scale, int64_t as_len,
+                     const float* weight_scale, int64_t ws_len,
+                     int32_t* acc_out, float* out_f32, uint16_t* out_bf16) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+        for (int64_t n = 0; n < N; ++n) row[n] = acc_in[m * ld_acc + n];
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t a = A[m * lda + k];
+            for (int64_t n = 0; n < N; ++n) {
+                int64_t b = b_trans ? W[n * ldw + k] : W[k * ldw + n];
+                row[n] += a * b;
+            }
+        }
+        float as = act_scale[as_len == 1 ? 0 : m];
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t acc = wrap_i32(row[n]);
+            float f = a8w8_epilogue(acc, as, weight_scale[ws_len == 1 ? 0 : n]);
+            if (acc_out) acc_out[m * N + n] = acc;
+            if (out_f32) out_f32[m * N + n] = f;
+            if (out_bf16) out_bf16[m * N + n] = oracle_f32_to_bf16(f);
+        }
+        free(row);
+    }
+}
+
 /* ---------------------------------------------------------------------- */
 /* MatMulInteger ([P5])                                                    */
 /* ---------------------------------------------------------------------- */
@@ -198,6 +234,37 @@ void oracle_matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K,
             int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
             for (int64_t k = 0; k < K; ++k) {
                 int64_t a = load_8bit(A, a_is_u8, bt * a_bstride + m * lda + k) - a_zp;
+                for (int64_t n = 0; n < N; ++n) {
+                    int64_t zb = b_zp ? b_zp[b_zp_len == 1 ? 0 : n] : 0;
+                    int64_t b = load_8bit(B, b_is_u8, bt * b_bstride + k * ldb + n) - zb;
+                    row[n] += a * b;
+                }
+            }
+            for (int64_t n = 0; n < N; ++n)
+                Y[bt * y_bstride + m * ldy + n] = wrap_i32(row[n]);
+            free(row);
+        }
+    }
+}
+
+/* MatMulInteger with one activation zero point per row ([P5] "What": a
+ * per-row zero point is accepted when M is static; it is the value
+ * subtracted from every element of that row of A, in every batch):
+ *   Y[b,m,n] = wrap32( sum_k (A[b,m,k] - a_zp[m]) * (B[b',k,n] - zb[n]) )
+ * a_zp has a_zp_len == 1 or M entries. */
+void oracle_matmul_integer_rows(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                const void* A, int a_is_u8, int64_t lda, int64_t a_bstride,
+                                const void* B, int b_is_u8, int64_t ldb, int64_t b_bstride,
+                                const int32_t* a_zp, int64_t a_zp_len,
+                                const int32_t* b_zp, int64_t b_zp_len,
+                                int32_t* Y, int64_t ldy, int64_t y_bstride) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bt = 0; bt < batch; ++bt) {
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+            const int64_t za = a_zp[a_zp_len == 1 ? 0 : m];
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t a = load_8bit(A, a_is_u8, bt * a_bstride + m * lda + k) - za;
                 for (int64_t n = 0; n < N; ++n) {
                     int64_t zb = b_zp ? b_zp[b_zp_len == 1 ? 0 : n] : 0;
                     int64_t b = load_8bit(B, b_is_u8, bt * b_bstride + k * ldb + n) - zb;

@@ -353,3 +353,99 @@ def test_w8a32_factorised_form_within_double_rounding():
         A64 = A.astype(np.float64)
         fact = np.float64(np.float32(0.02)) * (A64 @ W.astype(np.float64) - zp * A64.sum(1)[:, None])
         assert np.all(np.abs(R - fact) <= 1e-12 * B)
+
+
+# ---------------------------------------------------------------------------
+# A8W8 with an int32 accumulator input (pypto page, matmul-dequant-acc op)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_a8w8_acc_brute_force(seed):
+    """Independent pure-Python form, including accumulator inputs near the
+    int32 limits so that the wrap is exercised."""
+    g = si.rng(3000 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 9, size=3))
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=seed, lo=-128, hi=127)
+    edge = np.array([2**31 - 1, -2**31, 2**31 - 100, -2**31 + 7, 0], dtype=np.int64)
+    acc_in = np.where(si.randint(g, (M, N), 0, 1, np.int64) == 1,
+                      edge[si.randint(g, (M, N), 0, 4, np.int64)],
+                      si.randint(g, (M, N), -2**31, 2**31 - 1, np.int64)).astype(np.int32)
+    r = oracle.a8w8_acc(acc_in, A, W, s_a, s_w)
+    ref = brute.a8w8_acc(acc_in.astype(int).tolist(), A.astype(int).tolist(), W.astype(int).tolist(),
+                         [float(x) for x in s_a], [float(x) for x in s_w])
+    assert r["acc"].tolist() == [[c[0] for c in row] for row in ref]
+    assert r["f32"].tolist() == [[c[1] for c in row] for row in ref]
+
+
+def test_a8w8_acc_with_zero_activations_is_the_scaled_input():
+    """A = 0: the output is the fp32 chain applied to acc_in alone, computed
+    here with numpy's IEEE float32 arithmetic (RNE per multiply)."""
+    g = si.rng(17)
+    M, N, K = 30, 40, 64
+    A = np.zeros((M, K), np.int8)
+    _, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=5)
+    acc_in = si.randint(g, (M, N), -2**31, 2**31 - 1, np.int64).astype(np.int32)
+    r = oracle.a8w8_acc(acc_in, A, W, s_a, s_w)
+    f = (acc_in.astype(np.float32) * s_a[:, None]).astype(np.float32) * s_w[None, :]
+    np.testing.assert_array_equal(r["acc"], acc_in)
+    np.testing.assert_array_equal(r["f32"], f.astype(np.float32))
+
+
+def test_a8w8_acc_chains_k_chunks():
+    """Feeding the raw accumulator of one K chunk into the next gives the
+    result over the whole K (the K-chunked use the op exists for)."""
+    A, W, s_a, s_w = si.a8w8_inputs(20, 36, 300, seed=9, lo=-128, hi=127)
+    first = oracle.a8w8(A[:, :128], W[:128], s_a, s_w)["acc"]
+    r = oracle.a8w8_acc(first, A[:, 128:], W[128:], s_a, s_w)
+    whole = oracle.a8w8(A, W, s_a, s_w)
+    for key in ("acc", "f32", "bf16"):
+        np.testing.assert_array_equal(r[key], whole[key])
+
+
+# ---------------------------------------------------------------------------
+# MatMulInteger with a per-row activation zero point (onnx-to-hip page)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_matmul_integer_row_zero_points_brute_force(seed):
+    g = si.rng(4000 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 10, size=3))
+    a_dt = (np.uint8, np.int8)[seed % 2]
+    b_dt = (np.uint8, np.int8)[(seed // 2) % 2]
+    A = _rand8(g, (M, K), a_dt)
+    B = _rand8(g, (K, N), b_dt)
+    za = _rand8(g, (M,), a_dt)
+    zb = _rand8(g, (N,), b_dt)
+    Y = oracle.matmul_integer(A, B, za, zb)
+    exact = brute.matmul_integer_rows(A.astype(int).tolist(), B.astype(int).tolist(),
+                                      [int(x) for x in za], [int(x) for x in zb])
+    assert Y.tolist() == [[brute.wrap32(v) for v in r] for r in exact]
+
+
+def test_matmul_integer_constant_row_zero_points_equal_the_scalar():
+    A, B, zb = si.matmul_integer_inputs(3, 17, 23, 70, seed=12)
+    Y = oracle.matmul_integer(A, B, np.full(17, 131, np.uint8), zb)
+    np.testing.assert_array_equal(Y, oracle.matmul_integer(A, B, 131, zb))
+    # [M, 1] is the same per-row form
+    np.testing.assert_array_equal(oracle.matmul_integer(A, B, np.full((17, 1), 131, np.uint8), zb), Y)
+
+
+def test_row_zero_point_identity_used_by_the_kernels():
+    """With per-row ca[m]: sum (a-za[m])(b-zb[n]) = sum a'b' + cb[n] sum a'
+    + ca[m] sum b'[:,n] + K ca[m] cb[n], in exact integers."""
+    g = si.rng(98)
+    for trial in range(30):
+        M, N, K = (int(x) for x in g.integers(1, 12, size=3))
+        a_dt = (np.uint8, np.int8)[trial % 2]
+        b_dt = (np.uint8, np.int8)[(trial // 2) % 2]
+        A = _rand8(g, (M, K), a_dt).astype(np.int64)
+        B = _rand8(g, (K, N), b_dt).astype(np.int64)
+        za = _rand8(g, (M,), a_dt).astype(np.int64)
+        zb = _rand8(g, (N,), b_dt).astype(np.int64)
+        sa = 128 if a_dt == np.uint8 else 0
+        sb = 128 if b_dt == np.uint8 else 0
+        A1, B1 = A - sa, B - sb
+        ca, cb = sa - za, sb - zb
+        ident = (A1 @ B1 + np.outer(A1.sum(1), cb) + np.outer(ca, B1.sum(0)) + K * np.outer(ca, cb))
+        Y = oracle.matmul_integer(A.astype(a_dt), B.astype(b_dt), za.astype(a_dt), zb.astype(b_dt))
+        np.testing.assert_array_equal(Y, ident)

@@ -5,7 +5,9 @@ bf16), throughput in tera int8 ops per second, with inputs resident in HBM.
 One step is one call of the operator on that batch.  The same run also times
 the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
 K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
-4096^3, and the two small parity shapes) and reports them under "rows".
+4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
+at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
+points) and reports them under "rows".
 Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
 that no call finds its inputs in the 256 MB Infinity Cache.
 
@@ -109,7 +111,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="time one row only (prefill, decode, mmi, w8a32, small, ceilings)")
+                    help="time one row only (prefill, decode, mmi, acc, w8a32, small, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -238,6 +240,47 @@ def main():
             "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
             "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del sets
+
+    # ---- A8W8 with an int32 accumulator input; per-row MatMulInteger zp --
+    if want("acc"):
+        M = N = K = 8192
+        A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=505)
+        tA, tW, ta, tw = to(A), to(W), to(s_a), to(s_w)
+        del A, W
+        g = si.rng(606)
+        acc = torch.from_numpy(si.randint(g, (M, N), -2**20, 2**20, np.int32)).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = time_calls(lambda s: q.qgemm_a8w8_acc(acc, tA, tW, ta, tw, out_dtype=torch.bfloat16, out=out),
+                        [None], steps, warmup, stream)
+        ops = 2.0 * M * N * K
+        rows["a8w8_acc_prefill_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
+                                              "TOPS": ops / (ms * 1e-3) / 1e12,
+                                              "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+        del acc, out, tA, tW
+        m = 16
+        A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
+        base_w = to(W)
+        acc_m = torch.from_numpy(si.randint(g, (m, 8192), -2**20, 2**20, np.int32)).to(dev)
+        sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),
+                 torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)) for r in range(9)]
+        call = lambda s: q.qgemm_a8w8_acc(acc_m, s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4])
+        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 4 * m * 8192 + 2 * m * 8192
+        rows["a8w8_acc_decode_m16_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
+                                                 "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                                                 "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del sets, base_w
+        A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+        za = to(si.randint(g, (512,), 0, 255, np.uint8))
+        tB, tzb = to(B), to(zb)
+        sets = [(to(A), torch.empty((8, 512, 2048), dtype=torch.int32, device=dev)) for _ in range(13)]
+        call = lambda s: q.matmul_integer(s[0], tB, za, tzb, out=s[1])
+        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        ops = 2.0 * 8 * 512 * 2048 * 2048
+        rows["matmul_integer_row_zp_8x512x2048x2048"] = {
+            "kernel": q.last_kernel(), "us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
+            "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
         del sets
 
     # ---- W8A32 4096^3 -----------------------------------------------------

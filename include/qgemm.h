@@ -116,6 +116,34 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
                      void* stream);
 
 /*
+ * A8W8 with an int32 accumulator input ("Feature/a8w8 matmul dequant
+ * fusion", "Summary" and "What Changed": the matmul-dequant-acc op takes an
+ * INT32 accumulator input and lowers to matmul_acc / gemv_acc, which add the
+ * int8 product into it, before the same cast and scale chain):
+ *
+ *   acc[m,n] = acc_in[m,n] + sum_k A[m,k] * W[k,n]    exact, wraps mod 2^32
+ *   out[m,n] = cast_out( (((float)acc) * act_scale[m]) * weight_scale[n] )
+ *
+ * Bit-exact.  acc_in: int32 [M,N], row stride ld_acc >= N, device memory,
+ * read only (it may not overlap `out`).  Every other argument, the
+ * workspace (size from qgemm_workspace_bytes(QG_OP_A8W8, ...)) and the
+ * errors are those of qgemm_a8w8; in addition QG_ERR_INVALID_ARGUMENT for a
+ * NULL acc_in or ld_acc < N, QG_ERR_UNSUPPORTED if acc_in spans 2^31 bytes.
+ * The int32 accumulator of one K chunk (matmul_integer with int8 operands
+ * and zero points 0 computes it) fed into the call for the next chunk gives
+ * the result over the whole K.
+ */
+qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K,
+                         const int8_t* A, int64_t lda,
+                         const int8_t* W, int64_t ldw, int b_trans,
+                         const int32_t* acc_in, int64_t ld_acc,
+                         const float* act_scale, int64_t act_scale_len,
+                         const float* weight_scale, int64_t weight_scale_len,
+                         void* out, qg_dtype out_dtype, int64_t ldo,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * MatMulInteger ("feat(onnx-to-hip): lower quantized integer conv and
  * matmul", section "What", MatMulInteger and accumulator paragraphs):
  *
@@ -135,8 +163,9 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
  *      y_batch_stride >= (M-1)*ldy + N when batch > 1.
  *   workspace: reserved; pass NULL / 0.
  * Requires batch, M, N, K >= 1.  QG_ERR_UNSUPPORTED: an operand byte span
- * that reaches 2^31.  (Per-row activation zero points and ranks outside 2-4
- * are rejected by the Python binding, which maps ONNX ranks to batch.)
+ * that reaches 2^31.  (Per-row activation zero points: matmul_integer_row_zp.
+ * Ranks outside 2-4 are rejected by the Python binding, which maps ONNX
+ * ranks to batch.)
  */
 qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K,
                          const void* A, qg_dtype a_dtype, int64_t lda, int64_t a_batch_stride,
@@ -146,6 +175,26 @@ qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K,
                          int32_t* Y, int64_t ldy, int64_t y_batch_stride,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * MatMulInteger with one activation zero point per row of A (same page,
+ * "What": a per-row zero point is accepted when M is static):
+ *
+ *   Y[b,m,n] = wrap32( sum_k (A[b,m,k] - a_zp[m]) * (B[b,k,n] - zb[n]) )
+ *
+ * a_zero_point: device pointer to a_zero_point_len (1 or M) values of
+ * a_dtype; row m of every batch uses value m.  Everything else as in
+ * matmul_integer; QG_ERR_INVALID_ARGUMENT for a NULL a_zero_point or
+ * another length.  Bit-exact.
+ */
+qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                const void* A, qg_dtype a_dtype, int64_t lda, int64_t a_batch_stride,
+                                const void* B, qg_dtype b_dtype, int64_t ldb, int64_t b_batch_stride,
+                                const void* a_zero_point, int64_t a_zero_point_len,
+                                const void* b_zero_point, int64_t b_zero_point_len,
+                                int32_t* Y, int64_t ldy, int64_t y_batch_stride,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Workspace bytes the fastest kernel for this shape wants (0: none). */
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K);

@@ -8,8 +8,11 @@ this package is its thin Python binding, with the same call names:
 * ``qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32)``:
   int8 x int8 with int32 accumulation, per-row and per-column fp32 scales,
   fp32 or bf16 output.
+* ``qgemm_a8w8_acc(acc_in, A, W, act_scale, weight_scale, ...)``: the same
+  with an int32 accumulator input added before the cast.
 * ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
-  MatMulInteger, int32 output, shared weight never copied.
+  MatMulInteger, int32 output, shared weight never copied; per-row
+  activation zero points go to ``matmul_integer_row_zp``.
 
 ``calib_read`` and ``calib_mfma_i8`` measure the machine's HBM read and int8
 matrix-core ceilings for the roofline figures.
@@ -24,7 +27,9 @@ from ._binding import (  # noqa: F401
     calib_read,
     last_kernel,
     matmul_integer,
+    matmul_integer_row_zp,
     qgemm_a8w8,
+    qgemm_a8w8_acc,
     qgemm_w8a32,
     status_string,
     version,

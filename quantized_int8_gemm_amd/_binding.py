@@ -29,6 +29,10 @@ PROTOTYPES = {
                     _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
                         _i32, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
+    "qgemm_a8w8_acc": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64, _p, _i64,
+                        _p, _int, _i64, _p, _sz, _p], _int),
+    "matmul_integer_row_zp": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
+                               _p, _i64, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
     "qgemm_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
     "qgemm_status_string": ([_int], ctypes.c_char_p),
     "qgemm_last_kernel": ([], ctypes.c_char_p),
@@ -200,6 +204,21 @@ def qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=F
     act_scale: fp32 [M], [M, 1] or scalar; weight_scale: fp32 [N], [1, N] or
     scalar; out_dtype: torch.float32 (default) or torch.bfloat16.
     """
+    return _a8w8(None, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace)
+
+
+def qgemm_a8w8_acc(acc_in, A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=False, out=None,
+                   workspace=None):
+    """out = cast(((float)(acc_in + A @ W)_int32 * act_scale[m]) * weight_scale[n]).
+
+    acc_in: int32 [M, N] (unit column stride), added to the int8 product
+    (wrapping) before the cast.  Other arguments as qgemm_a8w8.
+    """
+    _need(acc_in, (torch.int32,), "acc_in")
+    return _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace)
+
+
+def _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace):
     _need(A, (torch.int8,), "A")
     _need(W, (torch.int8,), "W")
     if out_dtype not in (torch.float32, torch.bfloat16):
@@ -212,7 +231,9 @@ def qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=F
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, W is {tuple(W.shape)}")
     s_a, n_a = _act_scale(act_scale, M)
     s_w, n_w = _weight_scale(weight_scale, N)
-    dev = _on_gpu(A, W, s_a, s_w)
+    if acc_in is not None and tuple(acc_in.shape) != (M, N):
+        raise ValueError(f"acc_in must be [M, N] = [{M}, {N}]")
+    dev = _on_gpu(*([A, W, s_a, s_w] + ([acc_in] if acc_in is not None else [])))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     else:
@@ -223,11 +244,19 @@ def qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=F
         ws = _workspace(dev, workspace_bytes(QG_OP_A8W8, 1, M, N, K))
     else:
         ws = workspace
-    st = lib.qgemm_a8w8(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),
-                        _ptr(s_a), n_a, _ptr(s_w), n_w,
-                        _ptr(out), QG_FP32 if out_dtype == torch.float32 else QG_BF16, _rows(out, "out"),
-                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
-    _check(st, "qgemm_a8w8")
+    od = QG_FP32 if out_dtype == torch.float32 else QG_BF16
+    wsz = 0 if ws is None else ws.numel()
+    if acc_in is None:
+        st = lib.qgemm_a8w8(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),
+                            _ptr(s_a), n_a, _ptr(s_w), n_w, _ptr(out), od, _rows(out, "out"),
+                            _ptr(ws), wsz, _stream(dev))
+        _check(st, "qgemm_a8w8")
+    else:
+        st = lib.qgemm_a8w8_acc(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),
+                                _ptr(acc_in), _rows(acc_in, "acc_in"),
+                                _ptr(s_a), n_a, _ptr(s_w), n_w, _ptr(out), od, _rows(out, "out"),
+                                _ptr(ws), wsz, _stream(dev))
+        _check(st, "qgemm_a8w8_acc")
     return out
 
 
@@ -258,9 +287,10 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
     A: uint8/int8 of rank 2-4, [..., M, K]; B: uint8/int8 of rank 2-4,
     [..., K, N].  A rank-2 B, or one whose batch dimensions are all 1, is
     shared by every batch without a copy; a size-1 batch of A is likewise
-    reused.  a_zero_point: scalar of A's range (per-row zero points are not
-    supported); b_zero_point: None, scalar, [N] or [..., 1, N] per-column
-    values of B's dtype.  Returns int32 [*batch, M, N].
+    reused.  a_zero_point: scalar of A's range, or a tensor of A's dtype
+    with M per-row values ([M] or [M, 1]; calls matmul_integer_row_zp);
+    b_zero_point: None, scalar, [N] or [..., 1, N] per-column values of B's
+    dtype.  Returns int32 [*batch, M, N].
     """
     _need(A, (torch.uint8, torch.int8), "A")
     _need(B, (torch.uint8, torch.int8), "B")
@@ -270,11 +300,16 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
     K2, N = B.shape[-2:]
     if K != K2:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    za_rows = None
     if isinstance(a_zero_point, torch.Tensor):
-        if a_zero_point.numel() != 1:
-            raise NotImplementedError("per-row activation zero points are not supported")
         _need(a_zero_point, (A.dtype,), "a_zero_point")
-        a_zero_point = int(a_zero_point.item())
+        if a_zero_point.numel() == 1 and a_zero_point.dim() == 0:
+            a_zero_point = int(a_zero_point.item())
+        else:
+            if a_zero_point.numel() != M or (a_zero_point.dim() == 2 and a_zero_point.shape[1] != 1) \
+                    or a_zero_point.dim() > 2:
+                raise ValueError(f"a per-row a_zero_point must be [M] or [M, 1] with M={M}")
+            za_rows = a_zero_point.reshape(-1).contiguous()
     zb, zb_len = None, 0
     if b_zero_point is not None:
         if isinstance(b_zero_point, torch.Tensor):
@@ -295,20 +330,36 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
     b_bs = _batch_view(B, "B", batch_shape)
     A2 = A.reshape(-1, A.shape[-1]) if a_bs else A.reshape(A.shape[-2:])
     B2 = B.reshape(-1, B.shape[-1]) if b_bs else B.reshape(B.shape[-2:])
-    dev = _on_gpu(*([A, B] + ([zb] if zb is not None else [])))
+    dev = _on_gpu(*([A, B] + ([zb] if zb is not None else []) + ([za_rows] if za_rows is not None else [])))
     if out is None:
         out = torch.empty(tuple(batch_shape) + (M, N), dtype=torch.int32, device=dev)
     else:
         _need(out, (torch.int32,), "out")
         if tuple(out.shape) != tuple(batch_shape) + (M, N) or not out.is_contiguous():
             raise ValueError("out has the wrong shape or is not contiguous")
-    st = lib.matmul_integer(batch, M, N, K,
-                            _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
-                            _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
-                            int(a_zero_point), _ptr(zb), zb_len,
-                            _ptr(out), N, M * N, None, 0, _stream(dev))
-    _check(st, "matmul_integer")
+    if za_rows is None:
+        st = lib.matmul_integer(batch, M, N, K,
+                                _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
+                                _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
+                                int(a_zero_point), _ptr(zb), zb_len,
+                                _ptr(out), N, M * N, None, 0, _stream(dev))
+        _check(st, "matmul_integer")
+    else:
+        st = lib.matmul_integer_row_zp(batch, M, N, K,
+                                       _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
+                                       _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
+                                       _ptr(za_rows), za_rows.numel(), _ptr(zb), zb_len,
+                                       _ptr(out), N, M * N, None, 0, _stream(dev))
+        _check(st, "matmul_integer_row_zp")
     return out
+
+
+def matmul_integer_row_zp(A, B, a_zero_point, b_zero_point=None, out=None):
+    """MatMulInteger with one activation zero point per row of A
+    (a_zero_point: [M] or [M, 1] of A's dtype); see matmul_integer."""
+    if not isinstance(a_zero_point, torch.Tensor) or a_zero_point.dim() == 0:
+        raise ValueError("a_zero_point must be a tensor of M per-row values")
+    return matmul_integer(A, B, a_zero_point, b_zero_point, out)
 
 
 # ---------------------------------------------------------------------------

@@ -1,7 +1,8 @@
 // Skinny (decode-shaped) A8W8 kernel for M <= 16 on gfx950.
 //
 // Operator: "Feature/a8w8 matmul dequant fusion" -- int8 matmul into an
-// INT32 accumulator, cast to FP32, times act_scale[m], times
+// INT32 accumulator (optionally one given as input, the page's
+// matmul-dequant-acc op), cast to FP32, times act_scale[m], times
 // weight_scale[n], cast to the output type.  That page lowers logical M == 1
 // to a separate GEMV; here every M up to 16 takes this path, which is bound by
 // reading the weight once from HBM.
@@ -191,9 +192,25 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
     // Output row m, columns n .. n+3 (those < N): scales, then one vector
     // store when the four are in range and aligned.
     const bool vec_out = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+    const bool acc_vec = p.acc_in != nullptr && p.ld_acc % 4 == 0 &&
+                         (reinterpret_cast<uintptr_t>(p.acc_in) & 15) == 0;
     auto epilogue = [&](int m, int n, int4 v) {
         if (n >= p.N) return;
-        const int32_t vi[4] = {v.x, v.y, v.z, v.w};
+        int32_t vi[4] = {v.x, v.y, v.z, v.w};
+        if (p.acc_in != nullptr) {   // accumulator input, added before the cast (wrapping)
+            const int32_t* src = p.acc_in + (int64_t)m * p.ld_acc + n;
+            int32_t ai[4] = {0, 0, 0, 0};
+            if (acc_vec && n + 4 <= p.N) {
+                const int4 t = *reinterpret_cast<const int4*>(src);
+                ai[0] = t.x; ai[1] = t.y; ai[2] = t.z; ai[3] = t.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < p.N) ai[e] = src[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vi[e] = (int32_t)((uint32_t)vi[e] + (uint32_t)ai[e]);
+        }
         float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

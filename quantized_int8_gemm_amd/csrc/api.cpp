@@ -208,10 +208,16 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     return finish_launch(e, name);
 }
 
-qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
-                     int64_t ldw, int b_trans, const float* act_scale, int64_t act_scale_len,
-                     const float* weight_scale, int64_t weight_scale_len, void* out, qg_dtype out_dtype,
-                     int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// A8W8 with an optional int32 accumulator input (acc_in == NULL: none).
+qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                    int64_t ldw, int b_trans, const int32_t* acc_in, int64_t ld_acc, const float* act_scale,
+                    int64_t act_scale_len, const float* weight_scale, int64_t weight_scale_len, void* out,
+                    qg_dtype out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream,
+                    const char* op) {
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || W == nullptr || act_scale == nullptr || weight_scale == nullptr || out == nullptr)
         return QG_ERR_INVALID_ARGUMENT;
@@ -231,6 +237,7 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t l
     a.out = out; a.ldo = ldo; a.o_bstride = 0;
     a.act_scale = act_scale; a.as_stride = act_scale_len == 1 ? 0 : 1;
     a.weight_scale = weight_scale; a.ws_stride = weight_scale_len == 1 ? 0 : 1;
+    a.acc_in = acc_in; a.ld_acc = ld_acc;
     const int epi = out_dtype == QG_FP32 ? qg::EPI_F32 : qg::EPI_BF16;
     const bool vec = aligned16(A) && aligned16(W) && lda % 16 == 0 && ldw % 16 == 0 && K % 16 == 0 &&
                      (b_trans || N % 16 == 0);
@@ -253,23 +260,51 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t l
         a.split_steps = per;
         (void)hipGetLastError();
         e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name);
-        log_dispatch("a8w8", name, 1, M, N, K, splits);
+        log_dispatch(op, name, 1, M, N, K, splits);
     } else {
         const int cfg = pick_tile(1, M, N);
         (void)hipGetLastError();
         e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
-        log_dispatch("a8w8", name, 1, M, N, K, 1);
+        log_dispatch(op, name, 1, M, N, K, 1);
     }
     return finish_launch(e, name);
 }
 
-qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, qg_dtype a_dtype,
-                         int64_t lda, int64_t a_batch_stride, const void* B, qg_dtype b_dtype, int64_t ldb,
-                         int64_t b_batch_stride, int32_t a_zero_point, const void* b_zero_point,
-                         int64_t b_zero_point_len, int32_t* Y, int64_t ldy, int64_t y_batch_stride,
+}  // namespace
+
+extern "C" {
+
+qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                     int64_t ldw, int b_trans, const float* act_scale, int64_t act_scale_len,
+                     const float* weight_scale, int64_t weight_scale_len, void* out, qg_dtype out_dtype,
+                     int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+    return a8w8_impl(M, N, K, A, lda, W, ldw, b_trans, nullptr, 0, act_scale, act_scale_len, weight_scale,
+                     weight_scale_len, out, out_dtype, ldo, workspace, workspace_bytes, stream, "a8w8");
+}
+
+qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                         int64_t ldw, int b_trans, const int32_t* acc_in, int64_t ld_acc,
+                         const float* act_scale, int64_t act_scale_len, const float* weight_scale,
+                         int64_t weight_scale_len, void* out, qg_dtype out_dtype, int64_t ldo,
                          void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
+    if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
+    if (acc_in == nullptr || ld_acc < N) return QG_ERR_INVALID_ARGUMENT;
+    if ((M - 1) * ld_acc + N >= SPAN_LIMIT / 4) return QG_ERR_UNSUPPORTED;
+    return a8w8_impl(M, N, K, A, lda, W, ldw, b_trans, acc_in, ld_acc, act_scale, act_scale_len, weight_scale,
+                     weight_scale_len, out, out_dtype, ldo, workspace, workspace_bytes, stream, "a8w8_acc");
+}
+
+}  // extern "C"
+
+namespace {
+
+// MatMulInteger with a scalar activation zero point (a_zp_rows == NULL) or
+// one per row (device values of a_dtype, a_zp_len 1 or M).
+qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, qg_dtype a_dtype,
+                              int64_t lda, int64_t a_batch_stride, const void* B, qg_dtype b_dtype, int64_t ldb,
+                              int64_t b_batch_stride, int32_t a_zero_point, const void* a_zp_rows,
+                              int64_t a_zp_len, const void* b_zero_point, int64_t b_zero_point_len, int32_t* Y,
+                              int64_t ldy, int64_t y_batch_stride, void* stream) {
     if (!dims_ok(M, N, K) || batch < 1 || batch >= 65536) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || B == nullptr || Y == nullptr) return QG_ERR_INVALID_ARGUMENT;
     if ((a_dtype != QG_UINT8 && a_dtype != QG_INT8) || (b_dtype != QG_UINT8 && b_dtype != QG_INT8))
@@ -302,6 +337,13 @@ qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const v
     a.b_zp_u8 = b_u8 ? 1 : 0;
     a.ca = (a_u8 ? 128 : 0) - a_zero_point;
     a.sb = b_u8 ? 128 : 0;
+    if (a_zp_rows != nullptr) {
+        a.a_zp = a_zp_rows;
+        a.a_zp_stride = (a_zp_len == M && M > 1) ? 1 : 0;
+        a.a_zp_rows = (int)M;   // row index modulo M, also once the batch is folded into M
+        a.a_zp_u8 = a_u8 ? 1 : 0;
+        a.sa = a_u8 ? 128 : 0;
+    }
     // Fold the batch into M when B is shared and A / Y batches are contiguous
     // row blocks: one [batch*M, K] x [K, N] product with the same B.
     if (batch > 1 && b_batch_stride == 0 && a_batch_stride == M * lda && y_batch_stride == M * ldy &&
@@ -310,9 +352,9 @@ qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const v
         a.batch = 1;
     }
     // Row sums of A are needed when some cb[n] = sb - zb[n] may be non-zero;
-    // column sums of B when ca != 0.
+    // column sums of B when some ca[m] may be.
     const bool need_rowsum = b_zero_point != nullptr || b_u8;
-    const bool need_colsum = a.ca != 0;
+    const bool need_colsum = a.ca != 0 || a_zp_rows != nullptr;
     const int zp = (need_rowsum ? 1 : 0) | (need_colsum ? 2 : 0);
     const bool vec = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
                      N % 16 == 0 && (a.batch == 1 || (a_batch_stride % 16 == 0 && b_batch_stride % 16 == 0));
@@ -322,6 +364,38 @@ qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const v
     const hipError_t e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
     log_dispatch("matmul_integer", name, a.batch, a.M, N, K, 1);
     return finish_launch(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, qg_dtype a_dtype,
+                         int64_t lda, int64_t a_batch_stride, const void* B, qg_dtype b_dtype, int64_t ldb,
+                         int64_t b_batch_stride, int32_t a_zero_point, const void* b_zero_point,
+                         int64_t b_zero_point_len, int32_t* Y, int64_t ldy, int64_t y_batch_stride,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return matmul_integer_impl(batch, M, N, K, A, a_dtype, lda, a_batch_stride, B, b_dtype, ldb, b_batch_stride,
+                               a_zero_point, nullptr, 0, b_zero_point, b_zero_point_len, Y, ldy,
+                               y_batch_stride, stream);
+}
+
+qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
+                                qg_dtype a_dtype, int64_t lda, int64_t a_batch_stride, const void* B,
+                                qg_dtype b_dtype, int64_t ldb, int64_t b_batch_stride, const void* a_zero_point,
+                                int64_t a_zero_point_len, const void* b_zero_point, int64_t b_zero_point_len,
+                                int32_t* Y, int64_t ldy, int64_t y_batch_stride, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (a_zero_point == nullptr || (a_zero_point_len != 1 && a_zero_point_len != M))
+        return QG_ERR_INVALID_ARGUMENT;
+    const int32_t za0 = a_dtype == QG_UINT8 ? 128 : 0;   // in range; the kernel reads the real values
+    return matmul_integer_impl(batch, M, N, K, A, a_dtype, lda, a_batch_stride, B, b_dtype, ldb, b_batch_stride,
+                               za0, a_zero_point, a_zero_point_len, b_zero_point, b_zero_point_len, Y, ldy,
+                               y_batch_stride, stream);
 }
 
 }  // extern "C"

@@ -316,6 +316,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     char* out = reinterpret_cast<char*>(p.out) + (int64_t)bz * p.o_bstride * OUT_BYTES;
     const bool vec_out = ((p.ldo * OUT_BYTES) % 16 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
 
+    // ca[m] of the MatMulInteger correction: per row when a_zp is given.
+    auto row_ca = [&](int m) -> uint32_t {
+        if (p.a_zp == nullptr) return (uint32_t)p.ca;
+        const int idx = (m % p.a_zp_rows) * p.a_zp_stride;
+        const int32_t za = p.a_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.a_zp)[idx]
+                                     : (int32_t) reinterpret_cast<const int8_t*>(p.a_zp)[idx];
+        return (uint32_t)(p.sa - za);
+    };
+    // A8W8 accumulator input at row m, columns n .. n+3 (zero past N).
+    const bool acc_vec = p.acc_in != nullptr && p.ld_acc % 4 == 0 &&
+                         (reinterpret_cast<uintptr_t>(p.acc_in) & 15) == 0;
+    auto acc_in4 = [&](int m, int n) -> v4i {
+        const int32_t* src = p.acc_in + (int64_t)m * p.ld_acc + n;
+        if (acc_vec && n + 4 <= p.N) return *reinterpret_cast<const v4i*>(src);
+        v4i r = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) r[e] = src[e];
+        return r;
+    };
+
     if (!p.stage_out) {
         // Direct stores from the fragments (small grids, where the staging
         // round trip costs more latency than the wider stores save).
@@ -323,14 +344,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
             const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
-            uint32_t add_n[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
+            uint32_t colt[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
             float ws[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (EPI == EPI_I32) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     cbn[r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
-                    add_n[r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[r];
-                    if constexpr (COLSUM) add_n[r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
+                    colt[r] = (uint32_t)p.K * cbn[r];
+                    if constexpr (COLSUM) colt[r] += (uint32_t)__shfl(cs[b], 4 * g + r);
                 }
             } else {
 #pragma unroll
@@ -343,10 +364,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 const int64_t o = (int64_t)m * p.ldo + nq;
                 const bool full = nq + 4 <= p.N && vec4;
                 if constexpr (EPI == EPI_I32) {
+                    const uint32_t ca_m = COLSUM ? row_ca(m) : 0u;
                     uint32_t y[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        y[r] = (uint32_t)acc[a][b][r] + add_n[r];
+                        y[r] = (uint32_t)acc[a][b][r];
+                        if constexpr (COLSUM) y[r] += ca_m * colt[r];
                         if constexpr (ROWSUM) y[r] += cbn[r] * (uint32_t)rs[a];
                     }
                     int32_t* dst = reinterpret_cast<int32_t*>(out) + o;
@@ -359,10 +382,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                     }
                 } else {
                     const float as = as_r[a];
+                    v4i v = acc[a][b];
+                    if (p.acc_in != nullptr) {
+                        const v4i ai = acc_in4(m, nq);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
+                    }
                     float f[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        f[r] = (float)acc[a][b][r];
+                        f[r] = (float)v[r];
                         f[r] = f[r] * as;
                         f[r] = f[r] * ws[r];
                     }
@@ -397,7 +426,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     }
 
     // Per-column epilogue terms for fragment column block b.
-    uint32_t add_n[FN][EPI == EPI_I32 ? 4 : 1], cbn[FN][EPI == EPI_I32 ? 4 : 1];
+    uint32_t colt[FN][EPI == EPI_I32 ? 4 : 1], cbn[FN][EPI == EPI_I32 ? 4 : 1];
     float ws[FN][EPI == EPI_I32 ? 1 : 4];
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
@@ -406,8 +435,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 cbn[b][r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
-                add_n[b][r] = (uint32_t)p.K * (uint32_t)p.ca * cbn[b][r];
-                if constexpr (COLSUM) add_n[b][r] += (uint32_t)p.ca * (uint32_t)__shfl(cs[b], 4 * g + r);
+                colt[b][r] = (uint32_t)p.K * cbn[b][r];
+                if constexpr (COLSUM) colt[b][r] += (uint32_t)__shfl(cs[b], 4 * g + r);
             }
         } else {
 #pragma unroll
@@ -423,7 +452,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
             for (int a = 0; a < FM; ++a) {
                 const int row = (wm % PASS_WAVE_ROWS) * WM + a * 16 + i16;
+                const int m = m0 + wm * WM + a * 16 + i16;   // output row (may be >= M)
                 uint8_t* srow = smem + row * ROW_BYTES;
+                uint32_t ca_m = 0u;
+                if constexpr (EPI == EPI_I32 && COLSUM) ca_m = m < p.M ? row_ca(m) : 0u;
+                (void)m;
 #pragma unroll
                 for (int b = 0; b < FN; ++b) {
                     const int col = wn * WN + b * 16 + 4 * g;
@@ -431,17 +464,24 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                         uint32_t y[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            y[r] = (uint32_t)acc[a][b][r] + add_n[b][r];
+                            y[r] = (uint32_t)acc[a][b][r];
+                            if constexpr (COLSUM) y[r] += ca_m * colt[b][r];
                             if constexpr (ROWSUM) y[r] += cbn[b][r] * (uint32_t)rs[a];
                         }
                         const int c = col / 4;
                         *reinterpret_cast<u32x4*>(srow + ((c ^ (row & 15)) << 4)) = u32x4{y[0], y[1], y[2], y[3]};
                     } else {
                         const float as = as_r[a];
+                        v4i v = acc[a][b];
+                        if (p.acc_in != nullptr && m < p.M && n0 + col < p.N) {
+                            const v4i ai = acc_in4(m, n0 + col);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
+                        }
                         float f[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            f[r] = (float)acc[a][b][r];
+                            f[r] = (float)v[r];
                             f[r] = f[r] * as;
                             f[r] = f[r] * ws[b][r];
                         }

@@ -30,8 +30,9 @@
 //     When the zero-point correction needs them, the same fragments feed row
 //     sums of A and column sums of B through v_dot4 against ones.
 //  4. Epilogue from the accumulators: the fp32 cast and the two scale
-//     multiplies (each rounded, in that order) with an fp32 or bf16 store, or
-//     the MatMulInteger correction in wrapping int32 with an int32 store.
+//     multiplies (each rounded, in that order) with an fp32 or bf16 store
+//     (an int32 accumulator input, when given, is added first), or the
+//     MatMulInteger correction in wrapping int32 with an int32 store.
 #pragma once
 #include "device_common.h"
 #include "kernels.h"
@@ -333,7 +334,7 @@ void int8_tiled_kernel(Int8GemmArgs p) {
         const int n = n0 + S::col_of_row(wn * WN + j * 16 + l16);
         const bool n_ok = n < p.N;
         float ws = 0.f;
-        uint32_t cbn = 0, add_n = 0;
+        uint32_t cbn = 0, colt = 0;
         if constexpr (EPI == EPI_I32) {
             int32_t zb = 0;
             if (p.b_zp != nullptr && n_ok) {
@@ -342,8 +343,8 @@ void int8_tiled_kernel(Int8GemmArgs p) {
                                : (int32_t) reinterpret_cast<const int8_t*>(p.b_zp)[idx];
             }
             cbn = (uint32_t)(p.sb - zb);
-            add_n = (uint32_t)p.K * (uint32_t)p.ca * cbn;
-            if constexpr (COLSUM) add_n += (uint32_t)p.ca * (uint32_t)cs[j];
+            colt = (uint32_t)p.K * cbn;
+            if constexpr (COLSUM) colt += (uint32_t)cs[j];
         } else {
             if (n_ok) ws = p.weight_scale[n * p.ws_stride];
         }
@@ -357,11 +358,25 @@ void int8_tiled_kernel(Int8GemmArgs p) {
                 if (!(n_ok && m < p.M)) continue;
                 const int64_t o = (int64_t)m * p.ldo + n;
                 if constexpr (EPI == EPI_I32) {
-                    uint32_t y = (uint32_t)acc[i][j][r] + add_n;
+                    uint32_t y = (uint32_t)acc[i][j][r];
+                    if constexpr (COLSUM) {
+                        // ca[m]: per row when a_zp is given, else the scalar
+                        uint32_t ca_m = (uint32_t)p.ca;
+                        if (p.a_zp != nullptr) {
+                            const int idx = (m % p.a_zp_rows) * p.a_zp_stride;
+                            const int32_t za = p.a_zp_u8 ? (int32_t) reinterpret_cast<const uint8_t*>(p.a_zp)[idx]
+                                                         : (int32_t) reinterpret_cast<const int8_t*>(p.a_zp)[idx];
+                            ca_m = (uint32_t)(p.sa - za);
+                        }
+                        y += ca_m * colt;
+                    }
                     if constexpr (ROWSUM) y += cbn * (uint32_t)rsum;
                     reinterpret_cast<int32_t*>(out)[o] = (int32_t)y;
                 } else {
-                    float f = (float)acc[i][j][r];
+                    int32_t v = acc[i][j][r];
+                    if (p.acc_in != nullptr)
+                        v = (int32_t)((uint32_t)v + (uint32_t)p.acc_in[(int64_t)m * p.ld_acc + n]);
+                    float f = (float)v;
                     f = f * p.act_scale[m * p.as_stride];
                     f = f * ws;
                     if constexpr (EPI == EPI_F32) reinterpret_cast<float*>(out)[o] = f;

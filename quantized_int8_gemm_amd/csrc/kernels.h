@@ -22,10 +22,16 @@ struct Int8GemmArgs {
     // A8W8 epilogue: scales indexed by row / column (stride 0 = one value)
     const float* act_scale; int as_stride;
     const float* weight_scale; int ws_stride;
-    // MatMulInteger epilogue: Y = acc + cb[n]*rowsum + ca*colsum + K*ca*cb[n]
+    // A8W8 accumulator input: acc += acc_in[m*ld_acc + n] before the cast
+    // (NULL: none); int32, wrapping.
+    const int32_t* acc_in; int64_t ld_acc;
+    // MatMulInteger epilogue: Y = acc + cb[n]*rowsum[m] + ca[m]*(colsum[n] + K*cb[n])
     const void* b_zp; int b_zp_stride; int b_zp_u8;  // NULL means zero
-    int32_t ca;   // (128 if A is uint8 else 0) - a_zero_point
+    int32_t ca;   // (128 if A is uint8 else 0) - a_zero_point, when a_zp is NULL
     int32_t sb;   // 128 if B is uint8 else 0; cb[n] = sb - b_zp[n]
+    // Per-row activation zero points (NULL: the scalar ca above):
+    // ca[m] = sa - a_zp[(m % a_zp_rows) * a_zp_stride]
+    const void* a_zp; int a_zp_stride; int a_zp_rows; int a_zp_u8; int32_t sa;
     // split-K workspace (skinny kernel): counters then int32 partials
     void* workspace;
     int splits;

@@ -18,14 +18,15 @@ FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q\w+|matmul_integer)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q\w+|matmul_integer\w*)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
-                          "qgemm_calib_read", "qgemm_calib_mfma_i8"}
+                          "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_a8w8_acc",
+                          "matmul_integer_row_zp"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -159,9 +160,17 @@ def test_binding_rejects_bad_shapes():
         q.matmul_integer(torch.zeros(8, dtype=torch.uint8), torch.zeros(8, 3, dtype=torch.int8))
     with pytest.raises(ValueError):   # rank 5
         q.matmul_integer(torch.zeros(1, 1, 1, 2, 8, dtype=torch.uint8), torch.zeros(8, 3, dtype=torch.int8))
-    with pytest.raises(NotImplementedError):   # per-row activation zero point
+    with pytest.raises(ValueError):   # per-row activation zero point of the wrong length
         q.matmul_integer(torch.zeros(4, 8, dtype=torch.uint8), torch.zeros(8, 3, dtype=torch.int8),
-                         torch.zeros(4, dtype=torch.uint8))
+                         torch.zeros(3, dtype=torch.uint8))
+    with pytest.raises(ValueError):   # [1, M] is not a per-row shape
+        q.matmul_integer(torch.zeros(4, 8, dtype=torch.uint8), torch.zeros(8, 3, dtype=torch.int8),
+                         torch.zeros(1, 4, dtype=torch.uint8))
+    with pytest.raises(ValueError):   # acc_in of the wrong shape
+        q.qgemm_a8w8_acc(torch.zeros(4, 5, dtype=torch.int32), A, torch.zeros(8, 4, dtype=torch.int8),
+                         torch.ones(4), torch.ones(4))
+    with pytest.raises(TypeError):    # acc_in must be int32
+        q.qgemm_a8w8_acc(torch.zeros(4, 5), A, W, torch.ones(4), torch.ones(5))
     with pytest.raises(ValueError):   # per-column zero point of the wrong length
         q.matmul_integer(torch.zeros(4, 8, dtype=torch.uint8), torch.zeros(8, 3, dtype=torch.int8),
                          0, torch.zeros(2, dtype=torch.int8))
@@ -186,3 +195,18 @@ def test_calibration_rejects_bad_arguments():
     assert lib.qgemm_calib_mfma_i8(FAKE, (1 << 20) + 1, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
     assert lib.qgemm_calib_mfma_i8(None, 10, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
     assert lib.qgemm_calib_mfma_i8(FAKE, 10, FAKE, None, None) == b.QG_ERR_INVALID_ARGUMENT
+
+
+def test_a8w8_acc_and_row_zero_point_reject_bad_arguments():
+    lib = b.lib
+    # qgemm_a8w8_acc: NULL acc_in, ld_acc < N
+    for acc, ld in ((None, 16), (FAKE, 15)):
+        assert lib.qgemm_a8w8_acc(4, 16, 32, FAKE, 32, FAKE, 16, 0, acc, ld, FAKE, 4, FAKE, 16,
+                                  FAKE, b.QG_FP32, 16, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT
+    # the checks of qgemm_a8w8 still apply (act_scale length)
+    assert lib.qgemm_a8w8_acc(4, 16, 32, FAKE, 32, FAKE, 16, 0, FAKE, 16, FAKE, 3, FAKE, 16,
+                              FAKE, b.QG_FP32, 16, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT
+    # matmul_integer_row_zp: NULL zero points, a length other than 1 or M
+    for za, n in ((None, 4), (FAKE, 3), (FAKE, 0)):
+        assert lib.matmul_integer_row_zp(1, 4, 16, 32, FAKE, b.QG_UINT8, 32, 0, FAKE, b.QG_INT8, 16, 0,
+                                         za, n, None, 0, FAKE, 16, 0, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT

@@ -114,3 +114,55 @@ def test_matmul_integer_both_kernel_families(family, a_dt, b_dt, za):
         y = q.matmul_integer(to_dev(A), to_dev(B), za, to_dev(zb)).cpu().numpy()
         assert q.last_kernel().startswith("int8_dma" if family == "dma" else "int8_staged")
     np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, za, zb))
+
+
+@pytest.mark.parametrize("a_dt,b_dt", [(np.uint8, np.int8), (np.int8, np.uint8), (np.uint8, np.uint8)])
+@pytest.mark.parametrize("tile", range(6))
+def test_matmul_integer_row_zero_points_every_tile(tile, a_dt, b_dt):
+    """Per-row activation zero points with a shared B (batch folded into M,
+    so the row index wraps per batch), per-column b_zp, ragged edges."""
+    case(f"matmul_integer row zp tile {tile} {np.dtype(a_dt)}x{np.dtype(b_dt)} 3x200x528x512")
+    g = si.rng(500 + tile)
+    A = si.randint(g, (3, 200, 512), 0, 255, a_dt) if a_dt == np.uint8 else si.randint(g, (3, 200, 512), -128, 127, a_dt)
+    B = si.randint(g, (512, 528), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (512, 528), -128, 127, b_dt)
+    za = si.randint(g, (200,), 0, 255, a_dt) if a_dt == np.uint8 else si.randint(g, (200,), -128, 127, a_dt)
+    zb = si.randint(g, (528,), 0, 255, b_dt) if b_dt == np.uint8 else si.randint(g, (528,), -8, 8, b_dt)
+    with env(QGEMM_TILE=tile):
+        y = q.matmul_integer(to_dev(A), to_dev(B), to_dev(za), to_dev(zb)).cpu().numpy()
+        assert q.last_kernel().startswith("int8_dma"), q.last_kernel()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, za, zb))
+
+
+@pytest.mark.parametrize("family", ["dma", "staged"])
+def test_matmul_integer_row_zero_points_families_and_forms(family):
+    """[M, 1] zero points, a size-1 A batch broadcast against a batched B,
+    and K = 259 (register-staged kernel: bytes past K are cleared)."""
+    case(f"matmul_integer row zp family={family}")
+    g = si.rng(77)
+    A = si.randint(g, (1, 70, 512), 0, 255, np.uint8)
+    B = si.randint(g, (4, 512, 96), -128, 127, np.int8)
+    za = si.randint(g, (70, 1), 0, 255, np.uint8)
+    with env(QGEMM_FAMILY=family):
+        y = q.matmul_integer(to_dev(A), to_dev(B), to_dev(za), None).cpu().numpy()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, za, None))
+    A2 = si.randint(g, (2, 33, 259), -128, 127, np.int8)
+    B2 = si.randint(g, (259, 40), 0, 255, np.uint8)
+    za2 = si.randint(g, (33,), -128, 127, np.int8)
+    zb2 = si.randint(g, (40,), 0, 255, np.uint8)
+    with env(QGEMM_FAMILY=family):
+        y2 = q.matmul_integer_row_zp(to_dev(A2), to_dev(B2), to_dev(za2), to_dev(zb2)).cpu().numpy()
+        assert q.last_kernel().startswith("int8_staged")   # K % 64 != 0 with sums
+    np.testing.assert_array_equal(y2, oracle.matmul_integer(A2, B2, za2, zb2))
+
+
+def test_matmul_integer_row_zero_points_full_size_sampled():
+    """8 x 512 x 2048 x 2048 with per-row zero points: 16 sampled rows of
+    every batch against the oracle on those rows (with their zero points)."""
+    case("matmul_integer row zp 8x512x2048x2048 sampled rows")
+    A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+    g = si.rng(9)
+    za = si.randint(g, (512,), 0, 255, np.uint8)
+    y = q.matmul_integer(to_dev(A), to_dev(B), to_dev(za), to_dev(zb)).cpu().numpy()
+    rows = np.sort(g.choice(512, 16, replace=False))
+    ref = oracle.matmul_integer(A[:, rows], B, za[rows], zb)
+    np.testing.assert_array_equal(y[:, rows], ref)

@@ -51,6 +51,8 @@ def _load():
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
     lib.oracle_w8a32.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _p]
     lib.oracle_w8a32.restype = None
+    lib.oracle_w8a32_input_grad.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _p]
+    lib.oracle_w8a32_input_grad.restype = None
     lib.oracle_a8w8.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int,
                                 _p, _i64, _p, _i64, _p, _p, _p]
     lib.oracle_a8w8.restype = None
@@ -136,6 +138,26 @@ def w8a32(A, W, scale, zero_point):
     B = np.empty((M, N), dtype=np.float64)
     lib.oracle_w8a32(M, N, K, _ptr(A), K, _ptr(W), N, float(np.float32(scale)),
                      int(zero_point), _ptr(R), _ptr(B))
+    return R, B
+
+
+def w8a32_input_grad(dC, W, scale, zero_point):
+    """Gradient of the W8A32 matmul with respect to its activations:
+    R = dC @ ((W - zp) * scale)^T in double, plus the tolerance scale.
+
+    dC: fp32 [M,N]; W: int8 [K,N] (the forward weight); returns
+    (R float64 [M,K], bound float64 [M,K]).
+    """
+    lib = _load()
+    dC = _c(dC, np.float32)
+    W = _c(W, np.int8)
+    M, N = dC.shape
+    K, N2 = W.shape
+    assert N == N2
+    R = np.empty((M, K), dtype=np.float64)
+    B = np.empty((M, K), dtype=np.float64)
+    lib.oracle_w8a32_input_grad(M, N, K, _ptr(dC), N, _ptr(W), N, float(np.float32(scale)),
+                                int(zero_point), _ptr(R), _ptr(B))
     return R, B
 
 

@@ -17,6 +17,9 @@
  *  [P1] "feat(PULPOpen): matmul that dequantises an int8 weight in-kernel",
  *       intro paragraph and section "The kernel" (the identity
  *       sum_k a_k (b_k - zp) scale = scale (sum a_k b_k - zp sum a_k)).
+ *  [P4] "perf(pulpopen/gap9): share L3 storage between byte-identical
+ *       constants", intro (a frozen weight is read by the forward op and by
+ *       its gradient, dL/dx needs W).
  *  [P2] "Feature/a8w8 matmul dequant fusion", the walkthrough's sequence
  *       diagram (int8 matmul -> int32 accumulator -> cast to FP32 -> row scale
  *       by act_scale -> column scale by weight_scale -> cast to out_dtype),
@@ -101,6 +104,35 @@ void oracle_w8a32(int64_t M, int64_t N, int64_t K,
     }
     free(Wd);
     free(Wabs);
+}
+
+/* Input gradient of the W8A32 matmul.  [P1]'s intro: the frozen int8
+ * weight has two consumers, the forward matmul and its gradient; [P4]'s
+ * intro: dL/dx needs W.  With the forward C = A @ Wd, Wd = (W - zp) * scale,
+ * the gradient with respect to A is dA = dC @ Wd^T, here in double:
+ *   R[m,k] = sum_n dC[m,n] * (W[k,n] - zp) * scale
+ * and bound[m,k] = |scale| * sum_n |dC[m,n]| * |W[k,n] - zp|.
+ * dC: [M,N] (ldd), W: [K,N] (ldw) -- the forward weight as stored --,
+ * R and bound: [M,K] dense. */
+void oracle_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
+                             const float* dC, int64_t ldd,
+                             const int8_t* W, int64_t ldw,
+                             float scale, int32_t zero_point,
+                             double* R, double* bound) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0, b = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double g = (double)dC[m * ldd + n];
+                double centred = (double)W[k * ldw + n] - (double)zero_point;
+                s += g * (centred * (double)scale);
+                b += fabs(g) * (fabs(centred) * fabs((double)scale));
+            }
+            R[m * K + k] = s;
+            if (bound) bound[m * K + k] = b;
+        }
+    }
 }
 
 /* ---------------------------------------------------------------------- */

@@ -449,3 +449,51 @@ def test_row_zero_point_identity_used_by_the_kernels():
         ident = (A1 @ B1 + np.outer(A1.sum(1), cb) + np.outer(ca, B1.sum(0)) + K * np.outer(ca, cb))
         Y = oracle.matmul_integer(A.astype(a_dt), B.astype(b_dt), za.astype(a_dt), zb.astype(b_dt))
         np.testing.assert_array_equal(Y, ident)
+
+
+# ---------------------------------------------------------------------------
+# W8A32 input gradient (PULPOpen page intro; L3-sharing page intro)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_w8a32_input_grad_brute_force_exact(seed):
+    """Exact rational arithmetic: the gradient is the forward operator applied
+    to dC with the weight transposed."""
+    g = si.rng(3100 + seed)
+    M, N, K = (int(x) for x in g.integers(1, 8, size=3))
+    dC, _ = si.w8a32_inputs(M, K, N, seed=seed)          # dC: [M, N] fp32
+    _, W = si.w8a32_inputs(1, N, K, seed=seed + 50)       # W: [K, N] int8
+    scale, zp = float(np.float32(0.03)), int(g.integers(-9, 10))
+    R, B = oracle.w8a32_input_grad(dC, W, scale, zp)
+    Rx, Bx = brute.w8a32_exact(dC.tolist(), W.T.astype(int).tolist(), scale, zp)
+    for m in range(M):
+        for k in range(K):
+            assert abs(R[m, k] - float(Rx[m][k])) <= 1e-13 * float(Bx[m][k]) + 1e-300
+            assert abs(B[m, k] - float(Bx[m][k])) <= 1e-13 * float(Bx[m][k])
+
+
+def test_w8a32_input_grad_is_the_adjoint_of_the_forward():
+    """<dC, A @ Wd> == <dC @ Wd^T, A> for any A and dC: the defining property
+    of the input gradient (a wrong transpose or sign fails it)."""
+    A, W = si.w8a32_inputs(37, 29, 53, seed=21)
+    dC, _ = si.w8a32_inputs(37, 53, 29, seed=22)
+    scale, zp = 0.017, -4
+    fwd, fb = oracle.w8a32(A, W, scale, zp)
+    grad, gb = oracle.w8a32_input_grad(dC, W, scale, zp)
+    lhs = float((dC.astype(np.float64) * fwd).sum())
+    rhs = float((grad * A.astype(np.float64)).sum())
+    scale_of_terms = float((np.abs(dC.astype(np.float64)) * fb).sum())
+    assert abs(lhs - rhs) <= 1e-12 * scale_of_terms
+
+
+def test_w8a32_input_grad_matches_torch_autograd_in_double():
+    A, W = si.w8a32_inputs(24, 31, 40, seed=23)
+    dC, _ = si.w8a32_inputs(24, 40, 31, seed=24)
+    scale, zp = 0.05, 3
+    X = torch.from_numpy(A.astype(np.float64)).requires_grad_(True)
+    Wd = (torch.from_numpy(W.astype(np.float64)) - zp) * scale
+    (X @ Wd).backward(torch.from_numpy(dC.astype(np.float64)))
+    R, B = oracle.w8a32_input_grad(dC, W, np.float32(scale), zp)
+    # the oracle uses the fp32-rounded scale, torch the double one
+    rel = abs(float(np.float32(scale)) - scale) / scale
+    assert np.all(np.abs(R - X.grad.numpy()) <= (rel + 1e-13) * B + 1e-300)

@@ -7,7 +7,7 @@ the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
 K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
 at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
-points) and reports them under "rows".
+points, the W8A32 input gradient at 4096^3) and reports them under "rows".
 Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
 that no call finds its inputs in the 256 MB Infinity Cache.
 
@@ -292,7 +292,15 @@ def main():
         fl = 2.0 * 4096 ** 3
         rows["w8a32_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "TFLOPS": fl / (ms * 1e-3) / 1e12,
                               "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
-        del A, W, tA, tW, outc
+        # its input gradient: dA = dC @ ((W - zp) * scale)^T, same weight
+        dC, _ = si.w8a32_inputs(4096, 4096, 4096, seed=507)
+        tdC = to(dC)
+        ms = time_calls(lambda s: q.qgemm_w8a32_input_grad(tdC, tW, 0.01, -5, out=outc), [None], steps, warmup,
+                        stream)
+        rows["w8a32_input_grad_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
+                                         "TFLOPS": fl / (ms * 1e-3) / 1e12,
+                                         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
+        del A, W, tA, tW, outc, dC, tdC
 
     # ---- the small parity shapes (launch-latency bound) ------------------
     if want("small"):

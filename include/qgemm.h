@@ -79,6 +79,31 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
                       void* stream);
 
 /*
+ * Input gradient of the W8A32 matmul: the frozen int8 weight's second
+ * consumer ("feat(PULPOpen): matmul that dequantises an int8 weight
+ * in-kernel", intro; "perf(pulpopen/gap9): share L3 storage between
+ * byte-identical constants", intro: dL/dx needs W).  For the forward
+ * C = A @ ((W - zp) * scale) with W [K,N]:
+ *
+ *   dA[m,k] = sum_n dC[m,n] * (W[k,n] - zero_point) * scale
+ *           = scale * (sum_n dC[m,n] W[k,n] - zero_point * sum_n dC[m,n])
+ *
+ * evaluated in the factorised form in fp32, the dequantised weight never
+ * formed, W read in its forward layout.
+ *   dC: fp32 [M,N], row stride lddc >= N.   W: int8 [K,N], row stride ldw >= N.
+ *   dA: fp32 [M,K], row stride ldda >= K.    scale, zero_point: as qgemm_w8a32.
+ * Requires M, N, K >= 1.  QG_ERR_UNSUPPORTED if K*ldw or M*lddc*4 reaches
+ * 2^31 bytes.  Accuracy as qgemm_w8a32, with the sum over n:
+ * within 1e-5 * |scale| * sum_n |dC[m,n]| * |W[k,n] - zp| of the exact value.
+ */
+qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
+                                 const float* dC, int64_t lddc,
+                                 const int8_t* W, int64_t ldw,
+                                 float scale, int32_t zero_point,
+                                 float* dA, int64_t ldda,
+                                 void* stream);
+
+/*
  * A8W8 matmul with fused dequantisation ("Feature/a8w8 matmul dequant
  * fusion": sequence diagram and "What Changed"):
  *

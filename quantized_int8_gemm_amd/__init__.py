@@ -5,6 +5,8 @@ this package is its thin Python binding, with the same call names:
 
 * ``qgemm_w8a32(A, W, scale, zero_point=0)``: fp32 x int8 weight with a
   per-tensor scale and zero point, dequantisation folded into the epilogue.
+* ``qgemm_w8a32_input_grad(dC, W, scale, zero_point=0)``: its gradient
+  with respect to the activations, W in its forward layout.
 * ``qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32)``:
   int8 x int8 with int32 accumulation, per-row and per-column fp32 scales,
   fp32 or bf16 output.
@@ -31,6 +33,7 @@ from ._binding import (  # noqa: F401
     qgemm_a8w8,
     qgemm_a8w8_acc,
     qgemm_w8a32,
+    qgemm_w8a32_input_grad,
     status_string,
     version,
     workspace_bytes,

@@ -25,6 +25,7 @@ _p, _i64, _i32, _int, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 # C prototypes, in the order of include/qgemm.h.
 PROTOTYPES = {
     "qgemm_w8a32": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p], _int),
+    "qgemm_w8a32_input_grad": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p], _int),
     "qgemm_a8w8": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64,
                     _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
@@ -156,6 +157,33 @@ def qgemm_w8a32(A, W, scale, zero_point=0, out=None):
     return out
 
 
+
+
+def qgemm_w8a32_input_grad(dC, W, scale, zero_point=0, out=None):
+    """dA = dC @ ((W - zero_point) * scale)^T: the gradient of qgemm_w8a32
+    with respect to its activations, W in its forward [K, N] layout.
+
+    dC: fp32 [M, N]; W: int8 [K, N]; returns fp32 [M, K].
+    """
+    _need(dC, (torch.float32,), "dC")
+    _need(W, (torch.int8,), "W")
+    if dC.dim() != 2 or W.dim() != 2:
+        raise ValueError("dC and W must be 2-D")
+    M, N = dC.shape
+    K, N2 = W.shape
+    if N != N2:
+        raise ValueError(f"dC is {tuple(dC.shape)} but W is {tuple(W.shape)}; both need N columns")
+    dev = _on_gpu(dC, W)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=dev)
+    else:
+        _need(out, (torch.float32,), "out")
+        if tuple(out.shape) != (M, K):
+            raise ValueError("out has the wrong shape")
+    st = lib.qgemm_w8a32_input_grad(M, N, K, _ptr(dC), _rows(dC, "dC"), _ptr(W), _rows(W, "W"),
+                                    float(scale), int(zero_point), _ptr(out), _rows(out, "out"), _stream(dev))
+    _check(st, "qgemm_w8a32_input_grad")
+    return out
 # ---------------------------------------------------------------------------
 # A8W8
 # ---------------------------------------------------------------------------

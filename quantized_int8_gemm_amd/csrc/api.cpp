@@ -203,8 +203,31 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     const bool vec_w = (reinterpret_cast<uintptr_t>(W) & 3u) == 0 && ldw % 4 == 0 && N % 4 == 0;
     const char* name = "";
     (void)hipGetLastError();
-    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, (hipStream_t)stream, &name);
+    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, false, (hipStream_t)stream, &name);
     log_dispatch("w8a32", name, 1, M, N, K, 1);
+    return finish_launch(e, name);
+}
+
+qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* dC, int64_t lddc,
+                                 const int8_t* W, int64_t ldw, float scale, int32_t zero_point, float* dA,
+                                 int64_t ldda, void* stream) {
+    if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
+    if (dC == nullptr || W == nullptr || dA == nullptr) return QG_ERR_INVALID_ARGUMENT;
+    if (lddc < N || ldw < N || ldda < K) return QG_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale)) return QG_ERR_INVALID_ARGUMENT;
+    if ((K + 256) * ldw >= SPAN_LIMIT || (128 * lddc + N + 64) * 4 >= SPAN_LIMIT) return QG_ERR_UNSUPPORTED;
+
+    // The kernel's view: outputs = the K columns of dA, contraction = N.
+    qg::W8A32Args a{};
+    a.M = (int)M; a.N = (int)K; a.K = (int)N;
+    a.A = dC; a.lda = lddc; a.W = W; a.ldw = ldw;
+    a.scale = scale; a.zp = zero_point; a.C = dA; a.ldc = ldda;
+    const bool vec_a = aligned16(dC) && lddc % 4 == 0 && N % 4 == 0;
+    const bool vec_w = aligned16(W) && ldw % 16 == 0;
+    const char* name = "";
+    (void)hipGetLastError();
+    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, true, (hipStream_t)stream, &name);
+    log_dispatch("w8a32_input_grad", name, 1, M, K, N, 1);
     return finish_launch(e, name);
 }
 

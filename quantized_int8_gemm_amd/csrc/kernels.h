@@ -83,7 +83,8 @@ struct W8A32Args {
     float scale; int32_t zp;
     float* C; int64_t ldc;
 };
-hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, hipStream_t s,
+// wt: W is [N,K] (rows of the contraction), the input-gradient form.
+hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                         const char** name);
 
 // Calibration kernels (roofline ceilings; no part of the method).  Each

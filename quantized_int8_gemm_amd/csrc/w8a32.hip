@@ -19,6 +19,16 @@
 //    v_mfma_f32_16x16x4_f32; the same A values it feeds are summed into the
 //    row sum S2 (per lane, then across the four lane groups).
 //  * Epilogue: C = scale * (S1 - zp * S2), or scale * S1 when zp == 0.
+//
+// The same kernel with WT = true is the gradient with respect to the
+// activations (the frozen weight's second consumer: "feat(PULPOpen): matmul
+// that dequantises an int8 weight in-kernel", intro; "perf(pulpopen/gap9):
+// share L3 storage between byte-identical constants", intro):
+//   dA[m,k] = scale * (sum_n dC[m,n] W[k,n] - zp * sum_n dC[m,n]),
+// the same factorisation with the contraction over W's contiguous
+// dimension.  The kernel then sees W as [outputs][contraction] rows, which
+// is already the layout its LDS tile wants: each row segment is copied
+// as is, with no byte transpose.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,7 +44,9 @@ constexpr int A_STAGE = BM * AROW * 4;
 constexpr int W_STAGE = BN * WROW;
 constexpr int GROUP_M = 8;
 
-template <bool VEC>
+// WT == false: W is [K,N] (contraction over rows); true: W is [N,K] rows of
+// the contraction (p.N outputs, p.K contraction bytes per row).
+template <bool VEC, bool WT>
 __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_STAGE + W_STAGE)];
 
@@ -53,14 +65,17 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
     const int cols = p.N - n0 < BN ? p.N - n0 : BN;
     const int lda = (int)p.lda, ldw = (int)p.ldw;
     const float* A = p.A + (int64_t)m0 * p.lda;
-    const int8_t* W = p.W + n0;
+    const int8_t* W = WT ? p.W + (int64_t)n0 * p.ldw : p.W + n0;
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (uint32_t)(((rows - 1) * lda + p.K) * 4));
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(W, (uint32_t)((p.K - 1) * ldw + (p.N - n0)));
+    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(W, (uint32_t)((cols - 1) * ldw + p.K))
+                                             : make_rsrc(W, (uint32_t)((p.K - 1) * ldw + (p.N - n0)));
 
     // A: thread -> rows ar + 32*i, floats 4*ac .. 4*ac+3 of the chunk
     const int ar = tid >> 3, ac = tid & 7;
-    // W: thread -> rows 4*wr .. 4*wr+3 of the chunk, columns 4*wc .. 4*wc+3
+    // W: thread -> rows 4*wr .. 4*wr+3 of the chunk, columns 4*wc .. 4*wc+3;
+    // with WT, output row tr, contraction bytes 16*th .. 16*th+15.
     const int wr = tid & 7, wc = tid >> 3;
+    const int tr = tid >> 1, th = tid & 1;
 
     u32x4 a_st[4];
     uint32_t w_st[4];
@@ -79,6 +94,24 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
                 }
                 a_st[i] = u32x4{d[0], d[1], d[2], d[3]};
             }
+        }
+        if constexpr (WT) {
+            if constexpr (VEC) {
+                const u32x4 v = buffer_load16(w_rsrc, (uint32_t)(tr * ldw + k0 + 16 * th), 0u);
+                w_st[0] = v.x; w_st[1] = v.y; w_st[2] = v.z; w_st[3] = v.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t d = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = k0 + 16 * th + 4 * i + e;
+                        if (tr < cols && k < p.K) d |= (uint32_t)(uint8_t)W[(int64_t)tr * p.ldw + k] << (8 * e);
+                    }
+                    w_st[i] = d;
+                }
+            }
+            return;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -112,10 +145,15 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
             }
             *reinterpret_cast<u32x4*>(As + (ar + 32 * i) * AROW + ac * 4) = v;
         }
-        uint32_t y[4];
-        transpose4x4_bytes(w_st, y);
+        if constexpr (WT) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(Ws + (wc * 4 + c) * WROW + wr * 4) = y[c];
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(Ws + tr * WROW + 16 * th + 4 * i) = w_st[i];
+        } else {
+            uint32_t y[4];
+            transpose4x4_bytes(w_st, y);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(Ws + (wc * 4 + c) * WROW + wr * 4) = y[c];
+        }
     };
 
     v4f acc[4][4];
@@ -193,11 +231,18 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
 
 }  // namespace
 
-hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, hipStream_t s, const char** name) {
+hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s, const char** name) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    *name = "w8a32_tiled_128x128";
-    if (vec_a && vec_w) hipLaunchKernelGGL(w8a32_kernel<true>, dim3(tiles), dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL(w8a32_kernel<false>, dim3(tiles), dim3(NT), 0, s, a);
+    const bool vec = vec_a && vec_w;
+    if (wt) {
+        *name = "w8a32_input_grad_128x128";
+        if (vec) hipLaunchKernelGGL((w8a32_kernel<true, true>), dim3(tiles), dim3(NT), 0, s, a);
+        else hipLaunchKernelGGL((w8a32_kernel<false, true>), dim3(tiles), dim3(NT), 0, s, a);
+    } else {
+        *name = "w8a32_tiled_128x128";
+        if (vec) hipLaunchKernelGGL((w8a32_kernel<true, false>), dim3(tiles), dim3(NT), 0, s, a);
+        else hipLaunchKernelGGL((w8a32_kernel<false, false>), dim3(tiles), dim3(NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

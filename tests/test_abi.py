@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
                           "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_a8w8_acc",
-                          "matmul_integer_row_zp"}
+                          "matmul_integer_row_zp", "qgemm_w8a32_input_grad"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -210,3 +210,20 @@ def test_a8w8_acc_and_row_zero_point_reject_bad_arguments():
     for za, n in ((None, 4), (FAKE, 3), (FAKE, 0)):
         assert lib.matmul_integer_row_zp(1, 4, 16, 32, FAKE, b.QG_UINT8, 32, 0, FAKE, b.QG_INT8, 16, 0,
                                          za, n, None, 0, FAKE, 16, 0, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT
+
+
+def test_w8a32_input_grad_rejects_bad_arguments():
+    lib = b.lib
+    ok = dict(M=4, N=16, K=8, dC=FAKE, lddc=16, W=FAKE, ldw=16, scale=0.5, zp=0, dA=FAKE, ldda=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.qgemm_w8a32_input_grad(a["M"], a["N"], a["K"], a["dC"], a["lddc"], a["W"], a["ldw"],
+                                          a["scale"], a["zp"], a["dA"], a["ldda"], None)
+    for kw in (dict(M=0), dict(dC=None), dict(W=None), dict(dA=None), dict(lddc=15), dict(ldw=15),
+               dict(ldda=7), dict(scale=float("inf")), dict(scale=float("nan"))):
+        assert call(**kw) == b.QG_ERR_INVALID_ARGUMENT, kw
+    with pytest.raises(ValueError):
+        q.qgemm_w8a32_input_grad(torch.zeros(4, 16), torch.zeros(8, 15, dtype=torch.int8), 0.5)
+    with pytest.raises(TypeError):
+        q.qgemm_w8a32_input_grad(torch.zeros(4, 16), torch.zeros(8, 16), 0.5)

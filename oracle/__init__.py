@@ -78,6 +78,8 @@ def _load():
     lib.oracle_matmul_integer_at.restype = None
     lib.oracle_dot_f32acc.argtypes = [_i64, _p, _int, _p, _int, _i64, _i32, _i32]
     lib.oracle_dot_f32acc.restype = _i32
+    lib.oracle_dynamic_quantize_linear.argtypes = [_i64, _p, _p, _p, _p]
+    lib.oracle_dynamic_quantize_linear.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = _int
     _lib = lib
@@ -333,3 +335,22 @@ def dot_f32acc(a, b, a_zero_point=0, b_zero_point=0):
     b = _c(b, b.dtype)
     return int(lib.oracle_dot_f32acc(a.size, _ptr(a), _is_u8(a), _ptr(b), _is_u8(b), 1,
                                      int(a_zero_point), int(b_zero_point)))
+
+
+# ---------------------------------------------------------------------------
+# DynamicQuantizeLinear (uint8)
+# ---------------------------------------------------------------------------
+
+def dynamic_quantize_linear(x):
+    """ONNX DynamicQuantizeLinear to uint8 as the onnx-to-hip page lowers it.
+
+    x: float32 array of any shape.  Returns (y uint8 of x's shape,
+    scale float32, zero_point uint8).
+    """
+    lib = _load()
+    xs = _c(np.asarray(x, dtype=np.float32).reshape(-1), np.float32)
+    y = np.empty(xs.size, dtype=np.uint8)
+    sc = np.empty(1, dtype=np.float32)
+    zp = np.empty(1, dtype=np.int32)
+    lib.oracle_dynamic_quantize_linear(xs.size, _ptr(xs), _ptr(y), _ptr(sc), _ptr(zp))
+    return y.reshape(np.shape(x)), np.float32(sc[0]), np.uint8(zp[0])

@@ -121,3 +121,20 @@ def bf16_bits(x):
     else:
         pick = lo_bits if ((lo_bits >> 16) & 1) == 0 else hi_bits
     return (sign << 15) | (pick >> 16)
+
+
+def dynamic_quantize_linear(xs):
+    """DynamicQuantizeLinear on a list of fp32 values with every fp32 step
+    emulated: a binary32 operation equals the double operation rounded to
+    binary32 (double carries more than twice the bits, so the double
+    rounding is innocuous for + - * /).  Python's round() is ties-to-even.
+    The range includes 0; a zero scale becomes 1.  Returns (y, scale, zp)."""
+    mn = min([0.0] + list(xs))
+    mx = max([0.0] + list(xs))
+    scale = f32(f32(mx - mn) / 255.0)
+    if scale == 0.0:
+        scale = 1.0
+    zp = round(f32(0.0 - f32(mn / scale)))
+    zp = min(255, max(0, zp))
+    y = [min(255, max(0, round(f32(x / scale)) + zp)) for x in xs]
+    return y, scale, zp

@@ -26,12 +26,13 @@
  *       the Codex review (rank-1 [M]/[N] scales mean rows/columns) and the
  *       "What Changed" list (INT32 accumulator, FP32/BF16 outputs).
  *  [P5] "feat(onnx-to-hip): lower quantized integer conv and matmul",
- *       section "What", MatMulInteger paragraph (ranks 2-4, zero points,
- *       shared B) and the accumulator paragraph (f32 accumulation only while
+ *       section "What", DynamicQuantizeLinear paragraph, MatMulInteger
+ *       paragraph (ranks 2-4, zero points, shared B) and the accumulator paragraph (f32 accumulation only while
  *       65025*K fits the 24-bit mantissa, otherwise int64 accumulation stored
  *       as a wrapping int32).
  */
 #include <math.h>
+#include <fenv.h>
 #include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -345,4 +346,50 @@ int32_t oracle_dot_f32acc(int64_t K, const void* a, int a_is_u8,
         s = s + p;
     }
     return (int32_t)s;
+}
+
+/* ---------------------------------------------------------------------- */
+/* DynamicQuantizeLinear, uint8 ([P5])                                    */
+/* ---------------------------------------------------------------------- */
+
+/* [P5] "What", DynamicQuantizeLinear paragraph: reduce the input to its
+ * minimum and maximum, scale = (max - min) / 255 with a zero range selecting
+ * scale 1, a zero point rounded with ties to even, then quantize; the
+ * review's all-zero case gives scale 1, zero point 0 and an all-zero output.
+ * Readings where the page is silent:
+ *  - the range is widened to include 0 (min <= 0 <= max), the semantics of
+ *    the ONNX operator the page lowers: a real 0 then quantizes exactly to
+ *    the zero point, and the zero point needs no clamping;
+ *  - every step is fp32 arithmetic (the page reduces f32), each division
+ *    rounded to nearest even; a scale that comes out as 0 takes the
+ *    zero-range value 1;
+ *  - quantizing rounds x / scale to the nearest integer with ties to even,
+ *    adds the zero point and saturates to [0, 255].
+ * y: n bytes; scale_out and zp_out: one value each. */
+void oracle_dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y,
+                                    float* scale_out, int32_t* zp_out) {
+    float mn = 0.0f, mx = 0.0f;        /* the range always includes 0 */
+    for (int64_t i = 0; i < n; ++i) {
+        if (x[i] < mn) mn = x[i];
+        if (x[i] > mx) mx = x[i];
+    }
+    const int saved = fegetround();
+    fesetround(FE_TONEAREST);
+    volatile float range = mx - mn;    /* volatile: keep each fp32 rounding */
+    volatile float scale = range / 255.0f;
+    if (scale == 0.0f) scale = 1.0f;
+    volatile float q0 = mn / scale;
+    volatile float zf = rintf(0.0f - q0);   /* ties to even */
+    int32_t zp = (int32_t)zf;
+    if (zp < 0) zp = 0;
+    if (zp > 255) zp = 255;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float q = x[i] / scale;
+        int64_t v = (int64_t)rintf(q) + zp;
+        y[i] = (uint8_t)(v < 0 ? 0 : (v > 255 ? 255 : v));
+    }
+    fesetround(saved);
+    *scale_out = scale;
+    *zp_out = zp;
 }

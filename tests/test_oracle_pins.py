@@ -497,3 +497,63 @@ def test_w8a32_input_grad_matches_torch_autograd_in_double():
     # the oracle uses the fp32-rounded scale, torch the double one
     rel = abs(float(np.float32(scale)) - scale) / scale
     assert np.all(np.abs(R - X.grad.numpy()) <= (rel + 1e-13) * B + 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# DynamicQuantizeLinear, uint8 (onnx-to-hip page)
+# ---------------------------------------------------------------------------
+
+def _floats(s):
+    return np.array([float(t) for t in s.split()], dtype=np.float32)
+
+
+def test_dynamic_quantize_all_zero_case_from_page():
+    gv = load("dynamic_quantize_linear.txt")
+    y, sc, zp = oracle.dynamic_quantize_linear(np.zeros(8, np.float32))
+    assert sc == np.float32(float(gv["all_zero_scale"]))
+    assert int(zp) == int(gv["all_zero_zero_point"])
+    assert y.tolist() == [int(t) for t in gv["all_zero_output"].split()]
+
+
+@pytest.mark.parametrize("case_name", ["ties_pos", "ties_neg"])
+def test_dynamic_quantize_hand_worked_ties(case_name):
+    gv = load("dynamic_quantize_linear.txt")
+    y, sc, zp = oracle.dynamic_quantize_linear(_floats(gv[case_name + "_input"]))
+    assert sc == np.float32(float(gv[case_name + "_scale"]))
+    assert int(zp) == int(gv[case_name + "_zero_point"])
+    assert y.tolist() == [int(t) for t in gv[case_name + "_output"].split()]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_dynamic_quantize_brute_force(seed):
+    g = si.rng(5000 + seed)
+    n = int(g.integers(1, 300))
+    kind = seed % 4
+    if kind == 0:
+        x = g.standard_normal(n).astype(np.float32)
+    elif kind == 1:
+        x = (g.standard_normal(n) * 1e3 + 5e3).astype(np.float32)      # all positive
+    elif kind == 2:
+        x = -np.abs(g.standard_normal(n)).astype(np.float32) * 1e-3    # all non-positive
+    else:   # many exact ties: multiples of half a step
+        x = (si.randint(g, (n,), -300, 300, np.int64) * 0.5).astype(np.float32)
+    y, sc, zp = oracle.dynamic_quantize_linear(x)
+    by, bsc, bzp = brute.dynamic_quantize_linear([float(v) for v in x])
+    assert float(sc) == bsc and int(zp) == bzp
+    assert y.tolist() == by
+
+
+def test_dynamic_quantize_properties():
+    """For any input: 0 quantizes to the zero point, the minimum (when
+    negative) to 0, and every value dequantizes to within half a step."""
+    for seed in range(6):
+        g = si.rng(6000 + seed)
+        x = (g.standard_normal(5000) * (10.0 ** (seed - 3)) + (seed - 2) * 10.0 ** (seed - 3)).astype(np.float32)
+        x[17] = 0.0
+        y, sc, zp = oracle.dynamic_quantize_linear(x)
+        assert y[17] == zp
+        if x.min() < 0:
+            assert y[int(np.argmin(x))] == 0
+        assert int(y[int(np.argmax(x))]) >= 254
+        deq = (y.astype(np.float64) - int(zp)) * float(sc)
+        assert np.all(np.abs(deq - x.astype(np.float64)) <= 0.5 * float(sc) * (1 + 1e-5))

@@ -7,7 +7,9 @@ the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
 K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
 at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
-points, the W8A32 input gradient at 4096^3) and reports them under "rows".
+points, the W8A32 input gradient at 4096^3, DynamicQuantizeLinear on the
+[8, 512, 2048] fp32 activation and its chain into MatMulInteger) and reports
+them under "rows".
 Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
 that no call finds its inputs in the 256 MB Infinity Cache.
 
@@ -49,10 +51,13 @@ CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops p
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+HEADLINE_SOURCES = ("int8_dma_impl.h", "int8_dma_256x256w8.hip", "device_common.h")
+
+
 def source_hash():
-    """sha256 over the library's kernel and host sources."""
+    """sha256 over the sources the headline kernel is compiled from."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "quantized_int8_gemm_amd", "csrc", "*"))):
+    for f in sorted(os.path.join(ROOT, "quantized_int8_gemm_amd", "csrc", n) for n in HEADLINE_SOURCES):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -111,7 +116,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="time one row only (prefill, decode, mmi, acc, w8a32, small, ceilings)")
+                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, small, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -302,6 +307,32 @@ def main():
                                          "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
         del A, W, tA, tW, outc, dC, tdC
 
+    # ---- DynamicQuantizeLinear on [8, 512, 2048] fp32, and its chain ----
+    if want("dql"):
+        shape = (8, 512, 2048)
+        n = 8 * 512 * 2048
+        x = si.dql_inputs(shape, seed=303)
+        sets = [(to(x), torch.empty(shape, dtype=torch.uint8, device=dev)) for _ in range(13)]
+        call = lambda s: q.dynamic_quantize_linear(s[0], out=s[1])
+        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        nbytes = 4 * n + n + 4 + 1          # read x, write y (the scalars)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows["dynamic_quantize_linear_8x512x2048"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
+                                                     "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+        # fp32 activations -> uint8 + zero point (on the device) -> MatMulInteger
+        _, B, zb = si.matmul_integer_inputs(1, 1, 2048, 2048, seed=303)
+        tB, tzb = to(B), to(zb)
+        sets = [(s[0], s[1], torch.empty((8, 512, 2048), dtype=torch.int32, device=dev)) for s in sets]
+
+        def chain(s):
+            y, _, zp = q.dynamic_quantize_linear(s[0], out=s[1])
+            q.matmul_integer(y, tB, zp.reshape(1), tzb, out=s[2])
+        ms = time_calls(chain, sets, max(steps * 5, 50), warmup * 2, stream)
+        ops = 2.0 * 8 * 512 * 2048 * 2048
+        rows["dql_then_matmul_integer_8x512x2048x2048"] = {"kernels": "dql + " + q.last_kernel(), "us": ms * 1e3,
+                                                          "TOPS": ops / (ms * 1e-3) / 1e12}
+        del sets, x
+
     # ---- the small parity shapes (launch-latency bound) ------------------
     if want("small"):
         A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
@@ -343,11 +374,12 @@ def main():
     if not args.no_cpu_baseline and want("prefill"):
         import oracle
         A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
-        rows_probe = 2
+        rows_probe = 32
+        oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)    # starts the thread pool
         t0 = time.perf_counter()
         oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)
         dt = time.perf_counter() - t0
-        nrows = int(max(rows_probe, min(4096, rows_probe * 15.0 / max(dt, 1e-3))))
+        nrows = int(max(rows_probe, min(8192, rows_probe * 15.0 / max(dt, 1e-3))))
         t0 = time.perf_counter()
         oracle.a8w8(A[:nrows], W, s_a[:nrows], s_w)
         dt = time.perf_counter() - t0

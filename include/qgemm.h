@@ -51,7 +51,7 @@ typedef enum {
 } qg_dtype;
 
 /* Operation ids for qgemm_workspace_bytes. */
-enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2 };
+enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2, QG_OP_DYNAMIC_QUANTIZE_LINEAR = 3 };
 
 /*
  * W8A32: fp32 activations times an int8 weight with a per-tensor scale and
@@ -221,7 +221,42 @@ qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Workspace bytes the fastest kernel for this shape wants (0: none). */
+/*
+ * DynamicQuantizeLinear to uint8 ("feat(onnx-to-hip): lower quantized
+ * integer conv and matmul", section "What", DynamicQuantizeLinear paragraph),
+ * the step that produces MatMulInteger's uint8 activations and their zero
+ * point:
+ *
+ *   lo = min(0, min_i x[i])      hi = max(0, max_i x[i])
+ *   scale = (hi - lo) / 255,  replaced by 1 when it is 0
+ *   zp = clamp(round_half_even(0 - lo / scale), 0, 255)
+ *   y[i] = clamp(round_half_even(x[i] / scale) + zp, 0, 255)
+ *
+ * every step an fp32 operation rounded to nearest even (the division
+ * correctly rounded).  The page fixes the scale, the zero-range case and the
+ * ties-to-even zero point; widening the range to include 0 and saturating
+ * are the ONNX operator's definition the page lowers.  Bit-exact.
+ *   x: n fp32 values, contiguous, finite (NaN or Inf is outside the contract).
+ *   y: n uint8 values, contiguous.  n == 0 is allowed: scale 1, zp 0.
+ *   y_scale: device pointer to one fp32; y_zero_point: device pointer to one
+ *     uint8.  They may feed matmul_integer_row_zp directly (a_zero_point_len
+ *     1) with no host round trip.
+ *   workspace: device memory of at least
+ *     qgemm_workspace_bytes(QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, n, 1)
+ *     bytes (at most 8 KiB), 8-byte aligned; needs no initialisation and
+ *     holds nothing after the call.  Calls that overlap in time must not
+ *     share one.
+ * Two kernels on `stream`: a min/max pass, then a quantize pass.
+ * QG_ERR_INVALID_ARGUMENT for n < 0 or a NULL pointer (x and y may be NULL
+ * when n == 0); QG_ERR_WORKSPACE for a short workspace.
+ */
+qg_status dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y,
+                                  float* y_scale, uint8_t* y_zero_point,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Workspace bytes the fastest kernel for this shape wants (0: none).  For
+ * QG_OP_DYNAMIC_QUANTIZE_LINEAR, N is the element count n. */
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K);
 
 /* Static text for a status code. */

@@ -15,6 +15,8 @@ this package is its thin Python binding, with the same call names:
 * ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
   MatMulInteger, int32 output, shared weight never copied; per-row
   activation zero points go to ``matmul_integer_row_zp``.
+* ``dynamic_quantize_linear(x)``: ONNX DynamicQuantizeLinear to uint8,
+  returning (y, scale, zero_point) on the device.
 
 ``calib_read`` and ``calib_mfma_i8`` measure the machine's HBM read and int8
 matrix-core ceilings for the roofline figures.
@@ -23,10 +25,12 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     QG_OP_A8W8,
     QG_OP_MATMUL_INTEGER,
+    QG_OP_DYNAMIC_QUANTIZE_LINEAR,
     QG_OP_W8A32,
     QGemmError,
     calib_mfma_i8,
     calib_read,
+    dynamic_quantize_linear,
     last_kernel,
     matmul_integer,
     matmul_integer_row_zp,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 
 QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_UNSUPPORTED, QG_ERR_WORKSPACE, QG_ERR_HIP = range(5)
 QG_FP32, QG_BF16, QG_INT32, QG_INT8, QG_UINT8 = range(5)
-QG_OP_W8A32, QG_OP_A8W8, QG_OP_MATMUL_INTEGER = range(3)
+QG_OP_W8A32, QG_OP_A8W8, QG_OP_MATMUL_INTEGER, QG_OP_DYNAMIC_QUANTIZE_LINEAR = range(4)
 
 _p, _i64, _i32, _int, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_size_t)
@@ -34,6 +34,7 @@ PROTOTYPES = {
                         _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer_row_zp": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
                                _p, _i64, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
+    "dynamic_quantize_linear": ([_i64, _p, _p, _p, _p, _p, _sz, _p], _int),
     "qgemm_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
     "qgemm_status_string": ([_int], ctypes.c_char_p),
     "qgemm_last_kernel": ([], ctypes.c_char_p),
@@ -333,6 +334,9 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
         _need(a_zero_point, (A.dtype,), "a_zero_point")
         if a_zero_point.numel() == 1 and a_zero_point.dim() == 0:
             a_zero_point = int(a_zero_point.item())
+        elif a_zero_point.numel() == 1:
+            # one value for every row, read on the device (no host round trip)
+            za_rows = a_zero_point.reshape(-1).contiguous()
         else:
             if a_zero_point.numel() != M or (a_zero_point.dim() == 2 and a_zero_point.shape[1] != 1) \
                     or a_zero_point.dim() > 2:
@@ -388,6 +392,50 @@ def matmul_integer_row_zp(A, B, a_zero_point, b_zero_point=None, out=None):
     if not isinstance(a_zero_point, torch.Tensor) or a_zero_point.dim() == 0:
         raise ValueError("a_zero_point must be a tensor of M per-row values")
     return matmul_integer(A, B, a_zero_point, b_zero_point, out)
+
+
+# ---------------------------------------------------------------------------
+# DynamicQuantizeLinear (uint8)
+# ---------------------------------------------------------------------------
+
+_dql_workspaces = {}
+
+
+def dynamic_quantize_linear(x, out=None, workspace=None):
+    """ONNX DynamicQuantizeLinear to uint8 on the GPU.
+
+    x: float32 tensor of any shape (contiguous).  Returns (y, scale, zero_point):
+    y uint8 of x's shape, scale a 0-d float32 tensor and zero_point a 0-d uint8
+    tensor, all on x's device (no host round trip: zero_point can go straight
+    to matmul_integer_row_zp).  The min/max partials live in a workspace of
+    their own per (device, stream) unless one is passed."""
+    _need(x, (torch.float32,), "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    dev = _on_gpu(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    else:
+        _need(out, (torch.uint8,), "out")
+        if tuple(out.shape) != tuple(x.shape) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous uint8 tensor of x's shape")
+    scale = torch.empty((), dtype=torch.float32, device=dev)
+    zp = torch.empty((), dtype=torch.uint8, device=dev)
+    need = workspace_bytes(QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, n, 1)
+    if workspace is None:
+        key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+        ws = _dql_workspaces.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 8192), dtype=torch.uint8, device=dev)
+            _dql_workspaces[key] = ws
+    else:
+        _need(workspace, (torch.uint8, torch.int8), "workspace")
+        ws = workspace
+    st = lib.dynamic_quantize_linear(n, _ptr(x) if n else None, _ptr(out) if n else None, _ptr(scale), _ptr(zp),
+                                     _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "dynamic_quantize_linear")
+    return out, scale, zp
 
 
 # ---------------------------------------------------------------------------

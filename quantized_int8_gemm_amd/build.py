@@ -27,12 +27,14 @@ SOURCES = [
     "int8_dma_256x128w8.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
+    "dynamic_quantize.hip",
     "calibrate.hip",
     "api.cpp",
 ]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Wall", "-Wno-unused-function"]
 
 

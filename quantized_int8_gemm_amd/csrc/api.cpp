@@ -182,6 +182,7 @@ static bool a8w8_is_skinny(int64_t M, int b_trans) {
 
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
     (void)batch;
+    if (op == QG_OP_DYNAMIC_QUANTIZE_LINEAR) return N < 0 ? 0 : (size_t)qg::dql_partials(N) * 8;
     if (op != QG_OP_A8W8 || !dims_ok(M, N, K) || !a8w8_is_skinny(M, 0)) return 0;
     const int splits = a8w8_skinny_splits(M, N, K);
     return qg::skinny_workspace_bytes((int)M, (int)N, splits);
@@ -419,6 +420,25 @@ qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K, 
     return matmul_integer_impl(batch, M, N, K, A, a_dtype, lda, a_batch_stride, B, b_dtype, ldb, b_batch_stride,
                                za0, a_zero_point, a_zero_point_len, b_zero_point, b_zero_point_len, Y, ldy,
                                y_batch_stride, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+qg_status dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y, float* y_scale, uint8_t* y_zero_point,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || y_scale == nullptr || y_zero_point == nullptr || workspace == nullptr)
+        return QG_ERR_INVALID_ARGUMENT;
+    if (n > 0 && (x == nullptr || y == nullptr)) return QG_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0) return QG_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < (size_t)qg::dql_partials(n) * 8) return QG_ERR_WORKSPACE;
+    const bool vec = aligned16(x) && aligned16(y);
+    (void)hipGetLastError();
+    const hipError_t e = qg::launch_dynamic_quantize(x, n, y, y_scale, y_zero_point, workspace, vec,
+                                                     (hipStream_t)stream);
+    log_dispatch("dynamic_quantize_linear", "dql_minmax+dql_quantize", 1, 1, n, 1, qg::dql_partials(n));
+    return finish_launch(e, "dql_minmax+dql_quantize");
 }
 
 }  // extern "C"

@@ -87,6 +87,13 @@ struct W8A32Args {
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                         const char** name);
 
+// DynamicQuantizeLinear (uint8): a min/max pass writing one (min, max)
+// float pair per workgroup into the workspace, then a quantize pass.
+constexpr int DQL_MAX_PARTIALS = 1024;
+int dql_partials(int64_t n);
+hipError_t launch_dynamic_quantize(const float* x, int64_t n, uint8_t* y, float* y_scale, uint8_t* y_zp,
+                                   void* workspace, bool vec, hipStream_t s);
+
 // Calibration kernels (roofline ceilings; no part of the method).  Each
 // writes one word per wave: CALIB_*_BLOCKS * 4 words of sink.
 constexpr int CALIB_READ_BLOCKS = 2048;

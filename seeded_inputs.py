@@ -10,6 +10,8 @@ inputs.  Distributions follow the workloads the operators are measured on:
   column scales uniform over [0.001, 0.05).
 * MatMulInteger: uint8 activations uniform over [0, 255]; int8 weight uniform
   over [-128, 127]; per-column int8 weight zero points uniform over [-8, 8].
+* DynamicQuantizeLinear: fp32 activations ~ N(mean, std) of the shape of
+  MatMulInteger's activations, which it produces.
 
 Every generator takes an explicit seed and uses numpy's PCG64 generator, so a
 given (shape, seed) always yields the same bytes.
@@ -54,3 +56,9 @@ def matmul_integer_inputs(batch, M, N, K, seed, a_dtype=np.uint8, b_dtype=np.int
     else:
         zb = randint(g, (N,), 120, 136, np.uint8)
     return A, B, zb
+
+
+def dql_inputs(shape, seed, mean=0.0, std=1.0):
+    g = rng(seed)
+    x = g.standard_normal(shape, dtype=np.float32)
+    return (x * np.float32(std) + np.float32(mean)).astype(np.float32)

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q\w+|matmul_integer\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q\w+|matmul_integer\w*|dynamic_quantize_linear)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
                           "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_a8w8_acc",
-                          "matmul_integer_row_zp", "qgemm_w8a32_input_grad"}
+                          "matmul_integer_row_zp", "qgemm_w8a32_input_grad", "dynamic_quantize_linear"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -51,6 +51,12 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 0
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 8, 512, 2048, 2048) == 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 0, 8192, 8192) == 0
+    # DynamicQuantizeLinear: one (min, max) float pair per partial, at most 8 KiB
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 0, 1) == 8
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 4096, 1) == 8
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 4097, 1) == 16
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 8 * 512 * 2048, 1) == 8192
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 1 << 34, 1) == 8192
 
 
 def w8a32(**kw):
@@ -227,3 +233,21 @@ def test_w8a32_input_grad_rejects_bad_arguments():
         q.qgemm_w8a32_input_grad(torch.zeros(4, 16), torch.zeros(8, 15, dtype=torch.int8), 0.5)
     with pytest.raises(TypeError):
         q.qgemm_w8a32_input_grad(torch.zeros(4, 16), torch.zeros(8, 16), 0.5)
+
+
+def test_dynamic_quantize_linear_rejects_bad_arguments():
+    lib = b.lib
+    ok = dict(n=16, x=FAKE, y=FAKE, sc=FAKE, zp=FAKE, ws=FAKE, wsz=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.dynamic_quantize_linear(a["n"], a["x"], a["y"], a["sc"], a["zp"], a["ws"], a["wsz"], None)
+    for kw in (dict(n=-1), dict(x=None), dict(y=None), dict(sc=None), dict(zp=None), dict(ws=None),
+               dict(ws=ctypes.c_void_p(4100))):
+        assert call(**kw) == b.QG_ERR_INVALID_ARGUMENT, kw
+    assert call(wsz=7) == b.QG_ERR_WORKSPACE
+    assert call(n=4097, wsz=8) == b.QG_ERR_WORKSPACE
+    with pytest.raises(TypeError):
+        q.dynamic_quantize_linear(torch.zeros(8, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        q.dynamic_quantize_linear(torch.zeros(8))   # a CPU tensor

@@ -243,7 +243,7 @@ qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K,
  *     1) with no host round trip.
  *   workspace: device memory of at least
  *     qgemm_workspace_bytes(QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, n, 1)
- *     bytes (at most 8 KiB), 8-byte aligned; needs no initialisation and
+ *     bytes (at most 2 KiB), 8-byte aligned; needs no initialisation and
  *     holds nothing after the call.  Calls that overlap in time must not
  *     share one.
  * Two kernels on `stream`: a min/max pass, then a quantize pass.
@@ -277,7 +277,7 @@ const char* qgemm_version(void);
  * asynchronous on `stream`.
  *
  * qgemm_calib_read: reads `bytes` bytes of device memory at `buf` once,
- *   16-byte vectors with a grid stride.  buf 16-byte aligned, bytes a
+ *   each workgroup one contiguous share as non-temporal 16-byte vectors.  buf 16-byte aligned, bytes a
  *   positive multiple of 16; otherwise QG_ERR_INVALID_ARGUMENT.
  * qgemm_calib_mfma_i8: runs `iters` (1 .. 2^20) rounds of int8 matrix-core
  *   multiplies (v_mfma_i32_16x16x64_i8, 16 independent per wave per round)

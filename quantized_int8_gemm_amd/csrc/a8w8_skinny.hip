@@ -11,7 +11,8 @@
 // [K/S x 256] slab of W once; its four waves take 64-row steps round robin.
 //  * A lane (g = lane/16, c = lane%16) loads rows 16g .. 16g+15 of the step
 //    as 16-byte vectors at columns 16c .. 16c+15 (16 lanes cover 256
-//    contiguous bytes of a row), two steps ahead of the one being multiplied.
+//    contiguous bytes of a row), two steps ahead of the one being multiplied,
+//    with the non-temporal cache policy (every weight byte is read once).
 //  * The lane's 16 x 16 byte block is transposed in registers; column j of it
 //    is then exactly a matrix-core B fragment (16 k-bytes of column 16c + j),
 //    and row c of A is the matching A fragment, so v_mfma_i32_16x16x64_i8
@@ -59,7 +60,7 @@ __device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
 }
 
 template <bool VEC, int EPI>
-__global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
     __shared__ __attribute__((aligned(16))) int32_t red[WAVES][16][TN];
     __shared__ float ws_tile[TN];
     __shared__ float as_rows[16];
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(NT) void a8w8_skinny_kernel(Int8GemmArgs p) {
         const int k0 = step * KS;
         if constexpr (VEC) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb), 0u);
+            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb));
             abuf[b] = buffer_load16(a_rsrc, a_voff + (uint32_t)k0, 0u);
         } else {
 #pragma unroll

@@ -89,7 +89,7 @@ hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hip
 
 // DynamicQuantizeLinear (uint8): a min/max pass writing one (min, max)
 // float pair per workgroup into the workspace, then a quantize pass.
-constexpr int DQL_MAX_PARTIALS = 1024;
+constexpr int DQL_MAX_PARTIALS = 256;
 int dql_partials(int64_t n);
 hipError_t launch_dynamic_quantize(const float* x, int64_t n, uint8_t* y, float* y_scale, uint8_t* y_zp,
                                    void* workspace, bool vec, hipStream_t s);

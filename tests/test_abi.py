@@ -51,12 +51,12 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 0
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 8, 512, 2048, 2048) == 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 0, 8192, 8192) == 0
-    # DynamicQuantizeLinear: one (min, max) float pair per partial, at most 8 KiB
+    # DynamicQuantizeLinear: one (min, max) float pair per 128 KiB of x, at most 2 KiB
     assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 0, 1) == 8
-    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 4096, 1) == 8
-    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 4097, 1) == 16
-    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 8 * 512 * 2048, 1) == 8192
-    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 1 << 34, 1) == 8192
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 32768, 1) == 8
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 32769, 1) == 16
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 8 * 512 * 2048, 1) == 2048
+    assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 1 << 34, 1) == 2048
 
 
 def w8a32(**kw):
@@ -246,7 +246,7 @@ def test_dynamic_quantize_linear_rejects_bad_arguments():
                dict(ws=ctypes.c_void_p(4100))):
         assert call(**kw) == b.QG_ERR_INVALID_ARGUMENT, kw
     assert call(wsz=7) == b.QG_ERR_WORKSPACE
-    assert call(n=4097, wsz=8) == b.QG_ERR_WORKSPACE
+    assert call(n=32769, wsz=8) == b.QG_ERR_WORKSPACE
     with pytest.raises(TypeError):
         q.dynamic_quantize_linear(torch.zeros(8, dtype=torch.float64))
     with pytest.raises(ValueError):

@@ -22,6 +22,10 @@ function) with numpy arrays in and out, by calling the plain C loops in
 * ``dot_f32acc``: the f32-accumulator form that page selects only while
   65025*K fits fp32's 24-bit mantissa (used to pin that bound).
 * ``f32_to_bf16``: round-to-nearest-even conversion to bfloat16 bits.
+* ``dynamic_quantize_linear``: ONNX DynamicQuantizeLinear to uint8 as the
+  onnx-to-hip page lowers it.
+* ``conv_integer``: ONNX ConvInteger (NCHW / NCL, groups, padding, strides,
+  dilations, scalar activation and per-channel weight zero points).
 """
 import ctypes
 import os
@@ -80,6 +84,9 @@ def _load():
     lib.oracle_dot_f32acc.restype = _i32
     lib.oracle_dynamic_quantize_linear.argtypes = [_i64, _p, _p, _p, _p]
     lib.oracle_dynamic_quantize_linear.restype = None
+    lib.oracle_conv_integer.argtypes = [_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _i64, _p, _int, _i64,
+                                        _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _p, _i64, _p]
+    lib.oracle_conv_integer.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = _int
     _lib = lib
@@ -354,3 +361,53 @@ def dynamic_quantize_linear(x):
     zp = np.empty(1, dtype=np.int32)
     lib.oracle_dynamic_quantize_linear(xs.size, _ptr(xs), _ptr(y), _ptr(sc), _ptr(zp))
     return y.reshape(np.shape(x)), np.float32(sc[0]), np.uint8(zp[0])
+
+
+# ---------------------------------------------------------------------------
+# ConvInteger
+# ---------------------------------------------------------------------------
+
+def conv_output_size(size, k, pad_lo, pad_hi, stride, dilation):
+    return (size + pad_lo + pad_hi - dilation * (k - 1) - 1) // stride + 1
+
+
+def conv_integer(x, w, x_zero_point=0, w_zero_point=None, pads=None, strides=None, dilations=None, group=1):
+    """ONNX ConvInteger as the onnx-to-hip page lowers it ("What",
+    ConvInteger paragraph): int32 y = wrap32(sum (x - x_zp) (w - w_zp[m]))
+    over each output channel's group, taps outside the input contributing
+    nothing.
+
+    x: uint8/int8 [N, C, H, W] or [N, C, L]; w: uint8/int8 [M, C/group, kH, kW]
+    or [M, C/group, kL].  pads: (top, left, bottom, right) for rank 4,
+    (left, right) for rank 3; strides / dilations: per spatial axis.
+    w_zero_point: None, a scalar, or M values.  Returns int32 [N, M, OH, OW]
+    (or [N, M, OL])."""
+    lib = _load()
+    x = np.asarray(x)
+    w = np.asarray(w)
+    rank3 = x.ndim == 3
+    if rank3:
+        x = x[:, :, None, :]
+        w = w[:, :, None, :]
+        pads = (0, pads[0], 0, pads[1]) if pads is not None else None
+        strides = (1, strides[0]) if strides is not None else None
+        dilations = (1, dilations[0]) if dilations is not None else None
+    pads = tuple(pads) if pads is not None else (0, 0, 0, 0)
+    strides = tuple(strides) if strides is not None else (1, 1)
+    dilations = tuple(dilations) if dilations is not None else (1, 1)
+    N, C, H, W = x.shape
+    M, Cg, kH, kW = w.shape
+    assert C == Cg * group and M % group == 0
+    OH = conv_output_size(H, kH, pads[0], pads[2], strides[0], dilations[0])
+    OW = conv_output_size(W, kW, pads[1], pads[3], strides[1], dilations[1])
+    if w_zero_point is None:
+        zw = np.zeros(0, dtype=np.int32)
+    else:
+        zw = np.asarray(w_zero_point).reshape(-1).astype(np.int32)
+    xs = _c(x, x.dtype)
+    ws = _c(w, w.dtype)
+    y = np.empty((N, M, OH, OW), dtype=np.int32)
+    lib.oracle_conv_integer(N, C, H, W, _ptr(xs), _is_u8(xs), M, kH, kW, _ptr(ws), _is_u8(ws), group,
+                            pads[0], pads[1], pads[2], pads[3], strides[0], strides[1], dilations[0], dilations[1],
+                            int(x_zero_point), _ptr(zw) if zw.size else None, zw.size, _ptr(y))
+    return y[:, :, 0, :] if rank3 else y

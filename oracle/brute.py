@@ -138,3 +138,31 @@ def dynamic_quantize_linear(xs):
     zp = min(255, max(0, zp))
     y = [min(255, max(0, round(f32(x / scale)) + zp)) for x in xs]
     return y, scale, zp
+
+
+def conv_integer(x, w, x_zp, w_zp, pads, strides, dilations, group):
+    """ConvInteger on nested lists with Python integers: x [N][C][H][W],
+    w [M][C/group][kH][kW], w_zp a list of M values; pads (top, left,
+    bottom, right).  Taps outside the input are skipped.  Returns y
+    [N][M][OH][OW], each the exact sum wrapped to int32."""
+    N, C, H, W = len(x), len(x[0]), len(x[0][0]), len(x[0][0][0])
+    M, Cg, kH, kW = len(w), len(w[0]), len(w[0][0]), len(w[0][0][0])
+    Mg = M // group
+    OH = (H + pads[0] + pads[2] - dilations[0] * (kH - 1) - 1) // strides[0] + 1
+    OW = (W + pads[1] + pads[3] - dilations[1] * (kW - 1) - 1) // strides[1] + 1
+    y = [[[[0] * OW for _ in range(OH)] for _ in range(M)] for _ in range(N)]
+    for n in range(N):
+        for m in range(M):
+            g = m // Mg
+            for oh in range(OH):
+                for ow in range(OW):
+                    s = 0
+                    for c in range(Cg):
+                        for kh in range(kH):
+                            for kw in range(kW):
+                                ih = oh * strides[0] - pads[0] + kh * dilations[0]
+                                iw = ow * strides[1] - pads[1] + kw * dilations[1]
+                                if 0 <= ih < H and 0 <= iw < W:
+                                    s += (x[n][g * Cg + c][ih][iw] - x_zp) * (w[m][c][kh][kw] - w_zp[m])
+                    y[n][m][oh][ow] = wrap32(s)
+    return y

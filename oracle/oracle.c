@@ -29,7 +29,9 @@
  *       section "What", DynamicQuantizeLinear paragraph, MatMulInteger
  *       paragraph (ranks 2-4, zero points, shared B) and the accumulator paragraph (f32 accumulation only while
  *       65025*K fits the 24-bit mantissa, otherwise int64 accumulation stored
- *       as a wrapping int32).
+ *       as a wrapping int32), and the ConvInteger paragraph (rank-3 NCL and
+ *       rank-4 NCHW, scalar activation zero point, weight zero point scalar
+ *       or one per output channel, groups).
  */
 #include <math.h>
 #include <fenv.h>
@@ -392,4 +394,62 @@ void oracle_dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y,
     fesetround(saved);
     *scale_out = scale;
     *zp_out = zp;
+}
+
+/* ---------------------------------------------------------------------- */
+/* ConvInteger ([P5])                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* [P5] "What", ConvInteger paragraph, with the grouped, padded, strided case
+ * of its GPU numeric tests: an integer convolution of x [N, C, H, W] with
+ * w [M, C/group, kH, kW], each operand minus its zero point, summed exactly
+ * and stored as a wrapping int32 (the accumulator paragraph):
+ *
+ *   y[n, m, oh, ow] = wrap32( sum_{c < C/group, kh < kH, kw < kW}
+ *       (x[n, g*(C/group) + c, ih, iw] - x_zp) * (w[m, c, kh, kw] - w_zp[m]) )
+ *   g = m / (M/group),  ih = oh*sh - pt + kh*dh,  iw = ow*sw - pl + kw*dw,
+ *   OH = (H + pt + pb - dh*(kH - 1) - 1) / sh + 1, likewise OW.
+ *
+ * Reading where the page is silent: a tap outside the input contributes
+ * nothing, i.e. the input is padded with its own zero point (the page's
+ * lowering subtracts the zero point first and then convolves with zero
+ * padding, which is the same thing).  w_zp: w_zp_len 0 (none: all zero),
+ * 1 (scalar) or M (one per output channel).  A rank-3 NCL convolution is the
+ * H = kH = 1 case.  y: [N, M, OH, OW] int32. */
+void oracle_conv_integer(int64_t N, int64_t C, int64_t H, int64_t W,
+                         const void* x, int x_is_u8,
+                         int64_t M, int64_t kH, int64_t kW,
+                         const void* w, int w_is_u8, int64_t group,
+                         int64_t pt, int64_t pl, int64_t pb, int64_t pr,
+                         int64_t sh, int64_t sw, int64_t dh, int64_t dw,
+                         int32_t x_zp, const int32_t* w_zp, int64_t w_zp_len,
+                         int32_t* y) {
+    const int64_t Cg = C / group, Mg = M / group;
+    const int64_t OH = (H + pt + pb - dh * (kH - 1) - 1) / sh + 1;
+    const int64_t OW = (W + pl + pr - dw * (kW - 1) - 1) / sw + 1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            const int64_t g = m / Mg;
+            const int64_t zw = w_zp_len == 0 ? 0 : (w_zp_len == 1 ? w_zp[0] : w_zp[m]);
+            for (int64_t oh = 0; oh < OH; ++oh) {
+                for (int64_t ow = 0; ow < OW; ++ow) {
+                    int64_t s = 0;
+                    for (int64_t c = 0; c < Cg; ++c) {
+                        for (int64_t kh = 0; kh < kH; ++kh) {
+                            for (int64_t kw = 0; kw < kW; ++kw) {
+                                const int64_t ih = oh * sh - pt + kh * dh;
+                                const int64_t iw = ow * sw - pl + kw * dw;
+                                if (ih < 0 || ih >= H || iw < 0 || iw >= W) continue;
+                                const int64_t xv = load_8bit(x, x_is_u8, ((n * C + g * Cg + c) * H + ih) * W + iw);
+                                const int64_t wv = load_8bit(w, w_is_u8, ((m * Cg + c) * kH + kh) * kW + kw);
+                                s += (xv - x_zp) * (wv - zw);
+                            }
+                        }
+                    }
+                    y[((n * M + m) * OH + oh) * OW + ow] = wrap_i32(s);
+                }
+            }
+        }
+    }
 }

@@ -557,3 +557,125 @@ def test_dynamic_quantize_properties():
         assert int(y[int(np.argmax(x))]) >= 254
         deq = (y.astype(np.float64) - int(zp)) * float(sc)
         assert np.all(np.abs(deq - x.astype(np.float64)) <= 0.5 * float(sc) * (1 + 1e-5))
+
+
+# ---------------------------------------------------------------------------
+# ConvInteger (onnx-to-hip page, "What" and its GPU numeric tests)
+# ---------------------------------------------------------------------------
+
+def _conv_case(seed, N, C, H, W, M, kH, kW, group, x_u8, w_u8, per_channel):
+    g = si.rng(seed)
+    xlo, xhi = (0, 255) if x_u8 else (-128, 127)
+    wlo, whi = (0, 255) if w_u8 else (-128, 127)
+    x = si.randint(g, (N, C, H, W), xlo, xhi, np.uint8 if x_u8 else np.int8)
+    w = si.randint(g, (M, C // group, kH, kW), wlo, whi, np.uint8 if w_u8 else np.int8)
+    x_zp = int(si.randint(g, (), xlo, xhi, np.int64))
+    if per_channel:
+        w_zp = si.randint(g, (M,), wlo, whi, np.int64)
+    else:
+        w_zp = np.full(M, int(si.randint(g, (), wlo, whi, np.int64)))
+    return x, w, x_zp, w_zp
+
+
+def _torch_conv_fp64(x, w, x_zp, w_zp, pads, strides, dilations, group):
+    """The same convolution through torch's fp64 conv2d on the zero-point
+    shifted operands, padded with 0 after the shift (exact: every partial sum
+    is an integer far below 2^53)."""
+    xf = torch.from_numpy(x.astype(np.float64) - x_zp)
+    wf = torch.from_numpy(w.astype(np.float64) - np.asarray(w_zp, np.float64).reshape(-1, 1, 1, 1))
+    xf = torch.nn.functional.pad(xf, (pads[1], pads[3], pads[0], pads[2]), value=0.0)
+    y = torch.nn.functional.conv2d(xf, wf, stride=strides, dilation=dilations, groups=group)
+    return y.numpy()
+
+
+CONV_LIBRARY_CASES = [
+    # N, C, H, W, M, kH, kW, group, pads, strides, dilations, x_u8, w_u8, per_channel
+    (2, 6, 9, 11, 4, 3, 3, 1, (1, 1, 1, 1), (1, 1), (1, 1), True, False, True),
+    (1, 58, 7, 7, 6, 3, 3, 2, (1, 1, 1, 1), (2, 2), (1, 1), True, False, True),   # reduction 261, stride 2, 2 groups
+    (2, 8, 10, 6, 8, 3, 2, 4, (2, 0, 1, 3), (2, 1), (1, 2), False, True, False),
+    (3, 5, 6, 13, 7, 1, 5, 1, (0, 2, 0, 2), (1, 3), (1, 1), False, False, True),
+    (1, 4, 12, 12, 4, 3, 3, 4, (1, 1, 1, 1), (1, 1), (2, 2), True, True, True),    # depthwise, dilated
+]
+
+
+@pytest.mark.parametrize("case", CONV_LIBRARY_CASES)
+def test_conv_integer_equals_torch_conv2d_fp64(case):
+    N, C, H, W, M, kH, kW, group, pads, strides, dil, x_u8, w_u8, per_ch = case
+    x, w, x_zp, w_zp = _conv_case(sum(case[:7]), N, C, H, W, M, kH, kW, group, x_u8, w_u8, per_ch)
+    y = oracle.conv_integer(x, w, x_zp, w_zp, pads=pads, strides=strides, dilations=dil, group=group)
+    ref = _torch_conv_fp64(x, w, x_zp, w_zp, pads, strides, dil, group)
+    assert y.shape == ref.shape
+    np.testing.assert_array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_conv_integer_brute_force(seed):
+    g = si.rng(7000 + seed)
+    group = int(g.choice([1, 2]))
+    Cg, Mg = int(g.integers(1, 3)), int(g.integers(1, 3))
+    kH, kW = int(g.integers(1, 4)), int(g.integers(1, 4))
+    H, W = int(g.integers(kH, 6)), int(g.integers(kW, 6))
+    pads = tuple(int(v) for v in g.integers(0, 3, size=4))
+    strides = tuple(int(v) for v in g.integers(1, 3, size=2))
+    dil = tuple(int(v) for v in g.integers(1, 3, size=2))
+    if H + pads[0] + pads[2] < dil[0] * (kH - 1) + 1 or W + pads[1] + pads[3] < dil[1] * (kW - 1) + 1:
+        dil = (1, 1)
+    x, w, x_zp, w_zp = _conv_case(7100 + seed, 2, Cg * group, H, W, Mg * group, kH, kW, group,
+                                  seed % 2 == 0, seed % 3 == 0, True)
+    y = oracle.conv_integer(x, w, x_zp, w_zp, pads=pads, strides=strides, dilations=dil, group=group)
+    by = brute.conv_integer(x.astype(np.int64).tolist(), w.astype(np.int64).tolist(), x_zp,
+                            [int(v) for v in w_zp], pads, strides, dil, group)
+    assert y.tolist() == by
+
+
+def test_conv_integer_1x1_is_matmul_integer():
+    """A 1x1, stride-1, unpadded convolution of image n is the MatMulInteger
+    W [M, C] x X_n [C, H*W] with the weight zero points as per-row zero points
+    of the left operand and the activation zero point as B's."""
+    x, w, x_zp, w_zp = _conv_case(31, 3, 37, 5, 7, 9, 1, 1, 1, True, False, True)
+    y = oracle.conv_integer(x, w, x_zp, w_zp)
+    for n in range(3):
+        ref = oracle.matmul_integer(w.reshape(9, 37), x[n].reshape(37, 35), w_zp.reshape(9), x_zp)
+        np.testing.assert_array_equal(y[n].reshape(9, 35), ref)
+
+
+def test_conv_integer_259_channel_1x1_worked_value_from_page():
+    """The page's 259-channel 1x1 convolution; with every byte 255 and zero
+    points 0 each output is the length-259 dot product the page works out."""
+    gv = load("matmul_integer_accumulator.txt")
+    x = np.full((1, 259, 2, 3), 255, np.uint8)
+    w = np.full((2, 259, 1, 1), 255, np.uint8)
+    y = oracle.conv_integer(x, w, 0, None)
+    assert np.all(y == int(gv["u8_all_255_k259"]))
+
+
+def test_conv_integer_constant_fill_counts_in_bounds_taps():
+    """Constant operands: each output is (taps inside the input) * C/group *
+    (a - za)(b - zb); with a 3x3 window and padding 1 that is 9 inside, 6 on
+    an edge and 4 in a corner."""
+    a, za, b, zb = 200, 13, -7, 5
+    x = np.full((1, 4, 5, 6), a, np.uint8)
+    w = np.full((4, 2, 3, 3), b, np.int8)
+    y = oracle.conv_integer(x, w, za, np.full(4, zb), pads=(1, 1, 1, 1), group=2)[0]
+    unit = 2 * (a - za) * (b - zb)
+    taps = np.full((5, 6), 9)
+    taps[0, :] = taps[-1, :] = 6
+    taps[:, 0] = taps[:, -1] = 6
+    taps[0, 0] = taps[0, -1] = taps[-1, 0] = taps[-1, -1] = 4
+    for m in range(4):
+        np.testing.assert_array_equal(y[m], taps * unit)
+
+
+def test_conv_integer_wraps_like_matmul_integer():
+    gv = load("matmul_integer_accumulator.txt")
+    x = np.full((1, 40000, 1, 1), 255, np.uint8)
+    w = np.full((1, 40000, 1, 1), 255, np.uint8)
+    assert oracle.conv_integer(x, w, 0, None)[0, 0, 0, 0] == int(gv["u8_all_255_k40000_wrapped"])
+
+
+def test_conv_integer_rank3_is_rank4_with_unit_height():
+    x, w, x_zp, w_zp = _conv_case(41, 2, 6, 1, 17, 4, 1, 3, 2, False, False, True)
+    y4 = oracle.conv_integer(x, w, x_zp, w_zp, pads=(0, 2, 0, 1), strides=(1, 2), dilations=(1, 2), group=2)
+    y3 = oracle.conv_integer(x[:, :, 0, :], w[:, :, 0, :], x_zp, w_zp, pads=(2, 1), strides=(2,), dilations=(2,),
+                             group=2)
+    np.testing.assert_array_equal(y3, y4[:, :, 0, :])

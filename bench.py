@@ -8,8 +8,8 @@ K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
 at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
 points, the W8A32 input gradient at 4096^3, DynamicQuantizeLinear on the
-[8, 512, 2048] fp32 activation and its chain into MatMulInteger) and reports
-them under "rows".
+[8, 512, 2048] fp32 activation and its chain into MatMulInteger, ConvInteger on
+a 3x3 layer of 64 images) and reports them under "rows".
 Decode and MatMulInteger rotate through enough distinct buffers (> 512 MiB)
 that no call finds its inputs in the 256 MB Infinity Cache.
 
@@ -109,6 +109,14 @@ def measured_traffic():
     return t["traffic_bytes_per_dispatch"] if t.get("source_sha256") == source_hash() else None
 
 
+def conv_workspace_bytes(q, N, C, H, W, M, kH, kW, pad=1):
+    """Workspace of a stride-1 convolution padded by `pad` on every side."""
+    import ctypes
+    i64 = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    return int(q._binding.lib.conv_integer_workspace_bytes(N, C, H, W, M, kH, kW, 1, i64(pad, pad, pad, pad),
+                                                           i64(1, 1), i64(1, 1)))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +124,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, small, ceilings)")
+                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, conv, small, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -332,6 +340,23 @@ def main():
         rows["dql_then_matmul_integer_8x512x2048x2048"] = {"kernels": "dql + " + q.last_kernel(), "us": ms * 1e3,
                                                           "TOPS": ops / (ms * 1e-3) / 1e12}
         del sets, x
+
+    # ---- ConvInteger: a 3x3 tokenizer-sized layer -------------------------
+    if want("conv"):
+        N_, C_, H_, W_, M_ = 64, 64, 32, 32, 128
+        x, w, zw = si.conv_integer_inputs(N_, C_, H_, W_, M_, 3, 3, seed=808)
+        tw, tzw = to(w), to(zw)
+        sets = [(to(x), torch.empty((N_, M_, H_, W_), dtype=torch.int32, device=dev)) for _ in range(13)]
+        ws = torch.empty(conv_workspace_bytes(q, N_, C_, H_, W_, M_, 3, 3), dtype=torch.uint8, device=dev)
+        call = lambda s: q.conv_integer(s[0], tw, 128, tzw, pads=(1, 1, 1, 1), out=s[1], workspace=ws)
+        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        ops = 2.0 * N_ * M_ * H_ * W_ * C_ * 9
+        nbytes = N_ * C_ * H_ * W_ + M_ * C_ * 9 + M_ + 4 * N_ * M_ * H_ * W_
+        rows["conv_integer_64x64x32x32_k3x3_m128"] = {"kernels": q.last_kernel(), "us": ms * 1e3,
+                                                     "TOPS": ops / (ms * 1e-3) / 1e12,
+                                                     "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                                                     "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+        del sets, ws
 
     # ---- the small parity shapes (launch-latency bound) ------------------
     if want("small"):

@@ -255,6 +255,60 @@ qg_status dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/*
+ * ConvInteger ("feat(onnx-to-hip): lower quantized integer conv and matmul",
+ * section "What", ConvInteger paragraph; the grouped, padded, strided case of
+ * its GPU numeric tests):
+ *
+ *   y[n, m, oh, ow] = wrap32( sum_{c < C/group, kh, kw}
+ *       (x[n, g*(C/group) + c, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw] - x_zp)
+ *       * (w[m, c, kh, kw] - w_zp[m]) ),   g = m / (M/group)
+ *
+ * summed exactly and stored as a wrapping int32 (the page's int64-then-wrap
+ * result for any reduction length).  A tap outside the input contributes
+ * nothing: the input is padded with its own zero point (the page's lowering
+ * subtracts the zero point, then convolves with zero padding).  Bit-exact.
+ *   x: x_dtype QG_UINT8 or QG_INT8, [N, C, H, W] contiguous.  A rank-3 NCL
+ *      input is H = 1 (kH = 1, pads[0] = pads[2] = 0).
+ *   w: w_dtype QG_UINT8 or QG_INT8, [M, C/group, kH, kW] contiguous.
+ *   group >= 1 divides C and M.
+ *   pads: host int64[4] = {top, left, bottom, right} >= 0;
+ *   strides, dilations: host int64[2] = {h, w} >= 1.
+ *   OH = (H + top + bottom - dilations[0]*(kH-1) - 1) / strides[0] + 1 >= 1,
+ *   OW likewise.
+ *   x_zero_point: scalar within x_dtype's range.
+ *   w_zero_point: device pointer to w_dtype values, NULL (all zero,
+ *      w_zero_point_len 0), or w_zero_point_len 1 (scalar) or M (one per
+ *      output channel).
+ *   y: int32 [N, M, OH, OW] contiguous.
+ *   workspace: device memory of at least conv_integer_workspace_bytes(...)
+ *      bytes, 256-byte aligned, no initialisation needed; it receives the
+ *      packed weight and the column matrices.  Calls that overlap in time
+ *      must not share one.
+ * Kernels on `stream`: a weight pack, an im2col gather, and one batched int8
+ * matrix-core GEMM per group.  Requires N < 65536.  QG_ERR_INVALID_ARGUMENT:
+ * a bad size, dtype, zero point, pointer or alignment; QG_ERR_WORKSPACE: a
+ * short workspace; QG_ERR_UNSUPPORTED: one image's column matrix or one
+ * group's weight spans 2^31 bytes.
+ */
+qg_status conv_integer(int64_t N, int64_t C, int64_t H, int64_t W,
+                       const void* x, qg_dtype x_dtype,
+                       int64_t M, int64_t kH, int64_t kW,
+                       const void* w, qg_dtype w_dtype,
+                       int64_t group,
+                       const int64_t* pads, const int64_t* strides, const int64_t* dilations,
+                       int32_t x_zero_point,
+                       const void* w_zero_point, int64_t w_zero_point_len,
+                       int32_t* y,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Workspace bytes conv_integer needs for these sizes (0: sizes invalid). */
+size_t conv_integer_workspace_bytes(int64_t N, int64_t C, int64_t H, int64_t W,
+                                    int64_t M, int64_t kH, int64_t kW, int64_t group,
+                                    const int64_t* pads, const int64_t* strides,
+                                    const int64_t* dilations);
+
 /* Workspace bytes the fastest kernel for this shape wants (0: none).  For
  * QG_OP_DYNAMIC_QUANTIZE_LINEAR, N is the element count n. */
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K);

@@ -15,6 +15,8 @@ this package is its thin Python binding, with the same call names:
 * ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
   MatMulInteger, int32 output, shared weight never copied; per-row
   activation zero points go to ``matmul_integer_row_zp``.
+* ``conv_integer(x, w, x_zero_point, w_zero_point, pads, strides,
+  dilations, group)``: ONNX ConvInteger (NCHW / NCL), int32 output.
 * ``dynamic_quantize_linear(x)``: ONNX DynamicQuantizeLinear to uint8,
   returning (y, scale, zero_point) on the device.
 
@@ -30,6 +32,7 @@ from ._binding import (  # noqa: F401
     QGemmError,
     calib_mfma_i8,
     calib_read,
+    conv_integer,
     dynamic_quantize_linear,
     last_kernel,
     matmul_integer,

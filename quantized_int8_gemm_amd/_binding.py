@@ -35,6 +35,9 @@ PROTOTYPES = {
     "matmul_integer_row_zp": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
                                _p, _i64, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
     "dynamic_quantize_linear": ([_i64, _p, _p, _p, _p, _p, _sz, _p], _int),
+    "conv_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _i64, _p, _int, _i64, _p, _p, _p,
+                      _i32, _p, _i64, _p, _p, _sz, _p], _int),
+    "conv_integer_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, _p], _sz),
     "qgemm_workspace_bytes": ([_int, _i64, _i64, _i64, _i64], _sz),
     "qgemm_status_string": ([_int], ctypes.c_char_p),
     "qgemm_last_kernel": ([], ctypes.c_char_p),
@@ -392,6 +395,114 @@ def matmul_integer_row_zp(A, B, a_zero_point, b_zero_point=None, out=None):
     if not isinstance(a_zero_point, torch.Tensor) or a_zero_point.dim() == 0:
         raise ValueError("a_zero_point must be a tensor of M per-row values")
     return matmul_integer(A, B, a_zero_point, b_zero_point, out)
+
+
+# ---------------------------------------------------------------------------
+# ConvInteger
+# ---------------------------------------------------------------------------
+
+def _i64x(vals):
+    arr = (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def _auto_pads(auto_pad, sizes, kernel, strides, dilations):
+    """ONNX auto_pad: explicit (begin..., end...) pads for SAME_UPPER /
+    SAME_LOWER / VALID."""
+    begins, ends = [], []
+    for size, k, st, d in zip(sizes, kernel, strides, dilations):
+        if auto_pad == "VALID":
+            begins.append(0)
+            ends.append(0)
+            continue
+        out = -(-size // st)
+        total = max(0, (out - 1) * st + (k - 1) * d + 1 - size)
+        lo = total // 2 if auto_pad == "SAME_UPPER" else total - total // 2
+        begins.append(lo)
+        ends.append(total - lo)
+    return begins + ends
+
+
+def conv_integer(x, w, x_zero_point=0, w_zero_point=None, pads=None, strides=None, dilations=None, group=1,
+                 auto_pad="NOTSET", out=None, workspace=None):
+    """ONNX ConvInteger on the GPU: int32 y = sum (x - x_zp)(w - w_zp[m]) over
+    each output channel's group, taps outside the input contributing nothing.
+
+    x: uint8/int8 [N, C, H, W] (or [N, C, L]); w: uint8/int8
+    [M, C/group, kH, kW] (or [M, C/group, kL]).  pads in ONNX order
+    (begins then ends: top, left, bottom, right; or left, right), strides and
+    dilations per spatial axis, auto_pad NOTSET / SAME_UPPER / SAME_LOWER /
+    VALID.  x_zero_point: a scalar (int or one-element tensor of x's dtype);
+    w_zero_point: None, a scalar, or M values of w's dtype.
+    Returns int32 [N, M, OH, OW] (or [N, M, OL])."""
+    _need(x, (torch.uint8, torch.int8), "x")
+    _need(w, (torch.uint8, torch.int8), "w")
+    if x.dim() not in (3, 4) or w.dim() != x.dim():
+        raise ValueError("ConvInteger takes rank-3 (NCL) or rank-4 (NCHW) x and w of the same rank")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x and w must be contiguous")
+    nsp = x.dim() - 2
+    strides = list(strides) if strides is not None else [1] * nsp
+    dilations = list(dilations) if dilations is not None else [1] * nsp
+    if len(strides) != nsp or len(dilations) != nsp:
+        raise ValueError("strides and dilations need one value per spatial axis")
+    if auto_pad not in ("NOTSET", "SAME_UPPER", "SAME_LOWER", "VALID"):
+        raise ValueError(f"unknown auto_pad {auto_pad!r}")
+    if auto_pad != "NOTSET":
+        pads = _auto_pads(auto_pad, x.shape[2:], w.shape[2:], strides, dilations)
+    pads = list(pads) if pads is not None else [0] * (2 * nsp)
+    if len(pads) != 2 * nsp:
+        raise ValueError("pads need a begin and an end per spatial axis")
+    if nsp == 1:
+        N, C, L = x.shape
+        M, Cg, kL = w.shape
+        dims = (N, C, 1, L, M, 1, kL)
+        pads4, strides2, dil2 = [0, pads[0], 0, pads[1]], [1, strides[0]], [1, dilations[0]]
+    else:
+        N, C, H, W = x.shape
+        M, Cg, kH, kW = w.shape
+        dims = (N, C, H, W, M, kH, kW)
+        pads4, strides2, dil2 = pads, strides, dilations
+    if Cg * group != C or M % group != 0:
+        raise ValueError(f"w has {Cg} input channels per group; x has {C} channels in {group} groups")
+    if isinstance(x_zero_point, torch.Tensor):
+        _need(x_zero_point, (x.dtype,), "x_zero_point")
+        if x_zero_point.numel() != 1:
+            raise ValueError("x_zero_point must be a scalar")
+        x_zero_point = int(x_zero_point.item())
+    zw, zw_len = None, 0
+    if w_zero_point is not None:
+        if isinstance(w_zero_point, torch.Tensor):
+            _need(w_zero_point, (w.dtype,), "w_zero_point")
+            if w_zero_point.numel() not in (1, M):
+                raise ValueError(f"w_zero_point has {w_zero_point.numel()} values; expected 1 or M={M}")
+            zw = w_zero_point.reshape(-1).contiguous()
+        else:
+            zw = torch.tensor([int(w_zero_point)], dtype=w.dtype, device=w.device)
+        zw_len = zw.numel()
+    dev = _on_gpu(*([x, w] + ([zw] if zw is not None else [])))
+    p4, s2, d2 = _i64x(pads4), _i64x(strides2), _i64x(dil2)
+    need = lib.conv_integer_workspace_bytes(*dims, group, p4, s2, d2)
+    if need == 0:
+        raise ValueError("these sizes do not describe a valid convolution")
+    OH = (dims[2] + pads4[0] + pads4[2] - dil2[0] * (dims[5] - 1) - 1) // strides2[0] + 1
+    OW = (dims[3] + pads4[1] + pads4[3] - dil2[1] * (dims[6] - 1) - 1) // strides2[1] + 1
+    shape = (N, M, OW) if nsp == 1 else (N, M, OH, OW)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=dev)
+    else:
+        _need(out, (torch.int32,), "out")
+        if tuple(out.shape) != shape or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous int32 tensor of shape {shape}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, (torch.uint8, torch.int8), "workspace")
+    st = lib.conv_integer(*dims[:4], _ptr(x), _QG_OF[x.dtype], *dims[4:], _ptr(w), _QG_OF[w.dtype], group,
+                          p4, s2, d2, int(x_zero_point), _ptr(zw), zw_len, _ptr(out),
+                          _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, "conv_integer")
+    return out
 
 
 # ---------------------------------------------------------------------------

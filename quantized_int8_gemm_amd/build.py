@@ -28,6 +28,7 @@ SOURCES = [
     "a8w8_skinny.hip",
     "w8a32.hip",
     "dynamic_quantize.hip",
+    "conv_integer.hip",
     "calibrate.hip",
     "api.cpp",
 ]

@@ -442,3 +442,131 @@ qg_status dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y, float* 
 }
 
 }  // extern "C"
+
+namespace {
+
+// ConvInteger geometry and workspace layout: [packed w][pad to 256][col].
+struct ConvPlan {
+    qg::ConvGeom g;
+    size_t wp_bytes, col_off, total;
+};
+
+// Fills `plan` from the call's sizes; false if they do not describe a
+// convolution this library runs (every value must also fit the kernels'
+// 32-bit index arithmetic).
+bool conv_plan(int64_t N, int64_t C, int64_t H, int64_t W, int64_t M, int64_t kH, int64_t kW, int64_t group,
+               const int64_t* pads, const int64_t* strides, const int64_t* dilations, ConvPlan* plan) {
+    const int64_t lim = (int64_t)1 << 30;
+    if (pads == nullptr || strides == nullptr || dilations == nullptr) return false;
+    if (N < 1 || C < 1 || H < 1 || W < 1 || M < 1 || kH < 1 || kW < 1 || group < 1) return false;
+    if (N >= 65536 || C >= lim || H >= lim || W >= lim || M >= lim || kH >= lim || kW >= lim) return false;
+    if (C % group != 0 || M % group != 0) return false;
+    for (int i = 0; i < 4; ++i)
+        if (pads[i] < 0 || pads[i] >= lim) return false;
+    for (int i = 0; i < 2; ++i)
+        if (strides[i] < 1 || strides[i] >= lim || dilations[i] < 1 || dilations[i] >= lim) return false;
+    const int64_t eh = dilations[0] * (kH - 1) + 1, ew = dilations[1] * (kW - 1) + 1;
+    if (H + pads[0] + pads[2] < eh || W + pads[1] + pads[3] < ew) return false;
+    const int64_t OH = (H + pads[0] + pads[2] - eh) / strides[0] + 1;
+    const int64_t OW = (W + pads[1] + pads[3] - ew) / strides[1] + 1;
+    const int64_t Cg = C / group, Mg = M / group, Kg = Cg * kH * kW;
+    const int64_t Kp = (Kg + 63) / 64 * 64, P = OH * OW, Pp = (P + 15) / 16 * 16;
+    if (Kg >= lim || P >= lim || N * C * H * W >= ((int64_t)1 << 40)) return false;
+    // grid sizes of the staging kernels: N*(C + group) workgroups, or one
+    // lane per 16 column bytes
+    if (N * (C + group) >= ((int64_t)1 << 31) || N * group * Kp * Pp >= ((int64_t)1 << 42)) return false;
+    qg::ConvGeom& g = plan->g;
+    g.N = (int)N; g.C = (int)C; g.H = (int)H; g.W = (int)W; g.M = (int)M; g.kH = (int)kH; g.kW = (int)kW;
+    g.group = (int)group; g.Cg = (int)Cg; g.Mg = (int)Mg; g.Kg = (int)Kg; g.Kp = (int)Kp;
+    g.OH = (int)OH; g.OW = (int)OW; g.P = (int)P; g.Pp = (int)Pp;
+    g.pt = (int)pads[0]; g.pl = (int)pads[1]; g.sh = (int)strides[0]; g.sw = (int)strides[1];
+    g.dh = (int)dilations[0]; g.dw = (int)dilations[1];
+    plan->wp_bytes = (size_t)(group * Mg * Kp);
+    plan->col_off = (plan->wp_bytes + 255) / 256 * 256;
+    plan->total = plan->col_off + (size_t)N * group * Kp * Pp;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t conv_integer_workspace_bytes(int64_t N, int64_t C, int64_t H, int64_t W, int64_t M, int64_t kH, int64_t kW,
+                                    int64_t group, const int64_t* pads, const int64_t* strides,
+                                    const int64_t* dilations) {
+    ConvPlan plan;
+    if (!conv_plan(N, C, H, W, M, kH, kW, group, pads, strides, dilations, &plan)) return 0;
+    return plan.total;
+}
+
+qg_status conv_integer(int64_t N, int64_t C, int64_t H, int64_t W, const void* x, qg_dtype x_dtype, int64_t M,
+                       int64_t kH, int64_t kW, const void* w, qg_dtype w_dtype, int64_t group, const int64_t* pads,
+                       const int64_t* strides, const int64_t* dilations, int32_t x_zero_point,
+                       const void* w_zero_point, int64_t w_zero_point_len, int32_t* y, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    ConvPlan plan;
+    if (!conv_plan(N, C, H, W, M, kH, kW, group, pads, strides, dilations, &plan)) return QG_ERR_INVALID_ARGUMENT;
+    if (x == nullptr || w == nullptr || y == nullptr || workspace == nullptr) return QG_ERR_INVALID_ARGUMENT;
+    if ((x_dtype != QG_UINT8 && x_dtype != QG_INT8) || (w_dtype != QG_UINT8 && w_dtype != QG_INT8))
+        return QG_ERR_INVALID_ARGUMENT;
+    const bool x_u8 = x_dtype == QG_UINT8, w_u8 = w_dtype == QG_UINT8;
+    if (x_u8 ? (x_zero_point < 0 || x_zero_point > 255) : (x_zero_point < -128 || x_zero_point > 127))
+        return QG_ERR_INVALID_ARGUMENT;
+    if (w_zero_point == nullptr ? w_zero_point_len != 0 : (w_zero_point_len != 1 && w_zero_point_len != M))
+        return QG_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < plan.total) return QG_ERR_WORKSPACE;
+    const qg::ConvGeom& g = plan.g;
+    // 32-bit buffer offsets inside one GEMM operand: a packed group of w and
+    // one image's column matrix.
+    if ((int64_t)g.Kp * g.Pp + 256 >= SPAN_LIMIT || (int64_t)g.Mg * g.Kp + 256 >= SPAN_LIMIT)
+        return QG_ERR_UNSUPPORTED;
+
+    uint8_t* wp = reinterpret_cast<uint8_t*>(workspace);
+    uint8_t* col = wp + plan.col_off;
+    (void)hipGetLastError();
+    hipError_t e = qg::launch_conv_stage(g, x, (uint8_t)(x_zero_point & 0xff), w, w_zero_point,
+                                         (int)w_zero_point_len, wp, col, (hipStream_t)stream);
+    if (e != hipSuccess) return QG_ERR_HIP;
+
+    // One batched MatMulInteger per group: A = packed w of the group (shared
+    // by every image), B = the images' column matrices, Y = y's channels of
+    // the group, NCHW.
+    const bool vec = g.P % 16 == 0;
+    const char* name = "";
+    for (int gi = 0; gi < g.group; ++gi) {
+        qg::Int8GemmArgs a{};
+        a.M = g.Mg; a.N = g.P; a.K = g.Kp; a.batch = g.N;
+        a.A = reinterpret_cast<const int8_t*>(wp + (int64_t)gi * g.Mg * g.Kp); a.lda = g.Kp; a.a_bstride = 0;
+        a.B = reinterpret_cast<const int8_t*>(col + (int64_t)gi * g.Kp * g.Pp); a.ldb = g.Pp;
+        a.b_bstride = (int64_t)g.group * g.Kp * g.Pp;
+        a.a_flip = w_u8 ? 0x80808080u : 0u;
+        a.b_flip = x_u8 ? 0x80808080u : 0u;
+        a.out = y + (int64_t)gi * g.Mg * g.P; a.ldo = g.P; a.o_bstride = (int64_t)g.M * g.P;
+        a.b_zp = nullptr; a.b_zp_stride = 0; a.b_zp_u8 = 0;
+        a.sb = (x_u8 ? 128 : 0) - x_zero_point;   // cb[n] = sb: the activation zero point, constant
+        if (w_zero_point != nullptr) {
+            const bool per_channel = w_zero_point_len == M && M > 1;
+            a.a_zp = reinterpret_cast<const uint8_t*>(w_zero_point) + (per_channel ? (int64_t)gi * g.Mg : 0);
+            a.a_zp_stride = per_channel ? 1 : 0;
+            a.a_zp_rows = g.Mg;
+            a.a_zp_u8 = w_u8 ? 1 : 0;
+            a.sa = w_u8 ? 128 : 0;
+            a.ca = 0;
+        } else {
+            a.ca = w_u8 ? 128 : 0;
+        }
+        const bool need_rowsum = a.sb != 0;
+        const bool need_colsum = a.ca != 0 || a.a_zp != nullptr;
+        const int zp = (need_rowsum ? 1 : 0) | (need_colsum ? 2 : 0);
+        const int cfg = pick_tile(a.batch, a.M, a.N);
+        e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
+        if (e != hipSuccess) return QG_ERR_HIP;
+    }
+    log_dispatch("conv_integer", name, N, M, (int64_t)g.P, g.Kg, g.group);
+    static thread_local char label[64];
+    std::snprintf(label, sizeof label, "conv_im2col+%s", name);
+    return finish_launch(hipSuccess, label);
+}
+
+}  // extern "C"

@@ -87,6 +87,17 @@ struct W8A32Args {
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                         const char** name);
 
+// ConvInteger staging: geometry of one call (validated on the host).
+// Kg = Cg*kH*kW, Kp = Kg rounded up to 64, P = OH*OW, Pp = P rounded up to 16.
+struct ConvGeom {
+    int N, C, H, W, M, kH, kW, group, Cg, Mg, Kg, Kp, OH, OW, P, Pp;
+    int pt, pl, sh, sw, dh, dw;
+};
+// Packs w into [group][Mg][Kp] at wp and writes the column matrices
+// [N][group][Kp][Pp] at col (both in the caller's workspace).
+hipError_t launch_conv_stage(const ConvGeom& c, const void* x, uint8_t x_zp, const void* w, const void* w_zp,
+                             int w_zp_len, uint8_t* wp, uint8_t* col, hipStream_t s);
+
 // DynamicQuantizeLinear (uint8): a min/max pass writing one (min, max)
 // float pair per workgroup into the workspace, then a quantize pass.
 constexpr int DQL_MAX_PARTIALS = 256;

@@ -10,6 +10,9 @@ inputs.  Distributions follow the workloads the operators are measured on:
   column scales uniform over [0.001, 0.05).
 * MatMulInteger: uint8 activations uniform over [0, 255]; int8 weight uniform
   over [-128, 127]; per-column int8 weight zero points uniform over [-8, 8].
+* ConvInteger: uint8 activations uniform over [0, 255]; int8 weight uniform
+  over [-128, 127]; per-output-channel int8 weight zero points uniform over
+  [-8, 8] (the MatMulInteger recipe on a convolution's operands).
 * DynamicQuantizeLinear: fp32 activations ~ N(mean, std) of the shape of
   MatMulInteger's activations, which it produces.
 
@@ -62,3 +65,11 @@ def dql_inputs(shape, seed, mean=0.0, std=1.0):
     g = rng(seed)
     x = g.standard_normal(shape, dtype=np.float32)
     return (x * np.float32(std) + np.float32(mean)).astype(np.float32)
+
+
+def conv_integer_inputs(N, C, H, W, M, kH, kW, seed, group=1):
+    g = rng(seed)
+    x = randint(g, (N, C, H, W), 0, 255, np.uint8)
+    w = randint(g, (M, C // group, kH, kW), -128, 127, np.int8)
+    zw = randint(g, (M,), -8, 8, np.int8)
+    return x, w, zw

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q\w+|matmul_integer\w*|dynamic_quantize_linear)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q\w+|matmul_integer\w*|dynamic_quantize_linear|conv_integer\w*)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
                           "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_a8w8_acc",
-                          "matmul_integer_row_zp", "qgemm_w8a32_input_grad", "dynamic_quantize_linear"}
+                          "matmul_integer_row_zp", "qgemm_w8a32_input_grad", "dynamic_quantize_linear",
+                          "conv_integer", "conv_integer_workspace_bytes"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -251,3 +252,50 @@ def test_dynamic_quantize_linear_rejects_bad_arguments():
         q.dynamic_quantize_linear(torch.zeros(8, dtype=torch.float64))
     with pytest.raises(ValueError):
         q.dynamic_quantize_linear(torch.zeros(8))   # a CPU tensor
+
+
+def _i64a(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_conv_integer_workspace_and_rejects():
+    lib = b.lib
+    P0, S1, D1 = _i64a(0, 0, 0, 0), _i64a(1, 1), _i64a(1, 1)
+    # 1 x 64 x 32 x 32 input, 128 x 64 x 3 x 3 weight, pad 1: K = 576 (a multiple of 64),
+    # P = 1024; workspace = packed w (128 x 576) + columns (576 x 1024)
+    P1 = _i64a(1, 1, 1, 1)
+    assert lib.conv_integer_workspace_bytes(1, 64, 32, 32, 128, 3, 3, 1, P1, S1, D1) == 128 * 576 + 576 * 1024
+    # K padded to 64, P padded to 16: C/group*kH*kW = 29*9 = 261 -> 320; P = 4*4 -> 16
+    assert lib.conv_integer_workspace_bytes(1, 58, 7, 7, 6, 3, 3, 2, P1, _i64a(2, 2), D1) == \
+        256 * ((2 * 3 * 320 + 255) // 256) + 2 * 320 * 16
+    bad_geoms = [
+        (0, 4, 5, 5, 4, 3, 3, 1, P0, S1, D1), (1, 4, 5, 5, 4, 3, 3, 3, P0, S1, D1),   # N = 0; group does not divide C
+        (1, 4, 5, 5, 6, 3, 3, 4, P0, S1, D1),                                          # group does not divide M
+        (1, 4, 2, 5, 4, 3, 3, 1, P0, S1, D1),                                          # window taller than the input
+        (1, 4, 5, 5, 4, 3, 3, 1, _i64a(-1, 0, 0, 0), S1, D1), (1, 4, 5, 5, 4, 3, 3, 1, P0, _i64a(0, 1), D1),
+        (1, 4, 5, 5, 4, 3, 3, 1, P0, S1, _i64a(1, 0)), (1, 4, 5, 5, 4, 3, 3, 1, None, S1, D1),
+        (65536, 4, 5, 5, 4, 3, 3, 1, P0, S1, D1),
+    ]
+    for gm in bad_geoms:
+        assert lib.conv_integer_workspace_bytes(*gm) == 0, gm
+        assert lib.conv_integer(*gm[:4], FAKE, b.QG_UINT8, *gm[4:7], FAKE, b.QG_INT8, gm[7], gm[8], gm[9], gm[10],
+                                0, None, 0, FAKE, ctypes.c_void_p(4096), 1 << 30, None) == b.QG_ERR_INVALID_ARGUMENT, gm
+    ok = (1, 4, 5, 5, 4, 3, 3, 1)
+    WS = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        a = dict(x=FAKE, xd=b.QG_UINT8, w=FAKE, wd=b.QG_INT8, xz=0, wz=None, wzl=0, y=FAKE, ws=WS, wsz=1 << 30)
+        a.update(kw)
+        return lib.conv_integer(*ok[:4], a["x"], a["xd"], *ok[4:7], a["w"], a["wd"], ok[7], P0, S1, D1, a["xz"],
+                                a["wz"], a["wzl"], a["y"], a["ws"], a["wsz"], None)
+    for kw in (dict(x=None), dict(w=None), dict(y=None), dict(ws=None), dict(ws=ctypes.c_void_p(4096 + 16)),
+               dict(xd=b.QG_FP32), dict(wd=b.QG_BF16), dict(xz=256), dict(xz=-1), dict(xd=b.QG_INT8, xz=128),
+               dict(wz=FAKE, wzl=2), dict(wz=None, wzl=1), dict(wz=FAKE, wzl=0)):
+        assert call(**kw) == b.QG_ERR_INVALID_ARGUMENT, kw
+    assert call(wsz=100) == b.QG_ERR_WORKSPACE
+    with pytest.raises(TypeError):
+        q.conv_integer(torch.zeros(1, 4, 5, 5), torch.zeros(4, 4, 3, 3, dtype=torch.int8))
+    with pytest.raises(ValueError):
+        q.conv_integer(torch.zeros(1, 4, 5, 5, dtype=torch.uint8), torch.zeros(4, 3, 3, 3, dtype=torch.int8))
+    with pytest.raises(ValueError):
+        q.conv_integer(torch.zeros(1, 4, 5, dtype=torch.uint8), torch.zeros(4, 4, 3, 3, dtype=torch.int8))

@@ -89,64 +89,99 @@ __global__ __launch_bounds__(NT) void conv_im2col(ConvGeom c, const uint8_t* __r
     *reinterpret_cast<v4i*>(dst) = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
 }
 
-// Planes of up to this many bytes are staged in LDS by conv_im2col_lds.
-constexpr int PLANE_LDS_MAX = 65536 - 64;
+// LDS bytes conv_im2col_lds may use for its staged planes (guards included).
+constexpr int PLANE_LDS_MAX = 65536;
+constexpr int PPW_MAX = 1;           // planes per workgroup (1 measured fastest of 1..8)
 
-// One workgroup per (image n, input channel cc) plane, plus `group` extra
-// workgroups per image that fill the padding rows k >= Kg of each group.  The
-// plane is read once from memory into LDS (16-byte loads when its rows allow),
-// behind a 16-byte guard, then every column row the plane feeds --
-// k = ci*kH*kW + kh*kW + kw for the kH*kW taps -- is written 16 positions per
-// lane, one 16-byte store each.
-//  * Fast path (horizontal stride 1, the 16 positions inside one output row):
-//    they read the contiguous bytes iw0 .. iw0+15 of input row ih, fetched as
-//    five aligned LDS dwords and shifted into place with alignbyte; bytes of
-//    columns outside [0, W) are replaced by the zero point through a mask.
-//    Reads may touch the guard or a neighbouring row, always inside the LDS
-//    allocation, and those bytes are masked.
-//  * Otherwise each of the 16 positions is gathered on its own.
 constexpr int GUARD = 16;
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, int off) {
     return *reinterpret_cast<const uint32_t*>(base + off);
 }
 
+// q = x / d and r = x % d for 0 <= x, d < 2^22 with inv = 1.0f / d.  The
+// float quotient is within one of the true one there (x is exact in fp32 and
+// the product's relative error is below 2^-22), and one correction step
+// restores it; the launcher checks the bound.
+__device__ __forceinline__ void divmod_small(int x, int d, float inv, int& q, int& r) {
+    q = (int)((float)x * inv);
+    r = x - q * d;
+    if (r < 0) { --q; r += d; }
+    else if (r >= d) { ++q; r -= d; }
+}
+
+// Byte mask of the 4 bytes 4j..4j+3 selected by bits 4j..4j+3 of `bits16`.
+__device__ __forceinline__ uint32_t byte_mask(uint32_t bits16, int j) {
+    const uint32_t nib = (bits16 >> (4 * j)) & 0xFu;
+    return ((nib * 0x00204081u) & 0x01010101u) * 0xFFu;
+}
+
+// Workgroups [0, plane_blocks) each stage `ppw` consecutive (image, channel)
+// planes in LDS, every plane behind a 16-byte guard, loaded together so that
+// one memory latency covers them all; the workgroups after them fill the
+// padding rows k >= Kg, one per (image, group).  Then every column row the
+// staged planes feed -- k = ci*kH*kW + kh*kW + kw for the kH*kW taps -- is
+// written 16 positions per lane, one 16-byte store each.
+//  * Fast path (horizontal stride 1, the 16 positions inside one output row):
+//    they read the contiguous bytes iw0 .. iw0+15 of input row ih, fetched as
+//    five aligned LDS dwords and shifted into place with alignbyte; bytes of
+//    columns outside [0, W) are replaced by the zero point through a mask.
+//    Reads may touch the guard or a neighbouring row, always inside the
+//    plane's LDS slot, and those bytes are masked.
+//  * Otherwise each of the 16 positions is gathered on its own.
 __global__ __launch_bounds__(NT) void conv_im2col_lds(ConvGeom c, const uint8_t* __restrict__ x,
-                                                      uint8_t x_zp, uint8_t* __restrict__ col) {
+                                                      uint8_t x_zp, uint8_t* __restrict__ col, int ppw,
+                                                      int plane_blocks, int slot) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint8_t* plane = lds + GUARD;
-    const int per_img = c.C + c.group;
-    const int64_t n = blockIdx.x / per_img;
-    const int cc = blockIdx.x % per_img;
+    __shared__ int64_t row_base[PPW_MAX];   // first column row each staged plane feeds
     const int chunks = c.Pp / 16;
     const uint32_t z4 = (uint32_t)x_zp * 0x01010101u;
-    if (cc >= c.C) {
-        // padding rows of group cc - C
-        const int g = cc - c.C;
+    if ((int)blockIdx.x >= plane_blocks) {
+        // padding rows of one (image, group)
+        const int ng = blockIdx.x - plane_blocks;
         const int rows = c.Kp - c.Kg;
-        uint8_t* base = col + ((n * c.group + g) * c.Kp + c.Kg) * c.Pp;
+        uint8_t* base = col + ((int64_t)ng * c.Kp + c.Kg) * c.Pp;
         for (int i = threadIdx.x; i < rows * chunks; i += NT)
             *reinterpret_cast<v4i*>(base + (int64_t)(i / chunks) * c.Pp + (i % chunks) * 16) =
                 v4i{(int)z4, (int)z4, (int)z4, (int)z4};
         return;
     }
-    const int g = cc / c.Cg, ci = cc % c.Cg;
     const int hw = c.H * c.W;
-    const uint8_t* src = x + (n * c.C + cc) * (int64_t)hw;
+    const int64_t planes = (int64_t)c.N * c.C;
+    const int64_t q0 = (int64_t)blockIdx.x * ppw;
+    const int np = (int)(planes - q0 < ppw ? planes - q0 : ppw);
+    // planes q0 .. q0+np-1 are consecutive in memory: one contiguous span
+    const uint8_t* src = x + q0 * hw;
     if ((hw & 15) == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-        for (int i = threadIdx.x; i < hw / 16; i += NT)
-            *reinterpret_cast<v4i*>(plane + 16 * i) = *reinterpret_cast<const v4i*>(src + 16 * i);
+        const int vpp = hw / 16;   // vectors per plane
+        for (int pi = 0; pi < np; ++pi)
+            for (int v = threadIdx.x; v < vpp; v += NT)
+                *reinterpret_cast<v4i*>(lds + pi * slot + GUARD + 16 * v) =
+                    *reinterpret_cast<const v4i*>(src + (int64_t)pi * hw + 16 * v);
     } else {
-        for (int i = threadIdx.x; i < hw; i += NT) plane[i] = src[i];
+        for (int pi = 0; pi < np; ++pi)
+            for (int v = threadIdx.x; v < hw; v += NT) lds[pi * slot + GUARD + v] = src[(int64_t)pi * hw + v];
+    }
+    const int taps = c.kH * c.kW;
+    if ((int)threadIdx.x < np) {
+        const int64_t q = q0 + threadIdx.x;
+        const int64_t n = q / c.C;
+        const int cc = (int)(q - n * c.C);
+        const int g = cc / c.Cg, ci = cc - g * c.Cg;
+        row_base[threadIdx.x] = (n * c.group + g) * c.Kp + (int64_t)ci * taps;
     }
     __syncthreads();
-    const int taps = c.kH * c.kW;
-    uint8_t* rows = col + ((n * c.group + g) * c.Kp + (int64_t)ci * taps) * c.Pp;
-    for (int i = threadIdx.x; i < taps * chunks; i += NT) {
-        const int t = i / chunks, pc = i % chunks;
-        const int kh = t / c.kW, kw = t % c.kW;
+    const int per_plane = taps * chunks;
+    const float inv_pp = 1.0f / (float)per_plane, inv_chunks = 1.0f / (float)chunks;
+    const float inv_kw = 1.0f / (float)c.kW, inv_ow = 1.0f / (float)c.OW;
+    for (int i = threadIdx.x; i < np * per_plane; i += NT) {
+        int pi, rest, t, pc, kh, kw, oh, ow0;
+        divmod_small(i, per_plane, inv_pp, pi, rest);
+        divmod_small(rest, chunks, inv_chunks, t, pc);
+        divmod_small(t, c.kW, inv_kw, kh, kw);
         const int p0 = pc * 16;
-        const int oh = p0 / c.OW, ow0 = p0 % c.OW;
+        divmod_small(p0, c.OW, inv_ow, oh, ow0);
+        const uint8_t* plane = lds + pi * slot + GUARD;
         uint32_t d[4];
         if (c.sw == 1 && ow0 + 16 <= c.OW) {
             const int ih = oh * c.sh - c.pt + kh * c.dh;
@@ -162,14 +197,12 @@ __global__ __launch_bounds__(NT) void conv_im2col_lds(ConvGeom c, const uint8_t*
                 uint32_t wv[5];
 #pragma unroll
                 for (int j = 0; j < 5; ++j) wv[j] = lds_u32(plane, a0 + 4 * j);
+                // bit e set: byte e is column iw0 + e inside [0, W)
+                const uint32_t valid = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t v = __builtin_amdgcn_alignbyte(wv[j + 1], wv[j], sh);
-                    // byte e = 4j + b is kept when lo <= e < hi
-                    uint32_t keep = 0u;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        keep |= (4 * j + b >= lo && 4 * j + b < hi) ? (0xffu << (8 * b)) : 0u;
+                    const uint32_t keep = byte_mask(valid, j);
                     d[j] = (v & keep) | (z4 & ~keep);
                 }
             }
@@ -188,7 +221,8 @@ __global__ __launch_bounds__(NT) void conv_im2col_lds(ConvGeom c, const uint8_t*
                 if (++ow == c.OW) { ow = 0; ++oh_e; }
             }
         }
-        *reinterpret_cast<v4i*>(rows + (int64_t)t * c.Pp + p0) = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+        uint8_t* dst = col + (row_base[pi] + t) * c.Pp + p0;
+        *reinterpret_cast<v4i*>(dst) = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
     }
 }
 
@@ -200,12 +234,18 @@ hipError_t launch_conv_stage(const ConvGeom& c, const void* x, uint8_t x_zp, con
     hipLaunchKernelGGL(conv_pack_weight, dim3((unsigned)((wtotal + NT - 1) / NT)), dim3(NT), 0, s, c,
                        reinterpret_cast<const uint8_t*>(w), reinterpret_cast<const uint8_t*>(w_zp), w_zp_len, wp);
     const int64_t hw = (int64_t)c.H * c.W;
-    if (hw <= PLANE_LDS_MAX) {
-        // the plane behind a 16-byte guard, and room after it for the last
-        // row's five-dword window (at most 19 bytes past the plane)
-        const size_t lds = (size_t)(GUARD + (hw + 15) / 16 * 16 + 32);
-        hipLaunchKernelGGL(conv_im2col_lds, dim3((unsigned)((int64_t)c.N * (c.C + c.group))), dim3(NT), lds, s, c,
-                           reinterpret_cast<const uint8_t*>(x), x_zp, col);
+    // the LDS kernel's index arithmetic needs every divided value below 2^22
+    const int64_t lim = (int64_t)1 << 22;
+    const int64_t slot = GUARD + (hw + 15) / 16 * 16 + 32;   // guard, plane, room for the last window
+    const int64_t per_plane = (int64_t)c.kH * c.kW * (c.Pp / 16);
+    if (slot <= PLANE_LDS_MAX && per_plane * PPW_MAX < lim && c.Pp < lim) {
+        int ppw = (int)(PLANE_LDS_MAX / slot);
+        if (ppw > PPW_MAX) ppw = PPW_MAX;
+        const int64_t planes = (int64_t)c.N * c.C;
+        const int plane_blocks = (int)((planes + ppw - 1) / ppw);
+        const int blocks = plane_blocks + c.N * c.group;
+        hipLaunchKernelGGL(conv_im2col_lds, dim3((unsigned)blocks), dim3(NT), (size_t)(ppw * slot), s, c,
+                           reinterpret_cast<const uint8_t*>(x), x_zp, col, ppw, plane_blocks, (int)slot);
     } else {
         const int64_t ctotal = (int64_t)c.N * c.group * c.Kp * (c.Pp / 16);
         hipLaunchKernelGGL(conv_im2col, dim3((unsigned)((ctotal + NT - 1) / NT)), dim3(NT), 0, s, c,

@@ -51,7 +51,7 @@ CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops p
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-HEADLINE_SOURCES = ("int8_dma_impl.h", "int8_dma_256x256w8.hip", "device_common.h")
+HEADLINE_SOURCES = ("int8_dma_impl.h", "int8_dma_256x256w8k128.hip", "device_common.h")
 
 
 def source_hash():
@@ -133,7 +133,7 @@ def parse():
     ap.add_argument("--write-db")
     ap.add_argument("--copy-fetch-db")
     ap.add_argument("--copy-write-db")
-    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 4, false, 1, 0, 0>")
+    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 2, false, 1, 0, 0, 128>")
     return ap.parse_args()
 
 

@@ -25,6 +25,9 @@ SOURCES = [
     "int8_dma_128x128s3.hip",
     "int8_dma_256x256w8.hip",
     "int8_dma_256x128w8.hip",
+    "int8_dma_128x128k128.hip",
+    "int8_dma_256x128w8k128.hip",
+    "int8_dma_256x256w8k128.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
     "dynamic_quantize.hip",

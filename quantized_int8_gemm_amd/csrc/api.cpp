@@ -49,12 +49,15 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
 int pick_tile(int64_t batch, int64_t M, int64_t N) {
     const int forced = env_int("QGEMM_TILE", -1);
     if (forced >= 0 && forced < qg::NUM_TILE_CFGS) return forced;
-    // 256x256 tiles (eight waves) once there are at least two full waves of
-    // them; measured best for 8192^3.  Otherwise 128x128 tiles, two
-    // workgroups per compute unit (best for 4096x2048x2048 and smaller).
+    // 256x256 tiles (eight waves, 128-byte k stages) once there are at least
+    // two full waves of them; measured best for 8192^3 (3-4 % ahead of the
+    // same tile with 64-byte stages).  Otherwise 128x128 tiles with 128-byte
+    // k stages, two workgroups per compute unit (best for 4096x2048x2048 and
+    // smaller).  Either falls back to its 64-byte-stage sibling where K is not
+    // whole 128-byte stages and bytes past K would reach a sum.
     const int64_t t256 = batch * ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= 512) return qg::TILE_256x256_W8;
-    return qg::TILE_128x128;
+    if (t256 >= 512) return qg::TILE_256x256_W8_K128;
+    return qg::TILE_128x128_K128;
 }
 
 // Whether the multi-stage kernel writes its output tile through LDS in whole
@@ -63,7 +66,7 @@ int pick_tile(int64_t batch, int64_t M, int64_t N) {
 bool stage_output(int cfg, int64_t batch, int64_t M, int64_t N) {
     const int forced = env_int("QGEMM_STAGE", -1);
     if (forced >= 0) return forced != 0;
-    return cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8;
+    return cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128;
 }
 
 qg_status finish_launch(hipError_t e, const char* name) {
@@ -76,18 +79,36 @@ qg_status finish_launch(hipError_t e, const char* name) {
 // except those whose bytes past K would reach a sum: uint8 flips, zero-point
 // sums and a k-major B need K % 64 == 0.  Everything else runs the
 // register-staged kernel, which clears bytes past K itself.
-bool dma_ok(const qg::Int8GemmArgs& a, bool bkm, bool vec, int epi) {
+bool dma_ok(const qg::Int8GemmArgs& a, bool bkm, bool vec, int epi, int bk) {
     if (!vec || env_is("QGEMM_FAMILY", "staged")) return false;
-    const bool needs_k64 = bkm || epi == qg::EPI_I32;
-    return !needs_k64 || a.K % 64 == 0;
+    const bool needs_whole_chunks = bkm || epi == qg::EPI_I32;
+    return !needs_whole_chunks || a.K % bk == 0;
+}
+
+bool is_k128(int cfg) {
+    return cfg == qg::TILE_128x128_K128 || cfg == qg::TILE_256x128_W8_K128 || cfg == qg::TILE_256x256_W8_K128;
+}
+
+// The 64-byte-stage configuration of the same tile shape.
+int k64_of(int cfg) {
+    switch (cfg) {
+        case qg::TILE_128x128_K128: return qg::TILE_128x128;
+        case qg::TILE_256x128_W8_K128: return qg::TILE_256x128_W8;
+        case qg::TILE_256x256_W8_K128: return qg::TILE_256x256_W8;
+        default: return cfg;
+    }
 }
 
 hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, int epi, int zp,
                         hipStream_t s, const char** name) {
     static const char* dma_names[qg::NUM_TILE_CFGS] = {
         "int8_dma_256x256", "int8_dma_256x128s3", "int8_dma_128x128",
-        "int8_dma_128x128s3", "int8_dma_256x256w8", "int8_dma_256x128w8"};
-    if (dma_ok(a, bkm, vec, epi)) {
+        "int8_dma_128x128s3", "int8_dma_256x256w8", "int8_dma_256x128w8",
+        "int8_dma_128x128k128", "int8_dma_256x128w8k128", "int8_dma_256x256w8k128"};
+    // A 128-byte-stage configuration whose K is not whole stages, where bytes
+    // past K would reach a sum, runs its 64-byte-stage sibling.
+    if (is_k128(cfg) && !dma_ok(a, bkm, vec, epi, 128) && dma_ok(a, bkm, vec, epi, 64)) cfg = k64_of(cfg);
+    if (dma_ok(a, bkm, vec, epi, is_k128(cfg) ? 128 : 64)) {
         *name = dma_names[cfg];
         qg::Int8GemmArgs d = a;
         d.stage_out = stage_output(cfg, a.batch, a.M, a.N) ? 1 : 0;
@@ -97,13 +118,16 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
             case qg::TILE_128x128: return qg::launch_dma_128x128(d, bkm, epi, zp, s);
             case qg::TILE_128x128_S3: return qg::launch_dma_128x128s3(d, bkm, epi, zp, s);
             case qg::TILE_256x256_W8: return qg::launch_dma_256x256w8(d, bkm, epi, zp, s);
+            case qg::TILE_128x128_K128: return qg::launch_dma_128x128k128(d, bkm, epi, zp, s);
+            case qg::TILE_256x128_W8_K128: return qg::launch_dma_256x128w8k128(d, bkm, epi, zp, s);
+            case qg::TILE_256x256_W8_K128: return qg::launch_dma_256x256w8k128(d, bkm, epi, zp, s);
             default: return qg::launch_dma_256x128w8(d, bkm, epi, zp, s);
         }
     }
     // Register-staged kernel: the byte-wise (any alignment) variants exist
     // for the 128x128 tile only.
-    int shape = cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 ? 0
-              : cfg == qg::TILE_256x128_S3 || cfg == qg::TILE_256x128_W8 ? 1 : 2;
+    int shape = cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128 ? 0
+              : cfg == qg::TILE_256x128_S3 || cfg == qg::TILE_256x128_W8 || cfg == qg::TILE_256x128_W8_K128 ? 1 : 2;
     if (!vec) shape = 2;
     static const char* staged_names[] = {"int8_staged_256x256", "int8_staged_256x128", "int8_staged_128x128"};
     *name = staged_names[shape];

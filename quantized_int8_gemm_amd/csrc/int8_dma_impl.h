@@ -39,7 +39,6 @@
 namespace qg {
 namespace dma {
 
-constexpr int BK = 64;
 constexpr int GROUP_M = 8;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -75,14 +74,18 @@ __device__ __forceinline__ u32x4 xor4(u32x4 v, uint32_t f) {
     return u32x4{v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f};
 }
 
-// K-contiguous tile (A, or B as [N,K]): rows of 64 bytes (4 segments of
-// 16), segment s of row r at slot s ^ f(r) with f(r) = bits (r1 ^ r3, r2).
-// Rows r, r+2, r+4, r+6 then take four distinct slots, and so do rows r,
-// r+4, r+8, r+12, so a fragment read (16 consecutive rows, one segment) is
-// conflict-free whether the LDS serves 8 lanes over 32 banks or 16 lanes over
-// 64 banks per cycle.
+// K-contiguous tile (A, or B as [N,K]), rows of BK bytes.
+//  * BK = 64 (4 segments of 16): segment s of row r at slot s ^ f(r) with
+//    f(r) = bits (r1 ^ r3, r2).  Rows r, r+2, r+4, r+6 then take four
+//    distinct slots, and so do rows r, r+4, r+8, r+12.
+//  * BK = 128 (8 segments): slot s ^ ((r >> 1) & 7); the 16 rows of a
+//    fragment read take 16 distinct (row parity, slot) pairs.
+// Adding a multiple of 16 to r leaves the slot unchanged, so fragment blocks
+// 16 rows apart share one swizzle.
+template <int BK>
 __device__ __forceinline__ int kc_slot(int r, int s) {
-    return s ^ ((((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2));
+    if constexpr (BK == 64) return s ^ ((((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2));
+    else return s ^ ((r >> 1) & 7);
 }
 
 // [K,N] tile: rows of BN bytes; segment s of k-row r at slot
@@ -95,8 +98,10 @@ __device__ __forceinline__ int kn_slot(int r, int s) {
     return s ^ (r & 7) ^ (BN >= 256 ? (t << 3) : t);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP>
+template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP, int BK>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(Int8GemmArgs p) {
+    static_assert(BK == 64 || BK == 128, "64 or 128 k-bytes per stage");
+    constexpr int KB = BK / 64;                     // 64-k matrix-core blocks per stage
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
     constexpr int ROUND = NT * 16;                  // bytes one load round moves
     constexpr int WAVES_N = BN / WN;
@@ -139,14 +144,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     for (int q = 0; q < A_ROUNDS; ++q) {
         const int o = q * ROUND + wave * 1024 + lane * 16;
         const int r = o / BK, slot = (o % BK) / 16;
-        a_off[q] = (uint32_t)(r * lda + 16 * kc_slot(r, slot));
+        a_off[q] = (uint32_t)(r * lda + 16 * kc_slot<BK>(r, slot));
     }
 #pragma unroll
     for (int q = 0; q < B_ROUNDS; ++q) {
         const int o = q * ROUND + wave * 1024 + lane * 16;
         if constexpr (B_KMAJOR) {
             const int r = o / BK, slot = (o % BK) / 16;
-            b_off[q] = (uint32_t)(r * ldb + 16 * kc_slot(r, slot));
+            b_off[q] = (uint32_t)(r * ldb + 16 * kc_slot<BK>(r, slot));
         } else {
             const int r = o / BN, slot = (o % BN) / 16;
             b_off[q] = (uint32_t)(r * ldb + 16 * kn_slot<BN>(r, slot));
@@ -176,10 +181,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 
     // Fragment read offsets within a stage (per lane; the block index adds an
     // immediate).
-    const int a_rd = (wm * WM + i16) * BK + (kc_slot(i16, g) << 4);
+    // k-block kb of a stage: A segment 4*kb + g of row i16.
+    auto a_rd_at = [&](int kb) { return (wm * WM + i16) * BK + (kc_slot<BK>(i16, 4 * kb + g) << 4); };
     int b_rd = 0;
     if constexpr (B_KMAJOR) {
-        b_rd = A_BYTES + (wn * WN + i16) * BK + (kc_slot(i16, g) << 4);
+        b_rd = A_BYTES + (wn * WN + i16) * BK;
     } else {
         // ds_read_b64_tr_b8: lane (g, i) addresses k-row 16g + 8h + i/2,
         // bytes 8*(i&1) .. of the fragment's 16-column segment.
@@ -190,37 +196,41 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 
     auto compute = [&](int stage) {
         const uint8_t* S = smem + stage * STAGE;
-        u32x4 bf[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if constexpr (B_KMAJOR) {
-                bf[j] = *reinterpret_cast<const u32x4*>(S + b_rd + j * 16 * BK);
-            } else {
-                const int seg = (wn * WN) / 16 + j;
-                const uint8_t* base = S + b_rd + ((seg ^ b_x) << 4);
-                const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(base));
-                const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) v2i*)(base + 8 * BN));
-                bf[j] = u32x4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
+        for (int kb = 0; kb < KB; ++kb) {
+            u32x4 bf[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (B_KMAJOR) {
+                    bf[j] = *reinterpret_cast<const u32x4*>(S + b_rd + j * 16 * BK + (kc_slot<BK>(i16, 4 * kb + g) << 4));
+                } else {
+                    const int seg = (wn * WN) / 16 + j;
+                    const uint8_t* base = S + b_rd + kb * 64 * BN + ((seg ^ b_x) << 4);
+                    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i*)(base));
+                    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i*)(base + 8 * BN));
+                    bf[j] = u32x4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
+                }
+                if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
+                if constexpr (COLSUM)
+                    cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
             }
-            if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
-            if constexpr (COLSUM)
-                cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
-        }
-        // A fragments one block ahead, so each LDS read overlaps the
-        // previous block's matrix-core work.
-        u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd);
+            // A fragments one block ahead, so each LDS read overlaps the
+            // previous block's matrix-core work.
+            const int a_rd = a_rd_at(kb);
+            u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd);
 #pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            u32x4 af = af_next;
-            if (a + 1 < FM) af_next = *reinterpret_cast<const u32x4*>(S + a_rd + (a + 1) * 16 * BK);
-            __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
-            if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
-            if constexpr (ROWSUM)
-                rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
+            for (int a = 0; a < FM; ++a) {
+                u32x4 af = af_next;
+                if (a + 1 < FM) af_next = *reinterpret_cast<const u32x4*>(S + a_rd + (a + 1) * 16 * BK);
+                __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
+                if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
+                if constexpr (ROWSUM)
+                    rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
 #pragma unroll
-            for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(bf[b], af, acc[a][b]);
+                for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(bf[b], af, acc[a][b]);
+            }
         }
     };
 
@@ -529,41 +539,41 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     }
 }
 
-template <int BM, int BN, int WM, int WN, int ST, bool BKM, int EPI, int ZP, int FLIP>
+template <int BM, int BN, int WM, int WN, int ST, bool BKM, int EPI, int ZP, int FLIP, int BK>
 hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, ST, BKM, EPI, ZP, FLIP>), dim3(tiles, a.batch),
+    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, ST, BKM, EPI, ZP, FLIP, BK>), dim3(tiles, a.batch),
                        dim3((BM / WM) * (BN / WN) * 64), 0, s, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int ST, int EPI, int ZP>
+template <int BM, int BN, int WM, int WN, int ST, int EPI, int ZP, int BK>
 hipError_t by_flip(const Int8GemmArgs& a, int flip, hipStream_t s) {
     switch (flip) {
-        case 0: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 0>(a, s);
-        case 1: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 1>(a, s);
-        case 2: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 2>(a, s);
-        default: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 3>(a, s);
+        case 0: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 0, BK>(a, s);
+        case 1: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 1, BK>(a, s);
+        case 2: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 2, BK>(a, s);
+        default: return launch_one<BM, BN, WM, WN, ST, false, EPI, ZP, 3, BK>(a, s);
     }
 }
 
 // Every variant of one tile configuration: A8W8 (fp32 / bf16 out, B as
 // [K,N] or [N,K]) and MatMulInteger (B as [K,N], any flips and sums).
-template <int BM, int BN, int WM, int WN, int ST>
+template <int BM, int BN, int WM, int WN, int ST, int BK = 64>
 hipError_t launch_shape(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
     const int flip = (a.a_flip ? 1 : 0) | (a.b_flip ? 2 : 0);
     if (epi == EPI_I32) {
         switch (zp) {
-            case 0: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 0>(a, flip, s);
-            case 1: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 1>(a, flip, s);
-            case 2: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 2>(a, flip, s);
-            default: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 3>(a, flip, s);
+            case 0: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 0, BK>(a, flip, s);
+            case 1: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 1, BK>(a, flip, s);
+            case 2: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 2, BK>(a, flip, s);
+            default: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 3, BK>(a, flip, s);
         }
     }
-    if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32, 0, 0>(a, s)
-                                   : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16, 0, 0>(a, s);
-    return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32, 0, 0>(a, s)
-                          : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16, 0, 0>(a, s);
+    if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32, 0, 0, BK>(a, s)
+                                   : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16, 0, 0, BK>(a, s);
+    return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32, 0, 0, BK>(a, s)
+                          : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16, 0, 0, BK>(a, s);
 }
 
 }  // namespace dma

@@ -47,7 +47,10 @@ enum TileCfg {
     TILE_128x128_S3 = 3,  // four waves of 64x64, three stages (three workgroups per CU)
     TILE_256x256_W8 = 4,  // eight waves of 128x64, four stages
     TILE_256x128_W8 = 5,  // eight waves of 64x64, four stages
-    NUM_TILE_CFGS = 6
+    TILE_128x128_K128 = 6,     // four waves of 64x64, 128-byte k stages, two stages
+    TILE_256x128_W8_K128 = 7,  // eight waves of 64x64, 128-byte k stages, three stages
+    TILE_256x256_W8_K128 = 8,  // eight waves of 128x64, 128-byte k stages, two stages
+    NUM_TILE_CFGS = 9
 };
 
 // Register-staged kernel, one launcher per tile shape.  bkm: B is [N,K];
@@ -58,14 +61,18 @@ hipError_t launch_tiled_256x128(const Int8GemmArgs& a, bool bkm, bool vec, int e
 hipError_t launch_tiled_128x128(const Int8GemmArgs& a, bool bkm, bool vec, int epi, int zp, hipStream_t s);
 
 // Multi-stage kernel fed by direct global-to-LDS loads, one launcher per
-// configuration.  Needs 16-byte aligned rows; K % 64 == 0 when an operand is
-// uint8 or a zero-point sum is taken, or when B is [N,K].
+// configuration.  Needs 16-byte aligned rows; K a multiple of the stage's
+// k-bytes (64, or 128 for the *_K128 configurations) when an operand is uint8
+// or a zero-point sum is taken, or when B is [N,K].
 hipError_t launch_dma_256x256(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x128s3(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_128x128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_128x128s3(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x256w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x128w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_128x128k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x128w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,

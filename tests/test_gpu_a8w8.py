@@ -171,7 +171,7 @@ def test_a8w8_repeatable():
 
 
 @pytest.mark.parametrize("stage", [0, 1])
-@pytest.mark.parametrize("tile", range(6))
+@pytest.mark.parametrize("tile", range(9))
 def test_a8w8_every_tile_shape(tile, stage):
     """Every tile configuration, with the output written straight from the
     fragments (stage 0) and through LDS in whole rows (stage 1); ragged M and
@@ -196,3 +196,17 @@ def test_a8w8_both_kernel_families(M, N, K, family):
         check(A, W, s_a, s_w, expect_kernel="int8_dma" if family == "dma" else "int8_staged")
         check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True,
               expect_kernel="int8_dma" if (family == "dma" and K % 64 == 0) else "int8_staged")
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8])
+def test_a8w8_k128_stages_partial_last_chunk_and_fallback(tile):
+    """128-byte k stages: K = 1088 is not whole stages.  With B as [K,N] the
+    bytes past K meet zero weight rows, so the 128-byte kernel runs; with B
+    as [N,K] they would not, so its 64-byte sibling runs."""
+    case(f"a8w8 k128 tile {tile} 260x384x1088 and b_trans")
+    A, W, s_a, s_w = si.a8w8_inputs(260, 384, 1088, seed=90 + tile)
+    with env(QGEMM_TILE=tile, QGEMM_STAGE=0):
+        check(A, W, s_a, s_w, expect_kernel="int8_dma")
+        assert q.last_kernel().endswith("k128"), q.last_kernel()
+        check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True, expect_kernel="int8_dma")
+        assert not q.last_kernel().endswith("k128"), q.last_kernel()

@@ -90,7 +90,7 @@ def test_matmul_integer_wraps_mod_2_32():
 
 
 @pytest.mark.parametrize("stage", [0, 1])
-@pytest.mark.parametrize("tile", range(6))
+@pytest.mark.parametrize("tile", range(9))
 def test_matmul_integer_every_tile_shape(tile, stage):
     """Every tile configuration, output straight from the fragments (stage 0)
     or through LDS (stage 1), with ragged M and N edges."""
@@ -117,7 +117,7 @@ def test_matmul_integer_both_kernel_families(family, a_dt, b_dt, za):
 
 
 @pytest.mark.parametrize("a_dt,b_dt", [(np.uint8, np.int8), (np.int8, np.uint8), (np.uint8, np.uint8)])
-@pytest.mark.parametrize("tile", range(6))
+@pytest.mark.parametrize("tile", range(9))
 def test_matmul_integer_row_zero_points_every_tile(tile, a_dt, b_dt):
     """Per-row activation zero points with a shared B (batch folded into M,
     so the row index wraps per batch), per-column b_zp, ragged edges."""
@@ -166,3 +166,15 @@ def test_matmul_integer_row_zero_points_full_size_sampled():
     rows = np.sort(g.choice(512, 16, replace=False))
     ref = oracle.matmul_integer(A[:, rows], B, za[rows], zb)
     np.testing.assert_array_equal(y[:, rows], ref)
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8])
+def test_matmul_integer_k128_stages_fall_back_when_k_is_not_whole_stages(tile):
+    """K = 576 is whole 64-byte stages but not 128-byte ones: a zero-point sum
+    would see the bytes past K, so the 64-byte sibling of the tile runs."""
+    case(f"matmul_integer k128 tile {tile} fallback 2x200x512x576")
+    A, B, zb = si.matmul_integer_inputs(2, 200, 512, 576, seed=41 + tile)
+    with env(QGEMM_TILE=tile):
+        y = q.matmul_integer(to_dev(A), to_dev(B), 128, to_dev(zb)).cpu().numpy()
+        assert q.last_kernel().startswith("int8_dma") and not q.last_kernel().endswith("k128"), q.last_kernel()
+    np.testing.assert_array_equal(y, oracle.matmul_integer(A, B, 128, zb))

@@ -60,13 +60,19 @@ int pick_tile(int64_t batch, int64_t M, int64_t N) {
     return qg::TILE_128x128_K128;
 }
 
-// Whether the multi-stage kernel writes its output tile through LDS in whole
-// rows (fewer, wider stores) or straight from the fragments (less latency).
-// QGEMM_STAGE=0/1 forces the choice.
-bool stage_output(int cfg, int64_t batch, int64_t M, int64_t N) {
+// How the multi-stage kernel writes its output tile: 0 straight from the
+// fragments (less latency), 1 through LDS in whole rows with plain stores
+// (large grids), 2 through LDS with non-temporal stores (single-round
+// grids).  QGEMM_STAGE=0/1/2 forces the choice.
+int stage_output(int cfg, int64_t K) {
     const int forced = env_int("QGEMM_STAGE", -1);
-    if (forced >= 0) return forced != 0;
-    return cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128;
+    if (forced >= 0 && forced <= 2) return forced;
+    if (cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128) return 1;
+    // Smaller tiles: staged non-temporal rows once the main loop is long
+    // enough to absorb the staging barriers (MatMulInteger 8x512x2048x2048:
+    // 29.5 -> 27.6 us; A8W8 4096x2048x2048 bf16: 28.9 -> 22.9 us); straight
+    // fragment stores for short K (a K = 576 convolution: 37.8 us against 39.3).
+    return K >= 1024 ? 2 : 0;
 }
 
 qg_status finish_launch(hipError_t e, const char* name) {
@@ -111,7 +117,7 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
     if (dma_ok(a, bkm, vec, epi, is_k128(cfg) ? 128 : 64)) {
         *name = dma_names[cfg];
         qg::Int8GemmArgs d = a;
-        d.stage_out = stage_output(cfg, a.batch, a.M, a.N) ? 1 : 0;
+        d.stage_out = stage_output(cfg, a.K);
         switch (cfg) {
             case qg::TILE_256x256: return qg::launch_dma_256x256(d, bkm, epi, zp, s);
             case qg::TILE_256x128_S3: return qg::launch_dma_256x128s3(d, bkm, epi, zp, s);

@@ -301,7 +301,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // four consecutive columns.  Stored straight to memory these leave as 32-
     // or 64-byte pieces of rows; with stage_out set the finished values go
     // through LDS (free once the last chunk is multiplied) and leave as whole
-    // rows, 16 bytes per lane.  The direct stores are non-temporal: small
+    // rows, 16 bytes per lane: plain stores (stage_out 1) for grids of several
+    // rounds, whose lines L2 merges long before the end, or non-temporal ones
+    // (stage_out 2) for single-round grids that write everything at once.  The direct stores are non-temporal: small
     // grids finish all their tiles at once, and an output left in L2 would be
     // written back in one burst when the kernel ends (MatMulInteger
     // 4096x2048x2048: 32 -> 25 us).  The staged path serves large grids whose
@@ -523,7 +525,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             if (m >= p.M || n >= p.N) continue;
             char* dst = out + ((int64_t)m * p.ldo + n) * OUT_BYTES;
             if (vec_out && n + PER_CHUNK <= p.N) {
-                *reinterpret_cast<u32x4*>(dst) = v;
+                if (p.stage_out == 2)
+                    __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, reinterpret_cast<v4i*>(dst));
+                else
+                    *reinterpret_cast<u32x4*>(dst) = v;
             } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

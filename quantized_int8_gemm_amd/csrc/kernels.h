@@ -36,7 +36,8 @@ struct Int8GemmArgs {
     void* workspace;
     int splits;
     int split_steps;   // skinny kernel: 64-row steps per split (multiple of 8)
-    int stage_out;     // tiled kernel: write the output tile through LDS in whole rows
+    int stage_out;     // tiled kernel: 0 stores from the fragments; 1 / 2 writes the
+                       // output tile through LDS in whole rows, plain / non-temporal
 };
 
 // Tile configurations of the int8 GEMM kernels.

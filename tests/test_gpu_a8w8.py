@@ -170,7 +170,7 @@ def test_a8w8_repeatable():
         np.testing.assert_array_equal(run(A, W, s_a, s_w, torch.float32).cpu().numpy(), first)
 
 
-@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("stage", [0, 1, 2])
 @pytest.mark.parametrize("tile", range(9))
 def test_a8w8_every_tile_shape(tile, stage):
     """Every tile configuration, with the output written straight from the

@@ -35,7 +35,7 @@ def check(acc_in, A, W, s_a, s_w, b_trans=False, expect_kernel=None, acc_dev=Non
     np.testing.assert_array_equal(bf16_bits(h), ref["bf16"])
 
 
-@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("stage", [0, 1, 2])
 @pytest.mark.parametrize("tile", range(9))
 def test_a8w8_acc_every_tile_shape(tile, stage):
     case(f"a8w8_acc tile {tile} stage {stage} 520x704x512 and 300x700x256 b_trans")
@@ -83,7 +83,7 @@ def test_a8w8_acc_tiled_accumulator_view():
     big = torch.zeros((M, 520), dtype=torch.int32, device=dev())
     view = big[:, :N]
     view.copy_(to_dev(acc))
-    for stage in (0, 1):
+    for stage in (0, 1, 2):
         with env(QGEMM_STAGE=stage):
             check(acc, A, W, s_a, s_w, expect_kernel="int8_dma", acc_dev=view)
 

@@ -89,7 +89,7 @@ def test_matmul_integer_wraps_mod_2_32():
     assert (y == -1693967296).all()
 
 
-@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("stage", [0, 1, 2])
 @pytest.mark.parametrize("tile", range(9))
 def test_matmul_integer_every_tile_shape(tile, stage):
     """Every tile configuration, output straight from the fragments (stage 0)

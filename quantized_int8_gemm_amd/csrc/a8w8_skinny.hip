@@ -225,8 +225,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
                 *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) = make_float4(f[0], f[1], f[2], f[3]);
             } else {
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) =
-                    make_uint2((uint32_t)f32_to_bf16_rne(f[0]) | ((uint32_t)f32_to_bf16_rne(f[1]) << 16),
-                               (uint32_t)f32_to_bf16_rne(f[2]) | ((uint32_t)f32_to_bf16_rne(f[3]) << 16));
+                    make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
             }
             return;
         }

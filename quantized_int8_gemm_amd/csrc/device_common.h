@@ -55,12 +55,21 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t x[4], uint32_t
 // and so is a row written as eight segments by eight lanes.
 __device__ __forceinline__ int swz(int r) { return r & 7; }
 
-// IEEE binary32 -> bfloat16 bits, round to nearest, ties to even.
+// IEEE binary32 -> bfloat16 bits, round to nearest, ties to even, two
+// values at once (lo in bits 0..15) by the hardware's packed conversion
+// (v_cvt_pk_bf16_f32 in the default rounding mode, fp32 denormals kept):
+// one instruction where the integer rounding sequence takes about six per
+// value.  On every non-NaN input it equals the textbook rounding
+// (b + 0x7fff + ((b >> 16) & 1)) >> 16 of the bit pattern b; all 2^32
+// patterns were compared on the device.  A NaN becomes a quiet NaN.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t b = __float_as_uint(f);
-    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x007fffffu) != 0)
-        return (uint16_t)((b >> 16) | 0x0040u);
-    return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+    return (uint16_t)pack_bf16x2(f, 0.f);
 }
 
 // Workgroups are handed to the eight XCDs round robin (id % 8).  Renumber so

@@ -124,7 +124,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, conv, small, ceilings)")
+                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, conv, small, ceilings); \"vendor\" times torch._int_mm on the headline shape for comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -370,6 +370,17 @@ def main():
         o = torch.empty((64, 64), dtype=torch.float32, device=dev)
         ms = time_calls(lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o), [None], 100, 10, stream)
         rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
+
+    # ---- context only (opt-in): the vendor int8 GEMM on the same shape ---
+    # torch._int_mm (hipBLASLt underneath) writes the raw int32 product, no
+    # scales and twice the output bytes of bf16; timed for both weight
+    # layouts, as a measured point of comparison, never as a result.
+    if args.only == "vendor":
+        A8, W8 = tA.contiguous(), tW.contiguous()
+        for name, Bm in (("kn", W8), ("nk_transposed", W8.t().contiguous().t())):
+            ms = time_calls(lambda s, b=Bm: torch._int_mm(A8, b), [None], steps, warmup, stream)
+            rows[f"vendor_int_mm_8192_i32_{name}"] = {"kernel": "torch._int_mm", "us": ms * 1e3,
+                                                     "TOPS": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
 
     # ---- measured ceilings: streaming read, int8 matrix-core loop -------
     ceilings = None

@@ -32,6 +32,7 @@ SOURCES = [
     "w8a32.hip",
     "dynamic_quantize.hip",
     "conv_integer.hip",
+    "conv_implicit.hip",
     "calibrate.hip",
     "api.cpp",
 ]

@@ -475,10 +475,14 @@ qg_status dynamic_quantize_linear(int64_t n, const float* x, uint8_t* y, float* 
 
 namespace {
 
-// ConvInteger geometry and workspace layout: [packed w][pad to 256][col].
+// ConvInteger geometry and the path it takes: the implicit GEMM where its
+// plan fits (workspace: packed w, row sums, padded channel-minor x), else
+// im2col + the MatMulInteger GEMM (workspace: [packed w][pad to 256][col]).
 struct ConvPlan {
     qg::ConvGeom g;
     size_t wp_bytes, col_off, total;
+    bool implicit;
+    qg::ConvImplicitPlan ip;
 };
 
 // Fills `plan` from the call's sizes; false if they do not describe a
@@ -514,6 +518,9 @@ bool conv_plan(int64_t N, int64_t C, int64_t H, int64_t W, int64_t M, int64_t kH
     plan->wp_bytes = (size_t)(group * Mg * Kp);
     plan->col_off = (plan->wp_bytes + 255) / 256 * 256;
     plan->total = plan->col_off + (size_t)N * group * Kp * Pp;
+    // QGEMM_CONV=im2col keeps the column-matrix path (tests and comparisons)
+    plan->implicit = !env_is("QGEMM_CONV", "im2col") && qg::conv_implicit_plan(g, &plan->ip);
+    if (plan->implicit) plan->total = plan->ip.total;
     return true;
 }
 
@@ -547,6 +554,13 @@ qg_status conv_integer(int64_t N, int64_t C, int64_t H, int64_t W, const void* x
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.total) return QG_ERR_WORKSPACE;
     const qg::ConvGeom& g = plan.g;
+    if (plan.implicit) {
+        (void)hipGetLastError();
+        const hipError_t e = qg::launch_conv_implicit(g, plan.ip, x, x_u8, x_zero_point, w, w_u8, w_zero_point,
+                                                      (int)w_zero_point_len, workspace, y, (hipStream_t)stream);
+        log_dispatch("conv_integer", "conv_implicit", N, M, (int64_t)g.P, g.Kg, g.group);
+        return finish_launch(e, "conv_implicit");
+    }
     // 32-bit buffer offsets inside one GEMM operand: a packed group of w and
     // one image's column matrix.
     if ((int64_t)g.Kp * g.Pp + 256 >= SPAN_LIMIT || (int64_t)g.Mg * g.Kp + 256 >= SPAN_LIMIT)

@@ -106,6 +106,27 @@ struct ConvGeom {
 hipError_t launch_conv_stage(const ConvGeom& c, const void* x, uint8_t x_zp, const void* w, const void* w_zp,
                              int w_zp_len, uint8_t* wp, uint8_t* col, hipStream_t s);
 
+// ConvInteger as an implicit GEMM (no column matrix): the tiling and the
+// workspace layout of one call.  Eligible when Cg is a multiple of 64, there
+// are at most 9 taps and a tile's weights and input halo fit in LDS.
+struct ConvImplicitPlan {
+    int BM;              // output channels per tile (64 or 128)
+    int BW, BH;          // output tile: BH rows x BW columns (128 positions)
+    int TH, TWt;         // output tiles down / across
+    int HP, WP;          // rows / columns of the padded input xp
+    int Cgp, taps, cblks;
+    int HR, HC;          // halo rows / columns one tile reads
+    int a_pitch;         // LDS bytes per weight row (taps*64, padded to 64 mod 256)
+    int h_rounds;        // 4 KiB load rounds of the halo
+    int lds_bytes;
+    int64_t Kt;          // packed weight row bytes: Cgp * taps
+    size_t wp_off, rs_off, xp_off, total;   // packed weights, row sums, xp
+};
+bool conv_implicit_plan(const ConvGeom& c, ConvImplicitPlan* p);
+hipError_t launch_conv_implicit(const ConvGeom& c, const ConvImplicitPlan& p, const void* x, bool x_u8, int x_zp,
+                                const void* w, bool w_u8, const void* w_zp, int w_zp_len, void* ws, int32_t* y,
+                                hipStream_t s);
+
 // DynamicQuantizeLinear (uint8): a min/max pass writing one (min, max)
 // float pair per workgroup into the workspace, then a quantize pass.
 constexpr int DQL_MAX_PARTIALS = 256;

@@ -258,13 +258,21 @@ def _i64a(*v):
     return (ctypes.c_int64 * len(v))(*v)
 
 
-def test_conv_integer_workspace_and_rejects():
+def test_conv_integer_workspace_and_rejects(monkeypatch):
     lib = b.lib
     P0, S1, D1 = _i64a(0, 0, 0, 0), _i64a(1, 1), _i64a(1, 1)
-    # 1 x 64 x 32 x 32 input, 128 x 64 x 3 x 3 weight, pad 1: K = 576 (a multiple of 64),
-    # P = 1024; workspace = packed w (128 x 576) + columns (576 x 1024)
+    # 1 x 64 x 32 x 32 input, 128 x 64 x 3 x 3 weight, pad 1.  Implicit GEMM
+    # (channels per group a multiple of 64): packed w (128 x 576), row sums
+    # (128 int32), then the padded channel-minor input: 4 x 32 output tiles
+    # read padded rows and columns 0..33, 64 channels each.
     P1 = _i64a(1, 1, 1, 1)
+    assert lib.conv_integer_workspace_bytes(1, 64, 32, 32, 128, 3, 3, 1, P1, S1, D1) == \
+        128 * 576 + 128 * 4 + 34 * 34 * 64
+    # the im2col path: K = 576 (a multiple of 64), P = 1024; packed w
+    # (128 x 576) + columns (576 x 1024)
+    monkeypatch.setenv("QGEMM_CONV", "im2col")
     assert lib.conv_integer_workspace_bytes(1, 64, 32, 32, 128, 3, 3, 1, P1, S1, D1) == 128 * 576 + 576 * 1024
+    monkeypatch.delenv("QGEMM_CONV")
     # K padded to 64, P padded to 16: C/group*kH*kW = 29*9 = 261 -> 320; P = 4*4 -> 16
     assert lib.conv_integer_workspace_bytes(1, 58, 7, 7, 6, 3, 3, 2, P1, _i64a(2, 2), D1) == \
         256 * ((2 * 3 * 320 + 255) // 256) + 2 * 320 * 16

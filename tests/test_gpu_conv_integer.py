@@ -84,11 +84,13 @@ def test_conv_integer_wraps():
     run(x, w, 0, None)
 
 
-def test_conv_integer_tokenizer_layer_sampled():
+def test_conv_integer_tokenizer_layer_sampled(monkeypatch):
     """The benchmark's layer (uint8 [64, 64, 32, 32] activations, int8
-    [128, 64, 3, 3] weight, padding 1, zero points 128 and per channel), all
-    64 images on the GPU; the oracle checks images 0, 31 and 63 in full."""
-    case("conv tokenizer layer 64x64x32x32 * 128x64x3x3")
+    [128, 64, 3, 3] weight, padding 1, zero points 128 and per channel)
+    through the im2col path, all 64 images on the GPU; the oracle checks
+    images 0, 31 and 63 in full."""
+    case("conv tokenizer layer 64x64x32x32 * 128x64x3x3, im2col path")
+    monkeypatch.setenv("QGEMM_CONV", "im2col")
     x, w, zw = si.conv_integer_inputs(64, 64, 32, 32, 128, 3, 3, seed=808)
     y = q.conv_integer(to_dev(x), to_dev(w), 128, to_dev(zw), pads=(1, 1, 1, 1))
     assert q.last_kernel().startswith("conv_im2col+int8_dma"), q.last_kernel()

@@ -168,6 +168,38 @@ def time_calls(fn, sets, steps, warmup, stream):
     return start.elapsed_time(stop) / steps
 
 
+def time_graph(fn, sets, steps, replays, stream):
+    """Average milliseconds per call with `steps` calls captured in one HIP
+    graph and the graph replayed `replays` times: the GPU's own time per call,
+    without the per-call host work of an eager launch (which exceeds a
+    15-microsecond kernel).  The calls must allocate nothing (pass out= and
+    workspace=).  Spin-up and warm-up as in time_calls."""
+    import torch
+    t_end = time.perf_counter() + SPIN_UP_S
+    i = 0
+    while time.perf_counter() < t_end:
+        fn(sets[i % len(sets)])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(sets[i % len(sets)])
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (replays * steps)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -226,18 +258,24 @@ def main():
 
     # ---- decode: M in {1, 4, 16}, K = N = 8192, bf16 out ---------------
     if want("decode"):
+        # 9 rotating weight copies (576 MiB, beyond the 256 MB Infinity
+        # Cache); timed as a replayed HIP graph of 36 calls (the GPU's time
+        # per call) and as eager calls (bound by the host's per-call work)
         for m in (1, 4, 16):
             A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
             base_w = to(W)
             sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),
                      torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)) for r in range(9)]
-            call = lambda s: q.qgemm_a8w8(s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4])
-            ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+            ws = torch.zeros(q.workspace_bytes(q.QG_OP_A8W8, 1, m, 8192, 8192), dtype=torch.uint8, device=dev)
+            call = lambda s: q.qgemm_a8w8(s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4], workspace=ws)
+            ms_eager = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+            ms = time_graph(call, sets, 36, max(steps // 2, 5), stream)
             nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192
             gbs = nbytes / (ms * 1e-3) / 1e9
             rows[f"a8w8_decode_m{m}_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
-                                                   "frac_hbm_peak": gbs / PEAK_HBM_GBS}
-            del sets, base_w
+                                                   "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
+                                                   "us_eager": ms_eager * 1e3}
+            del sets, base_w, ws
 
     # ---- MatMulInteger 8 x 512 x 2048 x 2048, shared B -------------------
     if want("mmi"):
@@ -363,13 +401,19 @@ def main():
         A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
         sA, sW, sa, sw = to(A), to(W), to(s_a), to(s_w)
         o = torch.empty((256, 1024), dtype=torch.float32, device=dev)
-        ms = time_calls(lambda s: q.qgemm_a8w8(sA, sW, sa, sw, out=o), [None], 100, 10, stream)
-        rows["a8w8_256x1024x1024_fp32"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
+        call = lambda s: q.qgemm_a8w8(sA, sW, sa, sw, out=o)
+        ms_eager = time_calls(call, [None], 100, 10, stream)
+        ms = time_graph(call, [None], 50, 10, stream)
+        rows["a8w8_256x1024x1024_fp32"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "timing": "hip_graph",
+                                           "us_eager": ms_eager * 1e3}
         A, W = si.w8a32_inputs(64, 64, 128, seed=101)
         wA, wW = to(A), to(W)
         o = torch.empty((64, 64), dtype=torch.float32, device=dev)
-        ms = time_calls(lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o), [None], 100, 10, stream)
-        rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3}
+        call = lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o)
+        ms_eager = time_calls(call, [None], 100, 10, stream)
+        ms = time_graph(call, [None], 50, 10, stream)
+        rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "timing": "hip_graph",
+                                   "us_eager": ms_eager * 1e3}
 
     # ---- context only (opt-in): the vendor int8 GEMM on the same shape ---
     # torch._int_mm (hipBLASLt underneath) writes the raw int32 product, no

@@ -194,36 +194,50 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // slot = seg ^ b_x for this lane's transposed-read rows (16g + 8h + i/2)
     const int b_x = (i16 >> 1) ^ (BN >= 256 ? ((g & 1) << 3) : (g & 1));
 
+    // B fragments of k-block kb of a stage.
+    auto read_b = [&](const uint8_t* S, int kb, u32x4* bf) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (B_KMAJOR) {
+                bf[j] = *reinterpret_cast<const u32x4*>(S + b_rd + j * 16 * BK + (kc_slot<BK>(i16, 4 * kb + g) << 4));
+            } else {
+                const int seg = (wn * WN) / 16 + j;
+                const uint8_t* base = S + b_rd + kb * 64 * BN + ((seg ^ b_x) << 4);
+                const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(base));
+                const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) v2i*)(base + 8 * BN));
+                bf[j] = u32x4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
+            }
+        }
+    };
+
+    // Every k-block's B fragments are read at the start of the stage (the
+    // first k-block's, then its first A fragment, then the rest), and the A
+    // fragments one block ahead run on across the k-block boundary, so no
+    // k-block waits for reads issued just before its first multiply.
     auto compute = [&](int stage) {
         const uint8_t* S = smem + stage * STAGE;
+        u32x4 bfs[KB][FN];
+        read_b(S, 0, bfs[0]);
+        u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd_at(0));
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb) read_b(S, kb, bfs[kb]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            u32x4 bf[FN];
+            u32x4* bf = bfs[kb];
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                if constexpr (B_KMAJOR) {
-                    bf[j] = *reinterpret_cast<const u32x4*>(S + b_rd + j * 16 * BK + (kc_slot<BK>(i16, 4 * kb + g) << 4));
-                } else {
-                    const int seg = (wn * WN) / 16 + j;
-                    const uint8_t* base = S + b_rd + kb * 64 * BN + ((seg ^ b_x) << 4);
-                    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) v2i*)(base));
-                    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) v2i*)(base + 8 * BN));
-                    bf[j] = u32x4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
-                }
                 if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
                 if constexpr (COLSUM)
                     cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
             }
-            // A fragments one block ahead, so each LDS read overlaps the
-            // previous block's matrix-core work.
             const int a_rd = a_rd_at(kb);
-            u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd);
 #pragma unroll
             for (int a = 0; a < FM; ++a) {
                 u32x4 af = af_next;
                 if (a + 1 < FM) af_next = *reinterpret_cast<const u32x4*>(S + a_rd + (a + 1) * 16 * BK);
+                else if (kb + 1 < KB) af_next = *reinterpret_cast<const u32x4*>(S + a_rd_at(kb + 1));
                 __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
                 if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
                 if constexpr (ROWSUM)

@@ -216,13 +216,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // first k-block's, then its first A fragment, then the rest), and the A
     // fragments one block ahead run on across the k-block boundary, so no
     // k-block waits for reads issued just before its first multiply.
-    auto compute = [&](int stage) {
+    // The next chunk's global->LDS loads (next_kt >= 0) are issued right
+    // after this stage's first fragment reads, so those reads start as soon
+    // as the stage is ready.
+    auto compute = [&](int stage, int next_kt) {
         const uint8_t* S = smem + stage * STAGE;
         u32x4 bfs[KB][FN];
         read_b(S, 0, bfs[0]);
         u32x4 af_next = *reinterpret_cast<const u32x4*>(S + a_rd_at(0));
 #pragma unroll
         for (int kb = 1; kb < KB; ++kb) read_b(S, kb, bfs[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (next_kt >= 0) issue(next_kt, next_kt % STAGES);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             u32x4* bf = bfs[kb];
@@ -290,8 +296,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         else if (kt + 1 < nk) wait_vmcnt<LOADS>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-        compute(kt % STAGES);
+        compute(kt % STAGES, kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1);
     }
 
     // Complete row / column sums: add the four lane groups (k segments).

@@ -48,16 +48,17 @@ PEAK_HBM_GBS = 8000.0        # HBM3E
 COPY_BYTES = 256 << 20       # size of the calibration copy
 CEIL_READ_BYTES = 1 << 30    # streaming-read ceiling: 1 GiB, four times the Infinity Cache
 CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops per launch
+SPREAD_CALLS = 100           # single calls timed one by one for each row's median / p10 / p90
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 HEADLINE_SOURCES = ("int8_dma_impl.h", "int8_dma_256x256w8k128.hip", "device_common.h")
 
 
-def source_hash():
-    """sha256 over the sources the headline kernel is compiled from."""
+def source_hash(sources=HEADLINE_SOURCES):
+    """sha256 over the sources a kernel is compiled from (default: the headline's)."""
     h = hashlib.sha256()
-    for f in sorted(os.path.join(ROOT, "quantized_int8_gemm_amd", "csrc", n) for n in HEADLINE_SOURCES):
+    for f in sorted(os.path.join(ROOT, "quantized_int8_gemm_amd", "csrc", n) for n in sources):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -80,7 +81,8 @@ def _pmc_avg(db_dir, counter, match):
 
 
 def pmc_summary(args):
-    """Write profiles/traffic.json from four rocprofv3 --pmc runs."""
+    """Write the traffic summary (profiles/traffic.json for the headline, or
+    --traffic-out for another kernel) from four rocprofv3 --pmc runs."""
     fetch, nf = _pmc_avg(args.fetch_db, "FETCH_SIZE", args.kernel_match)
     write, nw = _pmc_avg(args.write_db, "WRITE_SIZE", args.kernel_match)
     cfetch, _ = _pmc_avg(args.copy_fetch_db, "FETCH_SIZE", "neg_kernel")
@@ -88,13 +90,14 @@ def pmc_summary(args):
     f_scale = COPY_BYTES / (cfetch * 1024.0)
     w_scale = COPY_BYTES / (cwrite * 1024.0)
     traffic = fetch * 1024.0 * f_scale + write * 1024.0 * w_scale
-    out = {"kernel_match": args.kernel_match, "source_sha256": source_hash(),
+    sources = tuple(args.sources.split(",")) if args.sources else HEADLINE_SOURCES
+    out = {"kernel_match": args.kernel_match, "source_sha256": source_hash(sources), "sources": list(sources),
            "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
            "dispatches": [nf, nw],
            "copy_bytes": COPY_BYTES, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
            "fetch_scale": f_scale, "write_scale": w_scale, "traffic_bytes_per_dispatch": traffic,
-           "workload": "a8w8_prefill_8192x8192x8192_bf16"}
-    with open(TRAFFIC_JSON, "w") as f:
+           "workload": args.workload}
+    with open(args.traffic_out or TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -134,6 +137,12 @@ def parse():
     ap.add_argument("--copy-fetch-db")
     ap.add_argument("--copy-write-db")
     ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 2, false, 1, 0, 0, 128>")
+    ap.add_argument("--workload", default="a8w8_prefill_8192x8192x8192_bf16",
+                    help="--pmc-summary: the workload the counters were taken on")
+    ap.add_argument("--sources", default=None,
+                    help="--pmc-summary: comma-separated csrc files of the kernel (default: the headline's)")
+    ap.add_argument("--traffic-out", default=None,
+                    help="--pmc-summary: output path (default profiles/traffic.json)")
     return ap.parse_args()
 
 
@@ -168,12 +177,36 @@ def time_calls(fn, sets, steps, warmup, stream):
     return start.elapsed_time(stop) / steps
 
 
-def time_graph(fn, sets, steps, replays, stream):
+def _spread(vals_us):
+    v = sorted(vals_us)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return {"n": len(v), "median_us": pick(0.5), "p10_us": pick(0.1), "p90_us": pick(0.9)}
+
+
+def per_call_spread(fn, sets, n, stream):
+    """Median, p10 and p90 of n single calls, each bracketed by its own HIP
+    events on the launching stream (run after a row's timed block, so the
+    calls find the clocks settled).  A call timed alone also carries its own
+    launch gap, so for calls of a few tens of microseconds the median reads
+    about 2 us above the back-to-back mean that "us" reports."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(sets[i % len(sets)])
+        b.record(stream)
+    torch.cuda.synchronize()
+    return _spread([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def time_graph(fn, sets, steps, replays, stream, spread=False):
     """Average milliseconds per call with `steps` calls captured in one HIP
     graph and the graph replayed `replays` times: the GPU's own time per call,
     without the per-call host work of an eager launch (which exceeds a
     15-microsecond kernel).  The calls must allocate nothing (pass out= and
-    workspace=).  Spin-up and warm-up as in time_calls."""
+    workspace=).  Spin-up and warm-up as in time_calls.  With spread=True it
+    also returns the per-call spread over `replays` more replays, each timed
+    on its own."""
     import torch
     t_end = time.perf_counter() + SPIN_UP_S
     i = 0
@@ -197,7 +230,17 @@ def time_graph(fn, sets, steps, replays, stream):
         g.replay()
     stop.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / (replays * steps)
+    ms = start.elapsed_time(stop) / (replays * steps)
+    if not spread:
+        return ms
+    # per-call time of each replay on its own (replay time / steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for a, b in evs:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return ms, _spread([a.elapsed_time(b) * 1e3 / steps for a, b in evs])
 
 
 def main():
@@ -248,11 +291,14 @@ def main():
         ops = 2.0 * M * N * K
         tops = ops / (head_ms * 1e-3) / 1e12
         rows["a8w8_prefill_8192_bf16"] = {"kernel": kernel, "us": head_ms * 1e3, "TOPS": tops,
-                                          "frac_int8_peak": tops / PEAK_INT8_TOPS}
+                                          "frac_int8_peak": tops / PEAK_INT8_TOPS,
+                                          "per_call": per_call_spread(call, [None], SPREAD_CALLS, stream)}
         outf = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ms = time_calls(lambda s: q.qgemm_a8w8(tA, tW, ta, tw, out=outf), [None], steps, warmup, stream)
-        rows["a8w8_prefill_8192_fp32"] = {"us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
-                                          "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+        callf = lambda s: q.qgemm_a8w8(tA, tW, ta, tw, out=outf)
+        ms = time_calls(callf, [None], steps, warmup, stream)
+        rows["a8w8_prefill_8192_fp32"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
+                                          "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                                          "per_call": per_call_spread(callf, [None], SPREAD_CALLS, stream)}
         del outf
     del A, W
 
@@ -269,12 +315,12 @@ def main():
             ws = torch.zeros(q.workspace_bytes(q.QG_OP_A8W8, 1, m, 8192, 8192), dtype=torch.uint8, device=dev)
             call = lambda s: q.qgemm_a8w8(s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4], workspace=ws)
             ms_eager = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
-            ms = time_graph(call, sets, 36, max(steps // 2, 5), stream)
+            ms, spread = time_graph(call, sets, 36, max(steps // 2, 5), stream, spread=True)
             nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192
             gbs = nbytes / (ms * 1e-3) / 1e9
             rows[f"a8w8_decode_m{m}_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
                                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
-                                                   "us_eager": ms_eager * 1e3}
+                                                   "us_eager": ms_eager * 1e3, "per_call": spread}
             del sets, base_w, ws
 
     # ---- MatMulInteger 8 x 512 x 2048 x 2048, shared B -------------------
@@ -290,7 +336,8 @@ def main():
             "kernel": q.last_kernel(), "us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
             "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
-            "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets
 
     # ---- A8W8 with an int32 accumulator input; per-row MatMulInteger zp --
@@ -302,12 +349,13 @@ def main():
         g = si.rng(606)
         acc = torch.from_numpy(si.randint(g, (M, N), -2**20, 2**20, np.int32)).to(dev)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        ms = time_calls(lambda s: q.qgemm_a8w8_acc(acc, tA, tW, ta, tw, out_dtype=torch.bfloat16, out=out),
-                        [None], steps, warmup, stream)
+        calla = lambda s: q.qgemm_a8w8_acc(acc, tA, tW, ta, tw, out_dtype=torch.bfloat16, out=out)
+        ms = time_calls(calla, [None], steps, warmup, stream)
         ops = 2.0 * M * N * K
         rows["a8w8_acc_prefill_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
                                               "TOPS": ops / (ms * 1e-3) / 1e12,
-                                              "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+                                              "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                                              "per_call": per_call_spread(calla, [None], SPREAD_CALLS, stream)}
         del acc, out, tA, tW
         m = 16
         A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
@@ -320,7 +368,8 @@ def main():
         nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 4 * m * 8192 + 2 * m * 8192
         rows["a8w8_acc_decode_m16_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
                                                  "GB/s": nbytes / (ms * 1e-3) / 1e9,
-                                                 "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                                                 "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                 "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets, base_w
         A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
         za = to(si.randint(g, (512,), 0, 255, np.uint8))
@@ -331,7 +380,8 @@ def main():
         ops = 2.0 * 8 * 512 * 2048 * 2048
         rows["matmul_integer_row_zp_8x512x2048x2048"] = {
             "kernel": q.last_kernel(), "us": ms * 1e3, "TOPS": ops / (ms * 1e-3) / 1e12,
-            "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+            "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets
 
     # ---- W8A32 4096^3 -----------------------------------------------------
@@ -339,18 +389,21 @@ def main():
         A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
         tA, tW = to(A), to(W)
         outc = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
-        ms = time_calls(lambda s: q.qgemm_w8a32(tA, tW, 0.01, -5, out=outc), [None], steps, warmup, stream)
+        callw = lambda s: q.qgemm_w8a32(tA, tW, 0.01, -5, out=outc)
+        ms = time_calls(callw, [None], steps, warmup, stream)
         fl = 2.0 * 4096 ** 3
         rows["w8a32_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "TFLOPS": fl / (ms * 1e-3) / 1e12,
-                              "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
+                              "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                              "per_call": per_call_spread(callw, [None], SPREAD_CALLS, stream)}
         # its input gradient: dA = dC @ ((W - zp) * scale)^T, same weight
         dC, _ = si.w8a32_inputs(4096, 4096, 4096, seed=507)
         tdC = to(dC)
-        ms = time_calls(lambda s: q.qgemm_w8a32_input_grad(tdC, tW, 0.01, -5, out=outc), [None], steps, warmup,
-                        stream)
+        callg = lambda s: q.qgemm_w8a32_input_grad(tdC, tW, 0.01, -5, out=outc)
+        ms = time_calls(callg, [None], steps, warmup, stream)
         rows["w8a32_input_grad_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
                                          "TFLOPS": fl / (ms * 1e-3) / 1e12,
-                                         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
+                                         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                                         "per_call": per_call_spread(callg, [None], SPREAD_CALLS, stream)}
         del A, W, tA, tW, outc, dC, tdC
 
     # ---- DynamicQuantizeLinear on [8, 512, 2048] fp32, and its chain ----
@@ -364,7 +417,8 @@ def main():
         nbytes = 4 * n + n + 4 + 1          # read x, write y (the scalars)
         gbs = nbytes / (ms * 1e-3) / 1e9
         rows["dynamic_quantize_linear_8x512x2048"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
-                                                     "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+                                                     "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                                                     "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         # fp32 activations -> uint8 + zero point (on the device) -> MatMulInteger
         _, B, zb = si.matmul_integer_inputs(1, 1, 2048, 2048, seed=303)
         tB, tzb = to(B), to(zb)
@@ -376,7 +430,8 @@ def main():
         ms = time_calls(chain, sets, max(steps * 5, 50), warmup * 2, stream)
         ops = 2.0 * 8 * 512 * 2048 * 2048
         rows["dql_then_matmul_integer_8x512x2048x2048"] = {"kernels": "dql + " + q.last_kernel(), "us": ms * 1e3,
-                                                          "TOPS": ops / (ms * 1e-3) / 1e12}
+                                                          "TOPS": ops / (ms * 1e-3) / 1e12,
+                                                          "per_call": per_call_spread(chain, sets, SPREAD_CALLS, stream)}
         del sets, x
 
     # ---- ConvInteger: a 3x3 tokenizer-sized layer -------------------------
@@ -393,7 +448,8 @@ def main():
         rows["conv_integer_64x64x32x32_k3x3_m128"] = {"kernels": q.last_kernel(), "us": ms * 1e3,
                                                      "TOPS": ops / (ms * 1e-3) / 1e12,
                                                      "GB/s": nbytes / (ms * 1e-3) / 1e9,
-                                                     "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS}
+                                                     "frac_int8_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                                                     "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets, ws
 
     # ---- the small parity shapes (launch-latency bound) ------------------
@@ -403,17 +459,17 @@ def main():
         o = torch.empty((256, 1024), dtype=torch.float32, device=dev)
         call = lambda s: q.qgemm_a8w8(sA, sW, sa, sw, out=o)
         ms_eager = time_calls(call, [None], 100, 10, stream)
-        ms = time_graph(call, [None], 50, 10, stream)
+        ms, spread = time_graph(call, [None], 50, 10, stream, spread=True)
         rows["a8w8_256x1024x1024_fp32"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "timing": "hip_graph",
-                                           "us_eager": ms_eager * 1e3}
+                                           "us_eager": ms_eager * 1e3, "per_call": spread}
         A, W = si.w8a32_inputs(64, 64, 128, seed=101)
         wA, wW = to(A), to(W)
         o = torch.empty((64, 64), dtype=torch.float32, device=dev)
         call = lambda s: q.qgemm_w8a32(wA, wW, 0.02, 3, out=o)
         ms_eager = time_calls(call, [None], 100, 10, stream)
-        ms = time_graph(call, [None], 50, 10, stream)
+        ms, spread = time_graph(call, [None], 50, 10, stream, spread=True)
         rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "timing": "hip_graph",
-                                   "us_eager": ms_eager * 1e3}
+                                   "us_eager": ms_eager * 1e3, "per_call": spread}
 
     # ---- context only (opt-in): the vendor int8 GEMM on the same shape ---
     # torch._int_mm (hipBLASLt underneath) writes the raw int32 product, no

@@ -41,6 +41,11 @@ namespace dma {
 
 constexpr int GROUP_M = 8;
 
+// Epilogue codes of this kernel beyond Int8Epilogue: fp32 / bf16 output with
+// an int32 accumulator input, so that the plain A8W8 kernels carry no code
+// for it.
+constexpr int EPI_F32_ACC = 3, EPI_BF16_ACC = 4;
+
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Buffer descriptor words for [base, base + bytes); loads past the end give 0.
@@ -110,6 +115,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_ROUNDS = A_BYTES / ROUND, B_ROUNDS = B_BYTES / ROUND;
     constexpr int LOADS = A_ROUNDS + B_ROUNDS;      // per thread per chunk
+    constexpr bool ACC = EPI == EPI_F32_ACC || EPI == EPI_BF16_ACC;   // int32 accumulator input
+    constexpr int OUT = ACC ? EPI - EPI_F32_ACC : EPI;                 // EPI_F32, EPI_BF16 or EPI_I32
     constexpr bool ROWSUM = (ZP & 1) != 0, COLSUM = (ZP & 2) != 0;
     constexpr bool FLIP_A = (FLIP & 1) != 0, FLIP_B = (FLIP & 2) != 0;
     static_assert(NT == 256 || NT == 512, "four or eight waves");
@@ -257,10 +264,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // The A8W8 epilogue's scales, loaded now so their latency hides behind
     // the main loop: rows wm*WM + 16a + i16 and columns wn*WN + 16b + i16
     // (each lane fetches the column scales its neighbours need).
-    float as_r[EPI == EPI_I32 ? 1 : FM], ws_c[EPI == EPI_I32 ? 1 : FN];
+    float as_r[OUT == EPI_I32 ? 1 : FM], ws_c[OUT == EPI_I32 ? 1 : FN];
     // MatMulInteger: cb for column wn*WN + 16b + i16 (sb - b_zp[n]), likewise.
-    int32_t cb_c[EPI == EPI_I32 ? FN : 1];
-    if constexpr (EPI == EPI_I32) {
+    int32_t cb_c[OUT == EPI_I32 ? FN : 1];
+    if constexpr (OUT == EPI_I32) {
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
             const int n = n0 + wn * WN + b * 16 + i16;
@@ -273,7 +280,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             cb_c[b] = p.sb - zb;
         }
     }
-    if constexpr (EPI != EPI_I32) {
+    if constexpr (OUT != EPI_I32) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
             const int m = m0 + wm * WM + a * 16 + i16;
@@ -332,7 +339,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // store touches fall in distinct banks, and so do the chunks of a row read
     // back.  A tile larger than the stage ring is staged in passes of whole
     // wave rows.
-    constexpr int OUT_BYTES = EPI == EPI_BF16 ? 2 : 4;
+    constexpr int OUT_BYTES = OUT == EPI_BF16 ? 2 : 4;
     constexpr int ROW_BYTES = BN * OUT_BYTES;
     constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
     constexpr int PER_CHUNK = 16 / OUT_BYTES;        // outputs per chunk
@@ -377,7 +384,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             const int nq = n0 + wn * WN + b * 16 + 4 * g;   // first of this lane's four columns
             uint32_t colt[4] = {0u, 0u, 0u, 0u}, cbn[4] = {0u, 0u, 0u, 0u};
             float ws[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI == EPI_I32) {
+            if constexpr (OUT == EPI_I32) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     cbn[r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
@@ -394,7 +401,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 if (m >= p.M || nq >= p.N) continue;
                 const int64_t o = (int64_t)m * p.ldo + nq;
                 const bool full = nq + 4 <= p.N && vec4;
-                if constexpr (EPI == EPI_I32) {
+                if constexpr (OUT == EPI_I32) {
                     const uint32_t ca_m = COLSUM ? row_ca(m) : 0u;
                     uint32_t y[4];
 #pragma unroll
@@ -414,7 +421,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 } else {
                     const float as = as_r[a];
                     v4i v = acc[a][b];
-                    if (p.acc_in != nullptr) {
+                    if constexpr (ACC) {
                         const v4i ai = acc_in4(m, nq);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
@@ -426,7 +433,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                         f[r] = f[r] * as;
                         f[r] = f[r] * ws[r];
                     }
-                    if constexpr (EPI == EPI_F32) {
+                    if constexpr (OUT == EPI_F32) {
                         float* dst = reinterpret_cast<float*>(out) + o;
                         if (full) {
                             __builtin_nontemporal_store(v4f{f[0], f[1], f[2], f[3]}, reinterpret_cast<v4f*>(dst));
@@ -457,12 +464,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     }
 
     // Per-column epilogue terms for fragment column block b.
-    uint32_t colt[FN][EPI == EPI_I32 ? 4 : 1], cbn[FN][EPI == EPI_I32 ? 4 : 1];
-    float ws[FN][EPI == EPI_I32 ? 1 : 4];
+    uint32_t colt[FN][OUT == EPI_I32 ? 4 : 1], cbn[FN][OUT == EPI_I32 ? 4 : 1];
+    float ws[FN][OUT == EPI_I32 ? 1 : 4];
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
         // this lane's four columns are wn*WN + 16b + 4g + r
-        if constexpr (EPI == EPI_I32) {
+        if constexpr (OUT == EPI_I32) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 cbn[b][r] = (uint32_t)__shfl(cb_c[b], 4 * g + r);
@@ -475,6 +482,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         }
     }
 
+    // Accumulator input (A8W8 _acc) with 16-byte rows: the four vectors of
+    // fragment row a are loaded together before any is used, so a wave waits
+    // for one load latency per row instead of one per fragment (8192^3 bf16:
+    // 498 -> 491 us; loading them a row ahead measured the same).  The loads
+    // go through a buffer window over rows [m0, m0 + rows_a) from column n0,
+    // with no per-element checks: the vector of every output in range lies
+    // wholly inside it (ld_acc is a multiple of 4, so no vector crosses the
+    // row pitch), rows past M read 0, and columns past N are never stored.
+    // Other accumulator layouts load per fragment, as the direct path does.
+    const bool acc_win = ACC && acc_vec && (int64_t)BM * p.ld_acc * 4 < ((int64_t)1 << 32) - 64;
+    const __amdgpu_buffer_rsrc_t acc_rsrc =
+        make_rsrc(acc_win ? p.acc_in + (int64_t)m0 * p.ld_acc + n0 : p.acc_in,
+                  acc_win ? (uint32_t)(((int64_t)rows_a * p.ld_acc - n0) * 4) : 0u);
+    v4i ai_buf[ACC ? FN : 1];
+    auto load_acc_row = [&](int a, v4i* dst) {
+        const uint32_t r = (uint32_t)(wm * WM + a * 16 + i16);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const uint32_t c = (uint32_t)(wn * WN + b * 16 + 4 * g);
+            dst[b] = __builtin_bit_cast(v4i, buffer_load16(acc_rsrc, (r * (uint32_t)p.ld_acc + c) * 4u, 0u));
+        }
+    };
+
     __syncthreads();   // every wave is done reading the stage ring
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -486,12 +516,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 const int m = m0 + wm * WM + a * 16 + i16;   // output row (may be >= M)
                 uint8_t* srow = smem + row * ROW_BYTES;
                 uint32_t ca_m = 0u;
-                if constexpr (EPI == EPI_I32 && COLSUM) ca_m = m < p.M ? row_ca(m) : 0u;
+                if constexpr (OUT == EPI_I32 && COLSUM) ca_m = m < p.M ? row_ca(m) : 0u;
+                if constexpr (ACC)
+                    if (acc_win) load_acc_row(a, ai_buf);
                 (void)m;
 #pragma unroll
                 for (int b = 0; b < FN; ++b) {
                     const int col = wn * WN + b * 16 + 4 * g;
-                    if constexpr (EPI == EPI_I32) {
+                    if constexpr (OUT == EPI_I32) {
                         uint32_t y[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
@@ -504,10 +536,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                     } else {
                         const float as = as_r[a];
                         v4i v = acc[a][b];
-                        if (p.acc_in != nullptr && m < p.M && n0 + col < p.N) {
-                            const v4i ai = acc_in4(m, n0 + col);
+                        if constexpr (ACC) {
+                            if (acc_win) {
+                                const v4i ai = ai_buf[b];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
+                                for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
+                            } else if (m < p.M && n0 + col < p.N) {
+                                const v4i ai = acc_in4(m, n0 + col);
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) v[r] = (int)((uint32_t)v[r] + (uint32_t)ai[r]);
+                            }
                         }
                         float f[4];
 #pragma unroll
@@ -516,7 +554,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                             f[r] = f[r] * as;
                             f[r] = f[r] * ws[b][r];
                         }
-                        if constexpr (EPI == EPI_F32) {
+                        if constexpr (OUT == EPI_F32) {
                             const int c = col / 4;
                             *reinterpret_cast<u32x4*>(srow + ((c ^ (row & 15)) << 4)) =
                                 u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
@@ -593,6 +631,12 @@ hipError_t launch_shape(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStr
             case 2: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 2, BK>(a, flip, s);
             default: return by_flip<BM, BN, WM, WN, ST, EPI_I32, 3, BK>(a, flip, s);
         }
+    }
+    if (a.acc_in != nullptr) {
+        if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32_ACC, 0, 0, BK>(a, s)
+                                       : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16_ACC, 0, 0, BK>(a, s);
+        return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32_ACC, 0, 0, BK>(a, s)
+                              : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16_ACC, 0, 0, BK>(a, s);
     }
     if (bkm) return epi == EPI_F32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32, 0, 0, BK>(a, s)
                                    : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16, 0, 0, BK>(a, s);

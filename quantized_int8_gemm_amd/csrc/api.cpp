@@ -64,10 +64,14 @@ int pick_tile(int64_t batch, int64_t M, int64_t N) {
 // fragments (less latency), 1 through LDS in whole rows with plain stores
 // (large grids), 2 through LDS with non-temporal stores (single-round
 // grids).  QGEMM_STAGE=0/1/2 forces the choice.
-int stage_output(int cfg, int64_t K) {
+int stage_output(int cfg, int64_t K, int epi) {
     const int forced = env_int("QGEMM_STAGE", -1);
     if (forced >= 0 && forced <= 2) return forced;
-    if (cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128) return 1;
+    // 256x256 tiles: plain row stores for bf16 output (8192^3: 407.7 us
+    // against 414.0 non-temporal), non-temporal ones for fp32, whose output
+    // is twice the bytes (447.6 -> 427.8 us).
+    if (cfg == qg::TILE_256x256 || cfg == qg::TILE_256x256_W8 || cfg == qg::TILE_256x256_W8_K128)
+        return epi == qg::EPI_F32 ? 2 : 1;
     // Smaller tiles: staged non-temporal rows once the main loop is long
     // enough to absorb the staging barriers (MatMulInteger 8x512x2048x2048:
     // 29.5 -> 27.6 us; A8W8 4096x2048x2048 bf16: 28.9 -> 22.9 us); straight
@@ -117,7 +121,7 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
     if (dma_ok(a, bkm, vec, epi, is_k128(cfg) ? 128 : 64)) {
         *name = dma_names[cfg];
         qg::Int8GemmArgs d = a;
-        d.stage_out = stage_output(cfg, a.K);
+        d.stage_out = stage_output(cfg, a.K, epi);
         switch (cfg) {
             case qg::TILE_256x256: return qg::launch_dma_256x256(d, bkm, epi, zp, s);
             case qg::TILE_256x128_S3: return qg::launch_dma_256x128s3(d, bkm, epi, zp, s);

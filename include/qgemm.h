@@ -23,6 +23,14 @@
  * Following the launch convention of "feat(onnx-to-hip): lower quantized
  * integer conv and matmul" ("What", last paragraph), a HIP error already
  * pending before the call is cleared and does not fail the call.
+ *
+ * Empty outputs: a matrix-multiply call (qgemm_w8a32, qgemm_w8a32_input_grad,
+ * qgemm_a8w8, qgemm_a8w8_acc, matmul_integer, matmul_integer_row_zp) whose
+ * output has no elements (a zero M or N, or a zero batch) checks only that
+ * no size is negative or past the limits, launches nothing and returns
+ * QG_OK; its pointers may then be NULL and qgemm_last_kernel() reads
+ * "none".  An empty reduction (K = 0; N = 0 for the W8A32 input gradient)
+ * under a non-empty output is QG_ERR_INVALID_ARGUMENT.
  */
 #ifndef QGEMM_H
 #define QGEMM_H

@@ -43,6 +43,16 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
     return M >= 1 && N >= 1 && K >= 1 && M < lim && N < lim && K < lim;
 }
 
+// An output with no elements (rows, cols or batch zero, none negative or
+// past the limits): the call has nothing to compute, launches nothing and
+// returns QG_OK; its pointers may be NULL.
+bool empty_output(int64_t rows, int64_t cols, int64_t inner, int64_t batch = 1) {
+    const int64_t lim = (int64_t)1 << 30;
+    if (rows < 0 || cols < 0 || inner < 0 || batch < 0) return false;
+    if (rows >= lim || cols >= lim || inner >= lim || batch >= 65536) return false;
+    return rows == 0 || cols == 0 || batch == 0;
+}
+
 // Tile configuration of the int8 GEMM for an (effective) problem shape:
 // large tiles when there are enough of them to fill the chip, smaller tiles
 // (several workgroups per compute unit) otherwise.  QGEMM_TILE forces one.
@@ -77,6 +87,11 @@ int stage_output(int cfg, int64_t K, int epi) {
     // 29.5 -> 27.6 us; A8W8 4096x2048x2048 bf16: 28.9 -> 22.9 us); straight
     // fragment stores for short K (a K = 576 convolution: 37.8 us against 39.3).
     return K >= 1024 ? 2 : 0;
+}
+
+qg_status empty_call() {
+    g_last_kernel = "none";
+    return QG_OK;
 }
 
 qg_status finish_launch(hipError_t e, const char* name) {
@@ -224,6 +239,7 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
 
 qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
                       int64_t ldw, float scale, int32_t zero_point, float* C, int64_t ldc, void* stream) {
+    if (empty_output(M, N, K)) return empty_call();
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || W == nullptr || C == nullptr) return QG_ERR_INVALID_ARGUMENT;
     if (lda < K || ldw < N || ldc < N) return QG_ERR_INVALID_ARGUMENT;
@@ -246,6 +262,7 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
 qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* dC, int64_t lddc,
                                  const int8_t* W, int64_t ldw, float scale, int32_t zero_point, float* dA,
                                  int64_t ldda, void* stream) {
+    if (empty_output(M, K, N)) return empty_call();      // dA is [M, K]; N is the reduction
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (dC == nullptr || W == nullptr || dA == nullptr) return QG_ERR_INVALID_ARGUMENT;
     if (lddc < N || ldw < N || ldda < K) return QG_ERR_INVALID_ARGUMENT;
@@ -276,6 +293,7 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
                     int64_t act_scale_len, const float* weight_scale, int64_t weight_scale_len, void* out,
                     qg_dtype out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream,
                     const char* op) {
+    if (empty_output(M, N, K)) return empty_call();
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || W == nullptr || act_scale == nullptr || weight_scale == nullptr || out == nullptr)
         return QG_ERR_INVALID_ARGUMENT;
@@ -345,6 +363,7 @@ qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K, const int8_t* A, int64
                          const float* act_scale, int64_t act_scale_len, const float* weight_scale,
                          int64_t weight_scale_len, void* out, qg_dtype out_dtype, int64_t ldo,
                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (empty_output(M, N, K)) return empty_call();
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (acc_in == nullptr || ld_acc < N) return QG_ERR_INVALID_ARGUMENT;
     if ((M - 1) * ld_acc + N >= SPAN_LIMIT / 4) return QG_ERR_UNSUPPORTED;
@@ -363,6 +382,7 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
                               int64_t b_batch_stride, int32_t a_zero_point, const void* a_zp_rows,
                               int64_t a_zp_len, const void* b_zero_point, int64_t b_zero_point_len, int32_t* Y,
                               int64_t ldy, int64_t y_batch_stride, void* stream) {
+    if (empty_output(M, N, K, batch)) return empty_call();
     if (!dims_ok(M, N, K) || batch < 1 || batch >= 65536) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || B == nullptr || Y == nullptr) return QG_ERR_INVALID_ARGUMENT;
     if ((a_dtype != QG_UINT8 && a_dtype != QG_INT8) || (b_dtype != QG_UINT8 && b_dtype != QG_INT8))
@@ -448,6 +468,7 @@ qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K, 
                                 size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
+    if (empty_output(M, N, K, batch)) return empty_call();
     if (a_zero_point == nullptr || (a_zero_point_len != 1 && a_zero_point_len != M))
         return QG_ERR_INVALID_ARGUMENT;
     const int32_t za0 = a_dtype == QG_UINT8 ? 128 : 0;   // in range; the kernel reads the real values

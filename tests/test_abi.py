@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every declared symbol, and
 rejects bad arguments before any HIP call.  No compute call is made here."""
 import ctypes
+import threading
 import os
 import re
 
@@ -41,7 +42,12 @@ def test_status_strings_and_version():
     assert q.status_string(3) == "workspace too small"
     assert q.status_string(4) == "HIP launch error"
     assert "gfx950" in q.version()
-    assert q.last_kernel() == ""
+    # the record is per thread: a thread that has launched nothing reads ""
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(q.last_kernel()))
+    t.start()
+    t.join()
+    assert seen == [""]
 
 
 def test_workspace_bytes():
@@ -85,11 +91,12 @@ def mmi(**kw):
                                 a["Y"], a["ldy"], a["ybs"], a["ws"], a["wsb"], a["stream"])
 
 
-INV, UNS = b.QG_ERR_INVALID_ARGUMENT, b.QG_ERR_UNSUPPORTED
+INV, UNS, OK = b.QG_ERR_INVALID_ARGUMENT, b.QG_ERR_UNSUPPORTED, b.QG_OK
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(M=0), INV), (dict(N=0), INV), (dict(K=0), INV), (dict(M=-3), INV),
+    (dict(M=0), OK), (dict(N=0), OK), (dict(M=0, A=None, C=None), OK), (dict(N=0, K=0), OK),
+    (dict(K=0), INV), (dict(M=-3), INV), (dict(M=0, N=-1), INV),
     (dict(A=None), INV), (dict(W=None), INV), (dict(C=None), INV),
     (dict(lda=3), INV), (dict(ldw=3), INV), (dict(ldc=3), INV),
     (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
@@ -100,7 +107,8 @@ def test_w8a32_rejects(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(M=0), INV), (dict(K=0), INV), (dict(N=0), INV),
+    (dict(M=0), OK), (dict(N=0), OK), (dict(M=0, A=None, out=None, s_a=None), OK),
+    (dict(K=0), INV), (dict(M=-1, N=0), INV),
     (dict(A=None), INV), (dict(W=None), INV), (dict(s_a=None), INV), (dict(s_w=None), INV),
     (dict(out=None), INV),
     (dict(lda=3), INV), (dict(ldw=3), INV), (dict(ldo=3), INV),
@@ -123,7 +131,8 @@ def test_a8w8_workspace_too_small():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(batch=0), INV), (dict(M=0), INV), (dict(K=0), INV), (dict(N=0), INV),
+    (dict(batch=0), OK), (dict(M=0), OK), (dict(N=0), OK), (dict(batch=0, A=None, Y=None), OK),
+    (dict(K=0), INV), (dict(batch=-1), INV), (dict(batch=0, M=-2), INV),
     (dict(A=None), INV), (dict(B=None), INV), (dict(Y=None), INV),
     (dict(adt=b.QG_FP32), INV), (dict(bdt=b.QG_BF16), INV), (dict(adt=b.QG_INT32), INV),
     (dict(lda=3), INV), (dict(ldb=3), INV), (dict(ldy=3), INV),
@@ -210,6 +219,11 @@ def test_a8w8_acc_and_row_zero_point_reject_bad_arguments():
     for acc, ld in ((None, 16), (FAKE, 15)):
         assert lib.qgemm_a8w8_acc(4, 16, 32, FAKE, 32, FAKE, 16, 0, acc, ld, FAKE, 4, FAKE, 16,
                                   FAKE, b.QG_FP32, 16, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT
+    # an empty output launches nothing, NULL pointers included
+    assert lib.qgemm_a8w8_acc(0, 16, 32, None, 32, FAKE, 16, 0, None, 16, None, 0, FAKE, 16,
+                              None, b.QG_FP32, 16, None, 0, None) == b.QG_OK
+    assert lib.matmul_integer_row_zp(1, 0, 16, 32, None, b.QG_UINT8, 32, 0, FAKE, b.QG_INT8, 16, 0,
+                                     None, 0, None, 0, None, 16, 0, None, 0, None) == b.QG_OK
     # the checks of qgemm_a8w8 still apply (act_scale length)
     assert lib.qgemm_a8w8_acc(4, 16, 32, FAKE, 32, FAKE, 16, 0, FAKE, 16, FAKE, 3, FAKE, 16,
                               FAKE, b.QG_FP32, 16, None, 0, None) == b.QG_ERR_INVALID_ARGUMENT
@@ -227,9 +241,13 @@ def test_w8a32_input_grad_rejects_bad_arguments():
         a = dict(ok, **kw)
         return lib.qgemm_w8a32_input_grad(a["M"], a["N"], a["K"], a["dC"], a["lddc"], a["W"], a["ldw"],
                                           a["scale"], a["zp"], a["dA"], a["ldda"], None)
-    for kw in (dict(M=0), dict(dC=None), dict(W=None), dict(dA=None), dict(lddc=15), dict(ldw=15),
+    for kw in (dict(N=0), dict(M=-1), dict(dC=None), dict(W=None), dict(dA=None), dict(lddc=15), dict(ldw=15),
                dict(ldda=7), dict(scale=float("inf")), dict(scale=float("nan"))):
         assert call(**kw) == b.QG_ERR_INVALID_ARGUMENT, kw
+    # an empty dA ([M, K] with M or K zero) is a call with nothing to do
+    for kw in (dict(M=0), dict(K=0), dict(M=0, dC=None, dA=None)):
+        assert call(**kw) == b.QG_OK, kw
+        assert q.last_kernel() == "none"
     with pytest.raises(ValueError):
         q.qgemm_w8a32_input_grad(torch.zeros(4, 16), torch.zeros(8, 15, dtype=torch.int8), 0.5)
     with pytest.raises(TypeError):

@@ -109,7 +109,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     constexpr int KB = BK / 64;                     // 64-k matrix-core blocks per stage
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
     constexpr int ROUND = NT * 16;                  // bytes one load round moves
-    constexpr int WAVES_N = BN / WN;
+    constexpr int WAVES_N = BN / WN, WAVES_M = BM / WM;
     constexpr int FM = WM / 16, FN = WN / 16;
     constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
     constexpr int STAGE = A_BYTES + B_BYTES;
@@ -126,6 +126,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm_s = __builtin_amdgcn_readfirstlane(wm);   // the same, known wave-uniform
+    const int wn_s = __builtin_amdgcn_readfirstlane(wn);
     const int g = lane >> 4, i16 = lane & 15;
 
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -180,11 +182,30 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     for (int a = 0; a < FM; ++a)
 #pragma unroll
         for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    // Row sums of A and column sums of B (after the flips) for the
+    // MatMulInteger correction.  With 64 x 64 wave tiles (SUM_MFMA) the row
+    // sums run on the matrix cores as products with an all-ones operand,
+    // which leaves the sum of row 16a + i in every register of lane (g, i),
+    // and the column sums stay per-lane v_dot4 sums (on the matrix cores they
+    // would need more registers than two workgroups per CU allow).  The
+    // waves that share a row (column) block take turns by k-block, and their
+    // partial sums are added through LDS after the loop (MatMulInteger
+    // 8x512x2048x2048, per-column weight zero points: 26.0 -> 24.1 us; with
+    // per-row activation zero points too: 29.2 -> 26.7 us).  Larger wave tiles
+    // keep every wave's own v_dot4 sums.  All of it wraps mod 2^32 alike.
+    constexpr bool SUM_MFMA = FM * FN <= 16;
+    const u32x4 ones = u32x4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
     int rs[FM], cs[FN];
+    v4i rs4[SUM_MFMA && ROWSUM ? FM : 1];
 #pragma unroll
     for (int a = 0; a < FM; ++a) rs[a] = 0;
 #pragma unroll
     for (int b = 0; b < FN; ++b) cs[b] = 0;
+    if constexpr (SUM_MFMA && ROWSUM) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) rs4[a] = v4i{0, 0, 0, 0};
+    }
+
 
     // Fragment read offsets within a stage (per lane; the block index adds an
     // immediate).
@@ -226,7 +247,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // The next chunk's global->LDS loads (next_kt >= 0) are issued right
     // after this stage's first fragment reads, so those reads start as soon
     // as the stage is ready.
-    auto compute = [&](int stage, int next_kt) {
+    auto compute = [&](int stage, int next_kt, int kt) {
         const uint8_t* S = smem + stage * STAGE;
         u32x4 bfs[KB][FN];
         read_b(S, 0, bfs[0]);
@@ -242,8 +263,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
-                if constexpr (COLSUM)
-                    cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
+                if constexpr (COLSUM) {
+                    if (!SUM_MFMA || (kt * KB + kb) % WAVES_M == wm_s)
+                        cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
+                }
             }
             const int a_rd = a_rd_at(kb);
 #pragma unroll
@@ -253,8 +276,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 else if (kb + 1 < KB) af_next = *reinterpret_cast<const u32x4*>(S + a_rd_at(kb + 1));
                 __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
                 if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
-                if constexpr (ROWSUM)
-                    rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
+                if constexpr (ROWSUM) {
+                    if constexpr (SUM_MFMA) {
+                        // wn_s is wave-uniform in a scalar register, so this is a
+                        // scalar branch around the multiply: a matrix instruction
+                        // under an EXEC mask alone would still run
+                        if ((kt * KB + kb) % WAVES_N == wn_s) rs4[a] = mfma_i8_16x16x64(ones, af, rs4[a]);
+                    }
+                    else rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
+                }
 #pragma unroll
                 for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(bf[b], af, acc[a][b]);
             }
@@ -303,11 +333,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         else if (kt + 1 < nk) wait_vmcnt<LOADS>();
         else wait_vmcnt<0>();
         __syncthreads();
-        compute(kt % STAGES, kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1);
+        compute(kt % STAGES, kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1, kt);
     }
 
-    // Complete row / column sums: add the four lane groups (k segments).
-    if constexpr (ROWSUM) {
+    // Complete row / column sums: add the four lane groups (k segments) of
+    // the v_dot4 sums; with SUM_MFMA, add the partial sums of the waves that
+    // took turns on a row or column block through LDS.
+    if constexpr (ROWSUM && !SUM_MFMA) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
             rs[a] += __shfl_xor(rs[a], 16);
@@ -319,6 +351,39 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         for (int b = 0; b < FN; ++b) {
             cs[b] += __shfl_xor(cs[b], 16);
             cs[b] += __shfl_xor(cs[b], 32);
+        }
+    }
+    if constexpr (SUM_MFMA && (ROWSUM || COLSUM)) {
+        __shared__ int rs_part[ROWSUM ? WAVES_N : 1][BM];
+        __shared__ int cs_part[COLSUM ? WAVES_M : 1][BN];
+        if (g == 0) {
+            if constexpr (ROWSUM) {
+#pragma unroll
+                for (int a = 0; a < FM; ++a) rs_part[wn][wm * WM + 16 * a + i16] = rs4[a][0];
+            }
+            if constexpr (COLSUM) {
+#pragma unroll
+                for (int b = 0; b < FN; ++b) cs_part[wm][wn * WN + 16 * b + i16] = cs[b];
+            }
+        }
+        __syncthreads();
+        if constexpr (ROWSUM) {
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                uint32_t t = 0u;
+#pragma unroll
+                for (int w = 0; w < WAVES_N; ++w) t += (uint32_t)rs_part[w][wm * WM + 16 * a + i16];
+                rs[a] = (int)t;
+            }
+        }
+        if constexpr (COLSUM) {
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                uint32_t t = 0u;
+#pragma unroll
+                for (int w = 0; w < WAVES_M; ++w) t += (uint32_t)cs_part[w][wn * WN + 16 * b + i16];
+                cs[b] = (int)t;
+            }
         }
     }
 
@@ -343,7 +408,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     constexpr int ROW_BYTES = BN * OUT_BYTES;
     constexpr int CPR = ROW_BYTES / 16;              // 16-byte chunks per row
     constexpr int PER_CHUNK = 16 / OUT_BYTES;        // outputs per chunk
-    constexpr int WAVES_M = BM / WM;
     constexpr int PASSES = (BM * ROW_BYTES + STAGES * STAGE - 1) / (STAGES * STAGE);
     static_assert(CPR >= 16, "staging swizzle spans 16 chunks");
     static_assert(WAVES_M % PASSES == 0, "passes of whole wave rows");

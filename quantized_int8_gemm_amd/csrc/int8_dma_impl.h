@@ -183,17 +183,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
         for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
     // Row sums of A and column sums of B (after the flips) for the
-    // MatMulInteger correction.  With 64 x 64 wave tiles (SUM_MFMA) the row
-    // sums run on the matrix cores as products with an all-ones operand,
-    // which leaves the sum of row 16a + i in every register of lane (g, i),
-    // and the column sums stay per-lane v_dot4 sums (on the matrix cores they
-    // would need more registers than two workgroups per CU allow).  The
-    // waves that share a row (column) block take turns by k-block, and their
-    // partial sums are added through LDS after the loop (MatMulInteger
-    // 8x512x2048x2048, per-column weight zero points: 26.0 -> 24.1 us; with
-    // per-row activation zero points too: 29.2 -> 26.7 us).  Larger wave tiles
-    // keep every wave's own v_dot4 sums.  All of it wraps mod 2^32 alike.
-    constexpr bool SUM_MFMA = FM * FN <= 16;
+    // MatMulInteger correction.  The waves that share a row (column) block
+    // take turns by k-block, and their partial sums are added through LDS
+    // after the loop, so each sum is taken once per tile instead of once per
+    // wave.  With 64 x 64 wave tiles, or when only row sums are needed
+    // (SUM_MFMA), the row sums run on the matrix cores, as products with an
+    // all-ones operand, which leaves the sum of row 16a + i in every register
+    // of lane (g, i); elsewhere, and for every column sum, they are per-lane
+    // v_dot4 sums completed by shuffles (on the matrix cores they would need
+    // more registers than the workgroups per CU allow).  MatMulInteger
+    // 8x512x2048x2048 with per-column weight zero points: 26.0 -> 24.1 us;
+    // with per-row activation zero points too: 29.2 -> 26.7 us; 8192^3 with
+    // per-column weight zero points: 551.7 -> 514.6 us.  All of it wraps mod
+    // 2^32 alike.
+    constexpr bool SUM_MFMA = FM * FN <= 16 || (ROWSUM && !COLSUM);
     const u32x4 ones = u32x4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
     int rs[FM], cs[FN];
     v4i rs4[SUM_MFMA && ROWSUM ? FM : 1];
@@ -264,7 +267,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             for (int j = 0; j < FN; ++j) {
                 if constexpr (FLIP_B) bf[j] = xor4(bf[j], 0x80808080u);
                 if constexpr (COLSUM) {
-                    if (!SUM_MFMA || (kt * KB + kb) % WAVES_M == wm_s)
+                    if ((kt * KB + kb) % WAVES_M == wm_s)
                         cs[j] = sum_i8x4(bf[j].w, sum_i8x4(bf[j].z, sum_i8x4(bf[j].y, sum_i8x4(bf[j].x, cs[j]))));
                 }
             }
@@ -277,13 +280,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 __builtin_amdgcn_sched_barrier(0);  // keep the next read ahead of this block's MFMAs
                 if constexpr (FLIP_A) af = xor4(af, 0x80808080u);
                 if constexpr (ROWSUM) {
-                    if constexpr (SUM_MFMA) {
-                        // wn_s is wave-uniform in a scalar register, so this is a
-                        // scalar branch around the multiply: a matrix instruction
-                        // under an EXEC mask alone would still run
-                        if ((kt * KB + kb) % WAVES_N == wn_s) rs4[a] = mfma_i8_16x16x64(ones, af, rs4[a]);
+                    // wn_s is wave-uniform in a scalar register, so this is a
+                    // scalar branch around the sum: a matrix instruction under
+                    // an EXEC mask alone would still run
+                    if ((kt * KB + kb) % WAVES_N == wn_s) {
+                        if constexpr (SUM_MFMA) rs4[a] = mfma_i8_16x16x64(ones, af, rs4[a]);
+                        else rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
                     }
-                    else rs[a] = sum_i8x4(af.w, sum_i8x4(af.z, sum_i8x4(af.y, sum_i8x4(af.x, rs[a]))));
                 }
 #pragma unroll
                 for (int b = 0; b < FN; ++b) acc[a][b] = mfma_i8_16x16x64(bf[b], af, acc[a][b]);
@@ -337,8 +340,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     }
 
     // Complete row / column sums: add the four lane groups (k segments) of
-    // the v_dot4 sums; with SUM_MFMA, add the partial sums of the waves that
-    // took turns on a row or column block through LDS.
+    // the v_dot4 sums, then the partial sums of the waves that took turns on
+    // a row or column block, through LDS.
     if constexpr (ROWSUM && !SUM_MFMA) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
@@ -353,13 +356,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
             cs[b] += __shfl_xor(cs[b], 32);
         }
     }
-    if constexpr (SUM_MFMA && (ROWSUM || COLSUM)) {
+    if constexpr (ROWSUM || COLSUM) {
         __shared__ int rs_part[ROWSUM ? WAVES_N : 1][BM];
         __shared__ int cs_part[COLSUM ? WAVES_M : 1][BN];
         if (g == 0) {
             if constexpr (ROWSUM) {
 #pragma unroll
-                for (int a = 0; a < FM; ++a) rs_part[wn][wm * WM + 16 * a + i16] = rs4[a][0];
+                for (int a = 0; a < FM; ++a) rs_part[wn][wm * WM + 16 * a + i16] = SUM_MFMA ? rs4[a][0] : rs[a];
             }
             if constexpr (COLSUM) {
 #pragma unroll

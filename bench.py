@@ -48,6 +48,7 @@ PEAK_HBM_GBS = 8000.0        # HBM3E
 COPY_BYTES = 256 << 20       # size of the calibration copy
 CEIL_READ_BYTES = 1 << 30    # streaming-read ceiling: 1 GiB, four times the Infinity Cache
 CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops per launch
+CEIL_MFMA_F32_ROUNDS = 200   # fp32 matrix-core ceiling: 200 rounds = 53.7 G flops per launch
 SPREAD_CALLS = 100           # single calls timed one by one for each row's median / p10 / p90
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -497,13 +498,22 @@ def main():
             nops = q.calib_mfma_i8(opnd, CEIL_MFMA_ROUNDS)
             ms = time_calls(lambda s, o=opnd: q.calib_mfma_i8(o, CEIL_MFMA_ROUNDS), [None], steps, warmup, stream)
             mf[name] = nops / (ms * 1e-3) / 1e12
+        # fp32 matrix-core loop (the W8A32 kernels' instruction), operands uniform in [-1, 1)
+        f32ops = to(si.rng(8).uniform(-1.0, 1.0, size=1024).astype(np.float32))
+        nfl = q.calib_mfma_f32(f32ops, CEIL_MFMA_F32_ROUNDS)
+        ms = time_calls(lambda s: q.calib_mfma_f32(f32ops, CEIL_MFMA_F32_ROUNDS), [None], steps, warmup, stream)
+        mf32 = nfl / (ms * 1e-3) / 1e12
         ceilings = {"hbm_read_GBs": hbm, "mfma_i8_random_TOPS": mf["random"], "mfma_i8_ones_TOPS": mf["ones"],
-                    "note": "streaming read of 1 GiB; int8 matrix-core loop on random / all-one operands"}
+                    "mfma_f32_random_TFLOPS": mf32,
+                    "note": "streaming read of 1 GiB; int8 matrix-core loop on random / all-one operands; "
+                            "fp32 matrix-core loop on operands uniform in [-1, 1)"}
         for name, r in rows.items():
             if "GB/s" in r and "frac_hbm_peak" in r and name.startswith("a8w8_decode"):
                 r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm
             if "TOPS" in r:
                 r["frac_mfma_random_ceiling"] = r["TOPS"] / mf["random"]
+            if "TFLOPS" in r:
+                r["frac_mfma_f32_ceiling"] = r["TFLOPS"] / mf32
 
     # ---- CPU baseline: the oracle on a bounded sample of the headline ----
     cpu = None

@@ -347,12 +347,19 @@ const char* qgemm_version(void);
  *   the operand bytes set how much the data paths toggle and hence the clock
  *   the chip holds.  *ops_out (host) receives the int8 operations performed
  *   (2 per multiply-add): QG_CALIB_MFMA_OPS_PER_ROUND * iters.
+ * qgemm_calib_mfma_f32: the same with fp32 matrix-core multiplies
+ *   (v_mfma_f32_16x16x4_f32, the W8A32 kernels' instruction) on 1024 fp32
+ *   operands (4096 bytes) that should lie in [-1, 1];
+ *   *flops_out (host) receives QG_CALIB_MFMA_F32_FLOPS_PER_ROUND * iters.
  */
 #define QG_CALIB_SINK_WORDS 8192
 #define QG_CALIB_MFMA_OPS_PER_ROUND 4294967296LL
+#define QG_CALIB_MFMA_F32_FLOPS_PER_ROUND 268435456LL
 qg_status qgemm_calib_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, void* stream,
                               int64_t* ops_out);
+qg_status qgemm_calib_mfma_f32(const void* operands, int iters, uint32_t* sink, void* stream,
+                               int64_t* flops_out);
 
 #ifdef __cplusplus
 }

@@ -44,6 +44,7 @@ PROTOTYPES = {
     "qgemm_version": ([], ctypes.c_char_p),
     "qgemm_calib_read": ([_p, _sz, _p, _p], _int),
     "qgemm_calib_mfma_i8": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
+    "qgemm_calib_mfma_f32": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
 }
 QG_CALIB_SINK_WORDS = 8192
 
@@ -587,3 +588,18 @@ def calib_mfma_i8(operands, iters, sink=None):
     _check(lib.qgemm_calib_mfma_i8(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(ops)),
            "qgemm_calib_mfma_i8")
     return int(ops.value)
+
+
+def calib_mfma_f32(operands, iters, sink=None):
+    """Run `iters` rounds of fp32 matrix-core multiplies on the 1024 float32
+    operands in `operands` (values in [-1, 1]).  Returns the number of
+    floating-point operations the launch performs."""
+    _need(operands, (torch.float32,), "operands")
+    if operands.numel() != 1024 or not operands.is_contiguous():
+        raise ValueError("operands must be 1024 contiguous float32 values")
+    dev = _on_gpu(operands)
+    sink = _sink(dev, sink)
+    flops = ctypes.c_int64(0)
+    _check(lib.qgemm_calib_mfma_f32(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(flops)),
+           "qgemm_calib_mfma_f32")
+    return int(flops.value)

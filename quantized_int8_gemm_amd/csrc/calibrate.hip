@@ -1,8 +1,8 @@
-// Calibration kernels for the roofline figures: a streaming read and a
-// matrix-core loop.  They implement no part of the quantised matmuls; they
+// Calibration kernels for the roofline figures: a streaming read and two
+// matrix-core loops.  They implement no part of the quantised matmuls; they
 // measure, on the machine at hand, the ceilings those kernels are held to
-// (HBM read bandwidth for the decode kernel, int8 matrix-core rate under
-// data-dependent clocks for the tiled kernel).
+// (HBM read bandwidth for the decode kernel, int8 and fp32 matrix-core rates
+// under data-dependent clocks for the tiled kernels).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -66,6 +66,35 @@ __global__ __launch_bounds__(CAL_NT) void calib_mfma_kernel(const u32x4* __restr
     if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// The same loop with v_mfma_f32_16x16x4_f32, the W8A32 kernels' instruction,
+// on fp32 operands from `ops` (1024 floats).  With operands in [-1, 1] an
+// accumulator grows by at most 4 per round, so it stays finite.
+__global__ __launch_bounds__(CAL_NT) void calib_mfma_f32_kernel(const float* __restrict__ ops, int iters,
+                                                                uint32_t* sink) {
+    const int l = threadIdx.x & 63;
+    float a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = ops[(l + 64 * i) & 1023];
+        b[i] = ops[(l + 64 * i + 7) & 1023];
+    }
+    v4f acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = mfma_f32_16x16x4(a[i & 3], b[i >> 2], acc[i]);
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        s ^= __float_as_uint(acc[i].x) ^ __float_as_uint(acc[i].y) ^ __float_as_uint(acc[i].z) ^
+             __float_as_uint(acc[i].w);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s ^= (uint32_t)__shfl_xor((int)s, o);
+    if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace
 
 hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
@@ -77,6 +106,12 @@ hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipS
 hipError_t launch_calib_mfma(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
     hipLaunchKernelGGL(calib_mfma_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
                        reinterpret_cast<const u32x4*>(ops), iters, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_mfma_f32(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(calib_mfma_f32_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
+                       reinterpret_cast<const float*>(ops), iters, sink);
     return hipGetLastError();
 }
 

@@ -32,6 +32,24 @@ def test_calib_mfma_counts_ops():
     assert n == 3 * 4294967296
 
 
+def test_calib_mfma_f32_counts_flops_and_stays_finite():
+    case("calib_mfma_f32 5 rounds")
+    ops = to_dev(si.rng(8).uniform(-1.0, 1.0, size=1024).astype(np.float32))
+    sink = torch.zeros(q._binding.QG_CALIB_SINK_WORDS, dtype=torch.int32, device=dev())
+    n = q.calib_mfma_f32(ops, 5, sink)
+    torch.cuda.synchronize()
+    assert n == 5 * 268435456
+    # every wave wrote its word; an all-zero operand set gives all-zero sums
+    zeros = torch.zeros(1024, dtype=torch.float32, device=dev())
+    q.calib_mfma_f32(zeros, 5, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+
+
 def test_calib_rejects_bad_operands():
     with pytest.raises(ValueError):
         q.calib_mfma_i8(torch.ones(100, dtype=torch.int8, device=dev()), 3)
+    with pytest.raises(ValueError):
+        q.calib_mfma_f32(torch.ones(100, dtype=torch.float32, device=dev()), 3)
+    with pytest.raises(TypeError):
+        q.calib_mfma_f32(torch.ones(1024, dtype=torch.int32, device=dev()), 3)

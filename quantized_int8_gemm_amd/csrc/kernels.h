@@ -111,7 +111,8 @@ hipError_t launch_conv_stage(const ConvGeom& c, const void* x, uint8_t x_zp, con
 // are at most 9 taps and a tile's weights and input halo fit in LDS.
 struct ConvImplicitPlan {
     int BM;              // output channels per tile (64 or 128)
-    int BW, BH;          // output tile: BH rows x BW columns (128 positions)
+    int BW, BH;          // output tile: BH rows x BW columns (NPOS positions)
+    int NPOS;            // positions per tile: 128 or 256
     int TH, TWt;         // output tiles down / across
     int HP, WP;          // rows / columns of the padded input xp
     int Cgp, taps, cblks;

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build_oracle(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+    cmd = ["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
            SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:

@@ -71,6 +71,40 @@ uint16_t oracle_f32_to_bf16(float f) {
 }
 
 /* ---------------------------------------------------------------------- */
+/* Row updates used by the loops below                                     */
+/* ---------------------------------------------------------------------- */
+
+/* The dequantised weight element of [P1]'s Dequant node, (w - zp) * scale,
+ * in double: w - zp is an integer of at most 9 bits and scale has 24, so the
+ * product is exact.  Its magnitude |w - zp| * |scale| scales the tolerance. */
+static inline double dequant(int8_t w, int32_t zp, double scale) {
+    return ((double)w - (double)zp) * scale;
+}
+
+/* y[i] = y[i] + a * dequant(w[i]) and yb[i] = yb[i] + |a| * |dequant(w[i])|
+ * for i < n: one rounded multiply, then one rounded add per element (no
+ * fused multiply-add: -ffp-contract=off).  Compiled for several instruction
+ * sets and picked at run time; every clone performs the same IEEE
+ * operations on each element. */
+__attribute__((target_clones("avx512f", "avx2", "default")))
+static void row_axpy_dequant(double* y, double* yb, double a, const int8_t* w, int32_t zp, double scale,
+                             int64_t n) {
+    const double abs_a = fabs(a), abs_scale = fabs(scale);
+    for (int64_t i = 0; i < n; ++i) {
+        const double centred = (double)w[i] - (double)zp;
+        y[i] = y[i] + a * (centred * scale);
+        yb[i] = yb[i] + abs_a * (fabs(centred) * abs_scale);
+    }
+}
+
+/* row[i] += a * b[i] for i < n, with a and b[i] 8-bit integers: the product
+ * is exact in int32 and the sum is kept in int64. */
+__attribute__((target_clones("avx512f", "avx2", "default")))
+static void row_axpy_i8(int64_t* row, int32_t a, const int8_t* b, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) row[i] += (int64_t)(a * (int32_t)b[i]);
+}
+
+/* ---------------------------------------------------------------------- */
 /* W8A32 ([P1]): naive dequantise-then-matmul                              */
 /* ---------------------------------------------------------------------- */
 
@@ -84,29 +118,22 @@ void oracle_w8a32(int64_t M, int64_t N, int64_t K,
                   const int8_t* W, int64_t ldw,
                   float scale, int32_t zero_point,
                   double* R, double* bound) {
-    double* Wd = (double*)malloc(sizeof(double) * (size_t)(K * N));
-    double* Wabs = (double*)malloc(sizeof(double) * (size_t)(K * N));
-    for (int64_t k = 0; k < K; ++k)
-        for (int64_t n = 0; n < N; ++n) {
-            double centred = (double)W[k * ldw + n] - (double)zero_point;
-            Wd[k * N + n] = centred * (double)scale;
-            Wabs[k * N + n] = fabs(centred) * fabs((double)scale);
-        }
+    /* Row m of R is built up one k at a time (k ascending), so every output
+     * sees exactly the sequence s = s + A[m,k] * Wd[k,n], k = 0 .. K-1, with
+     * Wd[k,n] = dequant(W[k,n]) formed as the row is read. */
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
+        double* s = (double*)calloc((size_t)N, sizeof(double));
+        double* b = (double*)calloc((size_t)N, sizeof(double));
+        for (int64_t k = 0; k < K; ++k)
+            row_axpy_dequant(s, b, (double)A[m * lda + k], W + k * ldw, zero_point, (double)scale, N);
         for (int64_t n = 0; n < N; ++n) {
-            double s = 0.0, b = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                double a = (double)A[m * lda + k];
-                s += a * Wd[k * N + n];
-                b += fabs(a) * Wabs[k * N + n];
-            }
-            R[m * N + n] = s;
-            if (bound) bound[m * N + n] = b;
+            R[m * N + n] = s[n];
+            if (bound) bound[m * N + n] = b[n];
         }
+        free(s);
+        free(b);
     }
-    free(Wd);
-    free(Wabs);
 }
 
 /* Input gradient of the W8A32 matmul.  [P1]'s intro: the frozen int8
@@ -122,20 +149,27 @@ void oracle_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
                              const int8_t* W, int64_t ldw,
                              float scale, int32_t zero_point,
                              double* R, double* bound) {
+    /* W transposed (a copy of its bytes, WT[n,k] = W[k,n]), so that the
+     * weight values one n contributes to row m of R are contiguous. */
+    int8_t* WT = (int8_t*)malloc((size_t)(K * N));
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) WT[n * K + k] = W[k * ldw + n];
+    /* Row m of R is built up one n at a time (n ascending): every output sees
+     * s = s + dC[m,n] * Wd[k,n], n = 0 .. N-1. */
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
+        double* s = (double*)calloc((size_t)K, sizeof(double));
+        double* b = (double*)calloc((size_t)K, sizeof(double));
+        for (int64_t n = 0; n < N; ++n)
+            row_axpy_dequant(s, b, (double)dC[m * ldd + n], WT + n * K, zero_point, (double)scale, K);
         for (int64_t k = 0; k < K; ++k) {
-            double s = 0.0, b = 0.0;
-            for (int64_t n = 0; n < N; ++n) {
-                double g = (double)dC[m * ldd + n];
-                double centred = (double)W[k * ldw + n] - (double)zero_point;
-                s += g * (centred * (double)scale);
-                b += fabs(g) * (fabs(centred) * fabs((double)scale));
-            }
-            R[m * K + k] = s;
-            if (bound) bound[m * K + k] = b;
+            R[m * K + k] = s[k];
+            if (bound) bound[m * K + k] = b[k];
         }
+        free(s);
+        free(b);
     }
+    free(WT);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -163,10 +197,11 @@ void oracle_a8w8(int64_t M, int64_t N, int64_t K,
         int64_t* row = (int64_t*)calloc((size_t)N, sizeof(int64_t));
         for (int64_t k = 0; k < K; ++k) {
             int64_t a = A[m * lda + k];
-            for (int64_t n = 0; n < N; ++n) {
-                int64_t b = b_trans ? W[n * ldw + k] : W[k * ldw + n];
-                row[n] += a * b;
+            if (!b_trans) {
+                row_axpy_i8(row, (int32_t)a, W + k * ldw, N);
+                continue;
             }
+            for (int64_t n = 0; n < N; ++n) row[n] += a * (int64_t)W[n * ldw + k];
         }
         float as = act_scale[as_len == 1 ? 0 : m];
         for (int64_t n = 0; n < N; ++n) {
@@ -226,10 +261,11 @@ void oracle_a8w8_acc(int64_t M, int64_t N, int64_t K,
         for (int64_t n = 0; n < N; ++n) row[n] = acc_in[m * ld_acc + n];
         for (int64_t k = 0; k < K; ++k) {
             int64_t a = A[m * lda + k];
-            for (int64_t n = 0; n < N; ++n) {
-                int64_t b = b_trans ? W[n * ldw + k] : W[k * ldw + n];
-                row[n] += a * b;
+            if (!b_trans) {
+                row_axpy_i8(row, (int32_t)a, W + k * ldw, N);
+                continue;
             }
+            for (int64_t n = 0; n < N; ++n) row[n] += a * (int64_t)W[n * ldw + k];
         }
         float as = act_scale[as_len == 1 ? 0 : m];
         for (int64_t n = 0; n < N; ++n) {

@@ -18,7 +18,13 @@ on an int8 matrix-core loop with random and with all-one operands (the
 library's calibration kernels); each row also reports its fraction of the
 matching measured ceiling beside the fraction of the spec peak.
 
-Prints one JSON line.  Options: --gpus N (only 1 is supported: this build
+After the GPU rows, the CPU oracle (plain loops, every host thread OpenMP
+offers) runs once on each row's full workload; its time and rate go into the
+row as "cpu_oracle" (the two small parity shapes also on one thread), and its
+time on the whole 8192^3 headline workload is the top-level "cpu_baseline".
+It is a reported baseline, not a target.
+
+Prints one JSON line.  Options: --gpus N (only 1 is supported: the path
 runs on one GPU), --steps K, --warmup W, --no-cpu-baseline, --only NAME.
 
 HBM traffic of the headline kernel comes from hardware counters taken by
@@ -103,6 +109,30 @@ def pmc_summary(args):
     print(json.dumps(out))
 
 
+def trace_summary(args):
+    """Per-kernel statistics of a rocprofv3 kernel-trace csv (every dispatch)
+    and, for the kernel named by --kernel-match, the mean over --window."""
+    import csv
+    durs = {}
+    with open(args.trace_summary, newline="") as f:
+        for r in csv.DictReader(f):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    out = {"kernels": []}
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        ds = [d for _, d in v]
+        out["kernels"].append({"kernel": name, "calls": len(ds), "total_us": sum(ds), "mean_us": sum(ds) / len(ds),
+                               "min_us": min(ds), "max_us": max(ds)})
+    hits = [k for k in durs if args.kernel_match in k]
+    if hits and args.window:
+        seq = [d for _, d in sorted(durs[hits[0]])]
+        a, b = (int(x) if x else None for x in args.window.split(":"))
+        w = seq[a:b]
+        out["window"] = {"kernel": hits[0], "slice": args.window, "calls": len(w), "mean_us": sum(w) / len(w),
+                         "min_us": min(w), "max_us": max(w)}
+    print(json.dumps(out, indent=1))
+
+
 def measured_traffic():
     """HBM bytes per launch from profiles/traffic.json, if the sources match."""
     try:
@@ -128,7 +158,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, conv, small, ceilings); \"vendor\" times torch._int_mm on the headline shape for comparison")
+                    help="time one row only (prefill, decode, mmi, acc, w8a32, dql, conv, small, ceilings)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--pmc-summary", action="store_true",
@@ -144,10 +174,22 @@ def parse():
                     help="--pmc-summary: comma-separated csrc files of the kernel (default: the headline's)")
     ap.add_argument("--traffic-out", default=None,
                     help="--pmc-summary: output path (default profiles/traffic.json)")
+    ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 --kernel-trace csv: per-kernel dispatch statistics, and for "
+                         "--kernel-match the mean over the dispatches in --window (a python slice of that "
+                         "kernel's dispatches in start order)")
+    ap.add_argument("--window", default=None,
+                    help="--trace-summary: slice of the matching kernel's dispatches, e.g. -120:-100")
     return ap.parse_args()
 
 
 SPIN_UP_S = 0.3
+
+
+def progress(msg):
+    """One line on stderr per finished step (stdout carries only the JSON line)."""
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
 
 
 def time_calls(fn, sets, steps, warmup, stream):
@@ -244,10 +286,127 @@ def time_graph(fn, sets, steps, replays, stream, spread=False):
     return ms, _spread([a.elapsed_time(b) * 1e3 / steps for a, b in evs])
 
 
+def cpu_oracle_rows(rows, si):
+    """Time the CPU oracle (test infrastructure, plain loops on every host
+    thread OpenMP offers) once on each measured row's full workload and
+    attach the result to the row as "cpu_oracle"; the two small parity
+    shapes are also timed on one thread.  Returns the top-level
+    cpu_baseline: the whole 8192^3 A8W8 workload."""
+    import oracle
+    threads = oracle.threads()
+    oracle.a8w8(*si.a8w8_inputs(4, 64, 64, seed=1))          # starts the thread pool
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def attach(name, dt, ops=None, nbytes=None, one_thread_s=None):
+        progress(f"oracle {name}: {dt:.2f} s on {threads} threads")
+        r = {"s": dt, "threads": threads}
+        if ops is not None:
+            r["TOPS"] = ops / dt / 1e12
+            r["GOPS"] = ops / dt / 1e9
+        if nbytes is not None:
+            r["GB/s"] = nbytes / dt / 1e9
+        if one_thread_s is not None:
+            r["s_1thread"] = one_thread_s
+            if ops is not None:
+                r["GOPS_1thread"] = ops / one_thread_s / 1e9
+        rows[name]["cpu_oracle"] = r
+
+    def one_thread(fn):
+        oracle.set_threads(1)
+        try:
+            return timed(fn)
+        finally:
+            oracle.set_threads(threads)
+
+    baseline = None
+    if "a8w8_prefill_8192_bf16" in rows:
+        A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
+        dt = timed(lambda: oracle.a8w8(A, W, s_a, s_w))   # acc, fp32 and bf16 outputs in one pass
+        ops = 2.0 * 8192 ** 3
+        attach("a8w8_prefill_8192_bf16", dt, ops=ops)
+        if "a8w8_prefill_8192_fp32" in rows:
+            attach("a8w8_prefill_8192_fp32", dt, ops=ops)
+        baseline = {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+                    "sample": f"the whole 8192x8192x8192 A8W8 workload, one oracle call ({dt:.1f} s)"}
+        del A, W
+    for m in (1, 4, 16):
+        name = f"a8w8_decode_m{m}_8192_bf16"
+        if name in rows:
+            A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
+            dt = timed(lambda: oracle.a8w8(A, W, s_a, s_w))
+            attach(name, dt, ops=2.0 * m * 8192 * 8192,
+                   nbytes=m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192)
+    mmi_ops = 2.0 * 8 * 512 * 2048 * 2048
+    mmi_bytes = 8 * 512 * 2048 + 2048 * 2048 + 2048 + 4 * 8 * 512 * 2048
+    if "matmul_integer_8x512x2048x2048" in rows:
+        A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+        dt = timed(lambda: oracle.matmul_integer(A, B, 128, zb))
+        attach("matmul_integer_8x512x2048x2048", dt, ops=mmi_ops, nbytes=mmi_bytes)
+    if "a8w8_acc_prefill_8192_bf16" in rows:
+        A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
+        acc = si.randint(si.rng(606), (8192, 8192), -2**20, 2**20, np.int32)
+        dt = timed(lambda: oracle.a8w8_acc(acc, A, W, s_a, s_w))
+        attach("a8w8_acc_prefill_8192_bf16", dt, ops=2.0 * 8192 ** 3)
+        del A, W, acc
+    if "a8w8_acc_decode_m16_8192_bf16" in rows:
+        g = si.rng(606)
+        si.randint(g, (8192, 8192), -2**20, 2**20, np.int32)   # the prefill row's draw comes first
+        acc_m = si.randint(g, (16, 8192), -2**20, 2**20, np.int32)
+        A, W, s_a, s_w = si.a8w8_inputs(16, 8192, 8192, seed=420)
+        dt = timed(lambda: oracle.a8w8_acc(acc_m, A, W, s_a, s_w))
+        attach("a8w8_acc_decode_m16_8192_bf16", dt, ops=2.0 * 16 * 8192 * 8192,
+               nbytes=16 * 8192 + 8192 * 8192 + 4 * 16 + 4 * 8192 + 4 * 16 * 8192 + 2 * 16 * 8192)
+    if "matmul_integer_row_zp_8x512x2048x2048" in rows:
+        A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
+        za = si.randint(si.rng(9), (512,), 0, 255, np.uint8)
+        dt = timed(lambda: oracle.matmul_integer(A, B, za, zb))
+        attach("matmul_integer_row_zp_8x512x2048x2048", dt, ops=mmi_ops)
+    if "w8a32_4096" in rows:
+        A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
+        dt = timed(lambda: oracle.w8a32(A, W, 0.01, -5))
+        attach("w8a32_4096", dt, ops=2.0 * 4096 ** 3)
+        if "w8a32_input_grad_4096" in rows:
+            dC, _ = si.w8a32_inputs(4096, 4096, 4096, seed=507)
+            dt = timed(lambda: oracle.w8a32_input_grad(dC, W, 0.01, -5))
+            attach("w8a32_input_grad_4096", dt, ops=2.0 * 4096 ** 3)
+    if "dynamic_quantize_linear_8x512x2048" in rows:
+        x = si.dql_inputs((8, 512, 2048), seed=303)
+        n = x.size
+        dt = timed(lambda: oracle.dynamic_quantize_linear(x))
+        attach("dynamic_quantize_linear_8x512x2048", dt, nbytes=4 * n + n + 4 + 1)
+        if "dql_then_matmul_integer_8x512x2048x2048" in rows:
+            _, B, zb = si.matmul_integer_inputs(1, 1, 2048, 2048, seed=303)
+
+            def chain():
+                y, _, zp = oracle.dynamic_quantize_linear(x)
+                oracle.matmul_integer(y, B, int(zp), zb)
+            attach("dql_then_matmul_integer_8x512x2048x2048", timed(chain), ops=mmi_ops)
+    if "conv_integer_64x64x32x32_k3x3_m128" in rows:
+        x, w, zw = si.conv_integer_inputs(64, 64, 32, 32, 128, 3, 3, seed=808)
+        dt = timed(lambda: oracle.conv_integer(x, w, 128, zw, pads=(1, 1, 1, 1)))
+        attach("conv_integer_64x64x32x32_k3x3_m128", dt, ops=2.0 * 64 * 128 * 32 * 32 * 64 * 9)
+    if "a8w8_256x1024x1024_fp32" in rows:
+        A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
+        fn = lambda: oracle.a8w8(A, W, s_a, s_w)
+        attach("a8w8_256x1024x1024_fp32", timed(fn), ops=2.0 * 256 * 1024 * 1024, one_thread_s=one_thread(fn))
+    if "w8a32_64x128x64" in rows:
+        A, W = si.w8a32_inputs(64, 64, 128, seed=101)
+        fn = lambda: oracle.w8a32(A, W, 0.02, 3)
+        attach("w8a32_64x128x64", timed(fn), ops=2.0 * 64 * 64 * 128, one_thread_s=one_thread(fn))
+    return baseline
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.copy_calibration:
         # an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
@@ -303,6 +462,7 @@ def main():
         del outf
     del A, W
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- decode: M in {1, 4, 16}, K = N = 8192, bf16 out ---------------
     if want("decode"):
         # 9 rotating weight copies (576 MiB, beyond the 256 MB Infinity
@@ -324,6 +484,7 @@ def main():
                                                    "us_eager": ms_eager * 1e3, "per_call": spread}
             del sets, base_w, ws
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- MatMulInteger 8 x 512 x 2048 x 2048, shared B -------------------
     if want("mmi"):
         A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
@@ -341,6 +502,7 @@ def main():
             "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- A8W8 with an int32 accumulator input; per-row MatMulInteger zp --
     if want("acc"):
         M = N = K = 8192
@@ -385,6 +547,7 @@ def main():
             "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- W8A32 4096^3 -----------------------------------------------------
     if want("w8a32"):
         A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
@@ -407,6 +570,7 @@ def main():
                                          "per_call": per_call_spread(callg, [None], SPREAD_CALLS, stream)}
         del A, W, tA, tW, outc, dC, tdC
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- DynamicQuantizeLinear on [8, 512, 2048] fp32, and its chain ----
     if want("dql"):
         shape = (8, 512, 2048)
@@ -435,6 +599,7 @@ def main():
                                                           "per_call": per_call_spread(chain, sets, SPREAD_CALLS, stream)}
         del sets, x
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- ConvInteger: a 3x3 tokenizer-sized layer -------------------------
     if want("conv"):
         N_, C_, H_, W_, M_ = 64, 64, 32, 32, 128
@@ -453,6 +618,7 @@ def main():
                                                      "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
         del sets, ws
 
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- the small parity shapes (launch-latency bound) ------------------
     if want("small"):
         A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
@@ -472,17 +638,7 @@ def main():
         rows["w8a32_64x128x64"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "timing": "hip_graph",
                                    "us_eager": ms_eager * 1e3, "per_call": spread}
 
-    # ---- context only (opt-in): the vendor int8 GEMM on the same shape ---
-    # torch._int_mm (hipBLASLt underneath) writes the raw int32 product, no
-    # scales and twice the output bytes of bf16; timed for both weight
-    # layouts, as a measured point of comparison, never as a result.
-    if args.only == "vendor":
-        A8, W8 = tA.contiguous(), tW.contiguous()
-        for name, Bm in (("kn", W8), ("nk_transposed", W8.t().contiguous().t())):
-            ms = time_calls(lambda s, b=Bm: torch._int_mm(A8, b), [None], steps, warmup, stream)
-            rows[f"vendor_int_mm_8192_i32_{name}"] = {"kernel": "torch._int_mm", "us": ms * 1e3,
-                                                     "TOPS": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
-
+    progress(f"GPU rows so far: {sorted(rows)}")
     # ---- measured ceilings: streaming read, int8 matrix-core loop -------
     ceilings = None
     if args.only is None or args.only == "ceilings":
@@ -515,23 +671,11 @@ def main():
             if "TFLOPS" in r:
                 r["frac_mfma_f32_ceiling"] = r["TFLOPS"] / mf32
 
-    # ---- CPU baseline: the oracle on a bounded sample of the headline ----
+    progress(f"GPU rows so far: {sorted(rows)}")
+    # ---- CPU baseline: the oracle beside every row ------------------------
     cpu = None
-    if not args.no_cpu_baseline and want("prefill"):
-        import oracle
-        A, W, s_a, s_w = si.a8w8_inputs(8192, 8192, 8192, seed=505)
-        rows_probe = 32
-        oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)    # starts the thread pool
-        t0 = time.perf_counter()
-        oracle.a8w8(A[:rows_probe], W, s_a[:rows_probe], s_w)
-        dt = time.perf_counter() - t0
-        nrows = int(max(rows_probe, min(8192, rows_probe * 15.0 / max(dt, 1e-3))))
-        t0 = time.perf_counter()
-        oracle.a8w8(A[:nrows], W, s_a[:nrows], s_w)
-        dt = time.perf_counter() - t0
-        cpu = {"value": 2.0 * nrows * N * K / dt / 1e12, "unit": "TOPS", "cores": oracle.threads(),
-               "kind": "oracle",
-               "sample": f"first {nrows} rows of the 8192x8192x8192 A8W8 workload ({dt:.1f} s)"}
+    if not args.no_cpu_baseline:
+        cpu = cpu_oracle_rows(rows, si)
 
     line = {
         "metric": "int8 GEMM TOPS and skinny-M GB/s; % of MI355X int8 MFMA / HBM peak",

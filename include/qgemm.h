@@ -128,13 +128,15 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
  *   weight_scale: fp32, weight_scale_len == N (per column) or 1.
  *   out: out_dtype QG_FP32 or QG_BF16, [M,N], row stride ldo >= N.
  *   workspace: NULL, or device memory of at least
- *     qgemm_workspace_bytes(QG_OP_A8W8, 1, M, N, K) bytes, zero-filled
- *     before its first use.  Decode shapes split K across workgroups: the
- *     front of the workspace holds one ticket counter per 256 columns, the
- *     rest the exact int32 partial sums.  Every call returns the tickets to
- *     zero when it completes, so the same workspace serves the next call on
- *     the same stream without clearing; calls that overlap in time must not
- *     share one.  With NULL, decode shapes use a single-pass kernel.
+ *     qgemm_workspace_bytes(QG_OP_A8W8, 1, M, N, K) bytes, 256-byte aligned
+ *     (else QG_ERR_INVALID_ARGUMENT), zero-filled before its first use.
+ *     Decode shapes split K across workgroups: the first 1024 bytes hold
+ *     one ticket counter per 256 columns (a header of fixed size, whatever
+ *     the shape), the rest the exact int32 partial sums.  Every call returns
+ *     the tickets to zero when it completes, so the same workspace serves
+ *     the next call on the same stream, of this or any other shape, without
+ *     clearing; calls that overlap in time must not share one.  With NULL,
+ *     decode shapes use a single-pass kernel.
  * Decode shapes (M <= 16, b_trans == 0) run a bandwidth-bound kernel that
  * streams W once; all other shapes run the tiled matrix-core kernel.
  * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
@@ -184,7 +186,9 @@ qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K,
  *
  * summed exactly and stored as a wrapping (two's-complement) int32, the
  * result the page's int64 accumulation gives for any K.  Bit-exact.
- *   A: a_dtype QG_UINT8 or QG_INT8, `batch` matrices [M,K], row stride
+ *   A: a_dtype QG_UINT8 or QG_INT8 (QG_FP32, QG_BF16, QG_INT32: a form the
+ *      page does not lower, QG_ERR_UNSUPPORTED; likewise for b_dtype),
+ *      `batch` matrices [M,K], row stride
  *      lda >= K, batch stride a_batch_stride (0: one A used by every batch,
  *      the page's size-1 batch expanded without a copy).
  *   B: b_dtype QG_UINT8 or QG_INT8, [K,N], row stride ldb >= N, batch stride
@@ -325,7 +329,11 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
 const char* qgemm_status_string(qg_status s);
 
 /* Name of the kernel the calling thread's last successful call launched
- * (static text; "" before the first launch). */
+ * (static text; "" before the first launch).  It lets a test or benchmark
+ * assert which kernel actually ran: "feat(PULPOpen): matmul that dequantises
+ * an int8 weight in-kernel" retracts its own measurement in a later comment
+ * because the intended int8 kernel was never emitted, and the fp32 kernel
+ * that ran instead read the int8 weight as float. */
 const char* qgemm_last_kernel(void);
 
 /* Library version string. */

@@ -98,6 +98,14 @@ def threads():
     return int(_load().oracle_threads())
 
 
+def set_threads(n):
+    """Run the oracle's loops on n OpenMP threads from now on."""
+    lib = _load()
+    lib.oracle_set_threads.argtypes = [_int]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads(int(n))
+
+
 def _ptr(a):
     return ctypes.c_void_p(a.ctypes.data) if a is not None else None
 

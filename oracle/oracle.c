@@ -43,6 +43,9 @@
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* Sets that number (the benchmark times some calls on one thread). */
+void oracle_set_threads(int n) { if (n >= 1) omp_set_num_threads(n); }
+
 /* ---------------------------------------------------------------------- */
 /* Helpers that are part of the definition                                 */
 /* ---------------------------------------------------------------------- */

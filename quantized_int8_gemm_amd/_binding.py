@@ -273,11 +273,11 @@ def _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, worksp
         _need(out, (out_dtype,), "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
+    od = QG_FP32 if out_dtype == torch.float32 else QG_BF16
     if workspace is None:
         ws = _workspace(dev, workspace_bytes(QG_OP_A8W8, 1, M, N, K))
     else:
         ws = workspace
-    od = QG_FP32 if out_dtype == torch.float32 else QG_BF16
     wsz = 0 if ws is None else ws.numel()
     if acc_in is None:
         st = lib.qgemm_a8w8(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),

@@ -246,8 +246,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
         return;
     }
 
-    // Split-K: workspace = [tickets: one int per column tile, padded to 256 B]
+    // Split-K: workspace = [tickets: one int per column tile, a fixed
+    //                       SKINNY_TICKET_BYTES header whatever the shape]
     //                      [partials: per column tile, S x 16 x TN int32]
+    // The header's size does not depend on N, so a workspace left by a call
+    // of one shape (tickets back at zero, partials arbitrary) serves a call
+    // of any other shape: its tickets never overlap old partials.
     // Partials and tickets cross workgroups (and XCDs, whose L2s are not
     // coherent with each other), so every access to them is device-coherent:
     // stores and loads with the device-scope cache policy (they bypass the
@@ -255,10 +259,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     // outstanding memory operations orders each thread's partial stores
     // before the barrier, and the barrier orders them before thread 0's
     // ticket; no cache-wide writeback or invalidate is needed.
-    const int tiles_n = gridDim.x;
     int* tickets = reinterpret_cast<int*>(p.workspace);
-    char* part = reinterpret_cast<char*>(p.workspace) + ((tiles_n * 4 + 255) / 256) * 256 +
-                 (size_t)tn * S * 16 * TN * 4;
+    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tn * S * 16 * TN * 4;
     // Partial tile of split s: rows m < M of [16][TN] int32, as 16-byte
     // vectors through a buffer resource with device-coherent cache policy.
     const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * 16 * TN * 4));
@@ -321,7 +323,7 @@ size_t skinny_workspace_bytes(int M, int N, int splits) {
     (void)M;
     if (splits <= 1) return 0;
     const size_t tiles_n = (size_t)(N + TN - 1) / TN;
-    return ((tiles_n * 4 + 255) / 256) * 256 + tiles_n * (size_t)splits * 16 * TN * 4;
+    return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * 16 * TN * 4;
 }
 
 // Steps (64 k-rows) per split: a multiple of 2*WAVES, chosen so that about
@@ -349,6 +351,7 @@ hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStrea
     dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
     *name = "a8w8_skinny";
     if (a.split_steps % (2 * WAVES) != 0 || (int64_t)a.split_steps * grid.y * KS < a.K) return hipErrorInvalidValue;
+    if (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)) return hipErrorInvalidValue;
     if (vec) {
         if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32>), grid, dim3(NT), 0, s, a);
         else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16>), grid, dim3(NT), 0, s, a);

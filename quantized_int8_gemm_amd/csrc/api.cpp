@@ -225,6 +225,12 @@ static void a8w8_skinny_plan(int64_t M, int64_t N, int64_t K, int* splits, int* 
     }
     *steps = per;
     *splits = qg::skinny_splits_for((int)N, (int)K, per);
+    // More column tiles than the fixed ticket header holds: one split over
+    // all of K (the natural plan already gives one split from 256 tiles on).
+    if (*splits > 1 && (N + 255) / 256 > qg::SKINNY_MAX_TICKETS) {
+        *steps = (int)(((K + 63) / 64 + 7) / 8) * 8;
+        *splits = 1;
+    }
 }
 
 static int a8w8_skinny_splits(int64_t M, int64_t N, int64_t K) {
@@ -312,6 +318,10 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
     if (act_scale_len != 1 && act_scale_len != M) return QG_ERR_INVALID_ARGUMENT;
     if (weight_scale_len != 1 && weight_scale_len != N) return QG_ERR_INVALID_ARGUMENT;
     if (out_dtype != QG_FP32 && out_dtype != QG_BF16) return QG_ERR_INVALID_ARGUMENT;
+    // The decode kernel's tickets take atomics and its partials 16-byte
+    // coherent stores: a workspace must start on a 256-byte boundary.
+    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return QG_ERR_INVALID_ARGUMENT;
     if (256 * lda + K + 256 >= SPAN_LIMIT || (b_trans ? 256 * ldw + K + 256 : (K + 256) * ldw) >= SPAN_LIMIT)
         return QG_ERR_UNSUPPORTED;
 
@@ -395,8 +405,12 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
     if (empty_output(M, N, K, batch)) return empty_call();
     if (!dims_ok(M, N, K) || batch < 1 || batch >= 65536) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || B == nullptr || Y == nullptr) return QG_ERR_INVALID_ARGUMENT;
-    if ((a_dtype != QG_UINT8 && a_dtype != QG_INT8) || (b_dtype != QG_UINT8 && b_dtype != QG_INT8))
+    // A dtype outside the enumeration is invalid; fp32 / bf16 / int32
+    // operands are well-formed forms the page does not lower (unsupported).
+    if (a_dtype < QG_FP32 || a_dtype > QG_UINT8 || b_dtype < QG_FP32 || b_dtype > QG_UINT8)
         return QG_ERR_INVALID_ARGUMENT;
+    if ((a_dtype != QG_UINT8 && a_dtype != QG_INT8) || (b_dtype != QG_UINT8 && b_dtype != QG_INT8))
+        return QG_ERR_UNSUPPORTED;
     if (lda < K || ldb < N || ldy < N) return QG_ERR_INVALID_ARGUMENT;
     if (a_batch_stride < 0 || b_batch_stride < 0 || y_batch_stride < 0) return QG_ERR_INVALID_ARGUMENT;
     if (batch > 1) {

@@ -61,12 +61,20 @@ __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
 
 // 16 bytes per lane from buffer offset `voff` into LDS at lds_base + 16*lane.
 // Written as inline assembly so that the compiler does not wait for these
-// loads before every LDS read; the kernel waits for them explicitly.
+// loads before every LDS read; the kernel waits for them explicitly.  The
+// block sets M0 (the LDS destination) itself, so M0 is declared clobbered:
+// the compiler then treats it as redefined here.  M0 is a reserved register,
+// which the compiler never saves around an asm statement (hence the
+// suppressed warning); in these kernels nothing else uses M0 at all -- every
+// M0 reference in their compiled code is this block's own s_mov_b32.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(m0) : "memory");
+                 :: "v"(voff), "s"(rsrc), "s"(m0) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt with vmcnt = n and the other counters unconstrained (gfx9 encoding).
 template <int N>
@@ -554,14 +562,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     // for one load latency per row instead of one per fragment (8192^3 bf16:
     // 498 -> 491 us; loading them a row ahead measured the same).  The loads
     // go through a buffer window over rows [m0, m0 + rows_a) from column n0,
-    // with no per-element checks: the vector of every output in range lies
-    // wholly inside it (ld_acc is a multiple of 4, so no vector crosses the
-    // row pitch), rows past M read 0, and columns past N are never stored.
-    // Other accumulator layouts load per fragment, as the direct path does.
-    const bool acc_win = ACC && acc_vec && (int64_t)BM * p.ld_acc * 4 < ((int64_t)1 << 32) - 64;
+    // with no per-element checks: the window ends at the tile's last element
+    // the caller must provide (row m0 + rows_a - 1, column N - 1), so rows
+    // past M and columns past N of the last row read 0 and nothing outside
+    // the (M-1)*ld_acc + N elements of acc_in is touched.  With N a multiple
+    // of 4 (and ld_acc too) no vector straddles that end; columns past N are
+    // never stored.  Other accumulator layouts load per fragment, as the
+    // direct path does.
+    const bool acc_win = ACC && acc_vec && p.N % 4 == 0 && (int64_t)BM * p.ld_acc * 4 < ((int64_t)1 << 32) - 64;
     const __amdgpu_buffer_rsrc_t acc_rsrc =
         make_rsrc(acc_win ? p.acc_in + (int64_t)m0 * p.ld_acc + n0 : p.acc_in,
-                  acc_win ? (uint32_t)(((int64_t)rows_a * p.ld_acc - n0) * 4) : 0u);
+                  acc_win ? (uint32_t)(((int64_t)(rows_a - 1) * p.ld_acc + (p.N - n0)) * 4) : 0u);
     v4i ai_buf[ACC ? FN : 1];
     auto load_acc_row = [&](int a, v4i* dst) {
         const uint32_t r = (uint32_t)(wm * WM + a * 16 + i16);

@@ -76,6 +76,11 @@ hipError_t launch_dma_256x128w8k128(const Int8GemmArgs& a, bool bkm, int epi, in
 hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
+// The split-K workspace starts with a ticket header of fixed size (one int
+// per 256-column tile, at most SKINNY_MAX_TICKETS tiles); shapes with more
+// column tiles run one split (they fill the chip without splitting K).
+constexpr int SKINNY_MAX_TICKETS = 256;
+constexpr size_t SKINNY_TICKET_BYTES = SKINNY_MAX_TICKETS * 4;
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,
                               const char** name);
 size_t skinny_workspace_bytes(int M, int N, int splits);

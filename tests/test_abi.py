@@ -115,6 +115,7 @@ def test_w8a32_rejects(kw, code):
     (dict(n_a=2), INV), (dict(n_a=0), INV), (dict(n_w=3), INV), (dict(n_w=5), INV),
     (dict(dt=b.QG_INT32), INV), (dict(dt=b.QG_INT8), INV), (dict(dt=7), INV),
     (dict(bt=2), INV), (dict(bt=1, ldw=3), INV),
+    (dict(ws=ctypes.c_void_p(4096 + 16), wsb=1 << 20), INV), (dict(ws=ctypes.c_void_p(4096 + 128), wsb=1 << 20), INV),
     (dict(K=100000, ldw=40000, N=40000, lda=100000, ldo=40000, n_a=1, n_w=1), UNS),
 ])
 def test_a8w8_rejects(kw, code):
@@ -134,7 +135,8 @@ def test_a8w8_workspace_too_small():
     (dict(batch=0), OK), (dict(M=0), OK), (dict(N=0), OK), (dict(batch=0, A=None, Y=None), OK),
     (dict(K=0), INV), (dict(batch=-1), INV), (dict(batch=0, M=-2), INV),
     (dict(A=None), INV), (dict(B=None), INV), (dict(Y=None), INV),
-    (dict(adt=b.QG_FP32), INV), (dict(bdt=b.QG_BF16), INV), (dict(adt=b.QG_INT32), INV),
+    (dict(adt=b.QG_FP32), UNS), (dict(bdt=b.QG_BF16), UNS), (dict(adt=b.QG_INT32), UNS),
+    (dict(adt=7), INV), (dict(bdt=-1), INV),
     (dict(lda=3), INV), (dict(ldb=3), INV), (dict(ldy=3), INV),
     (dict(za=256), INV), (dict(za=-1), INV), (dict(adt=b.QG_INT8, za=128), INV),
     (dict(adt=b.QG_INT8, za=-129), INV),

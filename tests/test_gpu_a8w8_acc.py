@@ -103,12 +103,12 @@ def test_a8w8_acc_chains_k_chunks_on_the_gpu(M):
     np.testing.assert_array_equal(whole.cpu().numpy(), oracle.a8w8(A, W, s_a, s_w)["f32"])
 
 
-def test_a8w8_acc_prefill_8192_sampled_rows():
+def test_a8w8_acc_prefill_8192_every_output():
     """The accumulator-input workload at full size (8192^3, the benchmark's
     inputs: accumulators uniform over [-2^20, 2^20]) in the launch
-    configuration the benchmark times, bf16 and fp32 out; the oracle checks
-    22 whole rows (the first, the last and 20 drawn)."""
-    case("a8w8_acc 8192x8192x8192 sampled rows")
+    configuration the benchmark times, bf16 and fp32 out: all 67.1M outputs
+    against the oracle."""
+    case("a8w8_acc 8192x8192x8192 every output")
     M = N = K = 8192
     A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=505)
     acc = si.randint(si.rng(606), (M, N), -2**20, 2**20, np.int32)
@@ -117,7 +117,7 @@ def test_a8w8_acc_prefill_8192_sampled_rows():
     assert q.last_kernel() == "int8_dma_256x256w8k128", q.last_kernel()
     f = q.qgemm_a8w8_acc(tacc, tA, tW, ta, tw).cpu().numpy()
     assert q.last_kernel() == "int8_dma_256x256w8k128", q.last_kernel()
-    rows = np.concatenate([[0, M - 1], si.rng(2).integers(1, M - 1, 20)])
-    ref = oracle.a8w8_acc(acc[rows], A[rows], W, s_a[rows], s_w)
-    np.testing.assert_array_equal(h[rows], ref["bf16"])
-    np.testing.assert_array_equal(f[rows], ref["f32"])
+    del tacc, tA, tW
+    ref = oracle.a8w8_acc(acc, A, W, s_a, s_w)
+    np.testing.assert_array_equal(h, ref["bf16"])
+    np.testing.assert_array_equal(f, ref["f32"])

@@ -30,11 +30,11 @@ def check(x, x_dev=None):
 
 def test_dql_golden_cases_from_page_and_hand_worked():
     gv = load("dynamic_quantize_linear.txt")
-    case("dql golden all_zero / ties_pos / ties_neg")
+    case("dql golden all_zero / ties_pos / ties_neg / unit_range / sym_range")
     y, sc, zp = check(np.zeros(8, np.float32))
     assert sc.item() == float(gv["all_zero_scale"]) and int(zp.item()) == int(gv["all_zero_zero_point"])
     assert y.cpu().tolist() == [int(t) for t in gv["all_zero_output"].split()]
-    for name in ("ties_pos", "ties_neg"):
+    for name in ("ties_pos", "ties_neg", "unit_range", "sym_range"):
         x = np.array([float(t) for t in gv[name + "_input"].split()], dtype=np.float32)
         y, sc, zp = check(x)
         assert sc.item() == float(gv[name + "_scale"]) and int(zp.item()) == int(gv[name + "_zero_point"])

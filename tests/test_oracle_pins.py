@@ -515,7 +515,7 @@ def test_dynamic_quantize_all_zero_case_from_page():
     assert y.tolist() == [int(t) for t in gv["all_zero_output"].split()]
 
 
-@pytest.mark.parametrize("case_name", ["ties_pos", "ties_neg"])
+@pytest.mark.parametrize("case_name", ["ties_pos", "ties_neg", "unit_range", "sym_range"])
 def test_dynamic_quantize_hand_worked_ties(case_name):
     gv = load("dynamic_quantize_linear.txt")
     y, sc, zp = oracle.dynamic_quantize_linear(_floats(gv[case_name + "_input"]))

@@ -3,7 +3,8 @@
  *
  * C ABI.  Every tensor pointer is a DEVICE pointer owned by the caller; the
  * library allocates no memory and keeps no state apart from a per-thread
- * record of the last kernel it launched.  Matrices are row-major with an
+ * record of the last kernel it launched and the static scratch array per
+ * GPU of qgemm_a8w8_noalloc.  Matrices are row-major with an
  * explicit leading dimension (elements between consecutive rows).  Every
  * compute call is asynchronous on `stream` (a hipStream_t; NULL is the null
  * stream): it validates its arguments on the host, clears any pending HIP
@@ -149,6 +150,32 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
                      void* out, qg_dtype out_dtype, int64_t ldo,
                      void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * qgemm_a8w8 for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, results (bit for bit) and errors as qgemm_a8w8,
+ * without the workspace arguments; it allocates nothing.  Decode shapes that
+ * split K use a scratch array the library holds in static device memory,
+ * QG_A8W8_NOALLOC_SCRATCH_BYTES on each GPU it runs on (held until the
+ * process ends); a shape whose split-K workspace
+ * (qgemm_workspace_bytes(QG_OP_A8W8, ...)) would exceed that returns
+ * QG_ERR_WORKSPACE with nothing launched (no shape of the default plan
+ * does).  The first call on a device looks up that device's copy and
+ * clears its ticket words with a small kernel on `stream`; every call
+ * leaves them at zero again.  All calls on one GPU share its array, which
+ * keeps the last call's partial sums: calls that overlap in time on one GPU
+ * (several streams or host threads) race, so the caller serialises them.
+ * `stream` must belong to the calling thread's current device.
+ */
+#define QG_A8W8_NOALLOC_SCRATCH_BYTES ((size_t)1024 + ((size_t)8 << 20))
+qg_status qgemm_a8w8_noalloc(int64_t M, int64_t N, int64_t K,
+                             const int8_t* A, int64_t lda,
+                             const int8_t* W, int64_t ldw, int b_trans,
+                             const float* act_scale, int64_t act_scale_len,
+                             const float* weight_scale, int64_t weight_scale_len,
+                             void* out, qg_dtype out_dtype, int64_t ldo,
+                             void* stream);
 
 /*
  * A8W8 with an int32 accumulator input ("Feature/a8w8 matmul dequant

@@ -12,6 +12,8 @@ this package is its thin Python binding, with the same call names:
   fp32 or bf16 output.
 * ``qgemm_a8w8_acc(acc_in, A, W, act_scale, weight_scale, ...)``: the same
   with an int32 accumulator input added before the cast.
+* ``qgemm_a8w8_noalloc(A, W, act_scale, weight_scale, ...)``: qgemm_a8w8
+  for callers that cannot allocate (its decode scratch is a static array).
 * ``matmul_integer(A, B, a_zero_point=0, b_zero_point=None)``: ONNX
   MatMulInteger, int32 output, shared weight never copied; per-row
   activation zero points go to ``matmul_integer_row_zp``.
@@ -41,6 +43,7 @@ from ._binding import (  # noqa: F401
     matmul_integer_row_zp,
     qgemm_a8w8,
     qgemm_a8w8_acc,
+    qgemm_a8w8_noalloc,
     qgemm_w8a32,
     qgemm_w8a32_input_grad,
     status_string,

@@ -30,6 +30,8 @@ PROTOTYPES = {
                     _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
                         _i32, _p, _i64, _p, _i64, _i64, _p, _sz, _p], _int),
+    "qgemm_a8w8_noalloc": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64,
+                            _p, _int, _i64, _p], _int),
     "qgemm_a8w8_acc": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64, _p, _i64,
                         _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer_row_zp": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
@@ -240,6 +242,14 @@ def qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=F
     return _a8w8(None, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace)
 
 
+def qgemm_a8w8_noalloc(A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=False, out=None):
+    """qgemm_a8w8 through the C entry point that allocates nothing: the
+    decode split-K scratch is the library's static device array (shared by
+    every call on the GPU; overlapping calls race).  Pass `out` to keep the
+    call itself free of allocations."""
+    return _a8w8(None, A, W, act_scale, weight_scale, out_dtype, b_trans, out, None, noalloc=True)
+
+
 def qgemm_a8w8_acc(acc_in, A, W, act_scale, weight_scale, out_dtype=torch.float32, b_trans=False, out=None,
                    workspace=None):
     """out = cast(((float)(acc_in + A @ W)_int32 * act_scale[m]) * weight_scale[n]).
@@ -251,7 +261,7 @@ def qgemm_a8w8_acc(acc_in, A, W, act_scale, weight_scale, out_dtype=torch.float3
     return _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace)
 
 
-def _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace):
+def _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, workspace, noalloc=False):
     _need(A, (torch.int8,), "A")
     _need(W, (torch.int8,), "W")
     if out_dtype not in (torch.float32, torch.bfloat16):
@@ -274,6 +284,12 @@ def _a8w8(acc_in, A, W, act_scale, weight_scale, out_dtype, b_trans, out, worksp
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
     od = QG_FP32 if out_dtype == torch.float32 else QG_BF16
+    if noalloc:
+        st = lib.qgemm_a8w8_noalloc(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"), int(bool(b_trans)),
+                                    _ptr(s_a), n_a, _ptr(s_w), n_w, _ptr(out), od, _rows(out, "out"),
+                                    _stream(dev))
+        _check(st, "qgemm_a8w8_noalloc")
+        return out
     if workspace is None:
         ws = _workspace(dev, workspace_bytes(QG_OP_A8W8, 1, M, N, K))
     else:

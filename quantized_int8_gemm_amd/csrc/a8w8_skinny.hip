@@ -24,6 +24,8 @@
 //    gives the same bits), runs the epilogue once and resets the ticket.
 // Rows past M and bytes past K read as zero through the buffer range checks
 // (or meet zero weight rows), so they add nothing.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -317,7 +319,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Ticket words to zero: one thread per ticket of the fixed header.
+__global__ __launch_bounds__(SKINNY_MAX_TICKETS) void clear_tickets_kernel(int* tickets) {
+    tickets[threadIdx.x] = 0;
+}
+
+// Split-K scratch held by the library for callers that cannot allocate (the
+// workspace-free A8W8 entry point): one copy per GPU, kept until the process
+// ends.  Host code never passes `scratch` itself to a kernel (its host-side
+// name is no device address); it uses the address hipGetSymbolAddress gives
+// for the current device.
+__device__ __attribute__((aligned(256))) uint8_t scratch[SKINNY_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[MAX_DEVICES];
+
 }  // namespace
+
+hipError_t skinny_scratch(hipStream_t s, void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        // Set-up, once per device with that device current: look up this
+        // device's copy of the array, then clear its tickets on the caller's
+        // stream ahead of the first kernel that uses them (a fill kernel, not
+        // a memset, so that a captured first call records a kernel node).
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(clear_tickets_kernel, dim3(1), dim3(SKINNY_MAX_TICKETS), 0, s, reinterpret_cast<int*>(p));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t skinny_workspace_bytes(int M, int N, int splits) {
     (void)M;

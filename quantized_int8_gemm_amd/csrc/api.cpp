@@ -304,11 +304,13 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* d
 namespace {
 
 // A8W8 with an optional int32 accumulator input (acc_in == NULL: none).
+// lib_scratch: the split-K workspace is the library's static scratch of the
+// current device (workspace / workspace_bytes are ignored).
 qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
                     int64_t ldw, int b_trans, const int32_t* acc_in, int64_t ld_acc, const float* act_scale,
                     int64_t act_scale_len, const float* weight_scale, int64_t weight_scale_len, void* out,
                     qg_dtype out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream,
-                    const char* op) {
+                    const char* op, bool lib_scratch = false) {
     if (empty_output(M, N, K)) return empty_call();
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || W == nullptr || act_scale == nullptr || weight_scale == nullptr || out == nullptr)
@@ -320,7 +322,7 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
     if (out_dtype != QG_FP32 && out_dtype != QG_BF16) return QG_ERR_INVALID_ARGUMENT;
     // The decode kernel's tickets take atomics and its partials 16-byte
     // coherent stores: a workspace must start on a 256-byte boundary.
-    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    if (!lib_scratch && workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return QG_ERR_INVALID_ARGUMENT;
     if (256 * lda + K + 256 >= SPAN_LIMIT || (b_trans ? 256 * ldw + K + 256 : (K + 256) * ldw) >= SPAN_LIMIT)
         return QG_ERR_UNSUPPORTED;
@@ -344,17 +346,22 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
         int splits, per;
         a8w8_skinny_plan(M, N, K, &splits, &per);
         const size_t need = qg::skinny_workspace_bytes((int)M, (int)N, splits);
-        if (need > 0 && workspace == nullptr) {
+        if (lib_scratch) {
+            workspace = nullptr;
+            if (need > qg::SKINNY_SCRATCH_BYTES) return QG_ERR_WORKSPACE;
+        } else if (need > 0 && workspace == nullptr) {
             // no workspace: one split covering all of K
             per = (int)(((K + 63) / 64 + 7) / 8) * 8;
             splits = 1;
         } else if (need > workspace_bytes) {
             return QG_ERR_WORKSPACE;
         }
+        (void)hipGetLastError();
+        if (lib_scratch && need > 0 && qg::skinny_scratch((hipStream_t)stream, &workspace) != hipSuccess)
+            return QG_ERR_HIP;
         a.workspace = workspace;
         a.splits = splits;
         a.split_steps = per;
-        (void)hipGetLastError();
         e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name);
         log_dispatch(op, name, 1, M, N, K, splits);
     } else {
@@ -376,6 +383,16 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t l
                      int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
     return a8w8_impl(M, N, K, A, lda, W, ldw, b_trans, nullptr, 0, act_scale, act_scale_len, weight_scale,
                      weight_scale_len, out, out_dtype, ldo, workspace, workspace_bytes, stream, "a8w8");
+}
+
+static_assert(QG_A8W8_NOALLOC_SCRATCH_BYTES == qg::SKINNY_SCRATCH_BYTES, "scratch size in the header");
+
+qg_status qgemm_a8w8_noalloc(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                             int64_t ldw, int b_trans, const float* act_scale, int64_t act_scale_len,
+                             const float* weight_scale, int64_t weight_scale_len, void* out, qg_dtype out_dtype,
+                             int64_t ldo, void* stream) {
+    return a8w8_impl(M, N, K, A, lda, W, ldw, b_trans, nullptr, 0, act_scale, act_scale_len, weight_scale,
+                     weight_scale_len, out, out_dtype, ldo, nullptr, 0, stream, "a8w8_noalloc", true);
 }
 
 qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,

@@ -81,6 +81,13 @@ hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, in
 // column tiles run one split (they fill the chip without splitting K).
 constexpr int SKINNY_MAX_TICKETS = 256;
 constexpr size_t SKINNY_TICKET_BYTES = SKINNY_MAX_TICKETS * 4;
+// Library-held split-K scratch for the workspace-free entry point: the ticket
+// header plus 8 MiB of partial sums (every shape the default plan splits
+// needs at most 510 column-tile slabs of 16 KiB: 8,356,864 bytes in all).
+constexpr size_t SKINNY_SCRATCH_BYTES = SKINNY_TICKET_BYTES + ((size_t)8 << 20);
+// The current device's copy of that scratch; the first call on a device
+// looks it up and clears its tickets with a kernel on `s`.
+hipError_t skinny_scratch(hipStream_t s, void** ptr);
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,
                               const char** name);
 size_t skinny_workspace_bytes(int M, int N, int splits);

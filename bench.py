@@ -650,9 +650,11 @@ def main():
         rnd = to(si.randint(g, (4096,), -128, 127, np.int8))
         ones = torch.ones(4096, dtype=torch.int8, device=dev)
         mf = {}
-        for name, opnd in (("random", rnd), ("ones", ones)):
-            nops = q.calib_mfma_i8(opnd, CEIL_MFMA_ROUNDS)
-            ms = time_calls(lambda s, o=opnd: q.calib_mfma_i8(o, CEIL_MFMA_ROUNDS), [None], steps, warmup, stream)
+        for name, opnd, shape in (("random", rnd, "16x16x64"), ("ones", ones, "16x16x64"),
+                                  ("random_32x32x32", rnd, "32x32x32")):
+            nops = q.calib_mfma_i8(opnd, CEIL_MFMA_ROUNDS, shape=shape)
+            ms = time_calls(lambda s, o=opnd, sh=shape: q.calib_mfma_i8(o, CEIL_MFMA_ROUNDS, shape=sh), [None],
+                            steps, warmup, stream)
             mf[name] = nops / (ms * 1e-3) / 1e12
         # fp32 matrix-core loop (the W8A32 kernels' instruction), operands uniform in [-1, 1)
         f32ops = to(si.rng(8).uniform(-1.0, 1.0, size=1024).astype(np.float32))
@@ -660,9 +662,11 @@ def main():
         ms = time_calls(lambda s: q.calib_mfma_f32(f32ops, CEIL_MFMA_F32_ROUNDS), [None], steps, warmup, stream)
         mf32 = nfl / (ms * 1e-3) / 1e12
         ceilings = {"hbm_read_GBs": hbm, "mfma_i8_random_TOPS": mf["random"], "mfma_i8_ones_TOPS": mf["ones"],
+                    "mfma_i8_32x32x32_random_TOPS": mf["random_32x32x32"],
                     "mfma_f32_random_TFLOPS": mf32,
-                    "note": "streaming read of 1 GiB; int8 matrix-core loop on random / all-one operands; "
-                            "fp32 matrix-core loop on operands uniform in [-1, 1)"}
+                    "note": "streaming read of 1 GiB; int8 matrix-core loop (v_mfma_i32_16x16x64_i8, the GEMM "
+                            "kernels' instruction) on random / all-one operands, and with v_mfma_i32_32x32x32_i8 "
+                            "on the random operands; fp32 matrix-core loop on operands uniform in [-1, 1)"}
         for name, r in rows.items():
             if "GB/s" in r and "frac_hbm_peak" in r and name.startswith("a8w8_decode"):
                 r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm

@@ -382,6 +382,9 @@ const char* qgemm_version(void);
  *   the operand bytes set how much the data paths toggle and hence the clock
  *   the chip holds.  *ops_out (host) receives the int8 operations performed
  *   (2 per multiply-add): QG_CALIB_MFMA_OPS_PER_ROUND * iters.
+ * qgemm_calib_mfma_i8_32x32: the same int8 work (same operands, same
+ *   *ops_out) with v_mfma_i32_32x32x32_i8, which does twice the operations
+ *   of the 16x16x64 form per operand byte read.
  * qgemm_calib_mfma_f32: the same with fp32 matrix-core multiplies
  *   (v_mfma_f32_16x16x4_f32, the W8A32 kernels' instruction) on 1024 fp32
  *   operands (4096 bytes) that should lie in [-1, 1];
@@ -393,6 +396,8 @@ const char* qgemm_version(void);
 qg_status qgemm_calib_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, void* stream,
                               int64_t* ops_out);
+qg_status qgemm_calib_mfma_i8_32x32(const void* operands, int iters, uint32_t* sink, void* stream,
+                                    int64_t* ops_out);
 qg_status qgemm_calib_mfma_f32(const void* operands, int iters, uint32_t* sink, void* stream,
                                int64_t* flops_out);
 

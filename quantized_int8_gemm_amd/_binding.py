@@ -46,6 +46,7 @@ PROTOTYPES = {
     "qgemm_version": ([], ctypes.c_char_p),
     "qgemm_calib_read": ([_p, _sz, _p, _p], _int),
     "qgemm_calib_mfma_i8": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
+    "qgemm_calib_mfma_i8_32x32": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
     "qgemm_calib_mfma_f32": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
 }
 QG_CALIB_SINK_WORDS = 8192
@@ -591,18 +592,22 @@ def calib_read(buf, sink=None):
     return sink
 
 
-def calib_mfma_i8(operands, iters, sink=None):
+def calib_mfma_i8(operands, iters, sink=None, shape="16x16x64"):
     """Run `iters` rounds of int8 matrix-core multiplies on the 4096 operand
-    bytes in `operands` (an int8 or uint8 GPU tensor).  Returns the number of
-    int8 operations the launch performs."""
+    bytes in `operands` (an int8 or uint8 GPU tensor), as
+    v_mfma_i32_16x16x64_i8 (shape "16x16x64") or v_mfma_i32_32x32x32_i8
+    ("32x32x32").  Returns the number of int8 operations the launch
+    performs (the same for both shapes)."""
     _need(operands, (torch.int8, torch.uint8), "operands")
     if operands.numel() != 4096 or not operands.is_contiguous():
         raise ValueError("operands must be 4096 contiguous bytes")
+    if shape not in ("16x16x64", "32x32x32"):
+        raise ValueError("shape must be 16x16x64 or 32x32x32")
     dev = _on_gpu(operands)
     sink = _sink(dev, sink)
     ops = ctypes.c_int64(0)
-    _check(lib.qgemm_calib_mfma_i8(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(ops)),
-           "qgemm_calib_mfma_i8")
+    fn = lib.qgemm_calib_mfma_i8 if shape == "16x16x64" else lib.qgemm_calib_mfma_i8_32x32
+    _check(fn(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(ops)), fn.__name__)
     return int(ops.value)
 
 

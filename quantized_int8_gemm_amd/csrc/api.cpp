@@ -189,6 +189,16 @@ qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, v
     return finish_launch(qg::launch_calib_mfma(operands, iters, sink, (hipStream_t)stream), "calib_mfma_i8");
 }
 
+qg_status qgemm_calib_mfma_i8_32x32(const void* operands, int iters, uint32_t* sink, void* stream,
+                                    int64_t* ops_out) {
+    if (operands == nullptr || sink == nullptr || iters < 1 || iters > (1 << 20) || ops_out == nullptr)
+        return QG_ERR_INVALID_ARGUMENT;
+    *ops_out = QG_CALIB_MFMA_OPS_PER_ROUND * (int64_t)iters;
+    (void)hipGetLastError();
+    return finish_launch(qg::launch_calib_mfma32(operands, iters, sink, (hipStream_t)stream),
+                         "calib_mfma_i8_32x32");
+}
+
 qg_status qgemm_calib_mfma_f32(const void* operands, int iters, uint32_t* sink, void* stream,
                                int64_t* flops_out) {
     static_assert((int64_t)qg::CALIB_MFMA_BLOCKS * 4 * 16 * 2048 == QG_CALIB_MFMA_F32_FLOPS_PER_ROUND, "flops");

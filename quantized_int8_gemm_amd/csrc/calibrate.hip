@@ -66,6 +66,43 @@ __global__ __launch_bounds__(CAL_NT) void calib_mfma_kernel(const u32x4* __restr
     if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// The same int8 work with v_mfma_i32_32x32x32_i8: eight independent 32x32
+// accumulators per wave (16 registers each), each multiply twice the
+// operations of a 16x16x64 one for the same operand bytes, so a round does
+// the same 16 * 32768 operations per wave with half the operand reads.
+typedef int v16i __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(CAL_NT) void calib_mfma32_kernel(const u32x4* __restrict__ ops, int iters, uint32_t* sink) {
+    const int l = threadIdx.x & 63;
+    v4i a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 t = ops[(l + 64 * i) & 255];
+        a[i] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const u32x4 t = ops[(l + 64 * i + 7) & 255];
+        b[i] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+    }
+    v16i acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s ^= (uint32_t)acc[i][j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s ^= (uint32_t)__shfl_xor((int)s, o);
+    if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
+}
+
 // The same loop with v_mfma_f32_16x16x4_f32, the W8A32 kernels' instruction,
 // on fp32 operands from `ops` (1024 floats).  With operands in [-1, 1] an
 // accumulator grows by at most 4 per round, so it stays finite.
@@ -105,6 +142,12 @@ hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipS
 
 hipError_t launch_calib_mfma(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
     hipLaunchKernelGGL(calib_mfma_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
+                       reinterpret_cast<const u32x4*>(ops), iters, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_mfma32(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(calib_mfma32_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
                        reinterpret_cast<const u32x4*>(ops), iters, sink);
     return hipGetLastError();
 }

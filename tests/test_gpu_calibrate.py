@@ -32,6 +32,20 @@ def test_calib_mfma_counts_ops():
     assert n == 3 * 4294967296
 
 
+def test_calib_mfma_32x32x32_counts_the_same_ops():
+    case("calib_mfma_i8 32x32x32 3 rounds")
+    ops = torch.ones(4096, dtype=torch.int8, device=dev())
+    sink = torch.full((q._binding.QG_CALIB_SINK_WORDS,), 7, dtype=torch.int32, device=dev())
+    n = q.calib_mfma_i8(ops, 3, sink, shape="32x32x32")
+    torch.cuda.synchronize()
+    assert n == q.calib_mfma_i8(ops, 3) == 3 * 4294967296
+    assert q.last_kernel() == "calib_mfma_i8"
+    # every wave wrote its word: an even number of equal all-ones sums XOR to 0
+    assert int(sink.abs().sum()) == 0
+    with pytest.raises(ValueError):
+        q.calib_mfma_i8(ops, 3, shape="16x16x32")
+
+
 def test_calib_mfma_f32_counts_flops_and_stays_finite():
     case("calib_mfma_f32 5 rounds")
     ops = to_dev(si.rng(8).uniform(-1.0, 1.0, size=1024).astype(np.float32))

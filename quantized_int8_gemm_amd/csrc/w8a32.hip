@@ -16,8 +16,12 @@
 //    current one is multiplied.  W stays int8 in LDS, transposed 4x4 bytes
 //    at a time so each k-quad of a column is one word.
 //  * Each lane widens its W bytes to fp32 in registers and feeds
-//    v_mfma_f32_16x16x4_f32; the same A values it feeds are summed into the
-//    row sum S2 (per lane, then across the four lane groups).
+//    v_mfma_f32_16x16x4_f32.  When zp != 0, the same A values are summed
+//    into the row sum S2 (per lane, then across the four lane groups); with
+//    zp == 0 the kernel is compiled without it.  Both waves of a row block
+//    take the same sum (12 adds per 64 matrix-core multiplies): splitting it
+//    between them by k-group needs 192 VGPRs instead of 160, which leaves
+//    two workgroups per CU instead of three.
 //  * Epilogue: C = scale * (S1 - zp * S2), or scale * S1 when zp == 0.
 //
 // The same kernel with WT = true is the gradient with respect to the
@@ -46,7 +50,7 @@ constexpr int GROUP_M = 8;
 
 // WT == false: W is [K,N] (contraction over rows); true: W is [N,K] rows of
 // the contraction (p.N outputs, p.K contraction bytes per row).
-template <bool VEC, bool WT>
+template <bool VEC, bool WT, bool ZP>
 __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_STAGE + W_STAGE)];
 
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 af[i] = *reinterpret_cast<const v4f*>(As + (i * 16 + l16) * AROW + kg * 16 + 4 * g);
-                rsum[i] += (af[i].x + af[i].y) + (af[i].z + af[i].w);
+                if constexpr (ZP) rsum[i] += (af[i].x + af[i].y) + (af[i].z + af[i].w);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -204,10 +208,12 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
     compute((nk - 1) & 1);
 
     // Row sums over the whole K: add the four lane groups.
+    if constexpr (ZP) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        rsum[i] += __shfl_xor(rsum[i], 16);
-        rsum[i] += __shfl_xor(rsum[i], 32);
+        for (int i = 0; i < 4; ++i) {
+            rsum[i] += __shfl_xor(rsum[i], 16);
+            rsum[i] += __shfl_xor(rsum[i], 32);
+        }
     }
     const float zp = (float)p.zp;
 #pragma unroll
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
                 const int n = n0 + wn * WNT + j * 16 + l16;
                 if (m < p.M && n < p.N) {
                     float v = acc[i][j][r];
-                    if (p.zp != 0) v = v - zp * s2;
+                    if constexpr (ZP) v = v - zp * s2;
                     p.C[(int64_t)m * p.ldc + n] = p.scale * v;
                 }
             }
@@ -234,14 +240,19 @@ __global__ __launch_bounds__(NT) void w8a32_kernel(W8A32Args p) {
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s, const char** name) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const bool vec = vec_a && vec_w;
-    if (wt) {
-        *name = "w8a32_input_grad_128x128";
-        if (vec) hipLaunchKernelGGL((w8a32_kernel<true, true>), dim3(tiles), dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((w8a32_kernel<false, true>), dim3(tiles), dim3(NT), 0, s, a);
-    } else {
-        *name = "w8a32_tiled_128x128";
-        if (vec) hipLaunchKernelGGL((w8a32_kernel<true, false>), dim3(tiles), dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((w8a32_kernel<false, false>), dim3(tiles), dim3(NT), 0, s, a);
+    const bool zp = a.zp != 0;
+    *name = wt ? "w8a32_input_grad_128x128" : "w8a32_tiled_128x128";
+    const dim3 grid(tiles), block(NT);
+    const int v = (vec ? 4 : 0) | (wt ? 2 : 0) | (zp ? 1 : 0);
+    switch (v) {
+        case 7: hipLaunchKernelGGL((w8a32_kernel<true, true, true>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((w8a32_kernel<true, true, false>), grid, block, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((w8a32_kernel<true, false, true>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((w8a32_kernel<true, false, false>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((w8a32_kernel<false, true, true>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((w8a32_kernel<false, true, false>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((w8a32_kernel<false, false, true>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((w8a32_kernel<false, false, false>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }

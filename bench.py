@@ -50,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # dense int8 matrix-core peak, tera-ops/s
 PEAK_FP32_TFLOPS = 157.3     # dense fp32 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0        # HBM3E
 COPY_BYTES = 256 << 20       # size of the calibration copy
 CEIL_READ_BYTES = 1 << 30    # streaming-read ceiling: 1 GiB, four times the Infinity Cache
@@ -553,21 +554,40 @@ def main():
         A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
         tA, tW = to(A), to(W)
         outc = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
-        callw = lambda s: q.qgemm_w8a32(tA, tW, 0.01, -5, out=outc)
-        ms = time_calls(callw, [None], steps, warmup, stream)
         fl = 2.0 * 4096 ** 3
-        rows["w8a32_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "TFLOPS": fl / (ms * 1e-3) / 1e12,
-                              "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
-                              "per_call": per_call_spread(callw, [None], SPREAD_CALLS, stream)}
+
+        def w8a32_row(call):
+            ms = time_calls(call, [None], steps, warmup, stream)
+            kern = q.last_kernel()
+            r = {"kernel": kern, "us": ms * 1e3, "TFLOPS": fl / (ms * 1e-3) / 1e12,
+                 "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                 "per_call": per_call_spread(call, [None], SPREAD_CALLS, stream)}
+            if "bf16x3" in kern:
+                # the exact three-way split: three bf16 products per algorithmic one
+                r["matrix_cores"] = "bf16, fp32 operand split exactly in three"
+                r["frac_bf16_peak_3x"] = 3 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+            else:
+                r["matrix_cores"] = "fp32"
+            return r
+
+        callw = lambda s: q.qgemm_w8a32(tA, tW, 0.01, -5, out=outc)
+        rows["w8a32_4096"] = w8a32_row(callw)
         # its input gradient: dA = dC @ ((W - zp) * scale)^T, same weight
         dC, _ = si.w8a32_inputs(4096, 4096, 4096, seed=507)
         tdC = to(dC)
         callg = lambda s: q.qgemm_w8a32_input_grad(tdC, tW, 0.01, -5, out=outc)
-        ms = time_calls(callg, [None], steps, warmup, stream)
-        rows["w8a32_input_grad_4096"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
-                                         "TFLOPS": fl / (ms * 1e-3) / 1e12,
-                                         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
-                                         "per_call": per_call_spread(callg, [None], SPREAD_CALLS, stream)}
+        rows["w8a32_input_grad_4096"] = w8a32_row(callg)
+        # the same two calls on the fp32 matrix cores, for comparison
+        prev = os.environ.get("QGEMM_W8A32")
+        os.environ["QGEMM_W8A32"] = "fp32"
+        try:
+            rows["w8a32_4096_fp32_cores"] = w8a32_row(callw)
+            rows["w8a32_input_grad_4096_fp32_cores"] = w8a32_row(callg)
+        finally:
+            if prev is None:
+                os.environ.pop("QGEMM_W8A32", None)
+            else:
+                os.environ["QGEMM_W8A32"] = prev
         del A, W, tA, tW, outc, dC, tdC
 
     progress(f"GPU rows so far: {sorted(rows)}")
@@ -672,7 +692,7 @@ def main():
                 r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm
             if "TOPS" in r:
                 r["frac_mfma_random_ceiling"] = r["TOPS"] / mf["random"]
-            if "TFLOPS" in r:
+            if "TFLOPS" in r and r.get("matrix_cores", "fp32") == "fp32":
                 r["frac_mfma_f32_ceiling"] = r["TFLOPS"] / mf32
 
     progress(f"GPU rows so far: {sorted(rows)}")

@@ -70,15 +70,25 @@ enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2, QG_OP_DYNAMIC_
  *   C[m,n] = sum_k A[m,k] * (W[k,n] - zero_point) * scale
  *          = scale * (sum_k A[m,k] W[k,n] - zero_point * sum_k A[m,k])
  *
- * evaluated in the second (factorised) form with fp32 arithmetic; the
- * dequantised weight is never formed.  zero_point == 0 drops the correction.
+ * evaluated in the second (factorised) form; the dequantised weight is
+ * never formed.  zero_point == 0 drops the correction.  The sum
+ * sum_k A[m,k] W[k,n] runs on the bf16 matrix cores with every A value split
+ * exactly into three bfloat16 parts (hi + lo + lo2 == A[m,k]; the int8 weight
+ * is exact in bfloat16), so each product is exact and only the fp32
+ * accumulation rounds; sum_k A[m,k] and the epilogue are fp32.  The
+ * environment variable QGEMM_W8A32=fp32 (read per call) selects the fp32
+ * matrix cores instead.
  *   A: fp32 [M,K], row stride lda >= K.    W: int8 [K,N], row stride ldw >= N.
  *   C: fp32 [M,N], row stride ldc >= N.    scale: finite fp32 (host value).
  *   zero_point: any int32 (host value).
  * Requires M, N, K >= 1.  QG_ERR_UNSUPPORTED if K*ldw or M*lda*4 reaches 2^31
  * bytes.  The result is not bit-defined (summation order is the kernel's);
  * it is within 1e-5 * |scale| * sum_k |A[m,k]| * |W[k,n] - zp| of the exact
- * value for the library's workloads.
+ * value for the library's workloads.  The split is exact for A values of
+ * magnitude 2^-103 and above (and zero); smaller ones may lose their bits
+ * below 2^-126.  An infinite A value gives NaN in its output row on the
+ * split path, and on both paths when zero_point != 0 (the factorised form
+ * subtracts zero_point * inf from an infinite sum).
  */
 qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
                       const float* A, int64_t lda,
@@ -97,8 +107,10 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
  *   dA[m,k] = sum_n dC[m,n] * (W[k,n] - zero_point) * scale
  *           = scale * (sum_n dC[m,n] W[k,n] - zero_point * sum_n dC[m,n])
  *
- * evaluated in the factorised form in fp32, the dequantised weight never
- * formed, W read in its forward layout.
+ * evaluated in the factorised form as qgemm_w8a32 evaluates it (the exact
+ * three-way bf16 split of dC on the bf16 matrix cores, or the fp32 matrix
+ * cores with QGEMM_W8A32=fp32), the dequantised weight never formed, W read
+ * in its forward layout.
  *   dC: fp32 [M,N], row stride lddc >= N.   W: int8 [K,N], row stride ldw >= N.
  *   dA: fp32 [M,K], row stride ldda >= K.    scale, zero_point: as qgemm_w8a32.
  * Requires M, N, K >= 1.  QG_ERR_UNSUPPORTED if K*ldw or M*lddc*4 reaches

@@ -4,7 +4,9 @@ The C-ABI library ``libqgemm.so`` (HIP kernels for gfx950) does the work;
 this package is its thin Python binding, with the same call names:
 
 * ``qgemm_w8a32(A, W, scale, zero_point=0)``: fp32 x int8 weight with a
-  per-tensor scale and zero point, dequantisation folded into the epilogue.
+  per-tensor scale and zero point, dequantisation folded into the epilogue
+  (bf16 matrix cores on an exact three-way split of A; QGEMM_W8A32=fp32
+  selects the fp32 matrix cores).
 * ``qgemm_w8a32_input_grad(dC, W, scale, zero_point=0)``: its gradient
   with respect to the activations, W in its forward layout.
 * ``qgemm_a8w8(A, W, act_scale, weight_scale, out_dtype=torch.float32)``:

@@ -30,6 +30,7 @@ SOURCES = [
     "int8_dma_256x256w8k128.hip",
     "a8w8_skinny.hip",
     "w8a32.hip",
+    "w8a32_split.hip",
     "dynamic_quantize.hip",
     "conv_integer.hip",
     "conv_implicit.hip",

@@ -29,6 +29,10 @@ int env_int(const char* name, int dflt) {
     return v != nullptr && *v ? std::atoi(v) : dflt;
 }
 
+// W8A32 runs on the bf16 matrix cores with the exact three-way split of its
+// fp32 operand unless QGEMM_W8A32=fp32 asks for the fp32 matrix cores.
+bool w8a32_split() { return !env_is("QGEMM_W8A32", "fp32"); }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 void log_dispatch(const char* op, const char* kernel, int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -280,7 +284,8 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     const bool vec_w = (reinterpret_cast<uintptr_t>(W) & 3u) == 0 && ldw % 4 == 0 && N % 4 == 0;
     const char* name = "";
     (void)hipGetLastError();
-    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, false, (hipStream_t)stream, &name);
+    const hipError_t e = w8a32_split() ? qg::launch_w8a32_split(a, vec_a, vec_w, false, (hipStream_t)stream, &name)
+                                         : qg::launch_w8a32(a, vec_a, vec_w, false, (hipStream_t)stream, &name);
     log_dispatch("w8a32", name, 1, M, N, K, 1);
     return finish_launch(e, name);
 }
@@ -304,7 +309,8 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* d
     const bool vec_w = aligned16(W) && ldw % 16 == 0;
     const char* name = "";
     (void)hipGetLastError();
-    const hipError_t e = qg::launch_w8a32(a, vec_a, vec_w, true, (hipStream_t)stream, &name);
+    const hipError_t e = w8a32_split() ? qg::launch_w8a32_split(a, vec_a, vec_w, true, (hipStream_t)stream, &name)
+                                         : qg::launch_w8a32(a, vec_a, vec_w, true, (hipStream_t)stream, &name);
     log_dispatch("w8a32_input_grad", name, 1, M, K, N, 1);
     return finish_launch(e, name);
 }

@@ -106,6 +106,10 @@ struct W8A32Args {
 // wt: W is [N,K] (rows of the contraction), the input-gradient form.
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                         const char** name);
+// The same operation on the bf16 matrix cores, with the fp32 operand split
+// exactly into three bf16 parts.
+hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
+                              const char** name);
 
 // ConvInteger staging: geometry of one call (validated on the host).
 // Kg = Cg*kH*kW, Kp = Kg rounded up to 64, P = OH*OW, Pp = P rounded up to 16.

@@ -56,6 +56,7 @@ COPY_BYTES = 256 << 20       # size of the calibration copy
 CEIL_READ_BYTES = 1 << 30    # streaming-read ceiling: 1 GiB, four times the Infinity Cache
 CEIL_MFMA_ROUNDS = 50        # matrix-core ceiling: 50 rounds = 215 G int8 ops per launch
 CEIL_MFMA_F32_ROUNDS = 200   # fp32 matrix-core ceiling: 200 rounds = 53.7 G flops per launch
+CEIL_MFMA_BF16_ROUNDS = 100  # bf16 matrix-core ceiling: 100 rounds = 215 G flops per launch
 SPREAD_CALLS = 100           # single calls timed one by one for each row's median / p10 / p90
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -681,12 +682,17 @@ def main():
         nfl = q.calib_mfma_f32(f32ops, CEIL_MFMA_F32_ROUNDS)
         ms = time_calls(lambda s: q.calib_mfma_f32(f32ops, CEIL_MFMA_F32_ROUNDS), [None], steps, warmup, stream)
         mf32 = nfl / (ms * 1e-3) / 1e12
+        # bf16 matrix-core loop (the W8A32 split's instruction), operands uniform in [-1, 1)
+        bfops = to(si.rng(9).uniform(-1.0, 1.0, size=2048).astype(np.float32)).to(torch.bfloat16)
+        nbf = q.calib_mfma_bf16(bfops, CEIL_MFMA_BF16_ROUNDS)
+        ms = time_calls(lambda s: q.calib_mfma_bf16(bfops, CEIL_MFMA_BF16_ROUNDS), [None], steps, warmup, stream)
+        mbf = nbf / (ms * 1e-3) / 1e12
         ceilings = {"hbm_read_GBs": hbm, "mfma_i8_random_TOPS": mf["random"], "mfma_i8_ones_TOPS": mf["ones"],
                     "mfma_i8_32x32x32_random_TOPS": mf["random_32x32x32"],
-                    "mfma_f32_random_TFLOPS": mf32,
+                    "mfma_f32_random_TFLOPS": mf32, "mfma_bf16_random_TFLOPS": mbf,
                     "note": "streaming read of 1 GiB; int8 matrix-core loop (v_mfma_i32_16x16x64_i8, the GEMM "
                             "kernels' instruction) on random / all-one operands, and with v_mfma_i32_32x32x32_i8 "
-                            "on the random operands; fp32 matrix-core loop on operands uniform in [-1, 1)"}
+                            "on the random operands; fp32 and bf16 matrix-core loops on operands uniform in [-1, 1)"}
         for name, r in rows.items():
             if "GB/s" in r and "frac_hbm_peak" in r and name.startswith("a8w8_decode"):
                 r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm
@@ -694,6 +700,8 @@ def main():
                 r["frac_mfma_random_ceiling"] = r["TOPS"] / mf["random"]
             if "TFLOPS" in r and r.get("matrix_cores", "fp32") == "fp32":
                 r["frac_mfma_f32_ceiling"] = r["TFLOPS"] / mf32
+            if "frac_bf16_peak_3x" in r:
+                r["frac_mfma_bf16_ceiling_3x"] = 3 * r["TFLOPS"] / mbf
 
     progress(f"GPU rows so far: {sorted(rows)}")
     # ---- CPU baseline: the oracle beside every row ------------------------

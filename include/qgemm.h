@@ -401,10 +401,16 @@ const char* qgemm_version(void);
  *   (v_mfma_f32_16x16x4_f32, the W8A32 kernels' instruction) on 1024 fp32
  *   operands (4096 bytes) that should lie in [-1, 1];
  *   *flops_out (host) receives QG_CALIB_MFMA_F32_FLOPS_PER_ROUND * iters.
+ * qgemm_calib_mfma_bf16: the same with bf16 matrix-core multiplies
+ *   (v_mfma_f32_16x16x32_bf16, the instruction of the W8A32 kernels' exact
+ *   bf16 split) on 2048 bf16 operands (4096 bytes) that should lie in
+ *   [-1, 1]; *flops_out (host) receives
+ *   QG_CALIB_MFMA_BF16_FLOPS_PER_ROUND * iters.
  */
 #define QG_CALIB_SINK_WORDS 8192
 #define QG_CALIB_MFMA_OPS_PER_ROUND 4294967296LL
 #define QG_CALIB_MFMA_F32_FLOPS_PER_ROUND 268435456LL
+#define QG_CALIB_MFMA_BF16_FLOPS_PER_ROUND 2147483648LL
 qg_status qgemm_calib_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 qg_status qgemm_calib_mfma_i8(const void* operands, int iters, uint32_t* sink, void* stream,
                               int64_t* ops_out);
@@ -412,6 +418,8 @@ qg_status qgemm_calib_mfma_i8_32x32(const void* operands, int iters, uint32_t* s
                                     int64_t* ops_out);
 qg_status qgemm_calib_mfma_f32(const void* operands, int iters, uint32_t* sink, void* stream,
                                int64_t* flops_out);
+qg_status qgemm_calib_mfma_bf16(const void* operands, int iters, uint32_t* sink, void* stream,
+                                int64_t* flops_out);
 
 #ifdef __cplusplus
 }

@@ -24,9 +24,9 @@ this package is its thin Python binding, with the same call names:
 * ``dynamic_quantize_linear(x)``: ONNX DynamicQuantizeLinear to uint8,
   returning (y, scale, zero_point) on the device.
 
-``calib_read``, ``calib_mfma_i8`` and ``calib_mfma_f32`` measure the machine's
-HBM read, int8 matrix-core and fp32 matrix-core ceilings for the roofline
-figures.
+``calib_read``, ``calib_mfma_i8``, ``calib_mfma_f32`` and ``calib_mfma_bf16``
+measure the machine's HBM read and int8, fp32 and bf16 matrix-core ceilings
+for the roofline figures.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     QG_OP_DYNAMIC_QUANTIZE_LINEAR,
     QG_OP_W8A32,
     QGemmError,
+    calib_mfma_bf16,
     calib_mfma_f32,
     calib_mfma_i8,
     calib_read,

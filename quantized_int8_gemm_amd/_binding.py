@@ -48,6 +48,7 @@ PROTOTYPES = {
     "qgemm_calib_mfma_i8": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
     "qgemm_calib_mfma_i8_32x32": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
     "qgemm_calib_mfma_f32": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
+    "qgemm_calib_mfma_bf16": ([_p, _int, _p, _p, ctypes.POINTER(ctypes.c_int64)], _int),
 }
 QG_CALIB_SINK_WORDS = 8192
 
@@ -623,4 +624,19 @@ def calib_mfma_f32(operands, iters, sink=None):
     flops = ctypes.c_int64(0)
     _check(lib.qgemm_calib_mfma_f32(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(flops)),
            "qgemm_calib_mfma_f32")
+    return int(flops.value)
+
+
+def calib_mfma_bf16(operands, iters, sink=None):
+    """Run `iters` rounds of bf16 matrix-core multiplies on the 2048 bfloat16
+    operands in `operands` (values in [-1, 1]).  Returns the number of
+    floating-point operations the launch performs."""
+    _need(operands, (torch.bfloat16,), "operands")
+    if operands.numel() != 2048 or not operands.is_contiguous():
+        raise ValueError("operands must be 2048 contiguous bfloat16 values")
+    dev = _on_gpu(operands)
+    sink = _sink(dev, sink)
+    flops = ctypes.c_int64(0)
+    _check(lib.qgemm_calib_mfma_bf16(_ptr(operands), int(iters), _ptr(sink), _stream(dev), ctypes.byref(flops)),
+           "qgemm_calib_mfma_bf16")
     return int(flops.value)

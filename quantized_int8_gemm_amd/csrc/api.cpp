@@ -213,6 +213,16 @@ qg_status qgemm_calib_mfma_f32(const void* operands, int iters, uint32_t* sink, 
     return finish_launch(qg::launch_calib_mfma_f32(operands, iters, sink, (hipStream_t)stream), "calib_mfma_f32");
 }
 
+qg_status qgemm_calib_mfma_bf16(const void* operands, int iters, uint32_t* sink, void* stream,
+                                int64_t* flops_out) {
+    static_assert((int64_t)qg::CALIB_MFMA_BLOCKS * 4 * 16 * 16384 == QG_CALIB_MFMA_BF16_FLOPS_PER_ROUND, "flops");
+    if (operands == nullptr || sink == nullptr || iters < 1 || iters > (1 << 20) || flops_out == nullptr)
+        return QG_ERR_INVALID_ARGUMENT;
+    *flops_out = QG_CALIB_MFMA_BF16_FLOPS_PER_ROUND * (int64_t)iters;
+    (void)hipGetLastError();
+    return finish_launch(qg::launch_calib_mfma_bf16(operands, iters, sink, (hipStream_t)stream), "calib_mfma_bf16");
+}
+
 const char* qgemm_last_kernel(void) { return g_last_kernel; }
 
 const char* qgemm_status_string(qg_status s) {

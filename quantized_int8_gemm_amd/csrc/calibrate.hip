@@ -1,8 +1,8 @@
-// Calibration kernels for the roofline figures: a streaming read and two
+// Calibration kernels for the roofline figures: a streaming read and
 // matrix-core loops.  They implement no part of the quantised matmuls; they
 // measure, on the machine at hand, the ceilings those kernels are held to
-// (HBM read bandwidth for the decode kernel, int8 and fp32 matrix-core rates
-// under data-dependent clocks for the tiled kernels).
+// (HBM read bandwidth for the decode kernel, int8, fp32 and bf16 matrix-core
+// rates under data-dependent clocks for the tiled kernels).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -132,6 +132,37 @@ __global__ __launch_bounds__(CAL_NT) void calib_mfma_f32_kernel(const float* __r
     if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// The same loop with v_mfma_f32_16x16x32_bf16, the instruction of the
+// W8A32 kernels' exact bf16 split, on bf16 operands from `ops` (2048
+// values).  With operands in [-1, 1] an accumulator grows by at most 32 per
+// round, so it stays finite.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(CAL_NT) void calib_mfma_bf16_kernel(const u32x4* __restrict__ ops, int iters,
+                                                                 uint32_t* sink) {
+    const int l = threadIdx.x & 63;
+    v8bf a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = __builtin_bit_cast(v8bf, ops[(l + 64 * i) & 255]);
+        b[i] = __builtin_bit_cast(v8bf, ops[(l + 64 * i + 7) & 255]);
+    }
+    v4f acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 3], b[i >> 2], acc[i], 0, 0, 0);
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        s ^= __float_as_uint(acc[i].x) ^ __float_as_uint(acc[i].y) ^ __float_as_uint(acc[i].z) ^
+             __float_as_uint(acc[i].w);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s ^= (uint32_t)__shfl_xor((int)s, o);
+    if (l == 0) sink[blockIdx.x * (CAL_NT / 64) + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace
 
 hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
@@ -155,6 +186,12 @@ hipError_t launch_calib_mfma32(const void* ops, int iters, uint32_t* sink, hipSt
 hipError_t launch_calib_mfma_f32(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
     hipLaunchKernelGGL(calib_mfma_f32_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
                        reinterpret_cast<const float*>(ops), iters, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_calib_mfma_bf16(const void* ops, int iters, uint32_t* sink, hipStream_t s) {
+    hipLaunchKernelGGL(calib_mfma_bf16_kernel, dim3(CALIB_MFMA_BLOCKS), dim3(CAL_NT), 0, s,
+                       reinterpret_cast<const u32x4*>(ops), iters, sink);
     return hipGetLastError();
 }
 

@@ -158,6 +158,7 @@ constexpr int CALIB_MFMA_BLOCKS = 2048;
 hipError_t launch_calib_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_calib_mfma(const void* ops, int iters, uint32_t* sink, hipStream_t s);
 hipError_t launch_calib_mfma_f32(const void* ops, int iters, uint32_t* sink, hipStream_t s);
+hipError_t launch_calib_mfma_bf16(const void* ops, int iters, uint32_t* sink, hipStream_t s);
 hipError_t launch_calib_mfma32(const void* ops, int iters, uint32_t* sink, hipStream_t s);
 
 }  // namespace qg

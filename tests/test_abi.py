@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"qgemm_w8a32", "qgemm_a8w8", "matmul_integer", "qgemm_workspace_bytes",
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
-                          "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_calib_mfma_i8_32x32", "qgemm_calib_mfma_f32", "qgemm_a8w8_acc",
+                          "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_calib_mfma_i8_32x32", "qgemm_calib_mfma_f32", "qgemm_calib_mfma_bf16", "qgemm_a8w8_acc",
                           "matmul_integer_row_zp", "qgemm_w8a32_input_grad", "dynamic_quantize_linear",
                           "conv_integer", "conv_integer_workspace_bytes", "qgemm_a8w8_noalloc"}
     lib = ctypes.CDLL(b.LIB_PATH)
@@ -213,7 +213,7 @@ def test_calibration_rejects_bad_arguments():
     assert lib.qgemm_calib_mfma_i8(FAKE, (1 << 20) + 1, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
     assert lib.qgemm_calib_mfma_i8(None, 10, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
     assert lib.qgemm_calib_mfma_i8(FAKE, 10, FAKE, None, None) == b.QG_ERR_INVALID_ARGUMENT
-    for fn in (lib.qgemm_calib_mfma_f32,):
+    for fn in (lib.qgemm_calib_mfma_f32, lib.qgemm_calib_mfma_bf16):
         assert fn(FAKE, 0, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
         assert fn(FAKE, (1 << 20) + 1, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT
         assert fn(None, 10, FAKE, None, ctypes.byref(ops)) == b.QG_ERR_INVALID_ARGUMENT

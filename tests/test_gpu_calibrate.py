@@ -60,6 +60,23 @@ def test_calib_mfma_f32_counts_flops_and_stays_finite():
     assert int(sink.abs().sum()) == 0
 
 
+def test_calib_mfma_bf16_counts_flops_and_stays_finite():
+    case("calib_mfma_bf16 5 rounds")
+    vals = si.rng(9).uniform(-1.0, 1.0, size=2048).astype(np.float32)
+    ops = torch.from_numpy(vals).to(dev()).to(torch.bfloat16)
+    sink = torch.zeros(q._binding.QG_CALIB_SINK_WORDS, dtype=torch.int32, device=dev())
+    n = q.calib_mfma_bf16(ops, 5, sink)
+    torch.cuda.synchronize()
+    assert n == 5 * 2147483648
+    assert q.last_kernel() == "calib_mfma_bf16"
+    zeros = torch.zeros(2048, dtype=torch.bfloat16, device=dev())
+    q.calib_mfma_bf16(zeros, 5, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    with pytest.raises(ValueError):
+        q.calib_mfma_bf16(torch.zeros(100, dtype=torch.bfloat16, device=dev()), 3)
+
+
 def test_calib_rejects_bad_operands():
     with pytest.raises(ValueError):
         q.calib_mfma_i8(torch.ones(100, dtype=torch.int8, device=dev()), 3)

@@ -28,10 +28,16 @@
 // split, and written to LDS as three bf16 planes [BM][32 k]; the chunk of W
 // (int8) is widened to bf16 in registers and written as [BN][32 k] (the
 // [K,N] weight is transposed 4x4 bytes at a time on the way).  Every LDS row
-// is 64 bytes, four 16-byte segments; segment c of row r sits at slot
-// c ^ (r >> 1) ^ (r >> 3) (two bits), so a fragment read (16 rows, one
-// segment) and the staging writes hit distinct banks.  A lane's B fragments
-// (16 k of column 16j + l16) stay in registers for the three planes.
+// is 64 bytes, four 16-byte segments.  In the A planes segment c of row r
+// sits at slot c ^ (r >> 1) ^ (r >> 3) (two bits); the W tile, whose staging
+// writes touch rows 4 apart ([K,N]) or two lanes per row (WT), also permutes
+// its rows within groups of four (row n at (n & ~3) | ((n ^ (n >> 2)) & 3))
+// and places segment c at c ^ (n >> 1) ^ (n >> 2) ^ (n >> 3).  Fragment reads
+// (16 rows, one segment) and every staging write then hit distinct banks,
+// for 32 or 64 banks of 4 bytes (an exhaustive check of the access patterns;
+// the first W layout, the A one, had 4-way conflicts on the [K,N] writes).
+// A lane's B fragments (16 k of column 16j + l16) stay in registers for the
+// three planes.
 //
 // With WT = true the same kernel is the gradient with respect to the
 // activations: dA[m,k] = scale * (sum_n dC[m,n] W[k,n] - zp * sum_n dC[m,n]),
@@ -49,6 +55,11 @@ constexpr int GROUP_M = 8;
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int seg3(int r, int c) { return (c ^ (r >> 1) ^ (r >> 3)) & 3; }
+
+// Byte offset of segment c of row n in the W tile.
+__device__ __forceinline__ int wslot(int n, int c) {
+    return (((n & ~3) | ((n ^ (n >> 2)) & 3)) << 6) + (((c ^ (n >> 1) ^ (n >> 2) ^ (n >> 3)) & 3) << 4);
+}
 
 // Two bf16 held in the high halves of a and b, packed a first.
 __device__ __forceinline__ uint32_t pk_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
@@ -211,7 +222,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint2 d0 = i8x4_to_bf16(w_st[2 * h]), d1 = i8x4_to_bf16(w_st[2 * h + 1]);
-                *reinterpret_cast<u32x4*>(Ws + tr * 64 + (seg3(tr, 2 * th + h) << 4)) = u32x4{d0.x, d0.y, d1.x, d1.y};
+                *reinterpret_cast<u32x4*>(Ws + wslot(tr, 2 * th + h)) = u32x4{d0.x, d0.y, d1.x, d1.y};
             }
         } else {
             uint32_t y[4];
@@ -219,7 +230,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int n = wc * 4 + c;
-                *reinterpret_cast<uint2*>(Ws + n * 64 + (seg3(n, wr >> 1) << 4) + 8 * (wr & 1)) = i8x4_to_bf16(y[c]);
+                *reinterpret_cast<uint2*>(Ws + wslot(n, wr >> 1) + 8 * (wr & 1)) = i8x4_to_bf16(y[c]);
             }
         }
     };
@@ -236,7 +247,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = wn * WN + j * 16 + l16;
-            bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(S + A_STAGE + n * 64 + (seg3(n, g) << 4)));
+            bfr[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(S + A_STAGE + wslot(n, g)));
         }
 #pragma unroll
         for (int pl = 0; pl < 3; ++pl) {

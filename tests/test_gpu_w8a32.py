@@ -88,6 +88,15 @@ def test_w8a32_split_big_tiles_ragged():
         check(A, W, 0.01, 7, "bf16x3")
 
 
+@pytest.mark.parametrize("zp", [0, 9])
+def test_w8a32_big_tiles_both_zero_point_forms(zp, path):
+    """4096 x 4096 outputs over K = 96 (the split path's 256 x 256 tiles),
+    with and without the zero-point correction compiled in."""
+    case(f"w8a32 4096x4096x96 zp={zp} {path}")
+    A, W = si.w8a32_inputs(4096, 4096, 96, seed=903 + zp)
+    check(A, W, 0.02, zp, path)
+
+
 def test_w8a32_4096_every_output(path):
     """The 4096^3 workload at full size: all 16.8M outputs within the bound,
     from the kernel the benchmark times."""

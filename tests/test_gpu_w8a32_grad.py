@@ -72,6 +72,15 @@ def test_w8a32_input_grad_unaligned_views(path):
     check(dC, W, 0.03, -7, path, dC_dev=vc, W_dev=vw)
 
 
+@pytest.mark.parametrize("zp", [0, -9])
+def test_w8a32_input_grad_big_tiles_both_zero_point_forms(zp, path):
+    """dA 4096 x 4096 over N = 80 (the split path's 256 x 256 tiles), with
+    and without the zero-point correction compiled in."""
+    case(f"w8a32_input_grad 4096x80x4096 zp={zp} {path}")
+    dC, W = inputs(4096, 80, 4096, seed=904 - zp)
+    check(dC, W, 0.02, zp, path)
+
+
 def test_w8a32_input_grad_4096_every_output(path):
     """4096^3 at full size, the forward workload's weight and scale: all
     16.8M outputs within the bound."""

@@ -335,7 +335,7 @@ def cpu_oracle_rows(rows, si):
         baseline = {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
                     "sample": f"the whole 8192x8192x8192 A8W8 workload, one oracle call ({dt:.1f} s)"}
         del A, W
-    for m in (1, 4, 16):
+    for m in (1, 4, 16, 64):
         name = f"a8w8_decode_m{m}_8192_bf16"
         if name in rows:
             A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
@@ -470,7 +470,9 @@ def main():
         # 9 rotating weight copies (576 MiB, beyond the 256 MB Infinity
         # Cache); timed as a replayed HIP graph of 36 calls (the GPU's time
         # per call) and as eager calls (bound by the host's per-call work)
-        for m in (1, 4, 16):
+        # and M = 64 (a batch of decode rows), past the decode kernel: the
+        # tiled kernel with K split across workgroups
+        for m in (1, 4, 16, 64):
             A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
             base_w = to(W)
             sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),

@@ -143,13 +143,18 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
  *   workspace: NULL, or device memory of at least
  *     qgemm_workspace_bytes(QG_OP_A8W8, 1, M, N, K) bytes, 256-byte aligned
  *     (else QG_ERR_INVALID_ARGUMENT), zero-filled before its first use.
- *     Decode shapes split K across workgroups: the first 1024 bytes hold
- *     one ticket counter per 256 columns (a header of fixed size, whatever
- *     the shape), the rest the exact int32 partial sums.  Every call returns
- *     the tickets to zero when it completes, so the same workspace serves
- *     the next call on the same stream, of this or any other shape, without
+ *     Decode shapes split K across workgroups, and so do tiled shapes whose
+ *     output has at most 128 tiles of 128 x 128 when K allows two or more
+ *     splits of at least 1024 (e.g. M = 17 .. 256 at N = K = 8192): the
+ *     first 1024 bytes hold one ticket counter per 256 columns (decode) or
+ *     per output tile (tiled), a header of fixed size whatever the shape,
+ *     the rest the exact int32 partial sums.  Every call returns the
+ *     tickets to zero when it completes, so the same workspace serves the
+ *     next call on the same stream, of this or any other shape, without
  *     clearing; calls that overlap in time must not share one.  With NULL,
- *     decode shapes use a single-pass kernel.
+ *     both run unsplit (decode shapes as a single-pass kernel).  A [N,K]
+ *     weight (b_trans == 1) at M <= 16 is sized as a decode shape and splits
+ *     only when the workspace passed holds its plan.
  * Decode shapes (M <= 16, b_trans == 0) run a bandwidth-bound kernel that
  * streams W once; all other shapes run the tiled matrix-core kernel.
  * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
@@ -167,13 +172,14 @@ qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
  * qgemm_a8w8 for callers that cannot allocate device memory: code under
  * stream capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same operation, arguments, results (bit for bit) and errors as qgemm_a8w8,
- * without the workspace arguments; it allocates nothing.  Decode shapes that
+ * without the workspace arguments; it allocates nothing.  Shapes that
  * split K use a scratch array the library holds in static device memory,
  * QG_A8W8_NOALLOC_SCRATCH_BYTES on each GPU it runs on (held until the
- * process ends); a shape whose split-K workspace
+ * process ends).  A decode shape whose split-K workspace
  * (qgemm_workspace_bytes(QG_OP_A8W8, ...)) would exceed that returns
  * QG_ERR_WORKSPACE with nothing launched (no shape of the default plan
- * does).  The first call on a device looks up that device's copy and
+ * does); a tiled shape takes as many splits as fit in it (e.g. 2 instead
+ * of 4 for 64 output tiles), or none.  The first call on a device looks up that device's copy and
  * clears its ticket words with a small kernel on `stream`; every call
  * leaves them at zero again.  All calls on one GPU share its array, which
  * keeps the last call's partial sums: calls that overlap in time on one GPU

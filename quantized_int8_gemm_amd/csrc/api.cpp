@@ -2,6 +2,7 @@
 // selection, launch, and the launch-status convention of
 // "feat(onnx-to-hip): lower quantized integer conv and matmul" ("What", last
 // paragraph): clear the pending HIP error, launch, return hipGetLastError().
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -269,12 +270,42 @@ static bool a8w8_is_skinny(int64_t M, int b_trans) {
     return !b_trans && M <= SKINNY_MAX_M;
 }
 
+// Split of K for the tiled A8W8 kernel (128x128 tiles, 128-byte stages):
+// an output of at most 128 tiles leaves most of the 256 CUs idle, so K is cut
+// into up to 8 splits of at least 1024 rows (whole stages) that together
+// give about one workgroup per CU.  max_splits caps the count (the static
+// scratch of the workspace-free entry point); QGEMM_TILE_SPLITS asks for one.
+static void a8w8_tiled_split_plan(int64_t M, int64_t N, int64_t K, int max_splits, int* splits, int* steps) {
+    *splits = 1;
+    *steps = 0;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > qg::SKINNY_MAX_TICKETS / 2) return;
+    int64_t S = env_int("QGEMM_TILE_SPLITS", 0);
+    if (S <= 0) S = std::min<int64_t>(std::min<int64_t>(256 / tiles, K / 1024), 8);
+    S = std::min<int64_t>(S, max_splits);
+    if (S < 2) return;
+    const int64_t stages = (K + 127) / 128;
+    const int64_t per = (stages + S - 1) / S;
+    const int64_t n = (stages + per - 1) / per;
+    if (n < 2) return;
+    *splits = (int)n;
+    *steps = (int)(per * 2);
+}
+
+static size_t a8w8_tiled_split_bytes(int64_t M, int64_t N, int splits) {
+    if (splits <= 1) return 0;
+    const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + 127) / 128);
+    return qg::SKINNY_TICKET_BYTES + tiles * (size_t)splits * 128 * 128 * 4;
+}
+
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
     (void)batch;
     if (op == QG_OP_DYNAMIC_QUANTIZE_LINEAR) return N < 0 ? 0 : (size_t)qg::dql_partials(N) * 8;
-    if (op != QG_OP_A8W8 || !dims_ok(M, N, K) || !a8w8_is_skinny(M, 0)) return 0;
-    const int splits = a8w8_skinny_splits(M, N, K);
-    return qg::skinny_workspace_bytes((int)M, (int)N, splits);
+    if (op != QG_OP_A8W8 || !dims_ok(M, N, K)) return 0;
+    if (a8w8_is_skinny(M, 0)) return qg::skinny_workspace_bytes((int)M, (int)N, a8w8_skinny_splits(M, N, K));
+    int splits, steps;
+    a8w8_tiled_split_plan(M, N, K, 8, &splits, &steps);
+    return a8w8_tiled_split_bytes(M, N, splits);
 }
 
 qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
@@ -392,9 +423,41 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
         log_dispatch(op, name, 1, M, N, K, splits);
     } else {
         const int cfg = pick_tile(1, M, N);
+        // Few output tiles and a long K: split K across workgroups (128x128
+        // tiles with 128-byte stages only, with a workspace).
+        int splits = 1, per = 0;
+        if (cfg == qg::TILE_128x128_K128 && dma_ok(a, b_trans != 0, vec, epi, 128) &&
+            (lib_scratch || workspace != nullptr)) {
+            const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+            const int cap = lib_scratch
+                ? (int)std::min<int64_t>(8, (int64_t)((qg::SKINNY_SCRATCH_BYTES - qg::SKINNY_TICKET_BYTES) /
+                                                      ((size_t)tiles * 128 * 128 * 4)))
+                : 8;
+            a8w8_tiled_split_plan(M, N, K, cap, &splits, &per);
+            // From a caller's workspace: the plan qgemm_workspace_bytes sized;
+            // a shorter workspace is an error, as for the decode kernel (a
+            // [N,K] weight at M <= 16 is sized as a decode shape: it splits
+            // only when the workspace holds the plan).
+            const size_t need = a8w8_tiled_split_bytes(M, N, splits);
+            if (!lib_scratch && need > workspace_bytes) {
+                if (a8w8_is_skinny(M, 0)) splits = 1;
+                else return QG_ERR_WORKSPACE;
+            }
+        }
         (void)hipGetLastError();
-        e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
-        log_dispatch(op, name, 1, M, N, K, 1);
+        if (splits > 1) {
+            if (lib_scratch && qg::skinny_scratch((hipStream_t)stream, &workspace) != hipSuccess) return QG_ERR_HIP;
+            qg::Int8GemmArgs d = a;
+            d.workspace = workspace;
+            d.splits = splits;
+            d.split_steps = per;
+            d.stage_out = stage_output(cfg, K, epi);
+            name = "int8_dma_128x128k128_splitk";
+            e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, (hipStream_t)stream);
+        } else {
+            e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
+        }
+        log_dispatch(op, name, 1, M, N, K, splits);
     }
     return finish_launch(e, name);
 }

@@ -7,4 +7,12 @@ namespace qg {
 hipError_t launch_dma_128x128k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
     return dma::launch_shape<128, 128, 64, 64, 2, 128>(a, bkm, epi, zp, s);
 }
+// Split over K: three stages (96 KiB, one workgroup per CU; the split grid
+// gives about one per CU).  Mid-sized M at K = N = 8192 (graph-timed, one box):
+// M = 32 27.2 -> 24.5 us, M = 64 27.3 -> 25.1, M = 128 28.6 -> 27.0,
+// M = 256 39.0 -> 32.8 against two stages; four stages 26.2 / 26.2 / 26.8 /
+// 32.4 us.
+hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s) {
+    return dma::launch_split<128, 128, 64, 64, 3, 128>(a, bkm, epi, s);
+}
 }  // namespace qg

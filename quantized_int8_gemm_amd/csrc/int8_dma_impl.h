@@ -111,7 +111,14 @@ __device__ __forceinline__ int kn_slot(int r, int s) {
     return s ^ (r & 7) ^ (BN >= 256 ? (t << 3) : t);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP, int BK>
+// SK: split-K (A8W8 only, no zero-point sums).  blockIdx.z is the split;
+// each split multiplies p.split_steps * 64 rows of K (whole stages) and
+// leaves its exact int32 partial tile in the workspace; the split that takes
+// the last ticket of its tile adds the others' partials to its own and runs
+// the epilogue.  Exchange as in the decode kernel: device-coherent 16-byte
+// stores and loads, one atomic ticket per tile in the fixed header, reset by
+// the last split.
+template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP, int BK, bool SK = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(Int8GemmArgs p) {
     static_assert(BK == 64 || BK == 128, "64 or 128 k-bytes per stage");
     constexpr int KB = BK / 64;                     // 64-k matrix-core blocks per stage
@@ -145,12 +152,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     const int rows_a = p.M - m0 < BM ? p.M - m0 : BM;
     const int cols_b = p.N - n0 < BN ? p.N - n0 : BN;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
-    const int8_t* A = p.A + (int64_t)bz * p.a_bstride + (int64_t)m0 * p.lda;
-    const int8_t* B = B_KMAJOR ? p.B + (int64_t)bz * p.b_bstride + (int64_t)n0 * p.ldb
-                               : p.B + (int64_t)bz * p.b_bstride + n0;
-    const v4i a_rsrc = rsrc_words(A, (uint32_t)((rows_a - 1) * lda + p.K));
-    const v4i b_rsrc = B_KMAJOR ? rsrc_words(B, (uint32_t)((cols_b - 1) * ldb + p.K))
-                                : rsrc_words(B, (uint32_t)((p.K - 1) * ldb + (p.N - n0)));
+    // This workgroup's rows of K: [kbeg, kbeg + Kl).
+    const int kbeg = SK ? (int)blockIdx.z * p.split_steps * 64 : 0;
+    const int Kl = SK ? (p.K - kbeg < p.split_steps * 64 ? p.K - kbeg : p.split_steps * 64) : p.K;
+    const int8_t* A = p.A + (int64_t)bz * p.a_bstride + (int64_t)m0 * p.lda + kbeg;
+    const int8_t* B = B_KMAJOR ? p.B + (int64_t)bz * p.b_bstride + (int64_t)n0 * p.ldb + kbeg
+                               : p.B + (int64_t)bz * p.b_bstride + (int64_t)kbeg * p.ldb + n0;
+    const v4i a_rsrc = rsrc_words(A, (uint32_t)((rows_a - 1) * lda + Kl));
+    const v4i b_rsrc = B_KMAJOR ? rsrc_words(B, (uint32_t)((cols_b - 1) * ldb + Kl))
+                                : rsrc_words(B, (uint32_t)((Kl - 1) * ldb + (p.N - n0)));
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
     // Per-lane global offsets (chunk 0) of each load round.  Round q of a
@@ -334,7 +344,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         }
     }
 
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (Kl + BK - 1) / BK;
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue(s, s);
@@ -345,6 +355,52 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         else wait_vmcnt<0>();
         __syncthreads();
         compute(kt % STAGES, kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1, kt);
+    }
+
+    if constexpr (SK) {
+        static_assert(!ROWSUM && !COLSUM, "split-K carries no zero-point sums");
+        const int S = (int)gridDim.z, sk = (int)blockIdx.z;
+        if (S > 1) {
+            constexpr int COHERENT = 16;   // sc1: device scope
+            constexpr int TILE_BYTES = BM * BN * 4;
+            const int tile = tm * tiles_n + tn;   // < SKINNY_MAX_TICKETS (host plan)
+            int* tickets = reinterpret_cast<int*>(p.workspace);
+            char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tile * S * TILE_BYTES;
+            const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * TILE_BYTES));
+            // lane-major partial tile: fragment (a, b) of wave w at ((w * FM + a) * FN + b) * 1024 + 16 * lane
+            const uint32_t mine = (uint32_t)(sk * TILE_BYTES + (wave * FM * FN) * 1024 + 16 * lane);
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    __builtin_amdgcn_raw_buffer_store_b128(acc[a][b], p_rsrc, mine + (uint32_t)((a * FN + b) * 1024), 0,
+                                                           COHERENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __shared__ int ticket;
+            __syncthreads();
+            if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (ticket != S - 1) return;
+            for (int s2 = 0; s2 < S; ++s2) {
+                if (s2 == sk) continue;
+                const uint32_t o = (uint32_t)(s2 * TILE_BYTES + (wave * FM * FN) * 1024 + 16 * lane);
+                v4i v[FM][FN];
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        v[a][b] = __builtin_bit_cast(
+                            v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o + (uint32_t)((a * FN + b) * 1024), 0, COHERENT));
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[a][b][r] = (int)((uint32_t)acc[a][b][r] + (uint32_t)v[a][b][r]);
+            }
+            if (tid == 0) __hip_atomic_store(&tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     // Complete row / column sums: add the four lane groups (k segments) of
@@ -679,12 +735,32 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
     }
 }
 
-template <int BM, int BN, int WM, int WN, int ST, bool BKM, int EPI, int ZP, int FLIP, int BK>
+template <int BM, int BN, int WM, int WN, int ST, bool BKM, int EPI, int ZP, int FLIP, int BK, bool SK = false>
 hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, ST, BKM, EPI, ZP, FLIP, BK>), dim3(tiles, a.batch),
-                       dim3((BM / WM) * (BN / WN) * 64), 0, s, a);
+    hipLaunchKernelGGL((int8_dma_kernel<BM, BN, WM, WN, ST, BKM, EPI, ZP, FLIP, BK, SK>),
+                       dim3(tiles, a.batch, SK ? a.splits : 1), dim3((BM / WM) * (BN / WN) * 64), 0, s, a);
     return hipGetLastError();
+}
+
+// A8W8 split over K (a.splits > 1, a.split_steps 64-row steps per split, a
+// whole number of stages; batch 1; a.workspace as the host plan sized it).
+template <int BM, int BN, int WM, int WN, int ST, int BK>
+hipError_t launch_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s) {
+    if (a.batch != 1 || a.workspace == nullptr || (a.split_steps * 64) % BK != 0 ||
+        ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) > SKINNY_MAX_TICKETS)
+        return hipErrorInvalidValue;
+    const bool f32 = epi == EPI_F32;
+    if (a.acc_in != nullptr) {
+        if (bkm) return f32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32_ACC, 0, 0, BK, true>(a, s)
+                            : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16_ACC, 0, 0, BK, true>(a, s);
+        return f32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32_ACC, 0, 0, BK, true>(a, s)
+                   : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16_ACC, 0, 0, BK, true>(a, s);
+    }
+    if (bkm) return f32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32, 0, 0, BK, true>(a, s)
+                        : launch_one<BM, BN, WM, WN, ST, true, EPI_BF16, 0, 0, BK, true>(a, s);
+    return f32 ? launch_one<BM, BN, WM, WN, ST, false, EPI_F32, 0, 0, BK, true>(a, s)
+               : launch_one<BM, BN, WM, WN, ST, false, EPI_BF16, 0, 0, BK, true>(a, s);
 }
 
 template <int BM, int BN, int WM, int WN, int ST, int EPI, int ZP, int BK>

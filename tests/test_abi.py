@@ -55,6 +55,11 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 16, 8192, 8192) > 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 1, 8192, 8192) > 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 8192, 8192, 8192) == 0
+    # a tiled output of 64 tiles over K = 8192 splits K four ways: the ticket
+    # header and four 64 KiB partial tiles per output tile
+    assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 8192) == 1024 + 64 * 4 * 128 * 128 * 4
+    assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 1024) == 0      # K too short to split
+    assert q.workspace_bytes(q.QG_OP_A8W8, 1, 2048, 4096, 8192) == 0    # 512 tiles fill the chip
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 0
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 8, 512, 2048, 2048) == 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 0, 8192, 8192) == 0
@@ -120,6 +125,14 @@ def test_w8a32_rejects(kw, code):
 ])
 def test_a8w8_rejects(kw, code):
     assert a8w8(**kw) == code
+
+
+def test_a8w8_split_k_workspace_too_small():
+    # a tiled shape whose split-K plan needs more workspace than was passed
+    M, N, K = 64, 8192, 8192
+    need = q.workspace_bytes(q.QG_OP_A8W8, 1, M, N, K)
+    st = a8w8(M=M, N=N, K=K, lda=K, ldw=N, ldo=N, n_a=M, n_w=N, ws=FAKE, wsb=need - 1)
+    assert st == b.QG_ERR_WORKSPACE
 
 
 def test_a8w8_workspace_too_small():

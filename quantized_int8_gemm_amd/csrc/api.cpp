@@ -423,12 +423,14 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
         log_dispatch(op, name, 1, M, N, K, splits);
     } else {
         const int cfg = pick_tile(1, M, N);
-        // Few output tiles and a long K: split K across workgroups (128x128
-        // tiles with 128-byte stages only, with a workspace).
+        // Few output tiles and a long K (128x128 tiles with 128-byte stages):
+        // the three-stage kernel, K split across workgroups when the output
+        // has at most 128 tiles and a workspace holds the partial sums.
+        const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+        const bool deep = cfg == qg::TILE_128x128_K128 && dma_ok(a, b_trans != 0, vec, epi, 128) &&
+                          tiles <= qg::SKINNY_MAX_TICKETS && K >= 2048;
         int splits = 1, per = 0;
-        if (cfg == qg::TILE_128x128_K128 && dma_ok(a, b_trans != 0, vec, epi, 128) &&
-            (lib_scratch || workspace != nullptr)) {
-            const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+        if (deep && (lib_scratch || workspace != nullptr)) {
             const int cap = lib_scratch
                 ? (int)std::min<int64_t>(8, (int64_t)((qg::SKINNY_SCRATCH_BYTES - qg::SKINNY_TICKET_BYTES) /
                                                       ((size_t)tiles * 128 * 128 * 4)))
@@ -445,14 +447,15 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
             }
         }
         (void)hipGetLastError();
-        if (splits > 1) {
-            if (lib_scratch && qg::skinny_scratch((hipStream_t)stream, &workspace) != hipSuccess) return QG_ERR_HIP;
+        if (deep) {
+            if (splits > 1 && lib_scratch && qg::skinny_scratch((hipStream_t)stream, &workspace) != hipSuccess)
+                return QG_ERR_HIP;
             qg::Int8GemmArgs d = a;
-            d.workspace = workspace;
+            d.workspace = splits > 1 ? workspace : nullptr;
             d.splits = splits;
-            d.split_steps = per;
+            d.split_steps = splits > 1 ? per : (int)(((K + 127) / 128) * 2);
             d.stage_out = stage_output(cfg, K, epi);
-            name = "int8_dma_128x128k128_splitk";
+            name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
             e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, (hipStream_t)stream);
         } else {
             e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);

@@ -747,7 +747,7 @@ hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
 // whole number of stages; batch 1; a.workspace as the host plan sized it).
 template <int BM, int BN, int WM, int WN, int ST, int BK>
 hipError_t launch_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s) {
-    if (a.batch != 1 || a.workspace == nullptr || (a.split_steps * 64) % BK != 0 ||
+    if (a.batch != 1 || (a.splits > 1 && a.workspace == nullptr) || (a.split_steps * 64) % BK != 0 ||
         ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) > SKINNY_MAX_TICKETS)
         return hipErrorInvalidValue;
     const bool f32 = epi == EPI_F32;

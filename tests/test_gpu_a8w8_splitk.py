@@ -2,7 +2,8 @@
 128 x 128 and a long K): every output against the oracle, bit for bit, for
 both output types, both weight layouts, the accumulator input, ragged last
 splits, forced split counts, a workspace reused across shapes, the
-workspace-free entry point, and the unsplit kernel without a workspace."""
+workspace-free entry point, and the same three-stage kernel unsplit (without
+a workspace, or for 129 to 256 tiles)."""
 import ctypes
 
 import numpy as np
@@ -97,8 +98,19 @@ def test_a8w8_noalloc_split_k():
         np.testing.assert_array_equal(bf16_bits(out), ref["bf16"])
 
 
+@pytest.mark.parametrize("M,N,K", [(384, 8192, 4096), (512, 4112, 2064), (300, 8192, 4096)])
+def test_a8w8_three_stage_unsplit_every_output(M, N, K):
+    """129 to 256 output tiles over a long K: the three-stage kernel without
+    a split (no workspace needed)."""
+    case(f"a8w8 three-stage unsplit M={M} N={N} K={K}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K + 1)
+    for dt in (torch.bfloat16, torch.float32):
+        check(A, W, s_a, s_w, out_dtype=dt, kernel="int8_dma_128x128k128x3")
+
+
 def test_a8w8_without_workspace_runs_unsplit():
-    """A NULL workspace through the C ABI: the unsplit tiled kernel, same bits."""
+    """A NULL workspace through the C ABI: the same three-stage kernel
+    unsplit, same bits."""
     case("a8w8 64x4096x4096 NULL workspace")
     from quantized_int8_gemm_amd import _binding as b
     M, N, K = 64, 4096, 4096
@@ -109,5 +121,5 @@ def test_a8w8_without_workspace_runs_unsplit():
                           b._ptr(out), b.QG_FP32, N, None, 0,
                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0
-    assert q.last_kernel() == "int8_dma_128x128k128", q.last_kernel()
+    assert q.last_kernel() == "int8_dma_128x128k128x3", q.last_kernel()
     np.testing.assert_array_equal(out.cpu().numpy(), oracle.a8w8(A, W, s_a, s_w)["f32"])

@@ -243,7 +243,18 @@ qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K,
  *      b_zero_point_len == 1 (scalar) or N (one per column).
  *   Y: int32, `batch` matrices [M,N], row stride ldy >= N, batch stride
  *      y_batch_stride >= (M-1)*ldy + N when batch > 1.
- *   workspace: reserved; pass NULL / 0.
+ *   workspace: NULL, or device memory of at least
+ *     qgemm_workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K) bytes,
+ *     256-byte aligned (else QG_ERR_INVALID_ARGUMENT), zero-filled before
+ *     its first use.  An output of at most 128 tiles of 128 x 128 (batches
+ *     folded into M) whose K allows two or more splits of at least 1024
+ *     splits K across workgroups: the first 1024 bytes hold one ticket per
+ *     output tile, the rest each split's exact int32 partial tile with its
+ *     partial row and column sums.  Tickets return to zero when a call
+ *     completes, so one workspace serves later calls on the same stream of
+ *     any shape; calls that overlap in time must not share one.  With NULL
+ *     the same kernel runs unsplit; QG_ERR_WORKSPACE when a workspace is
+ *     given but smaller than the split needs.
  * Requires batch, M, N, K >= 1.  QG_ERR_UNSUPPORTED: an operand byte span
  * that reaches 2^31.  (Per-row activation zero points: matmul_integer_row_zp.
  * Ranks outside 2-4 are rejected by the Python binding, which maps ONNX

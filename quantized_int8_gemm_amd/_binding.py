@@ -391,19 +391,21 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
         _need(out, (torch.int32,), "out")
         if tuple(out.shape) != tuple(batch_shape) + (M, N) or not out.is_contiguous():
             raise ValueError("out has the wrong shape or is not contiguous")
+    ws = _workspace(dev, workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K))
+    wsz = 0 if ws is None else ws.numel()
     if za_rows is None:
         st = lib.matmul_integer(batch, M, N, K,
                                 _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
                                 _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
                                 int(a_zero_point), _ptr(zb), zb_len,
-                                _ptr(out), N, M * N, None, 0, _stream(dev))
+                                _ptr(out), N, M * N, _ptr(ws), wsz, _stream(dev))
         _check(st, "matmul_integer")
     else:
         st = lib.matmul_integer_row_zp(batch, M, N, K,
                                        _ptr(A2), _QG_OF[A.dtype], _rows(A2, "A"), a_bs,
                                        _ptr(B2), _QG_OF[B.dtype], _rows(B2, "B"), b_bs,
                                        _ptr(za_rows), za_rows.numel(), _ptr(zb), zb_len,
-                                       _ptr(out), N, M * N, None, 0, _stream(dev))
+                                       _ptr(out), N, M * N, _ptr(ws), wsz, _stream(dev))
         _check(st, "matmul_integer_row_zp")
     return out
 

@@ -298,9 +298,23 @@ static size_t a8w8_tiled_split_bytes(int64_t M, int64_t N, int splits) {
     return qg::SKINNY_TICKET_BYTES + tiles * (size_t)splits * 128 * 128 * 4;
 }
 
+// MatMulInteger's split partials: the tile plus each lane's row and column
+// sums (4 + 4 ints for 64x64 waves: 8 KiB per 128x128 tile).
+static size_t mmi_tiled_split_bytes(int64_t M, int64_t N, int splits) {
+    if (splits <= 1) return 0;
+    const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + 127) / 128);
+    return qg::SKINNY_TICKET_BYTES + tiles * (size_t)splits * (128 * 128 * 4 + 8192);
+}
+
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
-    (void)batch;
     if (op == QG_OP_DYNAMIC_QUANTIZE_LINEAR) return N < 0 ? 0 : (size_t)qg::dql_partials(N) * 8;
+    if (op == QG_OP_MATMUL_INTEGER) {
+        // sized for the batch folded into M (contiguous A / Y batches, shared B)
+        if (batch < 1 || batch >= 65536 || !dims_ok(M, N, K) || batch * M >= ((int64_t)1 << 30)) return 0;
+        int splits, steps;
+        a8w8_tiled_split_plan(batch * M, N, K, 8, &splits, &steps);
+        return mmi_tiled_split_bytes(batch * M, N, splits);
+    }
     if (op != QG_OP_A8W8 || !dims_ok(M, N, K)) return 0;
     if (a8w8_is_skinny(M, 0)) return qg::skinny_workspace_bytes((int)M, (int)N, a8w8_skinny_splits(M, N, K));
     int splits, steps;
@@ -456,7 +470,7 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
             d.split_steps = splits > 1 ? per : (int)(((K + 127) / 128) * 2);
             d.stage_out = stage_output(cfg, K, epi);
             name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
-            e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, (hipStream_t)stream);
+            e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, 0, (hipStream_t)stream);
         } else {
             e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
         }
@@ -510,7 +524,8 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
                               int64_t lda, int64_t a_batch_stride, const void* B, qg_dtype b_dtype, int64_t ldb,
                               int64_t b_batch_stride, int32_t a_zero_point, const void* a_zp_rows,
                               int64_t a_zp_len, const void* b_zero_point, int64_t b_zero_point_len, int32_t* Y,
-                              int64_t ldy, int64_t y_batch_stride, void* stream) {
+                              int64_t ldy, int64_t y_batch_stride, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     if (empty_output(M, N, K, batch)) return empty_call();
     if (!dims_ok(M, N, K) || batch < 1 || batch >= 65536) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || B == nullptr || Y == nullptr) return QG_ERR_INVALID_ARGUMENT;
@@ -535,6 +550,8 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
     if (b_zero_point == nullptr && b_zero_point_len != 0 && b_zero_point_len != 1 && b_zero_point_len != N)
         return QG_ERR_INVALID_ARGUMENT;
     if (256 * lda + K + 256 >= SPAN_LIMIT || (K + 256) * ldb >= SPAN_LIMIT) return QG_ERR_UNSUPPORTED;
+    // split-K tickets take atomics and partials 16-byte coherent stores
+    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
 
     qg::Int8GemmArgs a{};
     a.M = (int)M; a.N = (int)N; a.K = (int)K; a.batch = (int)batch;
@@ -570,10 +587,32 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
     const bool vec = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
                      N % 16 == 0 && (a.batch == 1 || (a_batch_stride % 16 == 0 && b_batch_stride % 16 == 0));
     const int cfg = pick_tile(a.batch, a.M, N);
+    // Few output tiles and a long K: the three-stage kernel, K split across
+    // workgroups (partial tiles and row / column sums in the workspace) when
+    // the output has at most 128 tiles and a workspace is given.
+    const int64_t tiles = (((int64_t)a.M + 127) / 128) * ((N + 127) / 128);
+    const bool deep = a.batch == 1 && cfg == qg::TILE_128x128_K128 && dma_ok(a, false, vec, qg::EPI_I32, 128) &&
+                      tiles <= qg::SKINNY_MAX_TICKETS && K >= 2048;
+    int splits = 1, per = 0;
+    if (deep && workspace != nullptr) {
+        a8w8_tiled_split_plan(a.M, N, K, 8, &splits, &per);
+        if (mmi_tiled_split_bytes(a.M, N, splits) > workspace_bytes) return QG_ERR_WORKSPACE;
+    }
     const char* name = "";
+    hipError_t e;
     (void)hipGetLastError();
-    const hipError_t e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
-    log_dispatch("matmul_integer", name, a.batch, a.M, N, K, 1);
+    if (deep) {
+        qg::Int8GemmArgs d = a;
+        d.workspace = splits > 1 ? workspace : nullptr;
+        d.splits = splits;
+        d.split_steps = splits > 1 ? per : (int)(((K + 127) / 128) * 2);
+        d.stage_out = stage_output(cfg, K, qg::EPI_I32);
+        name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
+        e = qg::launch_dma_128x128k128_split(d, false, qg::EPI_I32, zp, (hipStream_t)stream);
+    } else {
+        e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
+    }
+    log_dispatch("matmul_integer", name, a.batch, a.M, N, K, splits);
     return finish_launch(e, name);
 }
 
@@ -586,11 +625,9 @@ qg_status matmul_integer(int64_t batch, int64_t M, int64_t N, int64_t K, const v
                          int64_t b_batch_stride, int32_t a_zero_point, const void* b_zero_point,
                          int64_t b_zero_point_len, int32_t* Y, int64_t ldy, int64_t y_batch_stride,
                          void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     return matmul_integer_impl(batch, M, N, K, A, a_dtype, lda, a_batch_stride, B, b_dtype, ldb, b_batch_stride,
                                a_zero_point, nullptr, 0, b_zero_point, b_zero_point_len, Y, ldy,
-                               y_batch_stride, stream);
+                               y_batch_stride, workspace, workspace_bytes, stream);
 }
 
 qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A,
@@ -599,15 +636,13 @@ qg_status matmul_integer_row_zp(int64_t batch, int64_t M, int64_t N, int64_t K, 
                                 int64_t a_zero_point_len, const void* b_zero_point, int64_t b_zero_point_len,
                                 int32_t* Y, int64_t ldy, int64_t y_batch_stride, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (empty_output(M, N, K, batch)) return empty_call();
     if (a_zero_point == nullptr || (a_zero_point_len != 1 && a_zero_point_len != M))
         return QG_ERR_INVALID_ARGUMENT;
     const int32_t za0 = a_dtype == QG_UINT8 ? 128 : 0;   // in range; the kernel reads the real values
     return matmul_integer_impl(batch, M, N, K, A, a_dtype, lda, a_batch_stride, B, b_dtype, ldb, b_batch_stride,
                                za0, a_zero_point, a_zero_point_len, b_zero_point, b_zero_point_len, Y, ldy,
-                               y_batch_stride, stream);
+                               y_batch_stride, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@ hipError_t launch_dma_128x128k128(const Int8GemmArgs& a, bool bkm, int epi, int 
 // against two stages (four stages 26.2 / 26.2 / 26.8 / 32.4 us); unsplit,
 // 129 to 256 tiles: M = 320 / 384 / 512 60.4 / 60.9 / 61.7 -> 43.4 / 46.0 /
 // 48.5 us against the two-stage kernel.
-hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s) {
-    return dma::launch_split<128, 128, 64, 64, 3, 128>(a, bkm, epi, s);
+hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
+    return dma::launch_split<128, 128, 64, 64, 3, 128>(a, bkm, epi, zp, s);
 }
 }  // namespace qg

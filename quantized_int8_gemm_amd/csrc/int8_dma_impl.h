@@ -111,13 +111,14 @@ __device__ __forceinline__ int kn_slot(int r, int s) {
     return s ^ (r & 7) ^ (BN >= 256 ? (t << 3) : t);
 }
 
-// SK: split-K (A8W8 only, no zero-point sums).  blockIdx.z is the split;
-// each split multiplies p.split_steps * 64 rows of K (whole stages) and
-// leaves its exact int32 partial tile in the workspace; the split that takes
-// the last ticket of its tile adds the others' partials to its own and runs
-// the epilogue.  Exchange as in the decode kernel: device-coherent 16-byte
-// stores and loads, one atomic ticket per tile in the fixed header, reset by
-// the last split.
+// SK: split-K.  blockIdx.z is the split; each split multiplies
+// p.split_steps * 64 rows of K (whole stages) and leaves its exact int32
+// partial tile, with its partial row / column sums when the MatMulInteger
+// correction needs them, in the workspace; the split that takes the last
+// ticket of its tile adds the others' partials to its own and runs the
+// epilogue.  Exchange as in the decode kernel: device-coherent 16-byte stores
+// and loads, one atomic ticket per tile in the fixed header, reset by the
+// last split.
 template <int BM, int BN, int WM, int WN, int STAGES, bool B_KMAJOR, int EPI, int ZP, int FLIP, int BK, bool SK = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(Int8GemmArgs p) {
     static_assert(BK == 64 || BK == 128, "64 or 128 k-bytes per stage");
@@ -357,52 +358,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
         compute(kt % STAGES, kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1, kt);
     }
 
-    if constexpr (SK) {
-        static_assert(!ROWSUM && !COLSUM, "split-K carries no zero-point sums");
-        const int S = (int)gridDim.z, sk = (int)blockIdx.z;
-        if (S > 1) {
-            constexpr int COHERENT = 16;   // sc1: device scope
-            constexpr int TILE_BYTES = BM * BN * 4;
-            const int tile = tm * tiles_n + tn;   // < SKINNY_MAX_TICKETS (host plan)
-            int* tickets = reinterpret_cast<int*>(p.workspace);
-            char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tile * S * TILE_BYTES;
-            const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * TILE_BYTES));
-            // lane-major partial tile: fragment (a, b) of wave w at ((w * FM + a) * FN + b) * 1024 + 16 * lane
-            const uint32_t mine = (uint32_t)(sk * TILE_BYTES + (wave * FM * FN) * 1024 + 16 * lane);
-#pragma unroll
-            for (int a = 0; a < FM; ++a)
-#pragma unroll
-                for (int b = 0; b < FN; ++b)
-                    __builtin_amdgcn_raw_buffer_store_b128(acc[a][b], p_rsrc, mine + (uint32_t)((a * FN + b) * 1024), 0,
-                                                           COHERENT);
-            __builtin_amdgcn_s_waitcnt(0);
-            __shared__ int ticket;
-            __syncthreads();
-            if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            if (ticket != S - 1) return;
-            for (int s2 = 0; s2 < S; ++s2) {
-                if (s2 == sk) continue;
-                const uint32_t o = (uint32_t)(s2 * TILE_BYTES + (wave * FM * FN) * 1024 + 16 * lane);
-                v4i v[FM][FN];
-#pragma unroll
-                for (int a = 0; a < FM; ++a)
-#pragma unroll
-                    for (int b = 0; b < FN; ++b)
-                        v[a][b] = __builtin_bit_cast(
-                            v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o + (uint32_t)((a * FN + b) * 1024), 0, COHERENT));
-#pragma unroll
-                for (int a = 0; a < FM; ++a)
-#pragma unroll
-                    for (int b = 0; b < FN; ++b)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[a][b][r] = (int)((uint32_t)acc[a][b][r] + (uint32_t)v[a][b][r]);
-            }
-            if (tid == 0) __hip_atomic_store(&tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
     // Complete row / column sums: add the four lane groups (k segments) of
     // the v_dot4 sums, then the partial sums of the waves that took turns on
     // a row or column block, through LDS.
@@ -451,6 +406,92 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                 for (int w = 0; w < WAVES_M; ++w) t += (uint32_t)cs_part[w][wn * WN + 16 * b + i16];
                 cs[b] = (int)t;
             }
+        }
+    }
+
+    // Split-K exchange (after the row / column sums of this split's K range
+    // are complete): each split stores its accumulators and sums, lane-major;
+    // the split that takes its tile's last ticket adds the others' into its
+    // own registers and runs the epilogue.
+    if constexpr (SK) {
+        const int S = (int)gridDim.z, sk = (int)blockIdx.z;
+        if (S > 1) {
+            constexpr int COHERENT = 16;   // sc1: device scope
+            constexpr int NWV = (BM / WM) * (BN / WN);
+            constexpr int TILE_BYTES = BM * BN * 4;
+            constexpr int SUMS = (ROWSUM ? FM : 0) + (COLSUM ? FN : 0);
+            constexpr int SUMS_V4 = (SUMS + 3) / 4;
+            constexpr int SLOT = TILE_BYTES + SUMS_V4 * NWV * 64 * 16;
+            const int tile = tm * tiles_n + tn;   // < SKINNY_MAX_TICKETS (host plan)
+            int* tickets = reinterpret_cast<int*>(p.workspace);
+            char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tile * S * SLOT;
+            const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
+            // fragment (a, b) of wave w at ((w * FM + a) * FN + b) * 1024 + 16 * lane; sum vector q
+            // at TILE_BYTES + ((q * NWV + w) * 64 + lane) * 16
+            auto frag_off = [&](int s2, int a, int b) {
+                return (uint32_t)(s2 * SLOT + ((wave * FM + a) * FN + b) * 1024 + 16 * lane);
+            };
+            auto sums_off = [&](int s2, int q) {
+                return (uint32_t)(s2 * SLOT + TILE_BYTES + ((q * NWV + wave) * 64 + lane) * 16);
+            };
+            int sv[SUMS_V4 * 4 > 0 ? SUMS_V4 * 4 : 1];
+#pragma unroll
+            for (int i = 0; i < SUMS_V4 * 4; ++i) sv[i] = 0;
+            if constexpr (ROWSUM) {
+#pragma unroll
+                for (int a = 0; a < FM; ++a) sv[a] = rs[a];
+            }
+            if constexpr (COLSUM) {
+#pragma unroll
+                for (int b = 0; b < FN; ++b) sv[(ROWSUM ? FM : 0) + b] = cs[b];
+            }
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    __builtin_amdgcn_raw_buffer_store_b128(acc[a][b], p_rsrc, frag_off(sk, a, b), 0, COHERENT);
+#pragma unroll
+            for (int q = 0; q < SUMS_V4; ++q)
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]},
+                                                       p_rsrc, sums_off(sk, q), 0, COHERENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __shared__ int ticket;
+            __syncthreads();
+            if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (ticket != S - 1) return;
+            for (int s2 = 0; s2 < S; ++s2) {
+                if (s2 == sk) continue;
+                v4i v[FM][FN];
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        v[a][b] = __builtin_bit_cast(
+                            v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, frag_off(s2, a, b), 0, COHERENT));
+                v4i w[SUMS_V4 > 0 ? SUMS_V4 : 1];
+#pragma unroll
+                for (int q = 0; q < SUMS_V4; ++q)
+                    w[q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, sums_off(s2, q), 0, COHERENT));
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[a][b][r] = (int)((uint32_t)acc[a][b][r] + (uint32_t)v[a][b][r]);
+#pragma unroll
+                for (int i = 0; i < SUMS_V4 * 4; ++i) sv[i] = (int)((uint32_t)sv[i] + (uint32_t)w[i / 4][i % 4]);
+            }
+            if constexpr (ROWSUM) {
+#pragma unroll
+                for (int a = 0; a < FM; ++a) rs[a] = sv[a];
+            }
+            if constexpr (COLSUM) {
+#pragma unroll
+                for (int b = 0; b < FN; ++b) cs[b] = sv[(ROWSUM ? FM : 0) + b];
+            }
+            if (tid == 0) __hip_atomic_store(&tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -743,13 +784,27 @@ hipError_t launch_one(const Int8GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// A8W8 split over K (a.splits > 1, a.split_steps 64-row steps per split, a
-// whole number of stages; batch 1; a.workspace as the host plan sized it).
+// The three-stage kernel, split over K when a.splits > 1 (a.split_steps
+// 64-row steps per split, a whole number of stages; batch 1; a.workspace as
+// the host plan sized it): A8W8 (B as [K,N] or [N,K]) or MatMulInteger.
 template <int BM, int BN, int WM, int WN, int ST, int BK>
-hipError_t launch_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s) {
+hipError_t launch_split(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s) {
     if (a.batch != 1 || (a.splits > 1 && a.workspace == nullptr) || (a.split_steps * 64) % BK != 0 ||
         ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) > SKINNY_MAX_TICKETS)
         return hipErrorInvalidValue;
+    if (epi == EPI_I32) {   // MatMulInteger: B as [K,N], any flips and sums
+        const int flip = (a.a_flip ? 1 : 0) | (a.b_flip ? 2 : 0);
+        switch (zp * 4 + flip) {
+#define QG_SPLIT_I32(Z, F) \
+    case Z * 4 + F: return launch_one<BM, BN, WM, WN, ST, false, EPI_I32, Z, F, BK, true>(a, s);
+            QG_SPLIT_I32(0, 0) QG_SPLIT_I32(0, 1) QG_SPLIT_I32(0, 2) QG_SPLIT_I32(0, 3)
+            QG_SPLIT_I32(1, 0) QG_SPLIT_I32(1, 1) QG_SPLIT_I32(1, 2) QG_SPLIT_I32(1, 3)
+            QG_SPLIT_I32(2, 0) QG_SPLIT_I32(2, 1) QG_SPLIT_I32(2, 2) QG_SPLIT_I32(2, 3)
+            QG_SPLIT_I32(3, 0) QG_SPLIT_I32(3, 1) QG_SPLIT_I32(3, 2) QG_SPLIT_I32(3, 3)
+#undef QG_SPLIT_I32
+            default: return hipErrorInvalidValue;
+        }
+    }
     const bool f32 = epi == EPI_F32;
     if (a.acc_in != nullptr) {
         if (bkm) return f32 ? launch_one<BM, BN, WM, WN, ST, true, EPI_F32_ACC, 0, 0, BK, true>(a, s)

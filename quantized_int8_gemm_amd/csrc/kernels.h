@@ -72,8 +72,9 @@ hipError_t launch_dma_128x128s3(const Int8GemmArgs& a, bool bkm, int epi, int zp
 hipError_t launch_dma_256x256w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x128w8(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_128x128k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
-// The same tile split over K (A8W8 only; a.splits, a.split_steps, a.workspace).
-hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, hipStream_t s);
+// The same tile with three stages, split over K when a.splits > 1 (a.splits,
+// a.split_steps, a.workspace): A8W8, or MatMulInteger (epi EPI_I32, zp sums).
+hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x128w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 

@@ -62,6 +62,13 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 2048, 4096, 8192) == 0    # 512 tiles fill the chip
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 0
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 8, 512, 2048, 2048) == 0
+    # MatMulInteger splits like A8W8, each partial tile followed by its row
+    # and column sums (8 KiB); batches are folded into M
+    mmi_split = 1024 + 64 * 4 * (128 * 128 * 4 + 8192)
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 64, 8192, 8192) == mmi_split
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 4, 16, 8192, 8192) == mmi_split
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 64, 8192, 1024) == 0
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 0, 64, 8192, 8192) == 0
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 0, 8192, 8192) == 0
     # DynamicQuantizeLinear: one (min, max) float pair per 128 KiB of x, at most 2 KiB
     assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 0, 1) == 8
@@ -133,6 +140,15 @@ def test_a8w8_split_k_workspace_too_small():
     need = q.workspace_bytes(q.QG_OP_A8W8, 1, M, N, K)
     st = a8w8(M=M, N=N, K=K, lda=K, ldw=N, ldo=N, n_a=M, n_w=N, ws=FAKE, wsb=need - 1)
     assert st == b.QG_ERR_WORKSPACE
+
+
+def test_matmul_integer_split_k_workspace_checks():
+    M, N, K = 64, 8192, 8192
+    need = q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, M, N, K)
+    kw = dict(M=M, N=N, K=K, lda=K, ldb=N, ldy=N, ybs=M * N, ws=FAKE)
+    assert mmi(wsb=need - 1, **kw) == b.QG_ERR_WORKSPACE
+    kw["ws"] = ctypes.c_void_p(4096 + 16)   # not 256-byte aligned
+    assert mmi(wsb=need, **kw) == b.QG_ERR_INVALID_ARGUMENT
 
 
 def test_a8w8_workspace_too_small():

@@ -24,6 +24,16 @@
 //    gives the same bits), runs the epilogue once and resets the ticket.
 // Rows past M and bytes past K read as zero through the buffer range checks
 // (or meet zero weight rows), so they add nothing.
+//
+// The same kernel computes MatMulInteger ("feat(onnx-to-hip): lower quantized
+// integer conv and matmul", section "What", MatMulInteger) for M <= 16 with B
+// as [K,N] and K a multiple of 64 (EPI_I32): uint8 operands are flipped to
+// int8 - 128 as they are multiplied, each lane also takes the row sums of its
+// A fragments and the column sums of its transposed weight block (v_dot4),
+// those sums travel with the partial tiles, and the epilogue applies
+// Y = acc + cb[n] * rowsum[m] + ca[m] * (colsum[n] + K * cb[n]) in wrapping
+// int32 arithmetic.  Steps past K are masked (their flips and A bytes
+// zeroed), so only the K rows of both operands reach the sums.
 #include <mutex>
 
 #include "device_common.h"
@@ -61,11 +71,24 @@ __device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
     }
 }
 
+// MatMulInteger's sums do not fit beside two waves per SIMD; its grid gives
+// one workgroup per CU anyway.
 template <bool VEC, int EPI>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I32 ? 1 : 2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
+    constexpr bool I32 = EPI == EPI_I32;
+    // A split's partial: 16 rows of the tile, then (MatMulInteger) a row of
+    // column sums and a row whose first 16 entries are the row sums.
+    constexpr int SLOT_ROWS = I32 ? 18 : 16;
     __shared__ __attribute__((aligned(16))) int32_t red[WAVES][16][TN];
-    __shared__ float ws_tile[TN];
-    __shared__ float as_rows[16];
+    __shared__ float ws_tile[I32 ? 1 : TN];
+    __shared__ float as_rows[I32 ? 1 : 16];
+    // MatMulInteger: per-wave sums, the tile's totals, cb[n] and ca[m]
+    __shared__ __attribute__((aligned(16))) int32_t cs_red[I32 ? WAVES : 1][I32 ? TN : 4];
+    __shared__ int32_t rs_red[I32 ? WAVES : 1][16];
+    __shared__ __attribute__((aligned(16))) int32_t cs_tot[I32 ? TN : 4];
+    __shared__ __attribute__((aligned(16))) int32_t rs_tot[16];
+    __shared__ int32_t cb_tile[I32 ? TN : 1];
+    __shared__ int32_t ca_rows[I32 ? 16 : 1];
     __shared__ int ticket;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -85,10 +108,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     const uint32_t w_voff = (uint32_t)(16 * g * ldb + 16 * c16);
     const uint32_t a_voff = (uint32_t)(c16 * lda + 16 * g);
 
-    // The epilogue's scales, loaded now so their latency hides behind the
-    // weight stream.
-    if (tid < TN) ws_tile[tid] = (n0 + tid < p.N) ? p.weight_scale[(n0 + tid) * p.ws_stride] : 0.f;
-    if (tid < 16) as_rows[tid] = (tid < p.M) ? p.act_scale[tid * p.as_stride] : 0.f;
+    // The epilogue's scales (MatMulInteger: zero-point terms), loaded now so
+    // their latency hides behind the weight stream.
+    if constexpr (I32) {
+        if (tid < TN) {
+            const int n = n0 + tid;
+            int zb = 0;
+            if (p.b_zp != nullptr && n < p.N)
+                zb = p.b_zp_u8 ? (int)static_cast<const uint8_t*>(p.b_zp)[n * p.b_zp_stride]
+                               : (int)static_cast<const int8_t*>(p.b_zp)[n * p.b_zp_stride];
+            cb_tile[tid] = n < p.N ? p.sb - zb : 0;
+        }
+        if (tid < 16) {
+            int ca = p.ca;
+            if (p.a_zp != nullptr) {
+                const int i = (tid % p.a_zp_rows) * p.a_zp_stride;
+                ca = p.sa - (p.a_zp_u8 ? (int)static_cast<const uint8_t*>(p.a_zp)[i]
+                                       : (int)static_cast<const int8_t*>(p.a_zp)[i]);
+            }
+            ca_rows[tid] = tid < p.M ? ca : 0;
+        }
+    } else {
+        if (tid < TN) ws_tile[tid] = (n0 + tid < p.N) ? p.weight_scale[(n0 + tid) * p.ws_stride] : 0.f;
+        if (tid < 16) as_rows[tid] = (tid < p.M) ? p.act_scale[tid * p.as_stride] : 0.f;
+    }
 
     u32x4 wbuf[2][16];
     u32x4 abuf[2];
@@ -130,6 +173,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     v4i acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = v4i{0, 0, 0, 0};
+    // MatMulInteger: this lane's sums of A row c16 and of weight columns
+    // 16 c16 + j over the k rows it multiplies (after the flips).
+    int rs = 0;
+    int cs[I32 ? 16 : 1];
+#pragma unroll
+    for (int j = 0; j < (I32 ? 16 : 1); ++j) cs[j] = 0;
+    const int nsteps = (p.K + KS - 1) / KS;
 
     // This wave's steps: s_begin + wave + WAVES*i, i < n_my.  Every split
     // spans a multiple of 2*WAVES steps (steps past K read as zeros and add
@@ -139,10 +189,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     // peeled so that nothing is fetched past the wave's range.
     const int first = s_begin + wave;
     const int n_my = per / WAVES;
-    auto consume = [&](int b) {
+    auto consume = [&](int b, int step) {
+        if constexpr (I32) {
+            // a step past K multiplies nothing: no flips, A bytes cleared
+            // (those of rows < M - 1 would be the next row's)
+            const bool live = step < nsteps;
+            const uint32_t fa = live ? p.a_flip : 0u, fb = live ? p.b_flip : 0u;
+            if (!live) abuf[b] = u32x4{0u, 0u, 0u, 0u};
+            abuf[b] = u32x4{abuf[b].x ^ fa, abuf[b].y ^ fa, abuf[b].z ^ fa, abuf[b].w ^ fa};
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                wbuf[b][r] = u32x4{wbuf[b][r].x ^ fb, wbuf[b][r].y ^ fb, wbuf[b][r].z ^ fb, wbuf[b][r].w ^ fb};
+            rs = sum_i8x4(abuf[b].w, sum_i8x4(abuf[b].z, sum_i8x4(abuf[b].y, sum_i8x4(abuf[b].x, rs))));
+        }
         transpose16x16_inplace(wbuf[b]);
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[j] = mfma_i8_16x16x64(abuf[b], wbuf[b][j], acc[j]);
+        if constexpr (I32) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                cs[j] = sum_i8x4(wbuf[b][j].w, sum_i8x4(wbuf[b][j].z, sum_i8x4(wbuf[b][j].y, sum_i8x4(wbuf[b][j].x, cs[j]))));
+        }
     };
     // Scheduling barriers keep each fetch's loads together, so that waiting
     // for one buffer never waits for the other buffer's loads.
@@ -150,18 +217,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     __builtin_amdgcn_sched_barrier(0);
     fetch(first + WAVES, 1);
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; i + 2 < n_my; i += 2) {
-        consume(0);
+    int i = 0;
+    for (; i + 2 < n_my; i += 2) {
+        consume(0, first + WAVES * i);
         __builtin_amdgcn_sched_barrier(0);
         fetch(first + WAVES * (i + 2), 0);
         __builtin_amdgcn_sched_barrier(0);
-        consume(1);
+        consume(1, first + WAVES * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
         fetch(first + WAVES * (i + 3), 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    consume(0);
-    consume(1);
+    consume(0, first + WAVES * i);
+    consume(1, first + WAVES * (i + 1));
 
     // Add the four waves' tiles through LDS.  Register r of MFMA j holds
     // row 4g + r, column 16*c16 + j, so for each r a lane owns 16 consecutive
@@ -179,7 +247,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
             *reinterpret_cast<v4i*>(&red[wave][4 * g + r][4 * chunk(4 * c16 + q)]) = v;
         }
     }
+    if constexpr (I32) {
+        // the four lane groups held different k rows: add them, then each
+        // wave leaves its sums in LDS
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            cs[j] += __shfl_xor(cs[j], 16);
+            cs[j] += __shfl_xor(cs[j], 32);
+        }
+        if (g == 0) {
+            rs_red[wave][c16] = rs;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<v4i*>(&cs_red[wave][16 * c16 + 4 * q]) =
+                    v4i{cs[4 * q], cs[4 * q + 1], cs[4 * q + 2], cs[4 * q + 3]};
+        }
+    }
     __syncthreads();
+    if constexpr (I32) {
+        // this workgroup's sums over its k range
+        if (tid < TN) {
+            uint32_t t = 0u;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) t += (uint32_t)cs_red[w][tid];
+            cs_tot[tid] = (int)t;
+        }
+        if (tid < 16) {
+            uint32_t t = 0u;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) t += (uint32_t)rs_red[w][tid];
+            rs_tot[tid] = (int)t;
+        }
+        __syncthreads();
+    }
 
     // Items: (row m < M, group of 4 columns); each thread takes some.
     auto tile_sum = [&](int m, int cg) -> int4 {
@@ -238,12 +340,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
             else reinterpret_cast<uint16_t*>(p.out)[o + e] = f32_to_bf16_rne(f[e]);
         }
     };
+    // MatMulInteger: Y = acc + cb[n] * rowsum[m] + ca[m] * (colsum[n] + K * cb[n]),
+    // wrapping, from the tile's totals in LDS.
+    const bool vec_y = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
+    auto epilogue_i32 = [&](int m, int n, int4 v) {
+        if (n >= p.N) return;
+        const uint32_t ca = (uint32_t)ca_rows[m], rsm = (uint32_t)rs_tot[m];
+        const int32_t vi[4] = {v.x, v.y, v.z, v.w};
+        int32_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = (n - n0 + e) & (TN - 1);
+            const uint32_t cb = (uint32_t)cb_tile[c];
+            y[e] = (int32_t)((uint32_t)vi[e] + cb * rsm + ca * ((uint32_t)cs_tot[c] + (uint32_t)p.K * cb));
+        }
+        int32_t* dst = reinterpret_cast<int32_t*>(p.out) + (int64_t)m * p.ldo + n;
+        if (vec_y && n + 4 <= p.N) {
+            *reinterpret_cast<int4*>(dst) = int4{y[0], y[1], y[2], y[3]};
+            return;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) dst[e] = y[e];
+    };
+    auto finish = [&](int m, int n, int4 v) {
+        if constexpr (I32) epilogue_i32(m, n, v);
+        else epilogue(m, n, v);
+    };
     const int items = M * (TN / 4);
 
     if (S == 1) {
         for (int it = tid; it < items; it += NT) {
             const int m = it / (TN / 4), cg = it % (TN / 4);
-            epilogue(m, n0 + cg * 4, tile_sum(m, cg));
+            finish(m, n0 + cg * 4, tile_sum(m, cg));
         }
         return;
     }
@@ -262,16 +391,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
     // before the barrier, and the barrier orders them before thread 0's
     // ticket; no cache-wide writeback or invalidate is needed.
     int* tickets = reinterpret_cast<int*>(p.workspace);
-    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tn * S * 16 * TN * 4;
-    // Partial tile of split s: rows m < M of [16][TN] int32, as 16-byte
-    // vectors through a buffer resource with device-coherent cache policy.
-    const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * 16 * TN * 4));
+    constexpr int SLOT = SLOT_ROWS * TN * 4;
+    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tn * S * SLOT;
+    // Partial of split s: rows m < M of [16][TN] int32 (MatMulInteger: then
+    // the column sums and the row sums), as 16-byte vectors through a buffer
+    // resource with device-coherent cache policy.
+    const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
     constexpr int COHERENT = 16;  // sc1: device scope, bypass the XCD-private cache level
     for (int it = tid; it < items; it += NT) {
         const int m = it / (TN / 4), cg = it % (TN / 4);
         const int4 s4 = tile_sum(m, cg);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, s4), p_rsrc,
-                                               ((split * 16 + m) * TN + cg * 4) * 4, 0, COHERENT);
+                                               (uint32_t)(split * SLOT + (m * TN + cg * 4) * 4), 0, COHERENT);
+    }
+    // MatMulInteger sums: 64 vectors of column sums (row 16), 4 of row sums (row 17)
+    constexpr int SUM_ITEMS = TN / 4 + 4;
+    auto sums_off = [&](int it) { return (uint32_t)((it < TN / 4 ? 16 * TN + 4 * it : 17 * TN + 4 * (it - TN / 4)) * 4); };
+    if constexpr (I32) {
+        if (tid < SUM_ITEMS) {
+            const int32_t* src = tid < TN / 4 ? &cs_tot[4 * tid] : &rs_tot[4 * (tid - TN / 4)];
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4i*>(src), p_rsrc,
+                                                   (uint32_t)(split * SLOT) + sums_off(tid), 0, COHERENT);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -293,28 +434,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void a8
         // an item past M reads past the buffer (zeros) and is not stored
         off[i] = it < items ? (uint32_t)((m * TN + cg * 4) * 4) : 0xFFFFFFF0u;
     }
+    // MatMulInteger: threads below SUM_ITEMS also add one vector of sums
+    v4i ssum = v4i{0, 0, 0, 0};
+    const uint32_t soff = (I32 && tid < SUM_ITEMS) ? sums_off(tid) : 0xFFFFFFF0u;
+    auto add4 = [](v4i a, v4i b) {
+        return v4i{(int)((uint32_t)a.x + (uint32_t)b.x), (int)((uint32_t)a.y + (uint32_t)b.y),
+                   (int)((uint32_t)a.z + (uint32_t)b.z), (int)((uint32_t)a.w + (uint32_t)b.w)};
+    };
     for (int s0 = 0; s0 < S; s0 += SU) {
         v4i v[IPT][SU];
 #pragma unroll
         for (int i = 0; i < IPT; ++i)
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
-                const uint32_t o = off[i] == 0xFFFFFFF0u ? off[i] : off[i] + (uint32_t)((s0 + u) * 16 * TN * 4);
+                const uint32_t o = off[i] == 0xFFFFFFF0u ? off[i] : off[i] + (uint32_t)((s0 + u) * SLOT);
                 v[i][u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o, 0, COHERENT));
             }
+        v4i w[I32 ? SU : 1];
+        if constexpr (I32) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const uint32_t o = soff == 0xFFFFFFF0u ? soff : soff + (uint32_t)((s0 + u) * SLOT);
+                w[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o, 0, COHERENT));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < IPT; ++i)
 #pragma unroll
-            for (int u = 0; u < SU; ++u)
-                sum[i] = v4i{(int)((uint32_t)sum[i].x + (uint32_t)v[i][u].x), (int)((uint32_t)sum[i].y + (uint32_t)v[i][u].y),
-                             (int)((uint32_t)sum[i].z + (uint32_t)v[i][u].z), (int)((uint32_t)sum[i].w + (uint32_t)v[i][u].w)};
+            for (int u = 0; u < SU; ++u) sum[i] = add4(sum[i], v[i][u]);
+        if constexpr (I32) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) ssum = add4(ssum, w[u]);
+        }
+    }
+    if constexpr (I32) {
+        // the totals over all splits replace this split's own in LDS
+        if (tid < SUM_ITEMS) *reinterpret_cast<v4i*>(tid < TN / 4 ? &cs_tot[4 * tid] : &rs_tot[4 * (tid - TN / 4)]) = ssum;
+        __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const int it = tid + i * NT;
         if (it >= items) continue;
         const int m = it / (TN / 4), cg = it % (TN / 4);
-        epilogue(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w});
+        finish(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w});
     }
     if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -361,11 +524,11 @@ hipError_t skinny_scratch(hipStream_t s, void** ptr) {
     return hipSuccess;
 }
 
-size_t skinny_workspace_bytes(int M, int N, int splits) {
+size_t skinny_workspace_bytes(int M, int N, int splits, bool sums) {
     (void)M;
     if (splits <= 1) return 0;
     const size_t tiles_n = (size_t)(N + TN - 1) / TN;
-    return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * 16 * TN * 4;
+    return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * (sums ? 18 : 16) * TN * 4;
 }
 
 // Steps (64 k-rows) per split: a multiple of 2*WAVES, chosen so that about
@@ -391,10 +554,14 @@ int skinny_splits(int M, int N, int K) {
 
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s, const char** name) {
     dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
-    *name = "a8w8_skinny";
+    *name = epi == EPI_I32 ? "matmul_integer_skinny" : "a8w8_skinny";
     if (a.split_steps % (2 * WAVES) != 0 || (int64_t)a.split_steps * grid.y * KS < a.K) return hipErrorInvalidValue;
     if (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)) return hipErrorInvalidValue;
-    if (vec) {
+    if (a.M > 16 || a.batch != 1) return hipErrorInvalidValue;
+    if (epi == EPI_I32) {   // 16-byte rows, B as [K,N], whole 64-row steps
+        if (!vec || a.K % KS != 0 || (a.a_zp != nullptr && a.a_zp_rows < 1)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_I32>), grid, dim3(NT), 0, s, a);
+    } else if (vec) {
         if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32>), grid, dim3(NT), 0, s, a);
         else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16>), grid, dim3(NT), 0, s, a);
     } else {

@@ -298,6 +298,12 @@ static size_t a8w8_tiled_split_bytes(int64_t M, int64_t N, int splits) {
     return qg::SKINNY_TICKET_BYTES + tiles * (size_t)splits * 128 * 128 * 4;
 }
 
+// MatMulInteger rows (batches folded) that the decode kernel takes when a
+// workspace is given: at most 16, over whole 64-row steps of K.
+static bool mmi_is_skinny(int64_t M, int64_t K) {
+    return a8w8_is_skinny(M, 0) && K % 64 == 0;
+}
+
 // MatMulInteger's split partials: the tile plus each lane's row and column
 // sums (4 + 4 ints for 64x64 waves: 8 KiB per 128x128 tile).
 static size_t mmi_tiled_split_bytes(int64_t M, int64_t N, int splits) {
@@ -312,6 +318,11 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
         // sized for the batch folded into M (contiguous A / Y batches, shared B)
         if (batch < 1 || batch >= 65536 || !dims_ok(M, N, K) || batch * M >= ((int64_t)1 << 30)) return 0;
         int splits, steps;
+        if (mmi_is_skinny(batch * M, K)) {
+            a8w8_skinny_plan(batch * M, N, K, &splits, &steps);
+            return qg::skinny_workspace_bytes((int)(batch * M), (int)N, splits, true);
+        }
+        if (K % 128 != 0) return 0;   // the split kernel's sums need whole 128-byte stages
         a8w8_tiled_split_plan(batch * M, N, K, 8, &splits, &steps);
         return mmi_tiled_split_bytes(batch * M, N, splits);
     }
@@ -586,6 +597,22 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
     const int zp = (need_rowsum ? 1 : 0) | (need_colsum ? 2 : 0);
     const bool vec = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 && K % 16 == 0 &&
                      N % 16 == 0 && (a.batch == 1 || (a_batch_stride % 16 == 0 && b_batch_stride % 16 == 0));
+    // At most 16 rows with a workspace: the decode kernel, which streams B
+    // once with K split across workgroups (its row and column sums travel
+    // with the partial tiles).
+    if (a.batch == 1 && vec && workspace != nullptr && mmi_is_skinny(a.M, K)) {
+        int splits, per;
+        a8w8_skinny_plan(a.M, N, K, &splits, &per);
+        if (qg::skinny_workspace_bytes(a.M, (int)N, splits, true) > workspace_bytes) return QG_ERR_WORKSPACE;
+        a.workspace = workspace;
+        a.splits = splits;
+        a.split_steps = per;
+        const char* name = "";
+        (void)hipGetLastError();
+        const hipError_t e = qg::launch_a8w8_skinny(a, true, qg::EPI_I32, (hipStream_t)stream, &name);
+        log_dispatch("matmul_integer", name, 1, a.M, N, K, splits);
+        return finish_launch(e, name);
+    }
     const int cfg = pick_tile(a.batch, a.M, N);
     // Few output tiles and a long K: the three-stage kernel, K split across
     // workgroups (partial tiles and row / column sums in the workspace) when

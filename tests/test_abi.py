@@ -69,6 +69,11 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 4, 16, 8192, 8192) == mmi_split
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 64, 8192, 1024) == 0
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 0, 64, 8192, 8192) == 0
+    # at most 16 rows: the decode kernel's partials, 16 output rows plus a row
+    # of column sums and one of row sums per split and 256-column tile
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 1, 8192, 8192) == 1024 + 32 * 8 * 18 * 256 * 4
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 4, 4, 8192, 8192) == 1024 + 32 * 8 * 18 * 256 * 4
+    assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 16, 8192, 8160) == 0   # K not whole 64-row steps
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 0, 8192, 8192) == 0
     # DynamicQuantizeLinear: one (min, max) float pair per 128 KiB of x, at most 2 KiB
     assert q.workspace_bytes(q.QG_OP_DYNAMIC_QUANTIZE_LINEAR, 1, 1, 0, 1) == 8

@@ -4,7 +4,7 @@ Headline: A8W8 8192 x 8192 x 8192 (int8 x int8 -> int32 -> fp32 scales ->
 bf16), throughput in tera int8 ops per second, with inputs resident in HBM.
 One step is one call of the operator on that batch.  The same run also times
 the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
-K = N = 8192 in GB/s, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
+K = N = 8192 in GB/s, MatMulInteger at M = 1 and 16 likewise, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
 at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
 points, the W8A32 input gradient at 4096^3, DynamicQuantizeLinear on the
@@ -342,6 +342,12 @@ def cpu_oracle_rows(rows, si):
             dt = timed(lambda: oracle.a8w8(A, W, s_a, s_w))
             attach(name, dt, ops=2.0 * m * 8192 * 8192,
                    nbytes=m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192)
+    for m in (1, 16):
+        name = f"matmul_integer_decode_m{m}_8192"
+        if name in rows:
+            A, B, zb = si.matmul_integer_inputs(1, m, 8192, 8192, seed=450 + m)
+            dt = timed(lambda: oracle.matmul_integer(A[0], B, 128, zb))
+            attach(name, dt, ops=2.0 * m * 8192 * 8192, nbytes=m * 8192 + 8192 * 8192 + 8192 + 4 * m * 8192)
     mmi_ops = 2.0 * 8 * 512 * 2048 * 2048
     mmi_bytes = 8 * 512 * 2048 + 2048 * 2048 + 2048 + 4 * 8 * 512 * 2048
     if "matmul_integer_8x512x2048x2048" in rows:
@@ -487,6 +493,23 @@ def main():
                                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
                                                    "us_eager": ms_eager * 1e3, "per_call": spread}
             del sets, base_w, ws
+        # MatMulInteger at decode shapes (uint8 activations with zero point
+        # 128, int8 weight with per-column zero points), same rotation
+        for m in (1, 16):
+            A, B, zb = si.matmul_integer_inputs(1, m, 8192, 8192, seed=450 + m)
+            base_b, tzb = to(B), to(zb)
+            sets = [(to(A[0]), base_b if r == 0 else base_b.clone(),
+                     torch.empty((m, 8192), dtype=torch.int32, device=dev)) for r in range(9)]
+            ws = torch.zeros(q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, m, 8192, 8192), dtype=torch.uint8,
+                             device=dev)
+            call = lambda s: q.matmul_integer(s[0], s[1], 128, tzb, out=s[2], workspace=ws)
+            ms, spread = time_graph(call, sets, 36, max(steps // 2, 5), stream, spread=True)
+            nbytes = m * 8192 + 8192 * 8192 + 8192 + 4 * m * 8192
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rows[f"matmul_integer_decode_m{m}_8192"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
+                                                        "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
+                                                        "per_call": spread}
+            del sets, base_b, ws
 
     progress(f"GPU rows so far: {sorted(rows)}")
     # ---- MatMulInteger 8 x 512 x 2048 x 2048, shared B -------------------
@@ -696,7 +719,7 @@ def main():
                             "kernels' instruction) on random / all-one operands, and with v_mfma_i32_32x32x32_i8 "
                             "on the random operands; fp32 and bf16 matrix-core loops on operands uniform in [-1, 1)"}
         for name, r in rows.items():
-            if "GB/s" in r and "frac_hbm_peak" in r and name.startswith("a8w8_decode"):
+            if "GB/s" in r and "frac_hbm_peak" in r and "_decode_" in name:
                 r["frac_hbm_read_ceiling"] = r["GB/s"] / hbm
             if "TOPS" in r:
                 r["frac_mfma_random_ceiling"] = r["TOPS"] / mf["random"]

@@ -246,15 +246,18 @@ qg_status qgemm_a8w8_acc(int64_t M, int64_t N, int64_t K,
  *   workspace: NULL, or device memory of at least
  *     qgemm_workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K) bytes,
  *     256-byte aligned (else QG_ERR_INVALID_ARGUMENT), zero-filled before
- *     its first use.  An output of at most 128 tiles of 128 x 128 (batches
- *     folded into M) whose K allows two or more splits of at least 1024
- *     splits K across workgroups: the first 1024 bytes hold one ticket per
- *     output tile, the rest each split's exact int32 partial tile with its
- *     partial row and column sums.  Tickets return to zero when a call
+ *     its first use.  With batches folded into M: at most 16 rows with K a
+ *     multiple of 64 run the decode kernel (B streamed once, K split across
+ *     workgroups; one ticket per 256 output columns); other outputs of at
+ *     most 128 tiles of 128 x 128 whose K allows two or more splits of at
+ *     least 1024 split K on the tiled kernel (one ticket per output tile).
+ *     The first 1024 bytes hold the tickets, the rest each split's exact
+ *     int32 partial tile with its partial row and column sums.  Tickets return to zero when a call
  *     completes, so one workspace serves later calls on the same stream of
  *     any shape; calls that overlap in time must not share one.  With NULL
- *     the same kernel runs unsplit; QG_ERR_WORKSPACE when a workspace is
- *     given but smaller than the split needs.
+ *     the tiled kernel runs unsplit (also for decode shapes);
+ *     QG_ERR_WORKSPACE when a workspace is given but smaller than the split
+ *     needs.
  * Requires batch, M, N, K >= 1.  QG_ERR_UNSUPPORTED: an operand byte span
  * that reaches 2^31.  (Per-row activation zero points: matmul_integer_row_zp.
  * Ranks outside 2-4 are rejected by the Python binding, which maps ONNX

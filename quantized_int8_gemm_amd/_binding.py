@@ -332,7 +332,7 @@ def _batch_view(t, name, batch_shape):
     return t.shape[-2] * t.shape[-1]
 
 
-def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
+def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None, workspace=None):
     """ONNX MatMulInteger: int32 wrap(sum_k (A - a_zp) * (B - b_zp)).
 
     A: uint8/int8 of rank 2-4, [..., M, K]; B: uint8/int8 of rank 2-4,
@@ -341,7 +341,10 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
     reused.  a_zero_point: scalar of A's range, or a tensor of A's dtype
     with M per-row values ([M] or [M, 1]; calls matmul_integer_row_zp);
     b_zero_point: None, scalar, [N] or [..., 1, N] per-column values of B's
-    dtype.  Returns int32 [*batch, M, N].
+    dtype.  Returns int32 [*batch, M, N].  workspace: None (a cached,
+    zeroed buffer per device and stream) or a zero-filled uint8 tensor of at
+    least workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K) bytes, which
+    calls on one stream may share.
     """
     _need(A, (torch.uint8, torch.int8), "A")
     _need(B, (torch.uint8, torch.int8), "B")
@@ -391,7 +394,11 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
         _need(out, (torch.int32,), "out")
         if tuple(out.shape) != tuple(batch_shape) + (M, N) or not out.is_contiguous():
             raise ValueError("out has the wrong shape or is not contiguous")
-    ws = _workspace(dev, workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K))
+    if workspace is None:
+        ws = _workspace(dev, workspace_bytes(QG_OP_MATMUL_INTEGER, batch, M, N, K))
+    else:
+        _need(workspace, (torch.uint8, torch.int8), "workspace")
+        ws = workspace
     wsz = 0 if ws is None else ws.numel()
     if za_rows is None:
         st = lib.matmul_integer(batch, M, N, K,
@@ -410,12 +417,12 @@ def matmul_integer(A, B, a_zero_point=0, b_zero_point=None, out=None):
     return out
 
 
-def matmul_integer_row_zp(A, B, a_zero_point, b_zero_point=None, out=None):
+def matmul_integer_row_zp(A, B, a_zero_point, b_zero_point=None, out=None, workspace=None):
     """MatMulInteger with one activation zero point per row of A
     (a_zero_point: [M] or [M, 1] of A's dtype); see matmul_integer."""
     if not isinstance(a_zero_point, torch.Tensor) or a_zero_point.dim() == 0:
         raise ValueError("a_zero_point must be a tensor of M per-row values")
-    return matmul_integer(A, B, a_zero_point, b_zero_point, out)
+    return matmul_integer(A, B, a_zero_point, b_zero_point, out, workspace)
 
 
 # ---------------------------------------------------------------------------

@@ -169,7 +169,7 @@ def parse():
     ap.add_argument("--write-db")
     ap.add_argument("--copy-fetch-db")
     ap.add_argument("--copy-write-db")
-    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 2, false, 1, 0, 0, 128>")
+    ap.add_argument("--kernel-match", default="int8_dma_kernel<256, 256, 128, 64, 2, false, 1, 0, 0, 128, false>")
     ap.add_argument("--workload", default="a8w8_prefill_8192x8192x8192_bf16",
                     help="--pmc-summary: the workload the counters were taken on")
     ap.add_argument("--sources", default=None,

@@ -64,14 +64,21 @@ bool empty_output(int64_t rows, int64_t cols, int64_t inner, int64_t batch = 1) 
 int pick_tile(int64_t batch, int64_t M, int64_t N) {
     const int forced = env_int("QGEMM_TILE", -1);
     if (forced >= 0 && forced < qg::NUM_TILE_CFGS) return forced;
-    // 256x256 tiles (eight waves, 128-byte k stages) once there are at least
-    // two full waves of them; measured best for 8192^3 (3-4 % ahead of the
-    // same tile with 64-byte stages).  Otherwise 128x128 tiles with 128-byte
-    // k stages, two workgroups per compute unit (best for 4096x2048x2048 and
-    // smaller).  Either falls back to its 64-byte-stage sibling where K is not
-    // whole 128-byte stages and bytes past K would reach a sum.
+    // 256x256 tiles (eight waves, 128-byte k stages, one workgroup per
+    // compute unit) from 160 of them on; measured best for 8192^3 (3-4 %
+    // ahead of the same tile with 64-byte stages) and, A8W8 bf16 event-timed,
+    // for one round of 160-256 tiles (2560x4096x4096 47.6 against 54.1 us on
+    // 128x128 tiles, 4096^3 59.3 / 73.1, 2048x8192x8192 109.2 / 135.5,
+    // 4096x4096x1024 22.1 / 23.4) and for 384-511 (6144x4096x4096 100.2 /
+    // 108.1).  A second round at most 3/8 full loses (5120x4096x4096, 320
+    // tiles: 97.1 against 92.6 us), as does a first round of at most 128
+    // tiles (2048x4096x4096: 48.0 / 38.2).  Otherwise 128x128 tiles with
+    // 128-byte k stages, two workgroups per compute unit (best for
+    // 4096x2048x2048 and smaller).  Either falls back to its 64-byte-stage
+    // sibling where K is not whole 128-byte stages and bytes past K would
+    // reach a sum.
     const int64_t t256 = batch * ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= 512) return qg::TILE_256x256_W8_K128;
+    if (t256 >= 512 || (t256 >= 160 && !(t256 > 256 && t256 <= 352))) return qg::TILE_256x256_W8_K128;
     return qg::TILE_128x128_K128;
 }
 

@@ -227,3 +227,35 @@ def test_a8w8_k128_stages_partial_last_chunk_and_fallback(tile):
         assert q.last_kernel().endswith("k128"), q.last_kernel()
         check(A, np.ascontiguousarray(W.T), s_a, s_w, b_trans=True, expect_kernel="int8_dma")
         assert not q.last_kernel().endswith("k128"), q.last_kernel()
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (2560, 4096, 256, "int8_dma_256x256w8k128"),   # 160 tiles of 256x256: one round of them
+    (3000, 4000, 384, "int8_dma_256x256w8k128"),   # 12 x 16 = 192 tiles, ragged in M and N
+    (5120, 4096, 128, "int8_dma_128x128k128"),     # 320: a second round at most 3/8 full
+    (2048, 4096, 256, "int8_dma_128x128k128"),     # 128: half a round
+])
+def test_a8w8_tile_choice_by_tile_count(M, N, K, kernel):
+    """The 256x256 tile is chosen by its tile count; every output of each
+    choice against the oracle."""
+    case(f"a8w8 tile choice M={M} N={N} K={K}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K + 3)
+    check(A, W, s_a, s_w, expect_kernel=kernel)
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (2560, 4096, 256, "int8_dma_256x256w8k128"),
+    (5120, 4096, 128, "int8_dma_128x128k128"),
+])
+def test_matmul_integer_tile_choice_by_tile_count(M, N, K, kernel):
+    """MatMulInteger (uint8 A with a per-row zero point, per-column weight
+    zero points: both sums) on the same tile choice."""
+    case(f"matmul_integer tile choice M={M} N={N} K={K}")
+    g = si.rng(M + K)
+    A = si.randint(g, (M, K), 0, 255, np.uint8)
+    B = si.randint(g, (K, N), -128, 127, np.int8)
+    za = si.randint(g, (M,), 0, 255, np.uint8)
+    zb = si.randint(g, (N,), -128, 127, np.int8)
+    y = q.matmul_integer(to_dev(A), to_dev(B), to_dev(za), to_dev(zb))
+    assert q.last_kernel() == kernel, q.last_kernel()
+    np.testing.assert_array_equal(y.cpu().numpy(), oracle.matmul_integer(A, B, za, zb))

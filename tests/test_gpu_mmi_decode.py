@@ -67,6 +67,14 @@ def test_matmul_integer_decode_folded_batches():
     check(A, B, 128, vals(g, 4096, np.int8))
 
 
+def test_matmul_integer_decode_folded_batches_per_row_zero_points():
+    """Per-row zero points of a [4, 4, K] activation: after the fold, row m of
+    the 16 takes zero point m % 4."""
+    case("matmul_integer decode batch 4x4x2048x4096 per-row zp")
+    g, A, B = operands(4, 4096, 2048, np.uint8, np.uint8, seed=804, batch=4)
+    check(A, B, vals(g, 4, np.uint8), vals(g, 4096, np.uint8))
+
+
 @pytest.mark.parametrize("splits", [3, 16, 64])
 def test_matmul_integer_decode_forced_splits(splits):
     case(f"matmul_integer decode forced splits={splits} 5x2048x8192")

@@ -69,6 +69,18 @@ def test_matmul_integer_split_k_folded_batches():
     check(A, B, 128, column_zp(g, 1024, np.int8), SPLITK)
 
 
+def test_matmul_integer_split_k_folded_batches_per_row_zero_points():
+    """Per-row zero points of a [3, 40, K] activation: after the fold, row m
+    of the 120 takes zero point m % 40."""
+    case("matmul_integer split-K batch 3x40x2048x4096 per-row zp")
+    g, A, B = operands(40, 2048, 4096, np.int8, np.int8, seed=703, batch=3)
+    check(A, B, vals_i8(g, 40), vals_i8(g, 2048), SPLITK)
+
+
+def vals_i8(g, n):
+    return si.randint(g, (n,), -128, 127, np.int8)
+
+
 @pytest.mark.parametrize("splits", [2, 3, 5, 8])
 def test_matmul_integer_split_k_forced_counts(splits):
     case(f"matmul_integer split-K forced splits={splits} 96x2048x8192")

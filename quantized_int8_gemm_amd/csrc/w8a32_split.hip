@@ -348,11 +348,15 @@ hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool w
                               const char** name) {
     const bool vec = vec_a && vec_w;
     // 256 x 256 tiles (eight waves of 64 x 128, one workgroup per CU) when
-    // there are enough of them to give every CU one and 256 rows of A stay
-    // within the 32-bit buffer offsets; 128 x 128 otherwise.
+    // there are more than 128 of them and 256 rows of A stay within the
+    // 32-bit buffer offsets; 128 x 128 otherwise.  The small tiles run more
+    // workgroups per CU but take two rounds from 129 large-tile counts on:
+    // 3072^3 201.1 against 283.4 us, 2560x4096x4096 260.7 / 358.4,
+    // 3584x4096x4096 281.5 / 440.0; at 128 (2048x4096x4096, one round of
+    // small tiles) they win, 237.7 against 268.9.
     const int64_t big = ((int64_t)(a.M + 255) / 256) * ((a.N + 255) / 256);
     const bool span_ok = (256 * a.lda + a.K + 64) * 4 < ((int64_t)1 << 31);
-    if (big >= 256 && span_ok) {
+    if (big > 128 && span_ok) {
         *name = wt ? "w8a32_input_grad_bf16x3_256x256" : "w8a32_bf16x3_256x256";
         launch_tile<256, 256, 64, 128>(a, vec, wt, s);
     } else {

@@ -68,9 +68,9 @@ W8A32_PATHS = ("bf16x3", "fp32")
 
 def w8a32_kernel(path, rows, outs, grad=False):
     """Kernel name the library reports for a W8A32 call of `rows` x `outs`
-    outputs on `path` (256 x 256 split tiles once they give every CU one)."""
+    outputs on `path` (256 x 256 split tiles from 129 of them on)."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
-    tile = "256x256" if ((rows + 255) // 256) * ((outs + 255) // 256) >= 256 else "128x128"
+    tile = "256x256" if ((rows + 255) // 256) * ((outs + 255) // 256) > 128 else "128x128"
     return f"w8a32_input_grad_bf16x3_{tile}" if grad else f"w8a32_bf16x3_{tile}"
 

@@ -88,6 +88,17 @@ def test_w8a32_split_big_tiles_ragged():
         check(A, W, 0.01, 7, "bf16x3")
 
 
+@pytest.mark.parametrize("M,N", [(2560, 4096), (2048, 4096), (2100, 4000)])
+def test_w8a32_tile_choice_by_tile_count(M, N):
+    """2560 x 4096 (160 tiles of 256 x 256) and 2100 x 4000 (144 ragged ones)
+    take the 256 x 256 split tiles, 2048 x 4096 (128) the 128 x 128 ones;
+    every output within the bound."""
+    case(f"w8a32 tile choice M={M} N={N} K=160")
+    A, W = si.w8a32_inputs(M, N, 160, seed=M + N + 905)
+    with env(QGEMM_W8A32="bf16x3"):
+        check(A, W, 0.01, -4, "bf16x3")
+
+
 @pytest.mark.parametrize("zp", [0, 9])
 def test_w8a32_big_tiles_both_zero_point_forms(zp, path):
     """4096 x 4096 outputs over K = 96 (the split path's 256 x 256 tiles),

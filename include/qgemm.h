@@ -60,7 +60,8 @@ typedef enum {
 } qg_dtype;
 
 /* Operation ids for qgemm_workspace_bytes. */
-enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2, QG_OP_DYNAMIC_QUANTIZE_LINEAR = 3 };
+enum { QG_OP_W8A32 = 0, QG_OP_A8W8 = 1, QG_OP_MATMUL_INTEGER = 2, QG_OP_DYNAMIC_QUANTIZE_LINEAR = 3,
+       QG_OP_W8A32_INPUT_GRAD = 4 };
 
 /*
  * W8A32: fp32 activations times an int8 weight with a per-tensor scale and
@@ -98,6 +99,30 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
                       void* stream);
 
 /*
+ * qgemm_w8a32 with a workspace (same operation, arguments and accuracy;
+ * qgemm_w8a32 is this call with NULL / 0).  workspace: NULL, or device
+ * memory of at least qgemm_workspace_bytes(QG_OP_W8A32, 1, M, N, K) bytes,
+ * 256-byte aligned (else QG_ERR_INVALID_ARGUMENT), zero-filled before its
+ * first use.  An output of at most 128 tiles of 128 x 128 (e.g. M <= 256 at
+ * N = 8192) then divides K among up to 8 workgroups per tile: the first
+ * 1024 bytes hold one ticket per output tile, the rest each split's fp32
+ * partial tile and partial row sums.  The last split to finish adds the
+ * partials in split order, so results do not depend on timing and repeat
+ * bit for bit; they differ from the unsplit call's only in the order of the
+ * fp32 additions.  Tickets return to zero when a call completes, so one
+ * workspace serves later calls on the same stream of any shape; calls that
+ * overlap in time must not share one.  QG_ERR_WORKSPACE: a workspace smaller
+ * than the split needs.
+ */
+qg_status qgemm_w8a32_ws(int64_t M, int64_t N, int64_t K,
+                         const float* A, int64_t lda,
+                         const int8_t* W, int64_t ldw,
+                         float scale, int32_t zero_point,
+                         float* C, int64_t ldc,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Input gradient of the W8A32 matmul: the frozen int8 weight's second
  * consumer ("feat(PULPOpen): matmul that dequantises an int8 weight
  * in-kernel", intro; "perf(pulpopen/gap9): share L3 storage between
@@ -123,6 +148,20 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
                                  float scale, int32_t zero_point,
                                  float* dA, int64_t ldda,
                                  void* stream);
+
+/*
+ * qgemm_w8a32_input_grad with a workspace, sized by
+ * qgemm_workspace_bytes(QG_OP_W8A32_INPUT_GRAD, 1, M, N, K) with this call's
+ * M, N, K; it divides the sum over n as qgemm_w8a32_ws divides the sum over
+ * k (dA of at most 128 tiles of 128 x 128), with the same rules.
+ */
+qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K,
+                                    const float* dC, int64_t lddc,
+                                    const int8_t* W, int64_t ldw,
+                                    float scale, int32_t zero_point,
+                                    float* dA, int64_t ldda,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * A8W8 matmul with fused dequantisation ("Feature/a8w8 matmul dequant

@@ -34,6 +34,7 @@ from ._binding import (  # noqa: F401
     QG_OP_MATMUL_INTEGER,
     QG_OP_DYNAMIC_QUANTIZE_LINEAR,
     QG_OP_W8A32,
+    QG_OP_W8A32_INPUT_GRAD,
     QGemmError,
     calib_mfma_bf16,
     calib_mfma_f32,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 
 QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_UNSUPPORTED, QG_ERR_WORKSPACE, QG_ERR_HIP = range(5)
 QG_FP32, QG_BF16, QG_INT32, QG_INT8, QG_UINT8 = range(5)
-QG_OP_W8A32, QG_OP_A8W8, QG_OP_MATMUL_INTEGER, QG_OP_DYNAMIC_QUANTIZE_LINEAR = range(4)
+QG_OP_W8A32, QG_OP_A8W8, QG_OP_MATMUL_INTEGER, QG_OP_DYNAMIC_QUANTIZE_LINEAR, QG_OP_W8A32_INPUT_GRAD = range(5)
 
 _p, _i64, _i32, _int, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_size_t)
@@ -26,6 +26,8 @@ _p, _i64, _i32, _int, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 PROTOTYPES = {
     "qgemm_w8a32": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p], _int),
     "qgemm_w8a32_input_grad": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p], _int),
+    "qgemm_w8a32_ws": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p, _sz, _p], _int),
+    "qgemm_w8a32_input_grad_ws": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _f32, _i32, _p, _i64, _p, _sz, _p], _int),
     "qgemm_a8w8": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _int, _p, _i64, _p, _i64,
                     _p, _int, _i64, _p, _sz, _p], _int),
     "matmul_integer": ([_i64, _i64, _i64, _i64, _p, _int, _i64, _i64, _p, _int, _i64, _i64,
@@ -139,11 +141,14 @@ def _ptr(t):
 # W8A32
 # ---------------------------------------------------------------------------
 
-def qgemm_w8a32(A, W, scale, zero_point=0, out=None):
+def qgemm_w8a32(A, W, scale, zero_point=0, out=None, workspace=None):
     """C = A @ ((W - zero_point) * scale) with the dequantisation folded in.
 
     A: fp32 [M, K]; W: int8 [K, N]; scale: Python float (per tensor);
     zero_point: Python int (per tensor, default 0).  Returns fp32 [M, N].
+    workspace: None (a cached, zeroed buffer per device and stream) or a
+    zero-filled uint8 tensor of at least workspace_bytes(QG_OP_W8A32, 1, M,
+    N, K) bytes; it lets small outputs divide K among workgroups.
     """
     _need(A, (torch.float32,), "A")
     _need(W, (torch.int8,), "W")
@@ -160,19 +165,29 @@ def qgemm_w8a32(A, W, scale, zero_point=0, out=None):
         _need(out, (torch.float32,), "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    st = lib.qgemm_w8a32(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"),
-                         float(scale), int(zero_point), _ptr(out), _rows(out, "out"), _stream(dev))
-    _check(st, "qgemm_w8a32")
+    ws = _w8a32_workspace(dev, workspace, QG_OP_W8A32, M, N, K)
+    st = lib.qgemm_w8a32_ws(M, N, K, _ptr(A), _rows(A, "A"), _ptr(W), _rows(W, "W"),
+                            float(scale), int(zero_point), _ptr(out), _rows(out, "out"),
+                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, "qgemm_w8a32_ws")
     return out
 
 
+def _w8a32_workspace(dev, workspace, op, M, N, K):
+    if workspace is not None:
+        _need(workspace, (torch.uint8, torch.int8), "workspace")
+        return workspace
+    return _workspace(dev, workspace_bytes(op, 1, M, N, K))
 
 
-def qgemm_w8a32_input_grad(dC, W, scale, zero_point=0, out=None):
+
+
+def qgemm_w8a32_input_grad(dC, W, scale, zero_point=0, out=None, workspace=None):
     """dA = dC @ ((W - zero_point) * scale)^T: the gradient of qgemm_w8a32
     with respect to its activations, W in its forward [K, N] layout.
 
-    dC: fp32 [M, N]; W: int8 [K, N]; returns fp32 [M, K].
+    dC: fp32 [M, N]; W: int8 [K, N]; returns fp32 [M, K].  workspace: as in
+    qgemm_w8a32, sized by workspace_bytes(QG_OP_W8A32_INPUT_GRAD, 1, M, N, K).
     """
     _need(dC, (torch.float32,), "dC")
     _need(W, (torch.int8,), "W")
@@ -189,9 +204,11 @@ def qgemm_w8a32_input_grad(dC, W, scale, zero_point=0, out=None):
         _need(out, (torch.float32,), "out")
         if tuple(out.shape) != (M, K):
             raise ValueError("out has the wrong shape")
-    st = lib.qgemm_w8a32_input_grad(M, N, K, _ptr(dC), _rows(dC, "dC"), _ptr(W), _rows(W, "W"),
-                                    float(scale), int(zero_point), _ptr(out), _rows(out, "out"), _stream(dev))
-    _check(st, "qgemm_w8a32_input_grad")
+    ws = _w8a32_workspace(dev, workspace, QG_OP_W8A32_INPUT_GRAD, M, N, K)
+    st = lib.qgemm_w8a32_input_grad_ws(M, N, K, _ptr(dC), _rows(dC, "dC"), _ptr(W), _rows(W, "W"),
+                                       float(scale), int(zero_point), _ptr(out), _rows(out, "out"),
+                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, "qgemm_w8a32_input_grad_ws")
     return out
 # ---------------------------------------------------------------------------
 # A8W8

@@ -321,6 +321,14 @@ static size_t mmi_tiled_split_bytes(int64_t M, int64_t N, int splits) {
 
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
     if (op == QG_OP_DYNAMIC_QUANTIZE_LINEAR) return N < 0 ? 0 : (size_t)qg::dql_partials(N) * 8;
+    if (op == QG_OP_W8A32 || op == QG_OP_W8A32_INPUT_GRAD) {
+        if (!dims_ok(M, N, K) || !w8a32_split()) return 0;
+        // the kernel's view: the input gradient's outputs are dA's K columns
+        const int64_t rows = M, outs = op == QG_OP_W8A32 ? N : K, red = op == QG_OP_W8A32 ? K : N;
+        int splits, split_k;
+        qg::w8a32_split_plan(rows, outs, red, red, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);
+        return qg::w8a32_split_bytes(rows, outs, splits);
+    }
     if (op == QG_OP_MATMUL_INTEGER) {
         // sized for the batch folded into M (contiguous A / Y batches, shared B)
         if (batch < 1 || batch >= 65536 || !dims_ok(M, N, K) || batch * M >= ((int64_t)1 << 30)) return 0;
@@ -340,8 +348,31 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
     return a8w8_tiled_split_bytes(M, N, splits);
 }
 
-qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
-                      int64_t ldw, float scale, int32_t zero_point, float* C, int64_t ldc, void* stream) {
+// W8A32 in the kernel's view: M x N outputs, contraction K (the input
+// gradient passes dA's columns as N and the forward N as K).  A workspace
+// lets the 128x128 split tiles divide the contraction among workgroups.
+static qg_status w8a32_run(qg::W8A32Args& a, bool vec_a, bool vec_w, bool wt, void* workspace, size_t workspace_bytes,
+                           void* stream, const char* op) {
+    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
+    int splits = 1, split_k = 0;
+    if (w8a32_split() && workspace != nullptr) {
+        qg::w8a32_split_plan(a.M, a.N, a.K, a.lda, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);
+        if (qg::w8a32_split_bytes(a.M, a.N, splits) > workspace_bytes) return QG_ERR_WORKSPACE;
+    }
+    a.workspace = splits > 1 ? workspace : nullptr;
+    a.splits = splits;
+    a.split_k = split_k;
+    const char* name = "";
+    (void)hipGetLastError();
+    const hipError_t e = w8a32_split() ? qg::launch_w8a32_split(a, vec_a, vec_w, wt, (hipStream_t)stream, &name)
+                                         : qg::launch_w8a32(a, vec_a, vec_w, wt, (hipStream_t)stream, &name);
+    log_dispatch(op, name, 1, a.M, a.N, a.K, splits);
+    return finish_launch(e, name);
+}
+
+qg_status qgemm_w8a32_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
+                         int64_t ldw, float scale, int32_t zero_point, float* C, int64_t ldc, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     if (empty_output(M, N, K)) return empty_call();
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (A == nullptr || W == nullptr || C == nullptr) return QG_ERR_INVALID_ARGUMENT;
@@ -355,17 +386,17 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     a.scale = scale; a.zp = zero_point; a.C = C; a.ldc = ldc;
     const bool vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
     const bool vec_w = (reinterpret_cast<uintptr_t>(W) & 3u) == 0 && ldw % 4 == 0 && N % 4 == 0;
-    const char* name = "";
-    (void)hipGetLastError();
-    const hipError_t e = w8a32_split() ? qg::launch_w8a32_split(a, vec_a, vec_w, false, (hipStream_t)stream, &name)
-                                         : qg::launch_w8a32(a, vec_a, vec_w, false, (hipStream_t)stream, &name);
-    log_dispatch("w8a32", name, 1, M, N, K, 1);
-    return finish_launch(e, name);
+    return w8a32_run(a, vec_a, vec_w, false, workspace, workspace_bytes, stream, "w8a32");
 }
 
-qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* dC, int64_t lddc,
-                                 const int8_t* W, int64_t ldw, float scale, int32_t zero_point, float* dA,
-                                 int64_t ldda, void* stream) {
+qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const int8_t* W,
+                      int64_t ldw, float scale, int32_t zero_point, float* C, int64_t ldc, void* stream) {
+    return qgemm_w8a32_ws(M, N, K, A, lda, W, ldw, scale, zero_point, C, ldc, nullptr, 0, stream);
+}
+
+qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K, const float* dC, int64_t lddc,
+                                    const int8_t* W, int64_t ldw, float scale, int32_t zero_point, float* dA,
+                                    int64_t ldda, void* workspace, size_t workspace_bytes, void* stream) {
     if (empty_output(M, K, N)) return empty_call();      // dA is [M, K]; N is the reduction
     if (!dims_ok(M, N, K)) return QG_ERR_INVALID_ARGUMENT;
     if (dC == nullptr || W == nullptr || dA == nullptr) return QG_ERR_INVALID_ARGUMENT;
@@ -380,12 +411,13 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* d
     a.scale = scale; a.zp = zero_point; a.C = dA; a.ldc = ldda;
     const bool vec_a = aligned16(dC) && lddc % 4 == 0 && N % 4 == 0;
     const bool vec_w = aligned16(W) && ldw % 16 == 0;
-    const char* name = "";
-    (void)hipGetLastError();
-    const hipError_t e = w8a32_split() ? qg::launch_w8a32_split(a, vec_a, vec_w, true, (hipStream_t)stream, &name)
-                                         : qg::launch_w8a32(a, vec_a, vec_w, true, (hipStream_t)stream, &name);
-    log_dispatch("w8a32_input_grad", name, 1, M, K, N, 1);
-    return finish_launch(e, name);
+    return w8a32_run(a, vec_a, vec_w, true, workspace, workspace_bytes, stream, "w8a32_input_grad");
+}
+
+qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K, const float* dC, int64_t lddc,
+                                 const int8_t* W, int64_t ldw, float scale, int32_t zero_point, float* dA,
+                                 int64_t ldda, void* stream) {
+    return qgemm_w8a32_input_grad_ws(M, N, K, dC, lddc, W, ldw, scale, zero_point, dA, ldda, nullptr, 0, stream);
 }
 
 }  // extern "C"

@@ -108,12 +108,21 @@ struct W8A32Args {
     const int8_t* W; int64_t ldw;
     float scale; int32_t zp;
     float* C; int64_t ldc;
+    // split of the contraction (bf16 split kernel, 128x128 tiles): `splits`
+    // ranges of split_k values (a multiple of 32), partials in `workspace`
+    void* workspace; int splits; int split_k;
 };
 // wt: W is [N,K] (rows of the contraction), the input-gradient form.
 hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                         const char** name);
 // The same operation on the bf16 matrix cores, with the fp32 operand split
 // exactly into three bf16 parts.
+// Split of the contraction for the 128x128 tiles of the bf16 split kernel
+// (splits = 1: none): outputs of at most 128 such tiles, up to 8 splits of at
+// least 512 values; forced > 0 asks for that many.  M x N outputs, K the
+// contraction, lda the row stride of the fp32 operand.
+void w8a32_split_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int forced, int* splits, int* split_k);
+size_t w8a32_split_bytes(int64_t M, int64_t N, int splits);
 hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                               const char** name);
 

@@ -39,10 +39,21 @@
 // A lane's B fragments (16 k of column 16j + l16) stay in registers for the
 // three planes.
 //
+// SK: the contraction split across workgroups (blockIdx.y is the split, each
+// takes p.split_k values of it).  Every split leaves its fp32 partial tile
+// (the fragments holding rows below M) and its partial S2 in the workspace,
+// with device-coherent stores, and takes a ticket; the split that takes the
+// last ticket adds the partials of all splits in split order (its own
+// included, read back), so the sum does not depend on which split finished
+// last and the result is the same on every run, then runs the epilogue and
+// resets the ticket.
+//
 // With WT = true the same kernel is the gradient with respect to the
 // activations: dA[m,k] = scale * (sum_n dC[m,n] W[k,n] - zp * sum_n dC[m,n]),
 // the contraction over W's contiguous dimension, whose rows are already the
 // [outputs][contraction] layout the LDS tile wants.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -91,7 +102,7 @@ __device__ __forceinline__ uint2 i8x4_to_bf16(uint32_t w) {
 
 // WT == false: W is [K,N]; true: W is [N,K] rows of the contraction (p.N
 // outputs, p.K contraction bytes per row).
-template <int BM, int BN, int WM, int WN, bool VEC, bool WT, bool ZP>
+template <int BM, int BN, int WM, int WN, bool VEC, bool WT, bool ZP, bool SK = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel(W8A32Args p) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
@@ -120,11 +131,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
     const int rows = p.M - m0 < BM ? p.M - m0 : BM;
     const int cols = p.N - n0 < BN ? p.N - n0 : BN;
     const int lda = (int)p.lda, ldw = (int)p.ldw;
-    const float* A = p.A + (int64_t)m0 * p.lda;
-    const int8_t* W = WT ? p.W + (int64_t)n0 * p.ldw : p.W + n0;
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (uint32_t)(((rows - 1) * lda + p.K) * 4));
-    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(W, (uint32_t)((cols - 1) * ldw + p.K))
-                                             : make_rsrc(W, (uint32_t)((p.K - 1) * ldw + (p.N - n0)));
+    // This workgroup's range of the contraction: [kbeg, kbeg + K).
+    const int kbeg = SK ? (int)blockIdx.y * p.split_k : 0;
+    const int K = SK ? (p.K - kbeg < p.split_k ? p.K - kbeg : p.split_k) : p.K;
+    const float* A = p.A + (int64_t)m0 * p.lda + kbeg;
+    const int8_t* W = WT ? p.W + (int64_t)n0 * p.ldw + kbeg : p.W + (int64_t)kbeg * p.ldw + n0;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (uint32_t)(((rows - 1) * lda + K) * 4));
+    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(W, (uint32_t)((cols - 1) * ldw + K))
+                                             : make_rsrc(W, (uint32_t)((K - 1) * ldw + (p.N - n0)));
 
     // A: lane -> rows ar + A_ROWS*i, floats 4*ac .. 4*ac+3 of the chunk.
     const int ar = tid >> 3, ac = tid & 7;
@@ -146,7 +160,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int k = k0 + ac * 4 + e;
-                    d[e] = (r < rows && k < p.K) ? __float_as_uint(A[(int64_t)r * p.lda + k]) : 0u;
+                    d[e] = (r < rows && k < K) ? __float_as_uint(A[(int64_t)r * p.lda + k]) : 0u;
                 }
                 a_st[i] = u32x4{d[0], d[1], d[2], d[3]};
             }
@@ -162,7 +176,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int k = k0 + 16 * th + 4 * i + e;
-                        if (tr < cols && k < p.K) d |= (uint32_t)(uint8_t)W[(int64_t)tr * p.ldw + k] << (8 * e);
+                        if (tr < cols && k < K) d |= (uint32_t)(uint8_t)W[(int64_t)tr * p.ldw + k] << (8 * e);
                     }
                     w_st[i] = d;
                 }
@@ -179,7 +193,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int n = wc * 4 + e;
-                    if (k < p.K && n < cols) d |= (uint32_t)(uint8_t)W[(int64_t)k * p.ldw + n] << (8 * e);
+                    if (k < K && n < cols) d |= (uint32_t)(uint8_t)W[(int64_t)k * p.ldw + n] << (8 * e);
                 }
                 w_st[i] = d;
             }
@@ -196,16 +210,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
     // range, and its bytes past K in a WT row meet those zero columns of A.
     auto stash = [&](int buf, int k0) {
         uint8_t* S = smem + buf * STAGE;
-        const bool k_full = k0 + BKF <= p.K;
+        const bool k_full = k0 + BKF <= K;
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i) {
             u32x4 v = a_st[i];
             if (VEC && !k_full) {
                 const int k = k0 + ac * 4;
-                if (k + 0 >= p.K) v.x = 0u;
-                if (k + 1 >= p.K) v.y = 0u;
-                if (k + 2 >= p.K) v.z = 0u;
-                if (k + 3 >= p.K) v.w = 0u;
+                if (k + 0 >= K) v.x = 0u;
+                if (k + 1 >= K) v.y = 0u;
+                if (k + 2 >= K) v.z = 0u;
+                if (k + 3 >= K) v.w = 0u;
             }
             if constexpr (ZP)
                 rs[i] += (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
@@ -271,7 +285,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
     // other's multiplies (4096^3: 339 -> 313 us forward, 331 -> 300 us
     // gradient, identical bits).  Each half still writes only its own share
     // of chunk kt+1, into the buffer nobody reads until the barrier.
-    const int nk = (p.K + BKF - 1) / BKF;
+    const int nk = (K + BKF - 1) / BKF;
     const bool early = NT == 512 && __builtin_amdgcn_readfirstlane(wave) >= 4;
     fetch(0);
     stash(0, 0);
@@ -302,6 +316,76 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
         __syncthreads();
     }
 
+    if constexpr (SK) {
+        const int S = (int)gridDim.y, sk = (int)blockIdx.y;
+        if (S > 1) {
+            constexpr int COHERENT = 16;   // sc1: device scope
+            constexpr int SLOT = BM * BN * 4 + BM * 4;
+            const int tile = tm * tiles_n + tn;   // < W8A32_MAX_TICKETS (host plan)
+            int* tickets = reinterpret_cast<int*>(p.workspace);
+            char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tile * S * SLOT;
+            const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
+            // fragment (i, j) of wave w at ((w * FM + i) * FN + j) * 1024 + 16 * lane;
+            // only fragments with a row below M travel (lane group g holds
+            // rows 16i + 4g .. 16i + 4g + 3 of the wave's tile)
+            auto frag_off = [&](int s2, int i, int j) {
+                return (uint32_t)(s2 * SLOT + ((wave * FM + i) * FN + j) * 1024 + 16 * lane);
+            };
+            auto live = [&](int i) { return wm * WM + i * 16 + 4 * g < rows; };
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (!live(i)) continue;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), p_rsrc, frag_off(sk, i, j), 0,
+                                                           COHERENT);
+            }
+            if (ZP && tid < BM / 4)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4i*>(&s2_rows[4 * tid]), p_rsrc,
+                                                       (uint32_t)(sk * SLOT + BM * BN * 4 + 16 * tid), 0, COHERENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            __shared__ int ticket;
+            __syncthreads();
+            if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (ticket != S - 1) return;
+            // The sum of all splits' partials, in split order.
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            v4f s2v = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int s2 = 0; s2 < S; ++s2) {
+                v4f v[FM][FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        v[i][j] = live(i) ? __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, frag_off(s2, i, j), 0,
+                                                                                                          COHERENT))
+                                          : v4f{0.f, 0.f, 0.f, 0.f};
+                v4f w = v4f{0.f, 0.f, 0.f, 0.f};
+                if (ZP && tid < BM / 4)
+                    w = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    p_rsrc, (uint32_t)(s2 * SLOT + BM * BN * 4 + 16 * tid), 0, COHERENT));
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + v[i][j][r];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2v[r] = s2v[r] + w[r];
+            }
+            if constexpr (ZP) {
+                __syncthreads();   // every thread has read its own split's S2 from LDS
+                if (tid < BM / 4) *reinterpret_cast<v4f*>(&s2_rows[4 * tid]) = s2v;
+                __syncthreads();
+            }
+            if (tid == 0) __hip_atomic_store(&tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
     // Register r of block (i, j) in lane (g, l16) holds row 16i + 4g + r,
     // column 16j + l16 of the wave's tile.
     const float zp = (float)p.zp;
@@ -325,6 +409,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void w8a32_split_kernel
     }
 }
 
+// The 128 x 128 tiles split over the contraction (a.splits > 1, a.split_k
+// values per split, a multiple of 32; at most SKINNY_MAX_TICKETS tiles; the
+// workspace as the host plan sized it).
+template <int BM, int BN, int WM, int WN>
+void launch_tile_split(const W8A32Args& a, bool vec, bool wt, hipStream_t s) {
+    const dim3 grid(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), a.splits), block((BM / WM) * (BN / WN) * 64);
+    const bool zp = a.zp != 0;
+    const int v = (vec ? 4 : 0) | (wt ? 2 : 0) | (zp ? 1 : 0);
+    switch (v) {
+        case 7: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, true, true, true, true>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, true, true, false, true>), grid, block, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, true, false, true, true>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, true, false, false, true>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, false, true, true, true>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, false, true, false, true>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, false, false, true, true>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((w8a32_split_kernel<BM, BN, WM, WN, false, false, false, true>), grid, block, 0, s, a); break;
+    }
+}
+
 template <int BM, int BN, int WM, int WN>
 void launch_tile(const W8A32Args& a, bool vec, bool wt, hipStream_t s) {
     const dim3 grid(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN)), block((BM / WM) * (BN / WN) * 64);
@@ -344,9 +448,46 @@ void launch_tile(const W8A32Args& a, bool vec, bool wt, hipStream_t s) {
 
 }  // namespace
 
+// Whether a call takes the 256 x 256 tiles (see launch_w8a32_split).
+static bool big_tiles(int64_t M, int64_t N, int64_t K, int64_t lda) {
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    return big > 128 && (256 * lda + K + 64) * 4 < ((int64_t)1 << 31);
+}
+
+void w8a32_split_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int forced, int* splits, int* split_k) {
+    *splits = 1;
+    *split_k = 0;
+    if (big_tiles(M, N, K, lda)) return;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > SKINNY_MAX_TICKETS / 2) return;
+    int64_t S = forced > 0 ? forced : std::min<int64_t>(std::min<int64_t>(256 / tiles, K / 512), 8);
+    if (S < 2) return;
+    const int64_t chunks = (K + BKF - 1) / BKF;
+    const int64_t per = (chunks + S - 1) / S;
+    const int64_t n = (chunks + per - 1) / per;
+    if (n < 2) return;
+    *splits = (int)n;
+    *split_k = (int)(per * BKF);
+}
+
+size_t w8a32_split_bytes(int64_t M, int64_t N, int splits) {
+    if (splits <= 1) return 0;
+    const size_t tiles = (size_t)((M + 127) / 128) * (size_t)((N + 127) / 128);
+    return SKINNY_TICKET_BYTES + tiles * (size_t)splits * (128 * 128 * 4 + 128 * 4);
+}
+
 hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                               const char** name) {
     const bool vec = vec_a && vec_w;
+    if (a.splits > 1) {
+        const int64_t tiles = ((int64_t)(a.M + 127) / 128) * ((a.N + 127) / 128);
+        if (big_tiles(a.M, a.N, a.K, a.lda) || a.workspace == nullptr || tiles > SKINNY_MAX_TICKETS ||
+            a.split_k % BKF != 0 || (int64_t)a.split_k * a.splits < a.K || (int64_t)a.split_k * (a.splits - 1) >= a.K)
+            return hipErrorInvalidValue;
+        *name = wt ? "w8a32_input_grad_bf16x3_128x128_splitk" : "w8a32_bf16x3_128x128_splitk";
+        launch_tile_split<128, 128, 64, 64>(a, vec, wt, s);
+        return hipGetLastError();
+    }
     // 256 x 256 tiles (eight waves of 64 x 128, one workgroup per CU) when
     // there are more than 128 of them and 256 rows of A stay within the
     // 32-bit buffer offsets; 128 x 128 otherwise.  The small tiles run more
@@ -354,9 +495,7 @@ hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool w
     // 3072^3 201.1 against 283.4 us, 2560x4096x4096 260.7 / 358.4,
     // 3584x4096x4096 281.5 / 440.0; at 128 (2048x4096x4096, one round of
     // small tiles) they win, 237.7 against 268.9.
-    const int64_t big = ((int64_t)(a.M + 255) / 256) * ((a.N + 255) / 256);
-    const bool span_ok = (256 * a.lda + a.K + 64) * 4 < ((int64_t)1 << 31);
-    if (big > 128 && span_ok) {
+    if (big_tiles(a.M, a.N, a.K, a.lda)) {
         *name = wt ? "w8a32_input_grad_bf16x3_256x256" : "w8a32_bf16x3_256x256";
         launch_tile<256, 256, 64, 128>(a, vec, wt, s);
     } else {

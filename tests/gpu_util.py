@@ -66,11 +66,24 @@ class env:
 W8A32_PATHS = ("bf16x3", "fp32")
 
 
-def w8a32_kernel(path, rows, outs, grad=False):
+def w8a32_kernel(path, rows, outs, grad=False, k=0):
     """Kernel name the library reports for a W8A32 call of `rows` x `outs`
-    outputs on `path` (256 x 256 split tiles from 129 of them on)."""
+    outputs over a contraction of `k` on `path`, through the binding (which
+    passes a workspace): 256 x 256 split tiles from 129 of them on, else
+    128 x 128 tiles, the contraction divided among workgroups when there
+    are at most 128 of those and it allows two or more pieces of 512."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
-    tile = "256x256" if ((rows + 255) // 256) * ((outs + 255) // 256) > 128 else "128x128"
+    if ((rows + 255) // 256) * ((outs + 255) // 256) > 128:
+        tile = "256x256"
+    else:
+        tile = "128x128"
+        tiles = ((rows + 127) // 128) * ((outs + 127) // 128)
+        splits = int(os.environ.get("QGEMM_W8A32_SPLITS", "0")) or min(256 // tiles, k // 512, 8)
+        if tiles <= 128 and splits >= 2:
+            chunks = (k + 31) // 32
+            per = (chunks + splits - 1) // splits
+            if (chunks + per - 1) // per >= 2:
+                tile += "_splitk"
     return f"w8a32_input_grad_bf16x3_{tile}" if grad else f"w8a32_bf16x3_{tile}"
 

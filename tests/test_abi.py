@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported():
                           "qgemm_status_string", "qgemm_last_kernel", "qgemm_version",
                           "qgemm_calib_read", "qgemm_calib_mfma_i8", "qgemm_calib_mfma_i8_32x32", "qgemm_calib_mfma_f32", "qgemm_calib_mfma_bf16", "qgemm_a8w8_acc",
                           "matmul_integer_row_zp", "qgemm_w8a32_input_grad", "dynamic_quantize_linear",
-                          "conv_integer", "conv_integer_workspace_bytes", "qgemm_a8w8_noalloc"}
+                          "conv_integer", "conv_integer_workspace_bytes", "qgemm_a8w8_noalloc",
+                          "qgemm_w8a32_ws", "qgemm_w8a32_input_grad_ws"}
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -60,7 +61,14 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 8192) == 1024 + 64 * 4 * 128 * 128 * 4
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 1024) == 0      # K too short to split
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 2048, 4096, 8192) == 0    # 512 tiles fill the chip
-    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 0
+    # W8A32: 128x128 tiles over K split four ways at M = 16, N = K = 8192 (64
+    # tiles): the ticket header, then per split a 64 KiB fp32 tile and 512
+    # bytes of row sums
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 1024 + 64 * 4 * (65536 + 512)
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 4096, 4096, 4096) == 0     # 256x256 tiles, unsplit
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 512) == 0        # K too short to split
+    # the input gradient's outputs are dA's K columns, its sum runs over N
+    assert q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, 16, 8192, 4096) == 1024 + 32 * 8 * (65536 + 512)
     assert q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 8, 512, 2048, 2048) == 0
     # MatMulInteger splits like A8W8, each partial tile followed by its row
     # and column sums (8 KiB); batches are folded into M
@@ -154,6 +162,20 @@ def test_matmul_integer_split_k_workspace_checks():
     assert mmi(wsb=need - 1, **kw) == b.QG_ERR_WORKSPACE
     kw["ws"] = ctypes.c_void_p(4096 + 16)   # not 256-byte aligned
     assert mmi(wsb=need, **kw) == b.QG_ERR_INVALID_ARGUMENT
+
+
+def test_w8a32_ws_workspace_checks():
+    M, N, K = 16, 8192, 8192
+    need = q.workspace_bytes(q.QG_OP_W8A32, 1, M, N, K)
+    args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
+    assert b.lib.qgemm_w8a32_ws(*args, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE
+    assert b.lib.qgemm_w8a32_ws(*args, ctypes.c_void_p(4096 + 64), need, None) == b.QG_ERR_INVALID_ARGUMENT
+    need = q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, M, N, K)
+    gargs = (M, N, K, FAKE, N, FAKE, N, 1.0, 0, FAKE, K)
+    assert b.lib.qgemm_w8a32_input_grad_ws(*gargs, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE
+    # the same argument checks as the calls without a workspace
+    assert b.lib.qgemm_w8a32_ws(M, N, K, FAKE, K - 1, FAKE, N, 1.0, 0, FAKE, N, None, 0, None) == \
+        b.QG_ERR_INVALID_ARGUMENT
 
 
 def test_a8w8_workspace_too_small():

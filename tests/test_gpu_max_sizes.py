@@ -64,7 +64,7 @@ def test_w8a32_at_the_span_limit(weight):
     case(f"w8a32 max span M={M} N={N} K={K}")
     A = si.rng(781).standard_normal((M, K), dtype=np.float32)
     c = q.qgemm_w8a32(to_dev(A), tW, 0.01, -5).cpu().numpy().astype(np.float64)
-    assert q.last_kernel() == w8a32_kernel("bf16x3", M, N)
+    assert q.last_kernel() == w8a32_kernel("bf16x3", M, N, k=K)
     R, bound = oracle.w8a32(A, W, 0.01, -5)
     assert np.all(np.abs(c - R) <= 1e-5 * bound)
 
@@ -86,6 +86,6 @@ def test_w8a32_input_grad_at_the_span_limit(weight):
     case(f"w8a32_input_grad max span M={M} N={N} K={K}")
     dC = si.rng(784).standard_normal((M, N), dtype=np.float32)
     d = q.qgemm_w8a32_input_grad(to_dev(dC), tW, 0.02, 3).cpu().numpy().astype(np.float64)
-    assert q.last_kernel() == w8a32_kernel("bf16x3", M, K, grad=True)
+    assert q.last_kernel() == w8a32_kernel("bf16x3", M, K, grad=True, k=N)
     R, bound = oracle.w8a32_input_grad(dC, W, 0.02, 3)
     assert np.all(np.abs(d - R) <= 1e-5 * bound)

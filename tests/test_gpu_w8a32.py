@@ -25,7 +25,7 @@ def path(request):
 def check(A, W, scale, zp, path):
     M, N = A.shape[0], W.shape[1]
     c = q.qgemm_w8a32(to_dev(A), to_dev(W), scale, zp).cpu().numpy().astype(np.float64)
-    assert q.last_kernel() == w8a32_kernel(path, M, N), q.last_kernel()
+    assert q.last_kernel() == w8a32_kernel(path, M, N, k=A.shape[1]), q.last_kernel()
     R, bound = oracle.w8a32(A, W, scale, zp)
     err = np.abs(c - R)
     worst = float((err / np.maximum(bound, 1e-300)).max())
@@ -67,7 +67,7 @@ def test_w8a32_identity_weight_returns_activations_bit_exact(sign, path):
          * np.where(g.random((96, n)) < 0.5, -1.0, 1.0).astype(np.float32))
     W = (sign * np.eye(n)).astype(np.int8)
     c = q.qgemm_w8a32(to_dev(A), to_dev(W), 1.0, 0).cpu().numpy()
-    assert q.last_kernel() == w8a32_kernel(path, 96, n)
+    assert q.last_kernel() == w8a32_kernel(path, 96, n, k=n)
     np.testing.assert_array_equal(c, sign * A)
 
 
@@ -114,7 +114,7 @@ def test_w8a32_4096_every_output(path):
     case(f"w8a32 4096x4096x4096 zp=-5 every output {path}")
     A, W = si.w8a32_inputs(4096, 4096, 4096, seed=506)
     c = q.qgemm_w8a32(to_dev(A), to_dev(W), 0.01, -5).cpu().numpy().astype(np.float64)
-    assert q.last_kernel() == w8a32_kernel(path, 4096, 4096), q.last_kernel()
+    assert q.last_kernel() == w8a32_kernel(path, 4096, 4096, k=4096), q.last_kernel()
     R, bound = oracle.w8a32(A, W, 0.01, -5)
     assert np.all(np.abs(c - R) <= TOL * bound)
 

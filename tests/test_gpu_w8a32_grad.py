@@ -31,7 +31,7 @@ def inputs(M, N, K, seed):
 def check(dC, W, scale, zp, path, dC_dev=None, W_dev=None):
     d = q.qgemm_w8a32_input_grad(to_dev(dC) if dC_dev is None else dC_dev,
                                  to_dev(W) if W_dev is None else W_dev, scale, zp)
-    assert q.last_kernel() == w8a32_kernel(path, dC.shape[0], W.shape[0], grad=True), q.last_kernel()
+    assert q.last_kernel() == w8a32_kernel(path, dC.shape[0], W.shape[0], grad=True, k=W.shape[1]), q.last_kernel()
     d = d.cpu().numpy().astype(np.float64)
     R, bound = oracle.w8a32_input_grad(dC, W, scale, zp)
     err = np.abs(d - R)
@@ -87,7 +87,7 @@ def test_w8a32_input_grad_4096_every_output(path):
     case(f"w8a32_input_grad 4096x4096x4096 zp=-5 every output {path}")
     dC, W = inputs(4096, 4096, 4096, seed=506)
     d = q.qgemm_w8a32_input_grad(to_dev(dC), to_dev(W), 0.01, -5).cpu().numpy().astype(np.float64)
-    assert q.last_kernel() == w8a32_kernel(path, 4096, 4096, grad=True), q.last_kernel()
+    assert q.last_kernel() == w8a32_kernel(path, 4096, 4096, grad=True, k=4096), q.last_kernel()
     R, bound = oracle.w8a32_input_grad(dC, W, 0.01, -5)
     assert np.all(np.abs(d - R) <= TOL * bound)
 
@@ -116,7 +116,7 @@ def test_w8a32_input_grad_identity_weight_bit_exact(path):
           * np.where(g.random((80, n)) < 0.5, -1.0, 1.0).astype(np.float32))
     W = np.eye(n, dtype=np.int8)
     d = q.qgemm_w8a32_input_grad(to_dev(dC), to_dev(W), 1.0, 0).cpu().numpy()
-    assert q.last_kernel() == w8a32_kernel(path, 80, n, grad=True)
+    assert q.last_kernel() == w8a32_kernel(path, 80, n, grad=True, k=n)
     np.testing.assert_array_equal(d, dC)
 
 

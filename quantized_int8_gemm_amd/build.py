@@ -31,6 +31,7 @@ SOURCES = [
     "a8w8_skinny.hip",
     "w8a32.hip",
     "w8a32_split.hip",
+    "w8a32_skinny.hip",
     "dynamic_quantize.hip",
     "conv_integer.hip",
     "conv_implicit.hip",

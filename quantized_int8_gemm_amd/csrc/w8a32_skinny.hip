@@ -1,0 +1,359 @@
+// Decode-shaped W8A32 (M <= 16, W as [K,N]) on the bf16 matrix cores of
+// gfx950, bound by reading the int8 weight once.
+//
+// Operator: "feat(PULPOpen): matmul that dequantises an int8 weight
+// in-kernel", section "The kernel": C = scale * (S1 - zp * S2) with
+// S1 = sum_k a_k b_k and S2 = sum_k a_k, the dequantised weight never
+// formed.  As in the tiled split kernel, every fp32 activation is split
+// exactly into three bf16 parts (hi + lo + lo2) and the int8 weight is exact
+// in bf16, so the matrix cores form every product exactly and only the fp32
+// accumulation rounds.
+//
+// Grid: (N / 256 column tiles) x (S splits of K), four waves taking 64-row
+// steps of K round robin, two steps in flight, the weight read with the
+// non-temporal policy (as the int8 decode kernel reads it):
+//  * lane (g = lane/16, c = lane%16) loads rows 16g .. 16g+15 of the step at
+//    columns 16c .. 16c+15 (16-byte vectors), and the 16 fp32 values of
+//    activation row c at the same 16 k;
+//  * the activation values become three bf16 planes, 8 k per half; for
+//    output column 16c + j, byte j of the lane's rows 8h .. 8h+7 widens to
+//    the matching 8 bf16, so v_mfma_f32_16x16x32_bf16 number (j, h, part)
+//    adds the products of those k for rows 0..15 and columns {16c + j}
+//    (96 multiplies per step, no LDS in the loop);
+//  * the waves' fp32 tiles are added through LDS in wave order; with S > 1
+//    each split leaves its partial (rows < M, and its 16 partial row sums
+//    S2) in the workspace with device-coherent stores and takes a ticket; the
+//    split that takes the last ticket adds all S partials in split order (so
+//    the sum does not depend on which split finished last), runs the
+//    epilogue and resets the ticket.
+// Values of A past K (the next row's, or beyond the buffer) are cleared
+// before they reach a product or S2; weight rows past K read as zero.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qg {
+namespace {
+
+constexpr int NT = 256;     // threads (four waves)
+constexpr int TN = 256;     // columns per workgroup
+constexpr int KS = 64;      // k rows per wave step
+constexpr int WAVES = 4;
+constexpr int SLOT_ROWS = 17;   // a split's partial: 16 tile rows, then the 16 row sums
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Two bf16 held in the high halves of a and b, packed a first.
+__device__ __forceinline__ uint32_t pk_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Eight fp32 values as their three bf16 parts (exact: see the tiled kernel).
+__device__ __forceinline__ void split8(const float* v, v8bf& hi, v8bf& lo, v8bf& lo2) {
+    uint32_t h[8], l[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t x = __float_as_uint(v[e]);
+        h[e] = x & 0xffff0000u;
+        const float r1 = v[e] - __uint_as_float(h[e]);
+        l[e] = __float_as_uint(r1) & 0xffff0000u;
+        q[e] = __float_as_uint(r1 - __uint_as_float(l[e]));
+    }
+    u32x4 H, L, Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        (&H.x)[e] = pk_hi(h[2 * e], h[2 * e + 1]);
+        (&L.x)[e] = pk_hi(l[2 * e], l[2 * e + 1]);
+        (&Q.x)[e] = pk_hi(q[2 * e], q[2 * e + 1]);
+    }
+    hi = __builtin_bit_cast(v8bf, H);
+    lo = __builtin_bit_cast(v8bf, L);
+    lo2 = __builtin_bit_cast(v8bf, Q);
+}
+
+// Byte j of eight 16-byte rows as eight bf16 (exact for int8).
+__device__ __forceinline__ v8bf column8(const u32x4* rows, int j) {
+    uint32_t f[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t w = (&rows[t].x)[j >> 2];
+        f[t] = __float_as_uint((float)(int8_t)(uint8_t)(w >> (8 * (j & 3))));
+    }
+    return __builtin_bit_cast(v8bf, u32x4{pk_hi(f[0], f[1]), pk_hi(f[2], f[3]), pk_hi(f[4], f[5]), pk_hi(f[6], f[7])});
+}
+
+template <bool ZP>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8a32_skinny_kernel(W8A32Args p) {
+    __shared__ __attribute__((aligned(16))) float red[WAVES][16][TN];
+    __shared__ float s2_red[WAVES][16];
+    __shared__ __attribute__((aligned(16))) float s2_tot[16];
+    __shared__ int ticket;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int tn = blockIdx.x, split = blockIdx.y, S = gridDim.y;
+    const int n0 = tn * TN;
+    const int cols = p.N - n0;
+    const int M = p.M, K = p.K;
+
+    // K range of this split: `per` 64-row steps, a multiple of 2*WAVES.
+    const int per = p.split_k / KS;
+    const int s_begin = split * per;
+
+    const int ldw = (int)p.ldw, lda = (int)p.lda;
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)(((M - 1) * lda + K) * 4));
+    const uint32_t w_voff = (uint32_t)(16 * g * ldw + 16 * c16);
+    const uint32_t a_voff = (uint32_t)((c16 * lda + 16 * g) * 4);
+
+    u32x4 wbuf[2][16];
+    u32x4 abuf[2][4];
+    // Loads of one step into buffer b; a step past this split's range reads
+    // rows that are never multiplied (or zeros past K), so no branch
+    // separates the loads.
+    auto fetch = [&](int step, int b) {
+        const int k0 = step * KS;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) abuf[b][q] = buffer_load16(a_rsrc, a_voff + (uint32_t)((k0 + 4 * q) * 4), 0u);
+    };
+
+    v4f acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    float s2 = 0.f;   // this lane's share of S2 for row c16
+
+    auto consume = [&](int b, int step) {
+        const int k0 = step * KS + 16 * g;
+        float a[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            a[4 * q] = __uint_as_float(abuf[b][q].x);
+            a[4 * q + 1] = __uint_as_float(abuf[b][q].y);
+            a[4 * q + 2] = __uint_as_float(abuf[b][q].z);
+            a[4 * q + 3] = __uint_as_float(abuf[b][q].w);
+        }
+        if (step * KS + KS > K) {   // a step reaching past K: clear those values
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (k0 + e >= K) a[e] = 0.f;
+        }
+        if constexpr (ZP) {
+            s2 += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])) +
+                  (((a[8] + a[9]) + (a[10] + a[11])) + ((a[12] + a[13]) + (a[14] + a[15])));
+        }
+        v8bf pa[2][3];
+        split8(a, pa[0][0], pa[0][1], pa[0][2]);
+        split8(a + 8, pa[1][0], pa[1][1], pa[1][2]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const v8bf bw = column8(&wbuf[b][8 * h], j);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h][pl], bw, acc[j], 0, 0, 0);
+            }
+        }
+    };
+
+    // This wave's steps: s_begin + wave + WAVES*i, i < n_my (even, the same
+    // for all waves); two in flight, the last pair peeled.
+    const int first = s_begin + wave;
+    const int n_my = per / WAVES;
+    fetch(first, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(first + WAVES, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    int i = 0;
+    for (; i + 2 < n_my; i += 2) {
+        consume(0, first + WAVES * i);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(first + WAVES * (i + 2), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(1, first + WAVES * (i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(first + WAVES * (i + 3), 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    consume(0, first + WAVES * i);
+    consume(1, first + WAVES * (i + 1));
+
+    // Register r of block j holds row 4g + r, column 16*c16 + j: four
+    // 16-byte chunks per row, placed as in the int8 decode kernel.
+    auto chunk = [](int ch) { return (ch & ~3) | ((ch ^ (ch >> 4)) & 3); };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (4 * g + r >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4f v = v4f{acc[4 * q][r], acc[4 * q + 1][r], acc[4 * q + 2][r], acc[4 * q + 3][r]};
+            *reinterpret_cast<v4f*>(&red[wave][4 * g + r][4 * chunk(4 * c16 + q)]) = v;
+        }
+    }
+    if constexpr (ZP) {
+        // lane groups held different k: (g0 + g1) + (g2 + g3) in every lane
+        s2 += __shfl_xor(s2, 16);
+        s2 += __shfl_xor(s2, 32);
+        if (g == 0) s2_red[wave][c16] = s2;
+    }
+    __syncthreads();
+    if (ZP && tid < 16) s2_tot[tid] = ((s2_red[0][tid] + s2_red[1][tid]) + s2_red[2][tid]) + s2_red[3][tid];
+
+    // Items: (row m < M, group of 4 columns); the waves' tiles in wave order.
+    auto tile_sum = [&](int m, int cg) -> v4f {
+        const int at = 4 * chunk(cg);
+        v4f s = *reinterpret_cast<const v4f*>(&red[0][m][at]);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) s = s + *reinterpret_cast<const v4f*>(&red[w][m][at]);
+        return s;
+    };
+    const float zp = (float)p.zp;
+    const bool vec_out = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+    auto epilogue = [&](int m, int n, v4f v) {
+        if (n >= p.N) return;
+        float f[4] = {v[0], v[1], v[2], v[3]};
+        const float s2m = ZP ? s2_tot[m] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (ZP) f[e] = f[e] - zp * s2m;
+            f[e] = p.scale * f[e];
+        }
+        float* dst = p.C + (int64_t)m * p.ldc + n;
+        if (vec_out && n + 4 <= p.N) {
+            *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+            return;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) dst[e] = f[e];
+    };
+    const int items = M * (TN / 4);
+
+    if (S == 1) {
+        if constexpr (ZP) __syncthreads();   // s2_tot
+        for (int it = tid; it < items; it += NT) {
+            const int m = it / (TN / 4), cg = it % (TN / 4);
+            epilogue(m, n0 + cg * 4, tile_sum(m, cg));
+        }
+        return;
+    }
+
+    // Split-K exchange (workspace: the fixed ticket header, one int per
+    // column tile, then per column tile S partials of SLOT_ROWS x TN fp32).
+    int* tickets = reinterpret_cast<int*>(p.workspace);
+    constexpr int SLOT = SLOT_ROWS * TN * 4;
+    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tn * S * SLOT;
+    const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
+    constexpr int COHERENT = 16;   // sc1: device scope
+    for (int it = tid; it < items; it += NT) {
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, tile_sum(m, cg)), p_rsrc,
+                                               (uint32_t)(split * SLOT + (m * TN + cg * 4) * 4), 0, COHERENT);
+    }
+    if constexpr (ZP) {
+        __syncthreads();   // s2_tot
+        if (tid < 4)
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const v4i*>(&s2_tot[4 * tid]), p_rsrc,
+                                                   (uint32_t)(split * SLOT + (16 * TN + 4 * tid) * 4), 0, COHERENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != S - 1) return;
+
+    // Every split's partial, added in split order, SU splits per round with
+    // their loads in flight together; loads past split S - 1 read zeros.
+    constexpr int SU = 8, IPT = 16 * (TN / 4) / NT;
+    v4f sum[IPT];
+    uint32_t off[IPT];
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) {
+        const int it = tid + q * NT;
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        sum[q] = v4f{0.f, 0.f, 0.f, 0.f};
+        off[q] = it < items ? (uint32_t)((m * TN + cg * 4) * 4) : 0xFFFFFFF0u;
+    }
+    v4f ssum = v4f{0.f, 0.f, 0.f, 0.f};
+    const uint32_t soff = (ZP && tid < 4) ? (uint32_t)((16 * TN + 4 * tid) * 4) : 0xFFFFFFF0u;
+    for (int s0 = 0; s0 < S; s0 += SU) {
+        v4f v[IPT][SU];
+        v4f w[ZP ? SU : 1];
+#pragma unroll
+        for (int q = 0; q < IPT; ++q)
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const uint32_t o = off[q] == 0xFFFFFFF0u ? off[q] : off[q] + (uint32_t)((s0 + u) * SLOT);
+                v[q][u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o, 0, COHERENT));
+            }
+        if constexpr (ZP) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const uint32_t o = soff == 0xFFFFFFF0u ? soff : soff + (uint32_t)((s0 + u) * SLOT);
+                w[u] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(p_rsrc, o, 0, COHERENT));
+            }
+        }
+        // splits past S - 1 read zeros: adding them changes nothing
+#pragma unroll
+        for (int q = 0; q < IPT; ++q)
+#pragma unroll
+            for (int u = 0; u < SU; ++u) sum[q] = sum[q] + v[q][u];
+        if constexpr (ZP) {
+#pragma unroll
+            for (int u = 0; u < SU; ++u) ssum = ssum + w[u];
+        }
+    }
+    if constexpr (ZP) {
+        if (tid < 4) *reinterpret_cast<v4f*>(&s2_tot[4 * tid]) = ssum;
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) {
+        const int it = tid + q * NT;
+        if (it >= items) continue;
+        const int m = it / (TN / 4), cg = it % (TN / 4);
+        epilogue(m, n0 + cg * 4, sum[q]);
+    }
+    if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+void w8a32_skinny_plan(int64_t N, int64_t K, int forced, int* splits, int* split_k) {
+    const int64_t tiles_n = (N + TN - 1) / TN;
+    const int64_t steps = (K + KS - 1) / KS;
+    int64_t per;
+    if (forced > 0) {
+        per = (steps + forced - 1) / forced;
+    } else {
+        const int64_t want = (256 + tiles_n - 1) / tiles_n;   // about one workgroup per CU
+        per = (steps + want - 1) / want;
+    }
+    per = ((per + 2 * WAVES - 1) / (2 * WAVES)) * (2 * WAVES);
+    int64_t n = (steps + per - 1) / per;
+    // more column tiles than the fixed ticket header holds: one split
+    if (n > 1 && tiles_n > SKINNY_MAX_TICKETS) {
+        per = ((steps + 2 * WAVES - 1) / (2 * WAVES)) * (2 * WAVES);
+        n = 1;
+    }
+    *splits = (int)n;
+    *split_k = (int)(per * KS);
+}
+
+size_t w8a32_skinny_bytes(int64_t N, int splits) {
+    if (splits <= 1) return 0;
+    const size_t tiles_n = (size_t)((N + TN - 1) / TN);
+    return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * SLOT_ROWS * TN * 4;
+}
+
+hipError_t launch_w8a32_skinny(const W8A32Args& a, hipStream_t s, const char** name) {
+    *name = "w8a32_skinny";
+    const dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
+    if (a.M < 1 || a.M > 16 || a.split_k % (KS * 2 * WAVES) != 0 || (int64_t)a.split_k * grid.y < a.K ||
+        (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)))
+        return hipErrorInvalidValue;
+    if (a.zp != 0) hipLaunchKernelGGL(w8a32_skinny_kernel<true>, grid, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL(w8a32_skinny_kernel<false>, grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -69,11 +69,15 @@ W8A32_PATHS = ("bf16x3", "fp32")
 def w8a32_kernel(path, rows, outs, grad=False, k=0):
     """Kernel name the library reports for a W8A32 call of `rows` x `outs`
     outputs over a contraction of `k` on `path`, through the binding (which
-    passes a workspace): 256 x 256 split tiles from 129 of them on, else
-    128 x 128 tiles, the contraction divided among workgroups when there
-    are at most 128 of those and it allows two or more pieces of 512."""
+    passes a workspace): the decode kernel for at most 16 rows, else 256 x
+    256 split tiles from 129 of them on, else 128 x 128 tiles, the
+    contraction divided among workgroups when there are at most 128 of
+    those and it allows two or more pieces of 512."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
+    if not grad and rows <= 16 and outs % 16 == 0 and k % 4 == 0 and \
+            os.environ.get("QGEMM_FORCE_KERNEL") != "tiled":
+        return "w8a32_skinny"   # contiguous operands: 16-byte aligned rows
     if ((rows + 255) // 256) * ((outs + 255) // 256) > 128:
         tile = "256x256"
     else:

@@ -65,6 +65,12 @@ def test_workspace_bytes():
     # tiles): the ticket header, then per split a 64 KiB fp32 tile and 512
     # bytes of row sums
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 1024 + 64 * 4 * (65536 + 512)
+    # at most 16 rows the size covers both the decode kernel (17 rows of 256
+    # floats per split and column tile) and the tiled one, which unaligned
+    # rows take: here the tiled one's 2 splits of 64 tiles
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 1024) == 1024 + 64 * 2 * (65536 + 512)
+    # wide outputs: the decode kernel alone splits nothing past 256 column tiles
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 2, 65792, 64) == 0
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 4096, 4096, 4096) == 0     # 256x256 tiles, unsplit
     assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 512) == 0        # K too short to split
     # the input gradient's outputs are dA's K columns, its sum runs over N
@@ -165,11 +171,17 @@ def test_matmul_integer_split_k_workspace_checks():
 
 
 def test_w8a32_ws_workspace_checks():
-    M, N, K = 16, 8192, 8192
+    M, N, K = 32, 8192, 8192   # tiled, K split four ways
     need = q.workspace_bytes(q.QG_OP_W8A32, 1, M, N, K)
     args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
     assert b.lib.qgemm_w8a32_ws(*args, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE
     assert b.lib.qgemm_w8a32_ws(*args, ctypes.c_void_p(4096 + 64), need, None) == b.QG_ERR_INVALID_ARGUMENT
+    # 16 aligned rows: the decode kernel, 8 splits of 32 column tiles
+    M = 16
+    decode_need = 1024 + 32 * 8 * 17 * 1024
+    args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
+    assert b.lib.qgemm_w8a32_ws(*args, FAKE, decode_need - 1, None) == b.QG_ERR_WORKSPACE
+    M, N, K = 16, 8192, 8192
     need = q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, M, N, K)
     gargs = (M, N, K, FAKE, N, FAKE, N, 1.0, 0, FAKE, K)
     assert b.lib.qgemm_w8a32_input_grad_ws(*gargs, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE

@@ -43,13 +43,15 @@ def within(c, R, bound):
     (257, 1000, 3000, 3),     # ragged M, N and K: 24 tiles, 5 splits of 608 (the last 568)
 ])
 def test_w8a32_split_k_every_output(M, N, K, zp):
+    """(At most 16 rows would take the decode kernel: the tiled one is forced.)"""
     case(f"w8a32 split-K M={M} N={N} K={K} zp={zp}")
     A, W = si.w8a32_inputs(M, N, K, seed=M + N + K)
-    c, kern = fwd(A, W, 0.013, zp)
+    with env(QGEMM_FORCE_KERNEL="tiled"):
+        c, kern = fwd(A, W, 0.013, zp)
+        c2, _ = fwd(A, W, 0.013, zp)
     assert kern == "w8a32_bf16x3_128x128_splitk", kern
     R, bound = oracle.w8a32(A, W, 0.013, zp)
     within(c, R, bound)
-    c2, _ = fwd(A, W, 0.013, zp)
     assert torch.equal(c, c2), "a repeated call differs"
 
 
@@ -92,7 +94,8 @@ def test_w8a32_split_k_workspace_reused_across_shapes():
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     for i, (M, N, K) in enumerate(shapes):
         A, W = si.w8a32_inputs(M, N, K, seed=960 + i)
-        c, kern = fwd(A, W, 0.01, 2, workspace=ws)
+        with env(QGEMM_FORCE_KERNEL="tiled"):
+            c, kern = fwd(A, W, 0.01, 2, workspace=ws)
         assert kern.endswith("_splitk"), kern
         within(c, *oracle.w8a32(A, W, 0.01, 2))
         dC, _ = si.w8a32_inputs(M, 1, N, seed=970 + i)      # [M, N]; dA is [M, K]
@@ -105,9 +108,9 @@ def test_w8a32_split_k_workspace_reused_across_shapes():
 def test_w8a32_without_workspace_runs_unsplit():
     """qgemm_w8a32 itself (no workspace) runs the 128 x 128 tiles unsplit,
     and so does the fp32 matrix-core path with one."""
-    case("w8a32 16x2048x4096 unsplit forms")
+    case("w8a32 32x2048x4096 unsplit forms")
     from quantized_int8_gemm_amd import _binding as b
-    M, N, K = 16, 2048, 4096
+    M, N, K = 32, 2048, 4096
     A, W = si.w8a32_inputs(M, N, K, seed=980)
     tA, tW = to_dev(A), to_dev(W)
     C = torch.empty(M, N, dtype=torch.float32, device=dev())

@@ -319,12 +319,16 @@ static size_t mmi_tiled_split_bytes(int64_t M, int64_t N, int splits) {
     return qg::SKINNY_TICKET_BYTES + tiles * (size_t)splits * (128 * 128 * 4 + 8192);
 }
 
-// The W8A32 decode kernel's shapes: the bf16 split path, at most 16 rows,
-// 16-byte aligned operand rows (QGEMM_FORCE_KERNEL=tiled turns it off).
-static bool w8a32_skinny_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* W, int64_t ldw) {
+// The W8A32 decode kernel's shapes (the kernel's view: M x N outputs,
+// contraction K): the bf16 split path, at most 16 rows, 16-byte aligned
+// operand rows; the forward also needs N % 16 == 0 (its weight rows are
+// read 16 outputs at a time).  QGEMM_FORCE_KERNEL=tiled turns it off.
+static bool w8a32_skinny_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* W, int64_t ldw,
+                            bool wt) {
     if (!w8a32_split() || M > 16 || env_is("QGEMM_FORCE_KERNEL", "tiled")) return false;
     const bool no_ptrs = A == nullptr && W == nullptr;   // sizing only (qgemm_workspace_bytes)
-    return (no_ptrs || (aligned16(A) && aligned16(W))) && lda % 4 == 0 && K % 4 == 0 && ldw % 16 == 0 && N % 16 == 0;
+    return (no_ptrs || (aligned16(A) && aligned16(W))) && lda % 4 == 0 && K % 4 == 0 && ldw % 16 == 0 &&
+           (wt || N % 16 == 0);
 }
 
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
@@ -339,9 +343,10 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
         size_t bytes = qg::w8a32_split_bytes(rows, outs, splits);
         // decode shapes take the decode kernel when their rows are aligned,
         // the tiled one otherwise: enough for either
-        if (op == QG_OP_W8A32 && w8a32_skinny_ok(M, N, K, nullptr, K, nullptr, N)) {
-            qg::w8a32_skinny_plan(N, K, forced, &splits, &split_k);
-            bytes = std::max(bytes, qg::w8a32_skinny_bytes(N, splits));
+        const bool wt = op == QG_OP_W8A32_INPUT_GRAD;
+        if (w8a32_skinny_ok(rows, outs, red, nullptr, red, nullptr, wt ? red : outs, wt)) {
+            qg::w8a32_skinny_plan(outs, red, forced, &splits, &split_k);
+            bytes = std::max(bytes, qg::w8a32_skinny_bytes(outs, splits));
         }
         return bytes;
     }
@@ -372,7 +377,7 @@ static qg_status w8a32_run(qg::W8A32Args& a, bool vec_a, bool vec_w, bool wt, vo
     if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
     // At most 16 rows against a [K,N] weight with 16-byte rows: the decode
     // kernel, K split across workgroups when a workspace is given.
-    if (!wt && w8a32_skinny_ok(a.M, a.N, a.K, a.A, a.lda, a.W, a.ldw)) {
+    if (w8a32_skinny_ok(a.M, a.N, a.K, a.A, a.lda, a.W, a.ldw, wt)) {
         int splits, split_k;
         qg::w8a32_skinny_plan(a.N, a.K, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);
         if (workspace == nullptr) {
@@ -385,7 +390,7 @@ static qg_status w8a32_run(qg::W8A32Args& a, bool vec_a, bool vec_w, bool wt, vo
         a.split_k = split_k;
         const char* name = "";
         (void)hipGetLastError();
-        const hipError_t e = qg::launch_w8a32_skinny(a, (hipStream_t)stream, &name);
+        const hipError_t e = qg::launch_w8a32_skinny(a, wt, (hipStream_t)stream, &name);
         log_dispatch(op, name, 1, a.M, a.N, a.K, splits);
         return finish_launch(e, name);
     }

@@ -1,5 +1,5 @@
-// Decode-shaped W8A32 (M <= 16, W as [K,N]) on the bf16 matrix cores of
-// gfx950, bound by reading the int8 weight once.
+// Decode-shaped W8A32 (M <= 16) and its input gradient on the bf16 matrix
+// cores of gfx950, bound by reading the int8 weight once.
 //
 // Operator: "feat(PULPOpen): matmul that dequantises an int8 weight
 // in-kernel", section "The kernel": C = scale * (S1 - zp * S2) with
@@ -28,6 +28,13 @@
 //    epilogue and resets the ticket.
 // Values of A past K (the next row's, or beyond the buffer) are cleared
 // before they reach a product or S2; weight rows past K read as zero.
+//
+// WT: the input gradient, dA = scale * (dC W^T - zp * rowsum(dC)), whose
+// contraction runs along W's rows (the outputs are W's rows).  Lane (g, c)
+// then loads, for j = 0..15, bytes 16g .. 16g+15 of the step from W row
+// 16c + j, which already hold 16 contraction values of output 16c + j in
+// order: they widen to the same bf16 fragments without a transpose, and
+// everything else is the forward kernel's.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -68,6 +75,17 @@ __device__ __forceinline__ void split8(const float* v, v8bf& hi, v8bf& lo, v8bf&
     lo2 = __builtin_bit_cast(v8bf, Q);
 }
 
+// Bytes 8h .. 8h+7 of a 16-byte vector as eight bf16 (exact for int8).
+__device__ __forceinline__ v8bf half8(const u32x4& v, int h) {
+    uint32_t f[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t w = (&v.x)[2 * h + (t >> 2)];
+        f[t] = __float_as_uint((float)(int8_t)(uint8_t)(w >> (8 * (t & 3))));
+    }
+    return __builtin_bit_cast(v8bf, u32x4{pk_hi(f[0], f[1]), pk_hi(f[2], f[3]), pk_hi(f[4], f[5]), pk_hi(f[6], f[7])});
+}
+
 // Byte j of eight 16-byte rows as eight bf16 (exact for int8).
 __device__ __forceinline__ v8bf column8(const u32x4* rows, int j) {
     uint32_t f[8];
@@ -79,7 +97,7 @@ __device__ __forceinline__ v8bf column8(const u32x4* rows, int j) {
     return __builtin_bit_cast(v8bf, u32x4{pk_hi(f[0], f[1]), pk_hi(f[2], f[3]), pk_hi(f[4], f[5]), pk_hi(f[6], f[7])});
 }
 
-template <bool ZP>
+template <bool ZP, bool WT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8a32_skinny_kernel(W8A32Args p) {
     __shared__ __attribute__((aligned(16))) float red[WAVES][16][TN];
     __shared__ float s2_red[WAVES][16];
@@ -98,9 +116,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     const int s_begin = split * per;
 
     const int ldw = (int)p.ldw, lda = (int)p.lda;
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
+    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K))
+                                             : make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)(((M - 1) * lda + K) * 4));
-    const uint32_t w_voff = (uint32_t)(16 * g * ldw + 16 * c16);
+    const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(16 * g * ldw + 16 * c16);
     const uint32_t a_voff = (uint32_t)((c16 * lda + 16 * g) * 4);
 
     u32x4 wbuf[2][16];
@@ -110,8 +129,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     // separates the loads.
     auto fetch = [&](int step, int b) {
         const int k0 = step * KS;
+        if constexpr (WT) {   // W row 16 c16 + j, contraction bytes k0 + 16g ..
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
+            for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)(j * ldw + k0));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) abuf[b][q] = buffer_load16(a_rsrc, a_voff + (uint32_t)((k0 + 4 * q) * 4), 0u);
     };
@@ -147,7 +171,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
         for (int j = 0; j < 16; ++j) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const v8bf bw = column8(&wbuf[b][8 * h], j);
+                const v8bf bw = WT ? half8(wbuf[b][j], h) : column8(&wbuf[b][8 * h], j);
 #pragma unroll
                 for (int pl = 0; pl < 3; ++pl)
                     acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h][pl], bw, acc[j], 0, 0, 0);
@@ -345,14 +369,19 @@ size_t w8a32_skinny_bytes(int64_t N, int splits) {
     return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * SLOT_ROWS * TN * 4;
 }
 
-hipError_t launch_w8a32_skinny(const W8A32Args& a, hipStream_t s, const char** name) {
-    *name = "w8a32_skinny";
+hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const char** name) {
+    *name = wt ? "w8a32_input_grad_skinny" : "w8a32_skinny";
     const dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
     if (a.M < 1 || a.M > 16 || a.split_k % (KS * 2 * WAVES) != 0 || (int64_t)a.split_k * grid.y < a.K ||
         (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)))
         return hipErrorInvalidValue;
-    if (a.zp != 0) hipLaunchKernelGGL(w8a32_skinny_kernel<true>, grid, dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL(w8a32_skinny_kernel<false>, grid, dim3(NT), 0, s, a);
+    if (wt) {
+        if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true>), grid, dim3(NT), 0, s, a);
+        else hipLaunchKernelGGL((w8a32_skinny_kernel<false, true>), grid, dim3(NT), 0, s, a);
+    } else {
+        if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, false>), grid, dim3(NT), 0, s, a);
+        else hipLaunchKernelGGL((w8a32_skinny_kernel<false, false>), grid, dim3(NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -75,9 +75,11 @@ def w8a32_kernel(path, rows, outs, grad=False, k=0):
     those and it allows two or more pieces of 512."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
-    if not grad and rows <= 16 and outs % 16 == 0 and k % 4 == 0 and \
+    # contiguous operands: the weight's rows (N bytes) 16-byte aligned when
+    # N % 16 == 0; N is `outs` forward and the contraction `k` for the gradient
+    if rows <= 16 and k % 4 == 0 and (k if grad else outs) % 16 == 0 and \
             os.environ.get("QGEMM_FORCE_KERNEL") != "tiled":
-        return "w8a32_skinny"   # contiguous operands: 16-byte aligned rows
+        return "w8a32_input_grad_skinny" if grad else "w8a32_skinny"
     if ((rows + 255) // 256) * ((outs + 255) // 256) > 128:
         tile = "256x256"
     else:

@@ -181,10 +181,13 @@ def test_w8a32_ws_workspace_checks():
     decode_need = 1024 + 32 * 8 * 17 * 1024
     args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
     assert b.lib.qgemm_w8a32_ws(*args, FAKE, decode_need - 1, None) == b.QG_ERR_WORKSPACE
-    M, N, K = 16, 8192, 8192
+    M, N, K = 32, 8192, 8192
     need = q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, M, N, K)
     gargs = (M, N, K, FAKE, N, FAKE, N, 1.0, 0, FAKE, K)
     assert b.lib.qgemm_w8a32_input_grad_ws(*gargs, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE
+    M = 16   # the decode kernel: 8 splits of 32 tiles of dA's columns
+    gargs = (M, N, K, FAKE, N, FAKE, N, 1.0, 0, FAKE, K)
+    assert b.lib.qgemm_w8a32_input_grad_ws(*gargs, FAKE, decode_need - 1, None) == b.QG_ERR_WORKSPACE
     # the same argument checks as the calls without a workspace
     assert b.lib.qgemm_w8a32_ws(M, N, K, FAKE, K - 1, FAKE, N, 1.0, 0, FAKE, N, None, 0, None) == \
         b.QG_ERR_INVALID_ARGUMENT

@@ -1,9 +1,9 @@
-"""W8A32 with at most 16 rows against a [K,N] weight on the decode kernel
-(the weight streamed once, K split across workgroups, the fp32 partials
-added in split order): every output within the bound, integer activations
-and an identity weight bit for bit, repeated calls bit for bit, forced and
-single splits, a partial last step of K, a workspace shared with the tiled
-kernels, and the shapes and switches that leave it."""
+"""W8A32 and its input gradient with at most 16 rows on the decode kernel
+(the weight streamed once, the contraction split across workgroups, the
+fp32 partials added in split order): every output within the bound,
+integer activations and an identity weight bit for bit, repeated calls bit
+for bit, forced and single splits, a partial last step, a workspace shared
+with the tiled kernels, and the shapes and switches that leave it."""
 import ctypes
 
 import numpy as np
@@ -143,3 +143,63 @@ def test_w8a32_decode_other_routes():
     c, kern = run(A2, W2, 0.01, -6)
     assert kern != DECODE, kern
     within(c, A2, W2, 0.01, -6)
+
+
+GRAD = "w8a32_input_grad_skinny"
+
+
+def run_grad(dC, W, scale, zp, **kw):
+    d = q.qgemm_w8a32_input_grad(to_dev(dC), to_dev(W), scale, zp, **kw)
+    return d, q.last_kernel()
+
+
+def within_grad(d, dC, W, scale, zp):
+    R, bound = oracle.w8a32_input_grad(dC, W, scale, zp)
+    err = np.abs(d.cpu().numpy().astype(np.float64) - R)
+    worst = float((err / np.maximum(bound, 1e-300)).max())
+    assert np.all(err <= TOL * bound), f"worst relative error {worst:.3e}"
+
+
+@pytest.mark.parametrize("M,N,K,zp", [
+    (1, 8192, 8192, 3),      # dA 1 x 8192 over a sum of 8192
+    (16, 4096, 2000, 0),     # ragged last tile of dA's columns
+    (5, 3008, 1024, -4),     # a partial last step of the sum (3008 = 47 x 64)
+])
+def test_w8a32_input_grad_decode_every_output(M, N, K, zp):
+    case(f"w8a32_input_grad decode M={M} N={N} K={K} zp={zp}")
+    dC, _ = si.w8a32_inputs(M, 1, N, seed=M + N + K + 7)   # [M, N]
+    _, W = si.w8a32_inputs(1, N, K, seed=K + 11)            # [K, N]
+    d, kern = run_grad(dC, W, 0.019, zp)
+    assert kern == GRAD, kern
+    within_grad(d, dC, W, 0.019, zp)
+    d2, _ = run_grad(dC, W, 0.019, zp)
+    assert torch.equal(d, d2), "a repeated call differs"
+
+
+def test_w8a32_input_grad_decode_identity_bit_exact():
+    """W = I: dA = dC exactly (one product per output)."""
+    case("w8a32_input_grad decode identity weight")
+    g = si.rng(80)
+    n = 320
+    mant = (1.0 + g.random((16, n))).astype(np.float32)
+    dC = (mant * np.exp2(g.integers(-100, 101, size=(16, n))).astype(np.float32)
+          * np.where(g.random((16, n)) < 0.5, -1.0, 1.0).astype(np.float32))
+    d, kern = run_grad(dC, np.eye(n, dtype=np.int8), 1.0, 0)
+    assert kern == GRAD, kern
+    np.testing.assert_array_equal(d.cpu().numpy(), dC)
+
+
+def test_w8a32_input_grad_decode_matches_forward_adjoint():
+    """<dC, A W'> == <A, dC W'^T> for W' = (W - zp) * scale: the decode
+    forward and gradient kernels are adjoint to within the sums' rounding."""
+    case("w8a32 decode adjoint 8x2048x4096")
+    A, W = si.w8a32_inputs(8, 2048, 4096, seed=1020)
+    dC, _ = si.w8a32_inputs(8, 1, 2048, seed=1021)
+    c, kern = run(A, W, 0.01, 3)
+    assert kern == DECODE, kern
+    d, kern = run_grad(dC, W, 0.01, 3)
+    assert kern == GRAD, kern
+    lhs = float((dC.astype(np.float64) * c.cpu().numpy().astype(np.float64)).sum())
+    rhs = float((A.astype(np.float64) * d.cpu().numpy().astype(np.float64)).sum())
+    scale_ = float(np.abs(dC).sum() * np.abs(A).max() * 131 * 0.01)
+    assert abs(lhs - rhs) <= 1e-5 * scale_

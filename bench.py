@@ -4,7 +4,8 @@ Headline: A8W8 8192 x 8192 x 8192 (int8 x int8 -> int32 -> fp32 scales ->
 bf16), throughput in tera int8 ops per second, with inputs resident in HBM.
 One step is one call of the operator on that batch.  The same run also times
 the other rows of the path (decode-shaped A8W8 at M = 1, 4, 16 with
-K = N = 8192 in GB/s, MatMulInteger at M = 1 and 16 likewise, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
+K = N = 8192 in GB/s, MatMulInteger, W8A32 and its gradient at M = 1 and 16
+likewise, batched MatMulInteger 8 x 512 x 2048 x 2048, W8A32
 4096^3, the two small parity shapes, A8W8 with an int32 accumulator input
 at 8192^3 and at decode M = 16, MatMulInteger with per-row activation zero
 points, the W8A32 input gradient at 4096^3, DynamicQuantizeLinear on the
@@ -401,6 +402,17 @@ def cpu_oracle_rows(rows, si):
         A, W, s_a, s_w = si.a8w8_inputs(256, 1024, 1024, seed=202)
         fn = lambda: oracle.a8w8(A, W, s_a, s_w)
         attach("a8w8_256x1024x1024_fp32", timed(fn), ops=2.0 * 256 * 1024 * 1024, one_thread_s=one_thread(fn))
+    for m in (1, 16):
+        name = f"w8a32_decode_m{m}_8192"
+        if name in rows:
+            A, W = si.w8a32_inputs(m, 8192, 8192, seed=520 + m)
+            dC, _ = si.w8a32_inputs(m, 1, 8192, seed=530 + m)
+            nbytes = 8192 * 8192 + 4 * m * 8192 * 2
+            attach(name, timed(lambda: oracle.w8a32(A, W, 0.01, -5)), ops=2.0 * m * 8192 * 8192, nbytes=nbytes)
+            gname = f"w8a32_input_grad_decode_m{m}_8192"
+            if gname in rows:
+                attach(gname, timed(lambda: oracle.w8a32_input_grad(dC, W, 0.01, -5)), ops=2.0 * m * 8192 * 8192,
+                       nbytes=nbytes)
     if "w8a32_64x128x64" in rows:
         A, W = si.w8a32_inputs(64, 64, 128, seed=101)
         fn = lambda: oracle.w8a32(A, W, 0.02, 3)
@@ -615,6 +627,28 @@ def main():
             else:
                 os.environ["QGEMM_W8A32"] = prev
         del A, W, tA, tW, outc, dC, tdC
+        # decode-sized W8A32 and its gradient (M = 1, 16 at N = K = 8192),
+        # graph-timed over 9 rotating weights like the int8 decode rows
+        for m in (1, 16):
+            A, W = si.w8a32_inputs(m, 8192, 8192, seed=520 + m)
+            dC, _ = si.w8a32_inputs(m, 1, 8192, seed=530 + m)
+            base_w = to(W)
+            sets = [(to(A), base_w if r == 0 else base_w.clone(), to(dC),
+                     torch.empty((m, 8192), dtype=torch.float32, device=dev)) for r in range(9)]
+            nbytes = 8192 * 8192 + 4 * m * 8192 * 2
+            for grad, name in ((False, f"w8a32_decode_m{m}_8192"), (True, f"w8a32_input_grad_decode_m{m}_8192")):
+                ws = torch.zeros(max(q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD if grad else q.QG_OP_W8A32,
+                                                       1, m, 8192, 8192), 256), dtype=torch.uint8, device=dev)
+                if grad:
+                    call = lambda s: q.qgemm_w8a32_input_grad(s[2], s[1], 0.01, -5, out=s[3], workspace=ws)
+                else:
+                    call = lambda s: q.qgemm_w8a32(s[0], s[1], 0.01, -5, out=s[3], workspace=ws)
+                ms, spread = time_graph(call, sets, 36, max(steps // 2, 5), stream, spread=True)
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                rows[name] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
+                              "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph", "per_call": spread}
+                del ws
+            del sets, base_w
 
     progress(f"GPU rows so far: {sorted(rows)}")
     # ---- DynamicQuantizeLinear on [8, 512, 2048] fp32, and its chain ----

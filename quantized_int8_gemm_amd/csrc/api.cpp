@@ -320,12 +320,12 @@ static size_t mmi_tiled_split_bytes(int64_t M, int64_t N, int splits) {
 }
 
 // The W8A32 decode kernel's shapes (the kernel's view: M x N outputs,
-// contraction K): the bf16 split path, at most 16 rows, 16-byte aligned
+// contraction K): the bf16 split path, at most 64 rows, 16-byte aligned
 // operand rows; the forward also needs N % 16 == 0 (its weight rows are
 // read 16 outputs at a time).  QGEMM_FORCE_KERNEL=tiled turns it off.
 static bool w8a32_skinny_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* W, int64_t ldw,
                             bool wt) {
-    if (!w8a32_split() || M > 16 || env_is("QGEMM_FORCE_KERNEL", "tiled")) return false;
+    if (!w8a32_split() || M > qg::SKINNY_W8A32_MAX_M || env_is("QGEMM_FORCE_KERNEL", "tiled")) return false;
     const bool no_ptrs = A == nullptr && W == nullptr;   // sizing only (qgemm_workspace_bytes)
     return (no_ptrs || (aligned16(A) && aligned16(W))) && lda % 4 == 0 && K % 4 == 0 && ldw % 16 == 0 &&
            (wt || N % 16 == 0);
@@ -345,8 +345,8 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
         // the tiled one otherwise: enough for either
         const bool wt = op == QG_OP_W8A32_INPUT_GRAD;
         if (w8a32_skinny_ok(rows, outs, red, nullptr, red, nullptr, wt ? red : outs, wt)) {
-            qg::w8a32_skinny_plan(outs, red, forced, &splits, &split_k);
-            bytes = std::max(bytes, qg::w8a32_skinny_bytes(outs, splits));
+            qg::w8a32_skinny_plan(rows, outs, red, forced, &splits, &split_k);
+            bytes = std::max(bytes, qg::w8a32_skinny_bytes(rows, outs, splits));
         }
         return bytes;
     }
@@ -375,14 +375,17 @@ size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_
 static qg_status w8a32_run(qg::W8A32Args& a, bool vec_a, bool vec_w, bool wt, void* workspace, size_t workspace_bytes,
                            void* stream, const char* op) {
     if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QG_ERR_INVALID_ARGUMENT;
-    // At most 16 rows against a [K,N] weight with 16-byte rows: the decode
-    // kernel, K split across workgroups when a workspace is given.
+    // At most 64 rows with 16-byte operand rows: the decode kernel (blocks
+    // of 16 rows), the contraction split across workgroups when a workspace
+    // is given.  Rows 17-64 measured against the split 128x128 tiles at
+    // N = K = 8192: 25-38 against 96 us (forward), 34-57 against 98 us
+    // (gradient); at 4096^2 12.6-16.6 against 33-36 us.
     if (w8a32_skinny_ok(a.M, a.N, a.K, a.A, a.lda, a.W, a.ldw, wt)) {
         int splits, split_k;
-        qg::w8a32_skinny_plan(a.N, a.K, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);
+        qg::w8a32_skinny_plan(a.M, a.N, a.K, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);
         if (workspace == nullptr) {
-            qg::w8a32_skinny_plan(a.N, a.K, 1, &splits, &split_k);
-        } else if (qg::w8a32_skinny_bytes(a.N, splits) > workspace_bytes) {
+            qg::w8a32_skinny_plan(a.M, a.N, a.K, 1, &splits, &split_k);
+        } else if (qg::w8a32_skinny_bytes(a.M, a.N, splits) > workspace_bytes) {
             return QG_ERR_WORKSPACE;
         }
         a.workspace = splits > 1 ? workspace : nullptr;

@@ -123,12 +123,14 @@ hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hip
 // contraction, lda the row stride of the fp32 operand.
 void w8a32_split_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int forced, int* splits, int* split_k);
 size_t w8a32_split_bytes(int64_t M, int64_t N, int splits);
-// Decode-shaped W8A32 (M <= 16, 16-byte aligned rows, K % 4 == 0; wt: the
+// Decode-shaped W8A32 (M <= SKINNY_W8A32_MAX_M in blocks of 16 rows, 16-byte
+// aligned rows, K % 4 == 0; wt: the
 // input gradient, W as [outputs][contraction]): 256-output tiles x splits of
 // the contraction (split_k a multiple of 512); the plan gives about one
 // workgroup per CU (forced > 0: that many splits).
-void w8a32_skinny_plan(int64_t N, int64_t K, int forced, int* splits, int* split_k);
-size_t w8a32_skinny_bytes(int64_t N, int splits);
+constexpr int SKINNY_W8A32_MAX_M = 64;   // blocks of 16 rows on the grid's third dimension
+void w8a32_skinny_plan(int64_t M, int64_t N, int64_t K, int forced, int* splits, int* split_k);
+size_t w8a32_skinny_bytes(int64_t M, int64_t N, int splits);
 hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const char** name);
 hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                               const char** name);

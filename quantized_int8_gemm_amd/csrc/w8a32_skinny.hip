@@ -9,7 +9,9 @@
 // in bf16, so the matrix cores form every product exactly and only the fp32
 // accumulation rounds.
 //
-// Grid: (N / 256 column tiles) x (S splits of K), four waves taking 64-row
+// Grid: (N / 256 column tiles) x (S splits of K) x (blocks of 16 rows: up to
+// SKINNY_W8A32_MAX_M rows, each block streaming the weight again, mostly
+// from the Infinity Cache), four waves taking 64-row
 // steps of K round robin, two steps in flight, the weight read with the
 // non-temporal policy (as the int8 decode kernel reads it):
 //  * lane (g = lane/16, c = lane%16) loads rows 16g .. 16g+15 of the step at
@@ -35,6 +37,8 @@
 // 16c + j, which already hold 16 contraction values of output 16c + j in
 // order: they widen to the same bf16 fragments without a transpose, and
 // everything else is the forward kernel's.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -109,7 +113,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     const int tn = blockIdx.x, split = blockIdx.y, S = gridDim.y;
     const int n0 = tn * TN;
     const int cols = p.N - n0;
-    const int M = p.M, K = p.K;
+    // blockIdx.z: the block of 16 rows (p.M up to 16 * gridDim.z)
+    const int rb = blockIdx.z;
+    const int M = p.M - 16 * rb < 16 ? p.M - 16 * rb : 16, K = p.K;
+    const float* Ab = p.A + (int64_t)16 * rb * p.lda;
+    float* Cb = p.C + (int64_t)16 * rb * p.ldc;
+    const int unit = rb * (int)gridDim.x + tn;   // this (row block, column tile)'s ticket
 
     // K range of this split: `per` 64-row steps, a multiple of 2*WAVES.
     const int per = p.split_k / KS;
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     const int ldw = (int)p.ldw, lda = (int)p.lda;
     const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K))
                                              : make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)(((M - 1) * lda + K) * 4));
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (uint32_t)(((M - 1) * lda + K) * 4));
     const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(16 * g * ldw + 16 * c16);
     const uint32_t a_voff = (uint32_t)((c16 * lda + 16 * g) * 4);
 
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
         return s;
     };
     const float zp = (float)p.zp;
-    const bool vec_out = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+    const bool vec_out = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(Cb) & 15) == 0);
     auto epilogue = [&](int m, int n, v4f v) {
         if (n >= p.N) return;
         float f[4] = {v[0], v[1], v[2], v[3]};
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
             if constexpr (ZP) f[e] = f[e] - zp * s2m;
             f[e] = p.scale * f[e];
         }
-        float* dst = p.C + (int64_t)m * p.ldc + n;
+        float* dst = Cb + (int64_t)m * p.ldc + n;
         if (vec_out && n + 4 <= p.N) {
             *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
             return;
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     // column tile, then per column tile S partials of SLOT_ROWS x TN fp32).
     int* tickets = reinterpret_cast<int*>(p.workspace);
     constexpr int SLOT = SLOT_ROWS * TN * 4;
-    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)tn * S * SLOT;
+    char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)unit * S * SLOT;
     const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
     constexpr int COHERENT = 16;   // sc1: device scope
     for (int it = tid; it < items; it += NT) {
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[tn], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) ticket = __hip_atomic_fetch_add(&tickets[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket != S - 1) return;
 
@@ -337,19 +346,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
         const int m = it / (TN / 4), cg = it % (TN / 4);
         epilogue(m, n0 + cg * 4, sum[q]);
     }
-    if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&tickets[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
-void w8a32_skinny_plan(int64_t N, int64_t K, int forced, int* splits, int* split_k) {
-    const int64_t tiles_n = (N + TN - 1) / TN;
+void w8a32_skinny_plan(int64_t M, int64_t N, int64_t K, int forced, int* splits, int* split_k) {
+    const int64_t tiles_n = ((M + 15) / 16) * ((N + TN - 1) / TN);   // (row block, column tile) units
     const int64_t steps = (K + KS - 1) / KS;
     int64_t per;
     if (forced > 0) {
         per = (steps + forced - 1) / forced;
     } else {
-        const int64_t want = (256 + tiles_n - 1) / tiles_n;   // about one workgroup per CU
+        // at most one workgroup per CU (the kernel holds a CU alone): 96
+        // units would otherwise give 3 splits, 288 workgroups, two rounds
+        const int64_t want = std::max<int64_t>(1, 256 / tiles_n);
         per = (steps + want - 1) / want;
     }
     per = ((per + 2 * WAVES - 1) / (2 * WAVES)) * (2 * WAVES);
@@ -363,17 +374,18 @@ void w8a32_skinny_plan(int64_t N, int64_t K, int forced, int* splits, int* split
     *split_k = (int)(per * KS);
 }
 
-size_t w8a32_skinny_bytes(int64_t N, int splits) {
+size_t w8a32_skinny_bytes(int64_t M, int64_t N, int splits) {
     if (splits <= 1) return 0;
-    const size_t tiles_n = (size_t)((N + TN - 1) / TN);
+    const size_t tiles_n = (size_t)((M + 15) / 16) * (size_t)((N + TN - 1) / TN);
     return SKINNY_TICKET_BYTES + tiles_n * (size_t)splits * SLOT_ROWS * TN * 4;
 }
 
 hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const char** name) {
     *name = wt ? "w8a32_input_grad_skinny" : "w8a32_skinny";
-    const dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
-    if (a.M < 1 || a.M > 16 || a.split_k % (KS * 2 * WAVES) != 0 || (int64_t)a.split_k * grid.y < a.K ||
-        (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)))
+    const dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1, (a.M + 15) / 16);
+    if (a.M < 1 || a.M > SKINNY_W8A32_MAX_M || a.split_k % (KS * 2 * WAVES) != 0 ||
+        (int64_t)a.split_k * grid.y < a.K ||
+        (grid.y > 1 && (a.workspace == nullptr || (int)(grid.x * grid.z) > SKINNY_MAX_TICKETS)))
         return hipErrorInvalidValue;
     if (wt) {
         if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true>), grid, dim3(NT), 0, s, a);

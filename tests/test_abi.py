@@ -171,7 +171,7 @@ def test_matmul_integer_split_k_workspace_checks():
 
 
 def test_w8a32_ws_workspace_checks():
-    M, N, K = 32, 8192, 8192   # tiled, K split four ways
+    M, N, K = 80, 8192, 8192   # tiled, K split four ways
     need = q.workspace_bytes(q.QG_OP_W8A32, 1, M, N, K)
     args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
     assert b.lib.qgemm_w8a32_ws(*args, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE
@@ -181,7 +181,7 @@ def test_w8a32_ws_workspace_checks():
     decode_need = 1024 + 32 * 8 * 17 * 1024
     args = (M, N, K, FAKE, K, FAKE, N, 1.0, 0, FAKE, N)
     assert b.lib.qgemm_w8a32_ws(*args, FAKE, decode_need - 1, None) == b.QG_ERR_WORKSPACE
-    M, N, K = 32, 8192, 8192
+    M, N, K = 80, 8192, 8192
     need = q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, M, N, K)
     gargs = (M, N, K, FAKE, N, FAKE, N, 1.0, 0, FAKE, K)
     assert b.lib.qgemm_w8a32_input_grad_ws(*gargs, FAKE, need - 1, None) == b.QG_ERR_WORKSPACE

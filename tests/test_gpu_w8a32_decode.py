@@ -1,4 +1,4 @@
-"""W8A32 and its input gradient with at most 16 rows on the decode kernel
+"""W8A32 and its input gradient with at most 64 rows on the decode kernel
 (the weight streamed once, the contraction split across workgroups, the
 fp32 partials added in split order): every output within the bound,
 integer activations and an identity weight bit for bit, repeated calls bit
@@ -48,6 +48,22 @@ def test_w8a32_decode_every_output(M, N, K, zp):
     within(c, A, W, 0.017, zp)
     c2, _ = run(A, W, 0.017, zp)
     assert torch.equal(c, c2), "a repeated call differs"
+
+
+@pytest.mark.parametrize("M", [17, 40, 64])
+def test_w8a32_decode_row_blocks(M):
+    """17 to 64 rows: blocks of 16 rows on the grid, the last one ragged,
+    forward and gradient."""
+    case(f"w8a32 decode row blocks M={M} 4096x4096")
+    A, W = si.w8a32_inputs(M, 4096, 4096, seed=1030 + M)
+    c, kern = run(A, W, 0.01, -2)
+    assert kern == DECODE, kern
+    within(c, A, W, 0.01, -2)
+    dC, _ = si.w8a32_inputs(M, 1, 4096, seed=1040 + M)
+    d = q.qgemm_w8a32_input_grad(to_dev(dC), to_dev(W), 0.01, -2)
+    assert q.last_kernel() == "w8a32_input_grad_skinny", q.last_kernel()
+    R, bound = oracle.w8a32_input_grad(dC, W, 0.01, -2)
+    assert np.all(np.abs(d.cpu().numpy().astype(np.float64) - R) <= TOL * bound)
 
 
 def test_w8a32_decode_integer_activations_bit_exact():
@@ -105,13 +121,13 @@ def test_w8a32_decode_workspace_shared_with_tiled_shapes():
     """One zeroed workspace for decode and tiled split calls in turn; the
     ticket header ends at zero."""
     case("w8a32 decode/tiled workspace sharing")
-    shapes = [(1, 8192, 8192), (64, 2048, 4096), (16, 4096, 4096), (1, 8192, 8192)]
+    shapes = [(1, 8192, 8192), (100, 2048, 4096), (16, 4096, 4096), (1, 8192, 8192)]
     need = max(q.workspace_bytes(q.QG_OP_W8A32, 1, *s) for s in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     for i, (M, N, K) in enumerate(shapes):
         A, W = si.w8a32_inputs(M, N, K, seed=1000 + i)
         c, kern = run(A, W, 0.01, 2, workspace=ws)
-        assert kern == (DECODE if M <= 16 else "w8a32_bf16x3_128x128_splitk"), kern
+        assert kern == (DECODE if M <= 64 else "w8a32_bf16x3_128x128_splitk"), kern
         within(c, A, W, 0.01, 2)
     assert int(ws[:1024].sum().item()) == 0
 

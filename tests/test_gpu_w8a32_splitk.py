@@ -43,7 +43,7 @@ def within(c, R, bound):
     (257, 1000, 3000, 3),     # ragged M, N and K: 24 tiles, 5 splits of 608 (the last 568)
 ])
 def test_w8a32_split_k_every_output(M, N, K, zp):
-    """(At most 16 rows would take the decode kernel: the tiled one is forced.)"""
+    """(At most 64 rows would take the decode kernel: the tiled one is forced.)"""
     case(f"w8a32 split-K M={M} N={N} K={K} zp={zp}")
     A, W = si.w8a32_inputs(M, N, K, seed=M + N + K)
     with env(QGEMM_FORCE_KERNEL="tiled"):
@@ -64,7 +64,7 @@ def test_w8a32_input_grad_split_every_output(M, N, K, zp):
     case(f"w8a32_input_grad split M={M} N={N} K={K} zp={zp}")
     dC, _ = si.w8a32_inputs(M, 1, N, seed=M + N + 1)   # [M, N]
     _, W = si.w8a32_inputs(1, N, K, seed=K + 5)         # [K, N]
-    with env(QGEMM_FORCE_KERNEL="tiled"):   # at most 16 rows would take the decode kernel
+    with env(QGEMM_FORCE_KERNEL="tiled"):   # at most 64 rows would take the decode kernel
         d, kern = grad(dC, W, 0.021, zp)
         d2, _ = grad(dC, W, 0.021, zp)
         assert kern == w8a32_kernel("bf16x3", M, K, grad=True, k=N), kern
@@ -78,7 +78,7 @@ def test_w8a32_input_grad_split_every_output(M, N, K, zp):
 def test_w8a32_split_k_forced_counts(splits):
     case(f"w8a32 split-K forced splits={splits} 64x2048x4096")
     A, W = si.w8a32_inputs(64, 2048, 4096, seed=950 + splits)
-    with env(QGEMM_W8A32_SPLITS=splits):
+    with env(QGEMM_W8A32_SPLITS=splits, QGEMM_FORCE_KERNEL="tiled"):
         c, kern = fwd(A, W, 0.01, 4)
     assert kern == "w8a32_bf16x3_128x128_splitk", kern
     R, bound = oracle.w8a32(A, W, 0.01, 4)
@@ -110,9 +110,9 @@ def test_w8a32_split_k_workspace_reused_across_shapes():
 def test_w8a32_without_workspace_runs_unsplit():
     """qgemm_w8a32 itself (no workspace) runs the 128 x 128 tiles unsplit,
     and so does the fp32 matrix-core path with one."""
-    case("w8a32 32x2048x4096 unsplit forms")
+    case("w8a32 80x2048x4096 unsplit forms")
     from quantized_int8_gemm_amd import _binding as b
-    M, N, K = 32, 2048, 4096
+    M, N, K = 80, 2048, 4096
     A, W = si.w8a32_inputs(M, N, K, seed=980)
     tA, tW = to_dev(A), to_dev(W)
     C = torch.empty(M, N, dtype=torch.float32, device=dev())

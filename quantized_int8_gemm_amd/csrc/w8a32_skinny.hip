@@ -139,9 +139,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     auto fetch = [&](int step, int b) {
         const int k0 = step * KS;
         if constexpr (WT) {   // W row 16 c16 + j, contraction bytes k0 + 16g ..
+            // cached: a step reads half of each 128-byte line, the other half
+            // is the next step's (1x8192x8192: 22.3 against 22.6 us; 64
+            // rows: 50.3 against 56.0)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)(j * ldw + k0));
-        } else {
+            for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16(w_rsrc, w_voff + (uint32_t)(j * ldw + k0), 0u);
+        } else {   // non-temporal even for several row blocks (M = 64: 37.0 against 43.9 us cached)
 #pragma unroll
             for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
         }

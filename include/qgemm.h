@@ -107,9 +107,9 @@ qg_status qgemm_w8a32(int64_t M, int64_t N, int64_t K,
  * (lda % 4 == 0, K % 4 == 0, ldw % 16 == 0, N % 16 == 0) run a decode
  * kernel that streams W once, 256 columns per workgroup, K divided among
  * workgroups (one ticket per 256 columns; without a workspace, one split).
- * Other outputs of at most 128 tiles of 128 x 128 (e.g. M <= 256 at
- * N = 8192) divide K among up to 8 workgroups per tile (one ticket per
- * tile).  The first 1024 bytes hold the tickets, the rest each split's fp32
+ * Other outputs of at most 256 tiles of 128 x 128 (e.g. M <= 512 at
+ * N = 8192) divide K among up to 8 workgroups per tile, about two per CU
+ * (one ticket per tile).  The first 1024 bytes hold the tickets, the rest each split's fp32
  * partial sums and partial row sums.  The last split to finish adds the
  * partials in split order, so results do not depend on timing and repeat
  * bit for bit; they differ from the unsplit call's only in the order of the
@@ -158,7 +158,7 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
  * qgemm_workspace_bytes(QG_OP_W8A32_INPUT_GRAD, 1, M, N, K) with this call's
  * M, N, K; it divides the sum over n as qgemm_w8a32_ws divides the sum over
  * k (at most 16 rows with 16-byte aligned rows of dC and W: the decode
- * kernel; else dA of at most 128 tiles of 128 x 128), with the same rules.
+ * kernel; else dA of at most 256 tiles of 128 x 128), with the same rules.
  */
 qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K,
                                     const float* dC, int64_t lddc,

@@ -118,9 +118,10 @@ hipError_t launch_w8a32(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hip
 // The same operation on the bf16 matrix cores, with the fp32 operand split
 // exactly into three bf16 parts.
 // Split of the contraction for the 128x128 tiles of the bf16 split kernel
-// (splits = 1: none): outputs of at most 128 such tiles, up to 8 splits of at
-// least 512 values; forced > 0 asks for that many.  M x N outputs, K the
-// contraction, lda the row stride of the fp32 operand.
+// (splits = 1: none): outputs of at most 256 such tiles, up to 8 splits of at
+// least 512 values, about two workgroups per CU; forced > 0 asks for that
+// many.  M x N outputs, K the contraction, lda the row stride of the fp32
+// operand.
 void w8a32_split_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int forced, int* splits, int* split_k);
 size_t w8a32_split_bytes(int64_t M, int64_t N, int splits);
 // Decode-shaped W8A32 (M <= SKINNY_W8A32_MAX_M in blocks of 16 rows, 16-byte

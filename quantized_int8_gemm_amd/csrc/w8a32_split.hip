@@ -458,9 +458,14 @@ void w8a32_split_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int forced, 
     *splits = 1;
     *split_k = 0;
     if (big_tiles(M, N, K, lda)) return;
+    // About two workgroups per CU (the 128x128 tiles run two per CU):
+    // graph-timed at N = K = 8192, 64 tiles (M = 80 / 128) take 70.3 / 77.1
+    // us with 8 splits against 98.7 / 102.9 with 4, and 128 tiles (M = 256)
+    // 128.7 with 4 against 181.9 with 2; at 4096^2, M = 256 / 384 / 512
+    // (64 / 96 / 128 tiles) 48.5 / 68.1 / 70.7 against 58.6 / 98.0 / 97.8.
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles > SKINNY_MAX_TICKETS / 2) return;
-    int64_t S = forced > 0 ? forced : std::min<int64_t>(std::min<int64_t>(256 / tiles, K / 512), 8);
+    if (tiles > SKINNY_MAX_TICKETS) return;
+    int64_t S = forced > 0 ? forced : std::min<int64_t>(std::min<int64_t>(512 / tiles, K / 512), 8);
     if (S < 2) return;
     const int64_t chunks = (K + BKF - 1) / BKF;
     const int64_t per = (chunks + S - 1) / S;

@@ -71,7 +71,7 @@ def w8a32_kernel(path, rows, outs, grad=False, k=0):
     outputs over a contraction of `k` on `path`, through the binding (which
     passes a workspace): the decode kernel for at most 64 rows, else 256 x
     256 split tiles from 129 of them on, else 128 x 128 tiles, the
-    contraction divided among workgroups when there are at most 128 of
+    contraction divided among workgroups when there are at most 256 of
     those and it allows two or more pieces of 512."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
@@ -85,8 +85,8 @@ def w8a32_kernel(path, rows, outs, grad=False, k=0):
     else:
         tile = "128x128"
         tiles = ((rows + 127) // 128) * ((outs + 127) // 128)
-        splits = int(os.environ.get("QGEMM_W8A32_SPLITS", "0")) or min(256 // tiles, k // 512, 8)
-        if tiles <= 128 and splits >= 2:
+        splits = int(os.environ.get("QGEMM_W8A32_SPLITS", "0")) or min(512 // tiles, k // 512, 8)
+        if tiles <= 256 and splits >= 2:
             chunks = (k + 31) // 32
             per = (chunks + splits - 1) // splits
             if (chunks + per - 1) // per >= 2:

@@ -61,10 +61,13 @@ def test_workspace_bytes():
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 8192) == 1024 + 64 * 4 * 128 * 128 * 4
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 8192, 1024) == 0      # K too short to split
     assert q.workspace_bytes(q.QG_OP_A8W8, 1, 2048, 4096, 8192) == 0    # 512 tiles fill the chip
-    # W8A32: 128x128 tiles over K split four ways at M = 16, N = K = 8192 (64
-    # tiles): the ticket header, then per split a 64 KiB fp32 tile and 512
-    # bytes of row sums
-    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 1024 + 64 * 4 * (65536 + 512)
+    # W8A32: 128x128 tiles over K split eight ways at M = 16, N = K = 8192 (64
+    # tiles, two workgroups per CU): the ticket header, then per split a 64 KiB
+    # fp32 tile and 512 bytes of row sums
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 16, 8192, 8192) == 1024 + 64 * 8 * (65536 + 512)
+    # 256 tiles (M = 512) still split, two ways; 512 do not
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 512, 8192, 8192) == 1024 + 256 * 2 * (65536 + 512)
+    assert q.workspace_bytes(q.QG_OP_W8A32, 1, 1024, 8192, 8192) == 0
     # at most 16 rows the size covers both the decode kernel (17 rows of 256
     # floats per split and column tile) and the tiled one, which unaligned
     # rows take: here the tiled one's 2 splits of 64 tiles

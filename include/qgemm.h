@@ -197,10 +197,12 @@ qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K,
  *     next call on the same stream, of this or any other shape, without
  *     clearing; calls that overlap in time must not share one.  With NULL,
  *     both run unsplit (decode shapes as a single-pass kernel).  A [N,K]
- *     weight (b_trans == 1) at M <= 16 is sized as a decode shape and splits
- *     only when the workspace passed holds its plan.
- * Decode shapes (M <= 16, b_trans == 0) run a bandwidth-bound kernel that
- * streams W once; all other shapes run the tiled matrix-core kernel.
+ *     weight (b_trans == 1) at M <= 16 whose rows are not 16-byte aligned
+ *     runs the tiled kernel, which splits only when the workspace passed
+ *     holds its plan (the size returned is the decode kernel's).
+ * Decode shapes (M <= 16, W as [K,N], or as [N,K] with 16-byte aligned rows
+ * and K % 16 == 0) run a bandwidth-bound kernel that streams W once; all
+ * other shapes run the tiled matrix-core kernel.
  * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
  */
 qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,

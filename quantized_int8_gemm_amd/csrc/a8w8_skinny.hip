@@ -73,7 +73,7 @@ __device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
 
 // MatMulInteger's sums do not fit beside two waves per SIMD; its grid gives
 // one workgroup per CU anyway.
-template <bool VEC, int EPI>
+template <bool VEC, int EPI, bool BKM = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I32 ? 1 : 2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
     constexpr bool I32 = EPI == EPI_I32;
     // A split's partial: 16 rows of the tile, then (MatMulInteger) a row of
@@ -102,10 +102,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     const int s_begin = split * per;
 
     const int ldb = (int)p.ldb, lda = (int)p.lda;
-    const int8_t* Wt = p.B + n0;
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wt, (uint32_t)((p.K - 1) * ldb + cols));
+    const int8_t* Wt = BKM ? p.B + (int64_t)n0 * ldb : p.B + n0;
+    const __amdgpu_buffer_rsrc_t w_rsrc = BKM ? make_rsrc(Wt, (uint32_t)((cols - 1) * ldb + p.K))
+                                              : make_rsrc(Wt, (uint32_t)((p.K - 1) * ldb + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)((p.M - 1) * lda + p.K));
-    const uint32_t w_voff = (uint32_t)(16 * g * ldb + 16 * c16);
+    const uint32_t w_voff = BKM ? (uint32_t)(16 * c16 * ldb + 16 * g) : (uint32_t)(16 * g * ldb + 16 * c16);
     const uint32_t a_voff = (uint32_t)(c16 * lda + 16 * g);
 
     // The epilogue's scales (MatMulInteger: zero-point terms), loaded now so
@@ -141,8 +142,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     auto fetch = [&](int step, int b) {
         const int k0 = step * KS;
         if constexpr (VEC) {
+            if constexpr (BKM) {
+                // W as [N,K]: row 16 c16 + j, k-bytes k0 + 16g ..  is already
+                // the B fragment of column 16 c16 + j (cached: each step
+                // reads half of every 128-byte line)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb));
+                for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16(w_rsrc, w_voff + (uint32_t)(j * ldb + k0), 0u);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldb));
+            }
             abuf[b] = buffer_load16(a_rsrc, a_voff + (uint32_t)k0, 0u);
         } else {
 #pragma unroll
@@ -202,7 +211,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
                 wbuf[b][r] = u32x4{wbuf[b][r].x ^ fb, wbuf[b][r].y ^ fb, wbuf[b][r].z ^ fb, wbuf[b][r].w ^ fb};
             rs = sum_i8x4(abuf[b].w, sum_i8x4(abuf[b].z, sum_i8x4(abuf[b].y, sum_i8x4(abuf[b].x, rs))));
         }
-        transpose16x16_inplace(wbuf[b]);
+        if constexpr (BKM) {
+            // bytes past K in a row of either operand are the next row's:
+            // a 16-byte piece there (K % 16 == 0) multiplies nothing
+            if (step * KS + 16 * g >= p.K) abuf[b] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            transpose16x16_inplace(wbuf[b]);
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[j] = mfma_i8_16x16x64(abuf[b], wbuf[b][j], acc[j]);
         if constexpr (I32) {
@@ -552,13 +567,17 @@ int skinny_splits(int M, int N, int K) {
     return skinny_splits_for(N, K, skinny_split_steps(N, K));
 }
 
-hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s, const char** name) {
+hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s, const char** name, bool bkm) {
     dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
     *name = epi == EPI_I32 ? "matmul_integer_skinny" : "a8w8_skinny";
     if (a.split_steps % (2 * WAVES) != 0 || (int64_t)a.split_steps * grid.y * KS < a.K) return hipErrorInvalidValue;
     if (grid.y > 1 && (a.workspace == nullptr || (int)grid.x > SKINNY_MAX_TICKETS)) return hipErrorInvalidValue;
     if (a.M > 16 || a.batch != 1) return hipErrorInvalidValue;
-    if (epi == EPI_I32) {   // 16-byte rows, B as [K,N], whole 64-row steps
+    if (bkm) {   // A8W8 with W as [N,K]: 16-byte rows, K % 16 == 0
+        if (!vec || epi == EPI_I32 || a.K % 16 != 0) return hipErrorInvalidValue;
+        if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32, true>), grid, dim3(NT), 0, s, a);
+        else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16, true>), grid, dim3(NT), 0, s, a);
+    } else if (epi == EPI_I32) {   // 16-byte rows, B as [K,N], whole 64-row steps
         if (!vec || a.K % KS != 0 || (a.a_zp != nullptr && a.a_zp_rows < 1)) return hipErrorInvalidValue;
         hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_I32>), grid, dim3(NT), 0, s, a);
     } else if (vec) {

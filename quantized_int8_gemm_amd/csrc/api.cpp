@@ -506,7 +506,10 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
 
     const char* name = "";
     hipError_t e;
-    if (a8w8_is_skinny(M, b_trans)) {
+    // Decode shapes: W as [K,N], or as [N,K] with 16-byte aligned rows (each
+    // weight row then already holds its column's k-bytes).
+    const bool skinny_bkm = b_trans != 0 && vec && a8w8_is_skinny(M, 0);
+    if (a8w8_is_skinny(M, b_trans) || skinny_bkm) {
         int splits, per;
         a8w8_skinny_plan(M, N, K, &splits, &per);
         const size_t need = qg::skinny_workspace_bytes((int)M, (int)N, splits);
@@ -526,7 +529,7 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
         a.workspace = workspace;
         a.splits = splits;
         a.split_steps = per;
-        e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name);
+        e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name, skinny_bkm);
         log_dispatch(op, name, 1, M, N, K, splits);
     } else {
         const int cfg = pick_tile(1, M, N);

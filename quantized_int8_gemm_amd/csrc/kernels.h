@@ -93,8 +93,9 @@ constexpr size_t SKINNY_SCRATCH_BYTES = SKINNY_TICKET_BYTES + ((size_t)8 << 20);
 hipError_t skinny_scratch(hipStream_t s, void** ptr);
 // epi EPI_F32 / EPI_BF16: A8W8; EPI_I32: MatMulInteger (16-byte rows, K a
 // multiple of 64, flips and zero points as in the tiled kernels).
+// bkm: A8W8 with W as [N,K] (vec only).
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s,
-                              const char** name);
+                              const char** name, bool bkm = false);
 // sums: MatMulInteger partials, which carry row and column sums too
 size_t skinny_workspace_bytes(int M, int N, int splits, bool sums = false);
 int skinny_splits(int M, int N, int K);

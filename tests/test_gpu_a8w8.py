@@ -259,3 +259,44 @@ def test_matmul_integer_tile_choice_by_tile_count(M, N, K, kernel):
     y = q.matmul_integer(to_dev(A), to_dev(B), to_dev(za), to_dev(zb))
     assert q.last_kernel() == kernel, q.last_kernel()
     np.testing.assert_array_equal(y.cpu().numpy(), oracle.matmul_integer(A, B, za, zb))
+
+
+@pytest.mark.parametrize("M,N,K,out", [
+    (1, 8192, 8192, "bf16"),    # 32 column tiles, 8 splits
+    (4, 4096, 4096, "f32"),
+    (16, 2000, 2048, "bf16"),   # ragged last column tile
+    (7, 1000, 3024, "f32"),     # K % 64 == 16: a piece of the last step lies past K
+])
+def test_a8w8_decode_weight_as_n_by_k(M, N, K, out):
+    """W given as [N,K] (b_trans) at decode shapes: the decode kernel reads
+    each weight row's k-bytes directly; every output against the oracle."""
+    case(f"a8w8 decode b_trans M={M} N={N} K={K} {out}")
+    A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K + 9)
+    Wt = np.ascontiguousarray(W.T)
+    ref = oracle.a8w8(A, Wt, s_a, s_w, b_trans=True)
+    res = run(A, Wt, s_a, s_w, torch.bfloat16 if out == "bf16" else torch.float32, b_trans=True)
+    assert q.last_kernel() == "a8w8_skinny", q.last_kernel()
+    got = bf16_bits(res) if out == "bf16" else res.cpu().numpy()
+    np.testing.assert_array_equal(got, ref[out])
+
+
+def test_a8w8_decode_weight_as_n_by_k_splits_acc_noalloc():
+    """[N,K] decode: every split count gives the same bits, as do the
+    accumulator-input form and the workspace-free entry point."""
+    case("a8w8 decode b_trans M=16 N=2048 K=8192 splits / acc / noalloc")
+    A, W, s_a, s_w = si.a8w8_inputs(16, 2048, 8192, seed=19)
+    Wt = np.ascontiguousarray(W.T)
+    ref = oracle.a8w8(A, Wt, s_a, s_w, b_trans=True)["bf16"]
+    for s in (1, 3, 16, 64):
+        with env(QGEMM_SPLITS=s):
+            np.testing.assert_array_equal(bf16_bits(run(A, Wt, s_a, s_w, torch.bfloat16, b_trans=True)), ref)
+        assert q.last_kernel() == "a8w8_skinny", q.last_kernel()
+    acc = si.randint(si.rng(20), (16, 2048), -(1 << 28), 1 << 28, np.int32)
+    out = q.qgemm_a8w8_acc(to_dev(acc), to_dev(A), to_dev(Wt), to_dev(s_a), to_dev(s_w),
+                           out_dtype=torch.float32, b_trans=True)
+    assert q.last_kernel() == "a8w8_skinny", q.last_kernel()
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.a8w8_acc(acc, A, W, s_a, s_w)["f32"])
+    out = q.qgemm_a8w8_noalloc(to_dev(A), to_dev(Wt), to_dev(s_a), to_dev(s_w), out_dtype=torch.bfloat16,
+                               b_trans=True)
+    assert q.last_kernel() == "a8w8_skinny", q.last_kernel()
+    np.testing.assert_array_equal(bf16_bits(out), ref)

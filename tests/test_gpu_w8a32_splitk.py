@@ -126,3 +126,25 @@ def test_w8a32_without_workspace_runs_unsplit():
         c, kern = fwd(A, W, 0.01, 6)
     assert kern == "w8a32_tiled_128x128", kern
     within(c, R, bound)
+
+
+def test_w8a32_split_k_unaligned_rows():
+    """Rows of A and W that are not 16-byte aligned (lda = K + 1, ldw = N + 3)
+    take the scalar loads, split over K like the vector path."""
+    case("w8a32 split-K unaligned 64x2048x4096")
+    M, N, K = 64, 2048, 4096
+    A, W = si.w8a32_inputs(M, N, K, seed=1100)
+    d = dev()
+    Ab = torch.zeros(M, K + 1, dtype=torch.float32, device=d)
+    Ab[:, :K] = to_dev(A)
+    Wb = torch.zeros(K, N + 3, dtype=torch.int8, device=d)
+    Wb[:, :N] = to_dev(W)
+    c = q.qgemm_w8a32(Ab[:, :K], Wb[:, :N], 0.01, 5)
+    assert q.last_kernel() == "w8a32_bf16x3_128x128_splitk", q.last_kernel()
+    within(c, *oracle.w8a32(A, W, 0.01, 5))
+    dC, _ = si.w8a32_inputs(M, 1, N, seed=1101)
+    Cb = torch.zeros(M, N + 1, dtype=torch.float32, device=d)
+    Cb[:, :N] = to_dev(dC)
+    g = q.qgemm_w8a32_input_grad(Cb[:, :N], Wb[:, :N], 0.01, 5)
+    assert q.last_kernel() == "w8a32_input_grad_bf16x3_128x128_splitk", q.last_kernel()
+    within(g, *oracle.w8a32_input_grad(dC, W, 0.01, 5))

@@ -539,7 +539,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
                          (reinterpret_cast<uintptr_t>(p.acc_in) & 15) == 0;
     auto acc_in4 = [&](int m, int n) -> v4i {
         const int32_t* src = p.acc_in + (int64_t)m * p.ld_acc + n;
-        if (acc_vec && n + 4 <= p.N) return *reinterpret_cast<const v4i*>(src);
+        if (acc_vec && n + 4 <= p.N) return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
         v4i r = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -676,7 +676,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void int8_dma_kernel(In
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
             const uint32_t c = (uint32_t)(wn * WN + b * 16 + 4 * g);
-            dst[b] = __builtin_bit_cast(v4i, buffer_load16(acc_rsrc, (r * (uint32_t)p.ld_acc + c) * 4u, 0u));
+            // non-temporal: each accumulator is read once, and cached reads
+            // of them evict weight panels (8192^3 bf16: 482.2 -> 452.2 us)
+            dst[b] = __builtin_bit_cast(v4i, buffer_load16_nt(acc_rsrc, (r * (uint32_t)p.ld_acc + c) * 4u));
         }
     };
 

@@ -860,11 +860,15 @@ qg_status conv_integer(int64_t N, int64_t C, int64_t H, int64_t W, const void* x
     if (workspace_bytes < plan.total) return QG_ERR_WORKSPACE;
     const qg::ConvGeom& g = plan.g;
     if (plan.implicit) {
+        // One launch when x's rows are 16-byte aligned (QGEMM_CONV=twopass
+        // keeps the padded-copy pass for comparisons).
+        const bool fused = !env_is("QGEMM_CONV", "twopass") && qg::conv_fused_ok(g, plan.ip, x, w);
+        const char* name = fused ? "conv_fused" : "conv_implicit";
         (void)hipGetLastError();
         const hipError_t e = qg::launch_conv_implicit(g, plan.ip, x, x_u8, x_zero_point, w, w_u8, w_zero_point,
-                                                      (int)w_zero_point_len, workspace, y, (hipStream_t)stream);
-        log_dispatch("conv_integer", "conv_implicit", N, M, (int64_t)g.P, g.Kg, g.group);
-        return finish_launch(e, "conv_implicit");
+                                                      (int)w_zero_point_len, workspace, y, fused, (hipStream_t)stream);
+        log_dispatch("conv_integer", name, N, M, (int64_t)g.P, g.Kg, g.group);
+        return finish_launch(e, name);
     }
     // 32-bit buffer offsets inside one GEMM operand: a packed group of w and
     // one image's column matrix.

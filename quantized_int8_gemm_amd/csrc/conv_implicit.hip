@@ -24,6 +24,15 @@
 //    against that tap's weights on the int8 matrix cores: a B fragment is
 //    16 channels of one position, read with ds_read_b128 at the position the
 //    tap moves it to, so no data is reordered per tap.
+// FUSED (one launch, no workspace): where x's rows are 16-byte aligned
+// (W % 16 == 0), the main kernel stages the halo straight from x: a lane
+// loads 16 columns of 4 channels (four 16-byte vectors), regroups them into
+// one 4-channel word per column with byte permutes and writes each word to
+// the position's 16-byte slot in LDS; halo positions outside the input get
+// x_zp.  Its weight rows come straight from w the same way (4 channels x the
+// taps of one output channel per lane, each tap's 4 bytes one word), their
+// row sums added into LDS.  The multiplies and the epilogue are the same.
+//
 // With a' = w - sa and b' = x - sb the flipped values (sa, sb = 128 for
 // uint8, else 0), ca[m] = sa - w_zp[m] and cb = sb - x_zp:
 //   sum (w - w_zp)(x - x_zp) = sum a'b' + cb*rowsum'(m) + ca[m]*colsum'(p)
@@ -40,6 +49,7 @@ namespace qg {
 namespace {
 
 constexpr int CI_NT = 256;
+constexpr int CONV_FUSED_MAX_DYN_LDS = 159 * 1024;
 
 struct ConvPrepArgs {
     ConvGeom c;
@@ -182,7 +192,31 @@ struct ConvImplicitArgs {
     const uint8_t* w_zp; int w_zp_len; int w_u8;  // ca[m] = sa - w_zp[m]
     int32_t sa, cb;                               // cb = sb - x_zp
     int32_t* y;
+    // FUSED: the operands themselves, their flips, x_zp (flipped) in every byte
+    const uint8_t* x; const uint8_t* w; uint32_t x_flip, w_flip, zf4;
 };
+
+// FUSED weight staging: output channel m's 4 channels c .. c+3 of the block,
+// all T taps (4*T consecutive bytes of w, already loaded as T words), as one
+// word per tap at the tap's slot of row r; returns the sum of the 4*T
+// flipped int8 values.
+template <int T>
+__device__ __forceinline__ int stage_w_quad(const uint32_t* wd, uint32_t flip, uint8_t* row, int r, int cq) {
+    int sum = 0;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        uint32_t d = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = e * T + t;   // channel c + e, tap t
+            const uint32_t b = ((wd[idx >> 2] >> (8 * (idx & 3))) & 0xffu) ^ flip;
+            d |= b << (8 * e);
+            sum += (int)(int8_t)(uint8_t)b;
+        }
+        *reinterpret_cast<uint32_t*>(row + ((4 * t + ((cq >> 2) ^ ((r >> 2) & 3))) << 4) + 4 * (cq & 3)) = d;
+    }
+    return sum;
+}
 
 // 16-byte slot of channel group j at halo column col: j ^ ((col >> 2) & 3),
 // so the 16 positions of a fragment read (16 consecutive columns) fall in 16
@@ -195,7 +229,7 @@ __device__ __forceinline__ int w_slot(int r, int t, int j) { return 4 * t + (j ^
 
 // BM output channels (64 or 128) x 128 positions per workgroup; four waves,
 // each 64 channels x (128 / (4 / (BM / 64))) positions.
-template <int BW, int BM, int NPOS>
+template <int BW, int BM, int NPOS, bool FUSED>
 __global__ __launch_bounds__(CI_NT) void conv_implicit_kernel(ConvImplicitArgs p) {
     constexpr int WAVES_M = BM / 64, WAVES_N = 4 / WAVES_M;
     constexpr int WNP = NPOS / WAVES_N;              // positions per wave
@@ -234,7 +268,13 @@ __global__ __launch_bounds__(CI_NT) void conv_implicit_kernel(ConvImplicitArgs p
             zw = p.w_u8 ? (int)p.w_zp[idx] : (int)(int8_t)p.w_zp[idx];
         }
         ca_r[a] = (uint32_t)(p.sa - zw);
-        rs_r[a] = (uint32_t)p.rowsum[mm];
+        rs_r[a] = FUSED ? 0u : (uint32_t)p.rowsum[mm];
+    }
+    // FUSED: the row sums of this tile's flipped weights, built while staging
+    __shared__ int rs_lds[FUSED ? BM : 1];
+    if constexpr (FUSED) {
+        if (tid < BM) rs_lds[tid] = 0;
+        __syncthreads();
     }
 
     const int a_bytes = BM * p.a_pitch;
@@ -277,29 +317,147 @@ __global__ __launch_bounds__(CI_NT) void conv_implicit_kernel(ConvImplicitArgs p
     const int h_r0 = h_p0 / p.hc, h_c0 = h_p0 - h_r0 * p.hc;
     for (int blk = 0; blk < p.cblocks; ++blk) {
         if (blk > 0) __syncthreads();   // every wave is done with the previous block
-        {   // weights: unit q*256 + tid of the A region is row ar, unit as
-            int ar = a_r0, as = a_s0;
-            const int64_t kblk = (int64_t)blk * p.taps * 64;
-            for (int q = 0; q < p.a_rounds; ++q) {
-                uint32_t off = OUT;
-                if (as < 4 * p.taps && m0 + ar < c.Mg) {
-                    const int tp = as >> 2, j = (as & 3) ^ ((ar >> 2) & 3);
-                    off = (uint32_t)((int64_t)(m0 + ar) * p.kt + kblk + 64 * tp + 16 * j);
+        if constexpr (FUSED) {
+            // weights: unit u = q * 256 + tid is row r = u / 16, channels
+            // 4 (u % 16) .. + 3; every unit's loads are issued before any is
+            // used (rows past Mg multiply into outputs never stored: skipped)
+            const bool need_rs = p.cb != 0;
+            constexpr int WU = BM * 16 / CI_NT;
+            auto wsrc = [&](int r, int cq) {
+                return p.w + ((int64_t)(g * c.Mg + m0 + r) * c.Cg + blk * 64 + 4 * cq) * p.taps;
+            };
+            if (p.taps == 9 || p.taps == 1) {
+                uint32_t wd[WU][9];
+#pragma unroll
+                for (int q = 0; q < WU; ++q) {
+                    const int u = q * CI_NT + tid, r = u >> 4, cq = u & 15;
+                    if (m0 + r >= c.Mg) continue;
+                    const uint8_t* src = wsrc(r, cq);
+                    if (p.taps == 9) {
+#pragma unroll
+                        for (int i = 0; i < 9; ++i) wd[q][i] = *reinterpret_cast<const uint32_t*>(src + 4 * i);
+                    } else {
+                        wd[q][0] = *reinterpret_cast<const uint32_t*>(src);
+                    }
                 }
-                dma::dma16(w_rsrc, off, lds0 + (uint32_t)(q * CI_NT + wave * 64) * 16u);
-                as += p.a_dr; ar += p.a_dq;
-                if (as >= a_upr) { as -= a_upr; ++ar; }
+#pragma unroll
+                for (int q = 0; q < WU; ++q) {
+                    const int u = q * CI_NT + tid, r = u >> 4, cq = u & 15;
+                    if (m0 + r >= c.Mg) continue;
+                    uint8_t* row = smem + r * p.a_pitch;
+                    const int sum = p.taps == 9 ? stage_w_quad<9>(wd[q], p.w_flip, row, r, cq)
+                                                : stage_w_quad<1>(wd[q], p.w_flip, row, r, cq);
+                    if (need_rs) atomicAdd(&rs_lds[r], sum);
+                }
+            } else for (int u = tid; u < BM * 16; u += CI_NT) {
+                const int r = u >> 4, cq = u & 15;
+                if (m0 + r >= c.Mg) continue;
+                const uint8_t* src = wsrc(r, cq);
+                uint8_t* row = smem + r * p.a_pitch;
+                int sum;
+                {
+                    sum = 0;
+                    for (int t = 0; t < p.taps; ++t) {
+                        uint32_t d = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t b = (uint32_t)src[e * p.taps + t] ^ p.w_flip;
+                            d |= b << (8 * e);
+                            sum += (int)(int8_t)(uint8_t)b;
+                        }
+                        *reinterpret_cast<uint32_t*>(row + ((4 * t + ((cq >> 2) ^ ((r >> 2) & 3))) << 4) + 4 * (cq & 3)) = d;
+                    }
+                }
+                if (need_rs) atomicAdd(&rs_lds[r], sum);
             }
-        }
-        {   // halo: unit q*256 + tid is position (hr_, hc_) of the halo, slot h_slot
-            int hr_ = h_r0, hc_ = h_c0;
-            for (int q = 0; q < p.h_rounds; ++q) {
-                uint32_t off = OUT;
-                if (hr_ < p.hr)
-                    off = (uint32_t)(((int64_t)hr_ * p.wp_cols + hc_) * p.cgp + blk * 64 + 16 * halo_slot(hc_, h_slot));
-                dma::dma16(x_rsrc, off, lds_h + (uint32_t)(q * CI_NT + wave * 64) * 16u);
-                hc_ += p.h_dr; hr_ += p.h_dq;
-                if (hc_ >= p.hc) { hc_ -= p.hc; ++hr_; }
+            // halo from x: positions inside the input, as units of 4 channels x
+            // one aligned 16-column piece of one halo row
+            uint8_t* Hd = smem + a_bytes;
+            const int ih0 = oh0 * c.sh - c.pt, iw0 = ow0 * c.sw - c.pl;
+            const int c_lo = iw0 > 0 ? iw0 : 0;
+            const int c_hi = iw0 + p.hc < c.W ? iw0 + p.hc : c.W;
+            const int cs0 = c_lo & ~15;
+            const int nchunks = c_hi > c_lo ? (c_hi - cs0 + 15) >> 4 : 0;
+            const int64_t plane = (int64_t)c.H * c.W;
+            const uint8_t* xblk = p.x + ((int64_t)n * c.C + (int64_t)g * c.Cg + blk * 64) * plane;
+            const int units = 16 * p.hr * nchunks;
+            // XU units per lane per round, their loads issued together
+            constexpr int XU = 2;
+            for (int u0 = tid; u0 < units; u0 += XU * CI_NT) {
+                u32x4 v[XU][4];
+                int rr_[XU], cs_[XU];
+                bool ok[XU];
+#pragma unroll
+                for (int q = 0; q < XU; ++q) {
+                    const int u = u0 + q * CI_NT;
+                    const int cq = u & 15, rk = u >> 4;
+                    const int r = rk / nchunks, k = rk - r * nchunks;
+                    const int ih = ih0 + r;
+                    rr_[q] = r;
+                    cs_[q] = cs0 + 16 * k;
+                    ok[q] = u < units && ih >= 0 && ih < c.H;
+                    if (!ok[q]) continue;
+                    const uint8_t* src = xblk + (int64_t)(4 * cq) * plane + (int64_t)ih * c.W + cs_[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[q][e] = *reinterpret_cast<const u32x4*>(src + (int64_t)e * plane);
+                }
+#pragma unroll
+                for (int q = 0; q < XU; ++q) {
+                    if (!ok[q]) continue;
+                    const int cq = (u0 + q * CI_NT) & 15, r = rr_[q], cs = cs_[q];
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        // columns cs + 4 k4 .. + 3: a 4x4 byte transpose turns the
+                        // four channels' words into one word per column
+                        uint32_t xin[4], col4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xin[e] = (&v[q][e].x)[k4];
+                        transpose4x4_bytes(xin, col4);
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const int iw = cs + 4 * k4 + i4;
+                            if (iw < c_lo || iw >= c_hi) continue;
+                            const int col = iw - iw0;
+                            *reinterpret_cast<uint32_t*>(Hd + 16 * (((r * p.hc + col) << 2) + halo_slot(col, cq >> 2)) +
+                                                         4 * (cq & 3)) = col4[i4] ^ (p.x_flip * 0x01010101u);
+                        }
+                    }
+                }
+            }
+            // positions outside the input hold x_zp
+            for (int pidx = tid; pidx < p.hr * p.hc; pidx += CI_NT) {
+                const int r = pidx / p.hc, col = pidx - r * p.hc;
+                const int ih = ih0 + r, iw = iw0 + col;
+                if (ih >= 0 && ih < c.H && iw >= 0 && iw < c.W) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x4*>(Hd + 16 * ((pidx << 2) + j)) = u32x4{p.zf4, p.zf4, p.zf4, p.zf4};
+            }
+        } else {
+            {   // weights: unit q*256 + tid of the A region is row ar, unit as
+                int ar = a_r0, as = a_s0;
+                const int64_t kblk = (int64_t)blk * p.taps * 64;
+                for (int q = 0; q < p.a_rounds; ++q) {
+                    uint32_t off = OUT;
+                    if (as < 4 * p.taps && m0 + ar < c.Mg) {
+                        const int tp = as >> 2, j = (as & 3) ^ ((ar >> 2) & 3);
+                        off = (uint32_t)((int64_t)(m0 + ar) * p.kt + kblk + 64 * tp + 16 * j);
+                    }
+                    dma::dma16(w_rsrc, off, lds0 + (uint32_t)(q * CI_NT + wave * 64) * 16u);
+                    as += p.a_dr; ar += p.a_dq;
+                    if (as >= a_upr) { as -= a_upr; ++ar; }
+                }
+            }
+            {   // halo: unit q*256 + tid is position (hr_, hc_) of the halo, slot h_slot
+                int hr_ = h_r0, hc_ = h_c0;
+                for (int q = 0; q < p.h_rounds; ++q) {
+                    uint32_t off = OUT;
+                    if (hr_ < p.hr)
+                        off = (uint32_t)(((int64_t)hr_ * p.wp_cols + hc_) * p.cgp + blk * 64 + 16 * halo_slot(hc_, h_slot));
+                    dma::dma16(x_rsrc, off, lds_h + (uint32_t)(q * CI_NT + wave * 64) * 16u);
+                    hc_ += p.h_dr; hr_ += p.h_dq;
+                    if (hc_ >= p.hc) { hc_ -= p.hc; ++hr_; }
+                }
             }
         }
         dma::wait_vmcnt<0>();
@@ -331,6 +489,10 @@ __global__ __launch_bounds__(CI_NT) void conv_implicit_kernel(ConvImplicitArgs p
         }
     }
 
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) rs_r[a] = (uint32_t)rs_lds[wm * 64 + 16 * a + i16];
+    }
     // column sums over the four lane groups (channel groups)
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
@@ -442,24 +604,65 @@ bool conv_implicit_plan(const ConvGeom& c, ConvImplicitPlan* p) {
 namespace {
 
 // LDS beyond 64 KiB per workgroup is granted per kernel (160 KiB on gfx950).
-template <int BW, int BM, int NPOS>
+template <int BW, int BM, int NPOS, bool FUSED>
 hipError_t launch_main(const dim3& grid, const ConvImplicitArgs& a, int lds, hipStream_t s) {
     static bool granted = false;
     if (!granted) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(conv_implicit_kernel<BW, BM, NPOS>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        // the fused form's row sums take 1 KiB of static LDS (the dynamic
+        // region is 1 KiB aligned)
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(conv_implicit_kernel<BW, BM, NPOS, FUSED>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 FUSED ? CONV_FUSED_MAX_DYN_LDS : 160 * 1024);
         if (e != hipSuccess) return e;
         granted = true;
     }
-    hipLaunchKernelGGL((conv_implicit_kernel<BW, BM, NPOS>), grid, dim3(CI_NT), (size_t)lds, s, a);
+    hipLaunchKernelGGL((conv_implicit_kernel<BW, BM, NPOS, FUSED>), grid, dim3(CI_NT), (size_t)lds, s, a);
     return hipGetLastError();
+}
+
+template <bool FUSED>
+hipError_t launch_main_cfg(const ConvImplicitPlan& p, const dim3& grid, const ConvImplicitArgs& a, hipStream_t s) {
+    if (p.BM == 128) return p.BW == 32 ? launch_main<32, 128, 128, FUSED>(grid, a, p.lds_bytes, s)
+                                       : launch_main<16, 128, 128, FUSED>(grid, a, p.lds_bytes, s);
+    if (p.NPOS == 256) return p.BW == 32 ? launch_main<32, 64, 256, FUSED>(grid, a, p.lds_bytes, s)
+                                         : launch_main<16, 64, 256, FUSED>(grid, a, p.lds_bytes, s);
+    return p.BW == 32 ? launch_main<32, 64, 128, FUSED>(grid, a, p.lds_bytes, s)
+                      : launch_main<16, 64, 128, FUSED>(grid, a, p.lds_bytes, s);
 }
 
 }  // namespace
 
+bool conv_fused_ok(const ConvGeom& c, const ConvImplicitPlan& p, const void* x, const void* w) {
+    return c.W % 16 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && (reinterpret_cast<uintptr_t>(w) & 3u) == 0 &&
+           p.lds_bytes <= CONV_FUSED_MAX_DYN_LDS;
+}
+
 hipError_t launch_conv_implicit(const ConvGeom& c, const ConvImplicitPlan& p, const void* x, bool x_u8, int x_zp,
                                 const void* w, bool w_u8, const void* w_zp, int w_zp_len, void* ws, int32_t* y,
-                                hipStream_t s) {
+                                bool fused, hipStream_t s) {
+    if (fused) {
+        if (!conv_fused_ok(c, p, x, w)) return hipErrorInvalidValue;
+        ConvImplicitArgs a{};
+        a.c = c;
+        a.bh = p.BH; a.th = p.TH; a.tw = p.TWt; a.hp_rows = p.HP; a.wp_cols = p.WP; a.cgp = p.Cgp; a.taps = p.taps;
+        a.cblocks = p.cblks; a.hr = p.HR; a.hc = p.HC; a.a_pitch = p.a_pitch;
+        a.a_rounds = p.BM * p.a_pitch / 16 / CI_NT; a.h_rounds = p.h_rounds;
+        a.a_dq = CI_NT / (p.a_pitch / 16); a.a_dr = CI_NT % (p.a_pitch / 16);
+        a.h_dq = 64 / p.HC; a.h_dr = 64 % p.HC;
+        a.kt = p.Kt;
+        a.w_zp = reinterpret_cast<const uint8_t*>(w_zp); a.w_zp_len = w_zp_len; a.w_u8 = w_u8 ? 1 : 0;
+        a.sa = w_u8 ? 128 : 0;
+        a.cb = (x_u8 ? 128 : 0) - x_zp;
+        a.y = y;
+        a.x = reinterpret_cast<const uint8_t*>(x);
+        a.w = reinterpret_cast<const uint8_t*>(w);
+        a.x_flip = x_u8 ? 0x80u : 0u;
+        a.w_flip = w_u8 ? 0x80u : 0u;
+        a.zf4 = (((uint32_t)x_zp ^ a.x_flip) & 0xffu) * 0x01010101u;
+        const int m_tiles = (c.Mg + p.BM - 1) / p.BM;
+        const dim3 grid((unsigned)(m_tiles * p.TH * p.TWt), (unsigned)(c.N * c.group));
+        return launch_main_cfg<true>(p, grid, a, s);
+    }
     uint8_t* base = reinterpret_cast<uint8_t*>(ws);
     int8_t* wp = reinterpret_cast<int8_t*>(base + p.wp_off);
     int32_t* rowsum = reinterpret_cast<int32_t*>(base + p.rs_off);
@@ -498,12 +701,7 @@ hipError_t launch_conv_implicit(const ConvGeom& c, const ConvImplicitPlan& p, co
     a.y = y;
     const int m_tiles = (c.Mg + p.BM - 1) / p.BM;
     const dim3 grid((unsigned)(m_tiles * p.TH * p.TWt), (unsigned)(c.N * c.group));
-    if (p.BM == 128) return p.BW == 32 ? launch_main<32, 128, 128>(grid, a, p.lds_bytes, s)
-                                       : launch_main<16, 128, 128>(grid, a, p.lds_bytes, s);
-    if (p.NPOS == 256) return p.BW == 32 ? launch_main<32, 64, 256>(grid, a, p.lds_bytes, s)
-                                         : launch_main<16, 64, 256>(grid, a, p.lds_bytes, s);
-    return p.BW == 32 ? launch_main<32, 64, 128>(grid, a, p.lds_bytes, s)
-                      : launch_main<16, 64, 128>(grid, a, p.lds_bytes, s);
+    return launch_main_cfg<false>(p, grid, a, s);
 }
 
 }  // namespace qg

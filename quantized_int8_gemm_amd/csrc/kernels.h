@@ -166,9 +166,12 @@ struct ConvImplicitPlan {
     size_t wp_off, rs_off, xp_off, total;   // packed weights, row sums, xp
 };
 bool conv_implicit_plan(const ConvGeom& c, ConvImplicitPlan* p);
+// fused: one launch that stages x and w itself (no workspace used); needs
+// conv_fused_ok (rows of x 16-byte aligned, w 4-byte aligned).
+bool conv_fused_ok(const ConvGeom& c, const ConvImplicitPlan& p, const void* x, const void* w);
 hipError_t launch_conv_implicit(const ConvGeom& c, const ConvImplicitPlan& p, const void* x, bool x_u8, int x_zp,
                                 const void* w, bool w_u8, const void* w_zp, int w_zp_len, void* ws, int32_t* y,
-                                hipStream_t s);
+                                bool fused, hipStream_t s);
 
 // DynamicQuantizeLinear (uint8): a min/max pass writing one (min, max)
 // float pair per workgroup into the workspace, then a quantize pass.

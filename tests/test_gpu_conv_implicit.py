@@ -5,7 +5,8 @@ columns (16- and 32-wide tiles), output channels past one 128-row tile and
 short of one, strides, dilations, asymmetric pads, groups, 1x1 / 1x3 / 3x1 /
 2x2 / 3x3 kernels, every operand dtype pairing and weight zero-point form,
 several 64-channel blocks, odd output widths (scalar stores), and the
-benchmark's 3x3 layer (sampled images)."""
+benchmark's 3x3 layer (sampled images); inputs whose rows are whole 16-byte
+vectors (W % 16 == 0) also through the one-launch fused form."""
 import numpy as np
 import pytest
 
@@ -19,12 +20,19 @@ pytestmark = pytest.mark.gpu
 
 
 def both_paths(monkeypatch, x, w, x_zp, w_zp, **kw):
+    """The default path (one fused launch where x's rows are 16-byte
+    aligned, W % 16 == 0; else the padded-copy pass and the implicit GEMM),
+    the two-pass form and the im2col path, each against the oracle."""
     ref = oracle.conv_integer(x, w, x_zp, w_zp, **kw)
     zw = None if w_zp is None else to_dev(np.asarray(w_zp).astype(w.dtype))
     tx, tw = to_dev(x), to_dev(w)
     y = q.conv_integer(tx, tw, x_zp, zw, **kw)
-    assert q.last_kernel() == "conv_implicit", q.last_kernel()
+    assert q.last_kernel() == ("conv_fused" if x.shape[-1] % 16 == 0 else "conv_implicit"), q.last_kernel()
     np.testing.assert_array_equal(y.cpu().numpy(), ref)
+    monkeypatch.setenv("QGEMM_CONV", "twopass")
+    y1 = q.conv_integer(tx, tw, x_zp, zw, **kw)
+    assert q.last_kernel() == "conv_implicit", q.last_kernel()
+    np.testing.assert_array_equal(y1.cpu().numpy(), ref)
     monkeypatch.setenv("QGEMM_CONV", "im2col")
     y2 = q.conv_integer(tx, tw, x_zp, zw, **kw)
     monkeypatch.delenv("QGEMM_CONV")
@@ -45,6 +53,16 @@ SHAPES = [
     (2, 64, 15, 6, 32, 3, 1, 1, (1, 0, 1, 0), (2, 1), (1, 1)),       # 3x1, row stride 2
     (2, 64, 11, 11, 24, 2, 2, 1, (0, 0, 1, 1), (1, 1), (1, 1)),      # 2x2, even kernel
     (1, 192, 6, 7, 130, 3, 3, 1, (1, 1, 1, 1), (1, 1), (1, 1)),      # three channel blocks, OW = 7
+    # W % 16 == 0: the fused launch
+    (2, 64, 19, 48, 40, 3, 3, 1, (1, 1, 1, 1), (1, 1), (1, 1)),      # ragged rows, Mg < 128
+    (2, 128, 12, 16, 72, 3, 3, 1, (1, 1, 1, 1), (2, 2), (1, 1)),     # stride 2, two channel blocks
+    (2, 64, 20, 32, 64, 3, 3, 1, (2, 2, 2, 2), (1, 1), (2, 2)),      # dilation 2
+    (2, 128, 10, 16, 96, 3, 3, 2, (1, 1, 1, 1), (1, 1), (1, 1)),     # two groups of 64 channels
+    (3, 64, 7, 48, 48, 1, 1, 1, (0, 0, 0, 0), (1, 1), (1, 1)),       # 1x1
+    (2, 64, 8, 32, 32, 1, 3, 1, (0, 1, 0, 1), (1, 2), (1, 1)),       # 1x3, column stride 2
+    (2, 64, 11, 16, 24, 2, 2, 1, (0, 0, 1, 1), (1, 1), (1, 1)),      # 2x2 (four taps: byte-wise weights)
+    (1, 192, 6, 16, 130, 3, 3, 1, (1, 2, 1, 0), (1, 1), (1, 1)),     # three channel blocks, asymmetric pads
+    (1, 64, 9, 64, 200, 3, 3, 1, (0, 3, 2, 0), (1, 1), (1, 1)),      # wide pads, two m tiles
 ]
 
 
@@ -90,10 +108,14 @@ def test_conv_implicit_tokenizer_layer_sampled(monkeypatch):
     x, w, zw = si.conv_integer_inputs(64, 64, 32, 32, 128, 3, 3, seed=808)
     tx, tw, tz = to_dev(x), to_dev(w), to_dev(zw)
     y = q.conv_integer(tx, tw, 128, tz, pads=(1, 1, 1, 1))
-    assert q.last_kernel() == "conv_implicit", q.last_kernel()
+    assert q.last_kernel() == "conv_fused", q.last_kernel()
     yc = y.cpu().numpy()
     for n in (0, 31, 63):
         np.testing.assert_array_equal(yc[n:n + 1], oracle.conv_integer(x[n:n + 1], w, 128, zw, pads=(1, 1, 1, 1)))
+    monkeypatch.setenv("QGEMM_CONV", "twopass")
+    y1 = q.conv_integer(tx, tw, 128, tz, pads=(1, 1, 1, 1))
+    assert q.last_kernel() == "conv_implicit", q.last_kernel()
+    np.testing.assert_array_equal(y1.cpu().numpy(), yc)
     monkeypatch.setenv("QGEMM_CONV", "im2col")
     y2 = q.conv_integer(tx, tw, 128, tz, pads=(1, 1, 1, 1))
     assert q.last_kernel().startswith("conv_im2col+")

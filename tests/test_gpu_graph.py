@@ -79,3 +79,56 @@ def test_tiled_graph_replays_match_eager():
         torch.cuda.synchronize()
 
     _replay_and_check(calls, [o1, o2], [e1, e2], extra)
+
+
+def test_split_and_decode_kernels_graph_replays_match_eager():
+    """The other kernels whose tickets live in the workspace, captured
+    together in one graph sharing one workspace: the W8A32 decode kernel and
+    its gradient, the W8A32 split tiles, the MatMulInteger decode kernel, the
+    int8 split tiles and the [N,K] A8W8 decode kernel."""
+    case("graph: W8A32 decode/split, MatMulInteger decode, A8W8 split-K and [N,K] decode")
+    d = torch.device("cuda:0")
+    Aw, Ww = si.w8a32_inputs(4, 4096, 4096, seed=920)
+    Aw2, Ww2 = si.w8a32_inputs(96, 2048, 4096, seed=921)
+    dC, _ = si.w8a32_inputs(4, 1, 4096, seed=922)
+    Am, Bm, zb = si.matmul_integer_inputs(1, 8, 4096, 4096, seed=923)
+    A8, W8, s_a, s_w = si.a8w8_inputs(64, 4096, 4096, seed=924)
+    A9, W9, s_a9, s_w9 = si.a8w8_inputs(8, 2048, 4096, seed=925)
+    t = {k: to_dev(v) for k, v in dict(Aw=Aw, Ww=Ww, Aw2=Aw2, Ww2=Ww2, dC=dC, Am=Am[0], Bm=Bm, zb=zb, A8=A8, W8=W8,
+                                        s_a=s_a, s_w=s_w, A9=A9, W9t=np.ascontiguousarray(W9.T), s_a9=s_a9,
+                                        s_w9=s_w9).items()}
+    need = max(q.workspace_bytes(q.QG_OP_W8A32, 1, 4, 4096, 4096), q.workspace_bytes(q.QG_OP_W8A32, 1, 96, 2048, 4096),
+               q.workspace_bytes(q.QG_OP_W8A32_INPUT_GRAD, 1, 4, 4096, 4096),
+               q.workspace_bytes(q.QG_OP_MATMUL_INTEGER, 1, 8, 4096, 4096),
+               q.workspace_bytes(q.QG_OP_A8W8, 1, 64, 4096, 4096), q.workspace_bytes(q.QG_OP_A8W8, 1, 8, 2048, 4096))
+    ws = torch.zeros(need, dtype=torch.uint8, device=d)
+    outs = [torch.empty(4, 4096, device=d), torch.empty(96, 2048, device=d), torch.empty(4, 4096, device=d),
+            torch.empty(8, 4096, dtype=torch.int32, device=d), torch.empty(64, 4096, dtype=torch.bfloat16, device=d),
+            torch.empty(8, 2048, dtype=torch.float32, device=d)]
+    calls = [
+        lambda: q.qgemm_w8a32(t["Aw"], t["Ww"], 0.01, 3, out=outs[0], workspace=ws),
+        lambda: q.qgemm_w8a32(t["Aw2"], t["Ww2"], 0.01, 3, out=outs[1], workspace=ws),
+        lambda: q.qgemm_w8a32_input_grad(t["dC"], t["Ww"], 0.01, 3, out=outs[2], workspace=ws),
+        lambda: q.matmul_integer(t["Am"], t["Bm"], 128, t["zb"], out=outs[3], workspace=ws),
+        lambda: q.qgemm_a8w8(t["A8"], t["W8"], t["s_a"], t["s_w"], out_dtype=torch.bfloat16, out=outs[4],
+                             workspace=ws),
+        lambda: q.qgemm_a8w8(t["A9"], t["W9t"], t["s_a9"], t["s_w9"], b_trans=True, out=outs[5], workspace=ws),
+    ]
+    kernels = ["w8a32_skinny", "w8a32_bf16x3_128x128_splitk", "w8a32_input_grad_skinny", "matmul_integer_skinny",
+               "int8_dma_128x128k128_splitk", "a8w8_skinny"]
+    eager = []
+    for c, o, k in zip(calls, outs, kernels):
+        c()
+        assert q.last_kernel() == k, (q.last_kernel(), k)
+        eager.append(o.clone())
+    np.testing.assert_array_equal(eager[3].cpu().numpy(), oracle.matmul_integer(Am[0], Bm, 128, zb))
+    np.testing.assert_array_equal(bf16_bits(eager[4]), oracle.a8w8(A8, W8, s_a, s_w)["bf16"])
+    tmp = torch.empty(4, 4096, device=d)
+
+    def extra():
+        q.qgemm_w8a32(t["Aw"], t["Ww"], 0.01, 3, out=tmp, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(tmp, eager[0])
+
+    _replay_and_check(calls, outs, eager, extra)
+    assert int(ws[:1024].sum().item()) == 0

@@ -48,6 +48,38 @@ def test_decode_on_two_streams_with_their_own_workspaces():
         assert int(w[:4 * tiles_n].view(torch.int32).abs().sum()) == 0
 
 
+def test_w8a32_and_matmul_integer_split_kernels_on_two_streams():
+    """The W8A32 decode and split kernels and the MatMulInteger decode kernel
+    on two streams at once, each stream with the binding's own workspace:
+    the same bits as one-stream calls, every ticket back at zero."""
+    case("streams: W8A32 decode / split and MatMulInteger decode on two streams, 6 rounds")
+    from quantized_int8_gemm_amd import _binding as b
+    d = torch.device("cuda:0")
+    Aw, Ww = si.w8a32_inputs(8, 4096, 4096, seed=950)
+    Aw2, Ww2 = si.w8a32_inputs(100, 2048, 4096, seed=951)
+    Am, Bm, zb = si.matmul_integer_inputs(1, 4, 4096, 4096, seed=952)
+    t = [to_dev(x) for x in (Aw, Ww, Aw2, Ww2, Am[0], Bm, zb)]
+    calls = [lambda: q.qgemm_w8a32(t[0], t[1], 0.01, 2), lambda: q.qgemm_w8a32(t[2], t[3], 0.01, 2),
+             lambda: q.matmul_integer(t[4], t[5], 128, t[6])]
+    ref = [c().clone() for c in calls]
+    np.testing.assert_array_equal(ref[2].cpu().numpy(), oracle.matmul_integer(Am[0], Bm, 128, zb))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    res = [[], []]
+    torch.cuda.synchronize()
+    for it in range(6):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                res[i].append([c() for c in calls])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for it in range(6):
+            for j in range(3):
+                assert torch.equal(res[i][it][j], ref[j]), (i, it, j)
+    for i in range(2):
+        ws = b._workspaces[(d, streams[i].cuda_stream)]
+        assert int(ws[:1024].sum().item()) == 0
+
+
 def test_dynamic_quantize_on_two_streams_with_the_bindings_workspaces():
     case("streams: DynamicQuantizeLinear [8, 512, 2048] on two streams, 6 calls each")
     xs = [si.dql_inputs((8, 512, 2048), seed=s) for s in (941, 942)]

@@ -343,6 +343,14 @@ def cpu_oracle_rows(rows, si):
             dt = timed(lambda: oracle.a8w8(A, W, s_a, s_w))
             attach(name, dt, ops=2.0 * m * 8192 * 8192,
                    nbytes=m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192)
+    for m in (1, 4, 16):
+        name = f"a8w8_decode_wnk_m{m}_8192_bf16"
+        if name in rows:
+            A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
+            Wt = np.ascontiguousarray(W.T)
+            dt = timed(lambda: oracle.a8w8(A, Wt, s_a, s_w, b_trans=True))
+            attach(name, dt, ops=2.0 * m * 8192 * 8192,
+                   nbytes=m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192)
     for m in (1, 16):
         name = f"matmul_integer_decode_m{m}_8192"
         if name in rows:
@@ -505,6 +513,22 @@ def main():
                                                    "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
                                                    "us_eager": ms_eager * 1e3, "per_call": spread}
             del sets, base_w, ws
+        # The same decode rows with the weight stored as [N,K] (b_trans, the
+        # usual layout of a linear layer's weight): whole columns per
+        # workgroup, no split-K exchange, no workspace
+        for m in (1, 4, 16):
+            A, W, s_a, s_w = si.a8w8_inputs(m, 8192, 8192, seed=404 + m)
+            base_w = to(np.ascontiguousarray(W.T))
+            sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),
+                     torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)) for r in range(9)]
+            call = lambda s: q.qgemm_a8w8(s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, b_trans=True, out=s[4])
+            ms, spread = time_graph(call, sets, 36, max(steps // 2, 5), stream, spread=True)
+            nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 2 * m * 8192
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rows[f"a8w8_decode_wnk_m{m}_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3, "GB/s": gbs,
+                                                       "frac_hbm_peak": gbs / PEAK_HBM_GBS, "timing": "hip_graph",
+                                                       "per_call": spread}
+            del sets, base_w
         # MatMulInteger at decode shapes (uint8 activations with zero point
         # 128, int8 weight with per-column zero points), same rotation
         for m in (1, 16):

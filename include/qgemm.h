@@ -202,7 +202,9 @@ qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K,
  *     holds its plan (the size returned is the decode kernel's).
  * Decode shapes (M <= 16, W as [K,N], or as [N,K] with 16-byte aligned rows
  * and K % 16 == 0) run a bandwidth-bound kernel that streams W once; all
- * other shapes run the tiled matrix-core kernel.
+ * other shapes run the tiled matrix-core kernel.  With W as [N,K] and
+ * N >= 4096 the decode kernel owns whole columns over all of K (no split,
+ * the workspace is not touched); otherwise it splits K as described above.
  * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
  */
 qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,

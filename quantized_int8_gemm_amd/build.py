@@ -29,6 +29,7 @@ SOURCES = [
     "int8_dma_256x128w8k128.hip",
     "int8_dma_256x256w8k128.hip",
     "a8w8_skinny.hip",
+    "a8w8_slab.hip",
     "w8a32.hip",
     "w8a32_split.hip",
     "w8a32_skinny.hip",

@@ -277,6 +277,22 @@ static bool a8w8_is_skinny(int64_t M, int b_trans) {
     return !b_trans && M <= SKINNY_MAX_M;
 }
 
+// Column slabs for W as [N,K] (each workgroup owns tn output columns over all
+// of K: whole weight lines per workgroup and no split-K exchange): the slab
+// width for a decode-shaped product, or 0 when it does not take this kernel.
+// It needs N / 16 >= 256 workgroups to occupy the chip; 16-column slabs up
+// to 8 rows or below N = 8192, 32-column slabs (A fragments reused over two
+// column fragments) otherwise.  QGEMM_FORCE_KERNEL=slab takes it whenever
+// the shape allows, =skinny or =tiled never; QGEMM_SLAB_TN picks the width.
+static int slab_width(const qg::Int8GemmArgs& a, bool b_trans) {
+    if (!b_trans || env_is("QGEMM_FORCE_KERNEL", "tiled") || env_is("QGEMM_FORCE_KERNEL", "skinny")) return 0;
+    const int forced = env_int("QGEMM_SLAB_TN", 0);
+    const int tn = forced > 0 ? forced : ((a.M <= 8 || a.N < 8192) ? 16 : 32);
+    if (!qg::slab_shape_ok(a, tn)) return 0;
+    if (env_is("QGEMM_FORCE_KERNEL", "slab")) return tn;
+    return a.N >= 16 * 256 ? tn : 0;
+}
+
 // Split of K for the tiled A8W8 kernel (128x128 tiles, 128-byte stages):
 // an output of at most 128 tiles leaves most of the 256 CUs idle, so K is cut
 // into up to 8 splits of at least 1024 rows (whole stages) that together
@@ -506,6 +522,13 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
 
     const char* name = "";
     hipError_t e;
+    // Decode rows with W as [N,K] across a wide N: column slabs, no workspace.
+    if (const int tn = slab_width(a, b_trans != 0)) {
+        (void)hipGetLastError();
+        e = qg::launch_a8w8_slab(a, tn, epi, (hipStream_t)stream, &name);
+        log_dispatch(op, name, 1, M, N, K, 1);
+        return finish_launch(e, name);
+    }
     // Decode shapes: W as [K,N], or as [N,K] with 16-byte aligned rows (each
     // weight row then already holds its column's k-bytes).
     const bool skinny_bkm = b_trans != 0 && vec && a8w8_is_skinny(M, 0);

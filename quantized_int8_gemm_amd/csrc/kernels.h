@@ -98,6 +98,13 @@ hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStrea
                               const char** name, bool bkm = false);
 // sums: MatMulInteger partials, which carry row and column sums too
 size_t skinny_workspace_bytes(int M, int N, int splits, bool sums = false);
+
+// Column-slab A8W8 kernel for decode rows with W as [N,K] (each workgroup
+// owns tn output columns over all of K, no workspace): M <= SLAB_MAX_M,
+// 16-byte aligned rows, K % 16 == 0; tn is 16 or 32.
+constexpr int SLAB_MAX_M = 16;
+bool slab_shape_ok(const Int8GemmArgs& a, int tn);
+hipError_t launch_a8w8_slab(const Int8GemmArgs& a, int tn, int epi, hipStream_t s, const char** name);
 int skinny_splits(int M, int N, int K);
 int skinny_split_steps(int N, int K);
 int skinny_splits_for(int N, int K, int split_steps);

@@ -261,20 +261,22 @@ def test_matmul_integer_tile_choice_by_tile_count(M, N, K, kernel):
     np.testing.assert_array_equal(y.cpu().numpy(), oracle.matmul_integer(A, B, za, zb))
 
 
-@pytest.mark.parametrize("M,N,K,out", [
-    (1, 8192, 8192, "bf16"),    # 32 column tiles, 8 splits
-    (4, 4096, 4096, "f32"),
-    (16, 2000, 2048, "bf16"),   # ragged last column tile
-    (7, 1000, 3024, "f32"),     # K % 64 == 16: a piece of the last step lies past K
+@pytest.mark.parametrize("M,N,K,out,forced", [
+    (1, 8192, 8192, "bf16", True),    # 32 column tiles, 8 splits
+    (4, 4096, 4096, "f32", True),
+    (16, 2000, 2048, "bf16", False),  # ragged last column tile
+    (7, 1000, 3024, "f32", False),    # K % 64 == 16: a piece of the last step lies past K
 ])
-def test_a8w8_decode_weight_as_n_by_k(M, N, K, out):
-    """W given as [N,K] (b_trans) at decode shapes: the decode kernel reads
-    each weight row's k-bytes directly; every output against the oracle."""
+def test_a8w8_decode_weight_as_n_by_k(M, N, K, out, forced):
+    """W given as [N,K] (b_trans) at decode shapes: the split-K decode kernel
+    reads each weight row's k-bytes directly (N >= 4096 takes column slabs
+    unless the split kernel is asked for); every output against the oracle."""
     case(f"a8w8 decode b_trans M={M} N={N} K={K} {out}")
     A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K + 9)
     Wt = np.ascontiguousarray(W.T)
     ref = oracle.a8w8(A, Wt, s_a, s_w, b_trans=True)
-    res = run(A, Wt, s_a, s_w, torch.bfloat16 if out == "bf16" else torch.float32, b_trans=True)
+    with env(**({"QGEMM_FORCE_KERNEL": "skinny"} if forced else {})):
+        res = run(A, Wt, s_a, s_w, torch.bfloat16 if out == "bf16" else torch.float32, b_trans=True)
     assert q.last_kernel() == "a8w8_skinny", q.last_kernel()
     got = bf16_bits(res) if out == "bf16" else res.cpu().numpy()
     np.testing.assert_array_equal(got, ref[out])

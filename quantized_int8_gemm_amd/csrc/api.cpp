@@ -347,6 +347,18 @@ static bool w8a32_skinny_ok(int64_t M, int64_t N, int64_t K, const void* A, int6
            (wt || N % 16 == 0);
 }
 
+// The input gradient's slab form (each workgroup owns 32 outputs, i.e. W
+// rows, over the whole contraction; no workspace) for at most 8 rows across
+// at least 8192 outputs.  Graph-timed at N = K = 8192: 17.3 / 17.4 / 18.7 /
+// 20.6 us at M = 1 / 2 / 4 / 8 against 22.7 - 23.4 on the split decode
+// kernel; at 16 rows 25.7 against 24.4 (every workgroup reads and splits all
+// of dC).  QGEMM_FORCE_KERNEL=slab takes it whenever the shape allows.
+static bool w8a32_grad_slab(const qg::W8A32Args& a) {
+    if (!w8a32_split() || env_is("QGEMM_FORCE_KERNEL", "tiled") || env_is("QGEMM_FORCE_KERNEL", "skinny")) return false;
+    if (!qg::w8a32_grad_slab_ok(a)) return false;
+    return env_is("QGEMM_FORCE_KERNEL", "slab") || (a.M <= 8 && a.N >= 8192);
+}
+
 size_t qgemm_workspace_bytes(int op, int64_t batch, int64_t M, int64_t N, int64_t K) {
     if (op == QG_OP_DYNAMIC_QUANTIZE_LINEAR) return N < 0 ? 0 : (size_t)qg::dql_partials(N) * 8;
     if (op == QG_OP_W8A32 || op == QG_OP_W8A32_INPUT_GRAD) {
@@ -396,6 +408,13 @@ static qg_status w8a32_run(qg::W8A32Args& a, bool vec_a, bool vec_w, bool wt, vo
     // is given.  Rows 17-64 measured against the split 128x128 tiles at
     // N = K = 8192: 25-38 against 96 us (forward), 34-57 against 98 us
     // (gradient); at 4096^2 12.6-16.6 against 33-36 us.
+    if (wt && w8a32_grad_slab(a)) {
+        const char* name = "";
+        (void)hipGetLastError();
+        const hipError_t e = qg::launch_w8a32_grad_slab(a, (hipStream_t)stream, &name);
+        log_dispatch(op, name, 1, a.M, a.N, a.K, 1);
+        return finish_launch(e, name);
+    }
     if (w8a32_skinny_ok(a.M, a.N, a.K, a.A, a.lda, a.W, a.ldw, wt)) {
         int splits, split_k;
         qg::w8a32_skinny_plan(a.M, a.N, a.K, env_int("QGEMM_W8A32_SPLITS", 0), &splits, &split_k);

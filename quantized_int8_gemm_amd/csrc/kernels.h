@@ -141,6 +141,12 @@ constexpr int SKINNY_W8A32_MAX_M = 64;   // blocks of 16 rows on the grid's thir
 void w8a32_skinny_plan(int64_t M, int64_t N, int64_t K, int forced, int* splits, int* split_k);
 size_t w8a32_skinny_bytes(int64_t M, int64_t N, int splits);
 hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const char** name);
+// Slab form of the W8A32 input gradient (kernel view: M <= 16 rows, N
+// outputs = W's rows, contraction K along them; each workgroup owns 16 or 32
+// outputs over all of K, no workspace): 16-byte aligned rows, lda % 4 == 0,
+// ldw % 16 == 0, K % 4 == 0.
+bool w8a32_grad_slab_ok(const W8A32Args& a);
+hipError_t launch_w8a32_grad_slab(const W8A32Args& a, hipStream_t s, const char** name);
 hipError_t launch_w8a32_split(const W8A32Args& a, bool vec_a, bool vec_w, bool wt, hipStream_t s,
                               const char** name);
 

@@ -352,6 +352,180 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     if (tid == 0) __hip_atomic_store(&tickets[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Slab form of the input gradient for at most 16 rows: the contraction
+// runs along W's rows, so a workgroup that owns TN = 16 NF outputs (W rows
+// n0 .. n0 + TN - 1) streams those rows whole, every 128-byte line used by
+// itself, over ALL of the contraction: N / TN workgroups occupy the chip and
+// nothing crosses workgroups (no partials, no ticket, no workspace).  Eight
+// waves take steps of 64 KB contraction values round robin, NB in flight.
+// Every workgroup reads and splits all of dC, which costs more than the
+// split form's exchange from about 16 rows on.
+// Lane (i16, g) loads 16 bytes of W row n0 + 16c + i16 at contraction bytes
+// 64kb + 16g (the B fragments of two v_mfma_f32_16x16x32_bf16, halves h = 0
+// and 1, once widened) and the 16 fp32 values of dC row i16 at the same
+// contraction indices, split into three bf16 planes; every product is exact
+// and only the fp32 accumulation rounds, as in the split form.  The waves'
+// tiles and row sums S2 are added through LDS in wave order and the epilogue
+// scale * (S1 - zp * S2) runs once per output.  Contraction values past K
+// are cleared before they reach a product or S2 (the weight bytes there are
+// the next row's).
+constexpr int GS_WAVES = 8;
+constexpr int GS_NT = 64 * GS_WAVES;
+
+template <bool ZP, int NF, int KB, int NB>
+__global__ __launch_bounds__(GS_NT) __attribute__((amdgpu_waves_per_eu(2))) void w8a32_grad_slab_kernel(W8A32Args p) {
+    constexpr int TS = 16 * NF;     // outputs per workgroup
+    constexpr int SK = 64 * KB;     // contraction values per wave step
+    __shared__ __attribute__((aligned(16))) float red[GS_WAVES][16][TS];
+    __shared__ float s2_red[GS_WAVES][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, i16 = lane & 15;
+    const int n0 = blockIdx.x * TS;
+    const int cols = p.N - n0;
+    const int M = p.M, K = p.K;
+    const int ldw = (int)p.ldw, lda = (int)p.lda;
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K));
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)(((M - 1) * lda + K) * 4));
+    const uint32_t w_voff = (uint32_t)(i16 * ldw + 16 * g);
+    const uint32_t a_voff = (uint32_t)((i16 * lda + 16 * g) * 4);
+    const int nsteps = (K + SK - 1) / SK;
+
+    u32x4 wbuf[NB][KB][NF];
+    u32x4 abuf[NB][KB][4];
+    // Loads of one step into buffer b; a step past K (a wave's last round)
+    // loads from past the buffer ends: zeros, no memory touched.
+    auto fetch = [&](int step, int b) {
+        const bool live = step < nsteps;
+        const uint32_t wo = live ? w_voff + (uint32_t)(step * SK) : 0x80000000u;
+        const uint32_t ao = live ? a_voff + (uint32_t)(step * SK * 4) : 0x80000000u;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int c = 0; c < NF; ++c)
+                wbuf[b][kb][c] = buffer_load16(w_rsrc, wo + (uint32_t)(16 * c * ldw + 64 * kb), 0u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) abuf[b][kb][q] = buffer_load16(a_rsrc, ao + (uint32_t)((64 * kb + 4 * q) * 4), 0u);
+        }
+    };
+
+    v4f acc[NF];
+#pragma unroll
+    for (int c = 0; c < NF; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    float s2 = 0.f;   // this lane's share of S2 for row i16
+
+    auto consume = [&](int b, int step) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = step * SK + 64 * kb + 16 * g;
+            float a[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[4 * q] = __uint_as_float(abuf[b][kb][q].x);
+                a[4 * q + 1] = __uint_as_float(abuf[b][kb][q].y);
+                a[4 * q + 2] = __uint_as_float(abuf[b][kb][q].z);
+                a[4 * q + 3] = __uint_as_float(abuf[b][kb][q].w);
+            }
+            if (k0 + 16 > K) {   // values reaching past K: cleared
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (k0 + e >= K) a[e] = 0.f;
+            }
+            if constexpr (ZP) {
+                s2 += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])) +
+                      (((a[8] + a[9]) + (a[10] + a[11])) + ((a[12] + a[13]) + (a[14] + a[15])));
+            }
+            v8bf pa[2][3];
+            split8(a, pa[0][0], pa[0][1], pa[0][2]);
+            split8(a + 8, pa[1][0], pa[1][1], pa[1][2]);
+#pragma unroll
+            for (int c = 0; c < NF; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const v8bf bw = half8(wbuf[b][kb][c], h);
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl)
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h][pl], bw, acc[c], 0, 0, 0);
+                }
+        }
+    };
+
+    // This wave's steps: wave + GS_WAVES * i, i < n_my (a multiple of NB, the
+    // same for every wave; steps past K add nothing), NB in flight.
+    const int n_my = (((nsteps + GS_WAVES - 1) / GS_WAVES) + NB - 1) / NB * NB;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        fetch(wave + GS_WAVES * b, b);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int i = 0;
+    for (; i + NB < n_my; i += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            consume(b, wave + GS_WAVES * (i + b));
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(wave + GS_WAVES * (i + NB + b), b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) consume(b, wave + GS_WAVES * (i + b));
+
+    // Register r of fragment c holds row 4g + r, output 16c + i16.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (4 * g + r >= M) continue;
+#pragma unroll
+        for (int c = 0; c < NF; ++c) red[wave][4 * g + r][16 * c + i16] = acc[c][r];
+    }
+    if constexpr (ZP) {
+        s2 += __shfl_xor(s2, 16);
+        s2 += __shfl_xor(s2, 32);
+        if (g == 0) s2_red[wave][i16] = s2;
+    }
+    __syncthreads();
+
+    const float zp = (float)p.zp;
+    const bool vec_out = (p.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0);
+    const int items = M * (TS / 4);
+    for (int it = tid; it < items; it += GS_NT) {
+        const int m = it / (TS / 4), cg = it % (TS / 4);
+        const int n = n0 + 4 * cg;
+        if (n >= p.N) continue;
+        v4f v = *reinterpret_cast<const v4f*>(&red[0][m][4 * cg]);
+#pragma unroll
+        for (int w = 1; w < GS_WAVES; ++w) v = v + *reinterpret_cast<const v4f*>(&red[w][m][4 * cg]);
+        float s2m = 0.f;
+        if constexpr (ZP) {
+            s2m = s2_red[0][m];
+#pragma unroll
+            for (int w = 1; w < GS_WAVES; ++w) s2m = s2m + s2_red[w][m];
+        }
+        float f[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (ZP) f[e] = f[e] - zp * s2m;
+            f[e] = p.scale * f[e];
+        }
+        float* dst = p.C + (int64_t)m * p.ldc + n;
+        if (vec_out && n + 4 <= p.N) {
+            *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+            continue;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) dst[e] = f[e];
+    }
+}
+
+template <int NF, int KB, int NB>
+hipError_t launch_grad_slab_cfg(const W8A32Args& a, hipStream_t s) {
+    const dim3 grid((a.N + 16 * NF - 1) / (16 * NF));
+    if (a.zp != 0) hipLaunchKernelGGL((w8a32_grad_slab_kernel<true, NF, KB, NB>), grid, dim3(GS_NT), 0, s, a);
+    else hipLaunchKernelGGL((w8a32_grad_slab_kernel<false, NF, KB, NB>), grid, dim3(GS_NT), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 void w8a32_skinny_plan(int64_t M, int64_t N, int64_t K, int forced, int* splits, int* split_k) {
@@ -398,6 +572,25 @@ hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const
         else hipLaunchKernelGGL((w8a32_skinny_kernel<false, false>), grid, dim3(NT), 0, s, a);
     }
     return hipGetLastError();
+}
+
+bool w8a32_grad_slab_ok(const W8A32Args& a) {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.W);
+    if ((al & 15) != 0 || a.lda % 4 != 0 || a.ldw % 16 != 0 || a.K % 4 != 0) return false;
+    if (a.M < 1 || a.M > 16 || a.N < 1 || a.K < 1) return false;
+    // 32-bit buffer offsets: a live step reads below K + 512 in a row
+    return (int64_t)48 * a.ldw + a.K + 512 < ((int64_t)1 << 31) &&
+           ((int64_t)16 * a.lda + a.K + 512) * 4 < ((int64_t)1 << 31);
+}
+
+// Steps: 64 contraction values two deep for one or two rows, 128 two deep
+// above (32 outputs per workgroup; 16-output slabs and four-deep forms
+// measured slower at N = K = 8192).
+hipError_t launch_w8a32_grad_slab(const W8A32Args& a, hipStream_t s, const char** name) {
+    *name = "w8a32_input_grad_slab";
+    if (!w8a32_grad_slab_ok(a)) return hipErrorInvalidValue;
+    if (a.M <= 2) return launch_grad_slab_cfg<2, 1, 2>(a, s);
+    return launch_grad_slab_cfg<2, 2, 2>(a, s);
 }
 
 }  // namespace qg

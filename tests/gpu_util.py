@@ -69,12 +69,18 @@ W8A32_PATHS = ("bf16x3", "fp32")
 def w8a32_kernel(path, rows, outs, grad=False, k=0):
     """Kernel name the library reports for a W8A32 call of `rows` x `outs`
     outputs over a contraction of `k` on `path`, through the binding (which
-    passes a workspace): the decode kernel for at most 64 rows, else 256 x
+    passes a workspace): for the gradient with at most 8 rows across 8192
+    outputs or more, the slab kernel; the decode kernel for at most 64 rows, else 256 x
     256 split tiles from 129 of them on, else 128 x 128 tiles, the
     contraction divided among workgroups when there are at most 256 of
     those and it allows two or more pieces of 512."""
     if path == "fp32":
         return "w8a32_input_grad_128x128" if grad else "w8a32_tiled_128x128"
+    # the gradient's slab form: at most 8 rows across at least 8192 outputs
+    forced = os.environ.get("QGEMM_FORCE_KERNEL")
+    if grad and k % 16 == 0 and forced not in ("tiled", "skinny") and \
+            ((rows <= 8 and outs >= 8192) or (forced == "slab" and rows <= 16)):
+        return "w8a32_input_grad_slab"
     # contiguous operands: the weight's rows (N bytes) 16-byte aligned when
     # N % 16 == 0; N is `outs` forward and the contraction `k` for the gradient
     if rows <= 64 and k % 4 == 0 and (k if grad else outs) % 16 == 0 and \

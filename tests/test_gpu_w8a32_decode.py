@@ -186,7 +186,7 @@ def test_w8a32_input_grad_decode_every_output(M, N, K, zp):
     dC, _ = si.w8a32_inputs(M, 1, N, seed=M + N + K + 7)   # [M, N]
     _, W = si.w8a32_inputs(1, N, K, seed=K + 11)            # [K, N]
     d, kern = run_grad(dC, W, 0.019, zp)
-    assert kern == GRAD, kern
+    assert kern == ("w8a32_input_grad_slab" if (M <= 8 and K >= 8192) else GRAD), kern
     within_grad(d, dC, W, 0.019, zp)
     d2, _ = run_grad(dC, W, 0.019, zp)
     assert torch.equal(d, d2), "a repeated call differs"

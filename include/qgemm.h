@@ -159,7 +159,7 @@ qg_status qgemm_w8a32_input_grad(int64_t M, int64_t N, int64_t K,
  * M, N, K; it divides the sum over n as qgemm_w8a32_ws divides the sum over
  * k (at most 16 rows with 16-byte aligned rows of dC and W: the decode
  * kernel; else dA of at most 256 tiles of 128 x 128), with the same rules.
- * At most 8 rows across K >= 8192 outputs (16-byte aligned rows, N % 16 ==
+ * At most 8 rows across K >= 8192 outputs (16-byte aligned rows, N % 4 ==
  * 0) take a form in which each workgroup owns whole rows of W over all of
  * n; it leaves the workspace untouched.
  */

@@ -28,6 +28,7 @@ SOURCES = [
     "int8_dma_128x128k128.hip",
     "int8_dma_256x128w8k128.hip",
     "int8_dma_256x256w8k128.hip",
+    "int8_dma_64x128k128.hip",
     "a8w8_skinny.hip",
     "a8w8_slab.hip",
     "w8a32.hip",

@@ -61,7 +61,7 @@ bool empty_output(int64_t rows, int64_t cols, int64_t inner, int64_t batch = 1) 
 // Tile configuration of the int8 GEMM for an (effective) problem shape:
 // large tiles when there are enough of them to fill the chip, smaller tiles
 // (several workgroups per compute unit) otherwise.  QGEMM_TILE forces one.
-int pick_tile(int64_t batch, int64_t M, int64_t N) {
+int pick_tile(int64_t batch, int64_t M, int64_t N, int64_t K) {
     const int forced = env_int("QGEMM_TILE", -1);
     if (forced >= 0 && forced < qg::NUM_TILE_CFGS) return forced;
     // 256x256 tiles (eight waves, 128-byte k stages, one workgroup per
@@ -79,6 +79,16 @@ int pick_tile(int64_t batch, int64_t M, int64_t N) {
     // reach a sum.
     const int64_t t256 = batch * ((M + 255) / 256) * ((N + 255) / 256);
     if (t256 >= 512 || (t256 >= 160 && !(t256 > 256 && t256 <= 352))) return qg::TILE_256x256_W8_K128;
+    // At most 256 tiles of 128 x 128 over K <= 2048: 64x128 tiles, twice the
+    // workgroups with half the multiplies each between first load and last
+    // store.  A8W8 bf16, graph-timed with the operands cached: 256 / 1024 /
+    // 2048 x 1024 x 1024 6.2 / 6.3 / 6.7 against 8.0 / 8.1 / 8.2 us, 256 /
+    // 1024 / 2048 x 2048 x 2048 9.0 / 9.4 / 12.6 against 11.8 / 13.7 / 14.2
+    // (split or three-stage 128x128 tiles); from 512 tiles or a longer K it
+    // loses (4096x2048x2048 26.6 against 19.3, 64x8192x8192 39.9 against
+    // 19.9 split).
+    const int64_t t128 = batch * ((M + 127) / 128) * ((N + 127) / 128);
+    if (K <= 2048 && t128 <= 256) return qg::TILE_64x128_K128;
     return qg::TILE_128x128_K128;
 }
 
@@ -123,13 +133,16 @@ bool dma_ok(const qg::Int8GemmArgs& a, bool bkm, bool vec, int epi, int bk) {
 }
 
 bool is_k128(int cfg) {
-    return cfg == qg::TILE_128x128_K128 || cfg == qg::TILE_256x128_W8_K128 || cfg == qg::TILE_256x256_W8_K128;
+    return cfg == qg::TILE_128x128_K128 || cfg == qg::TILE_256x128_W8_K128 || cfg == qg::TILE_256x256_W8_K128 ||
+           cfg == qg::TILE_64x128_K128;
 }
 
-// The 64-byte-stage configuration of the same tile shape.
+// The 64-byte-stage configuration of the same tile shape (of the nearest
+// shape that has one, for 64x128).
 int k64_of(int cfg) {
     switch (cfg) {
         case qg::TILE_128x128_K128: return qg::TILE_128x128;
+        case qg::TILE_64x128_K128: return qg::TILE_128x128;
         case qg::TILE_256x128_W8_K128: return qg::TILE_256x128_W8;
         case qg::TILE_256x256_W8_K128: return qg::TILE_256x256_W8;
         default: return cfg;
@@ -141,7 +154,7 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
     static const char* dma_names[qg::NUM_TILE_CFGS] = {
         "int8_dma_256x256", "int8_dma_256x128s3", "int8_dma_128x128",
         "int8_dma_128x128s3", "int8_dma_256x256w8", "int8_dma_256x128w8",
-        "int8_dma_128x128k128", "int8_dma_256x128w8k128", "int8_dma_256x256w8k128"};
+        "int8_dma_128x128k128", "int8_dma_256x128w8k128", "int8_dma_256x256w8k128", "int8_dma_64x128k128"};
     // A 128-byte-stage configuration whose K is not whole stages, where bytes
     // past K would reach a sum, runs its 64-byte-stage sibling.
     if (is_k128(cfg) && !dma_ok(a, bkm, vec, epi, 128) && dma_ok(a, bkm, vec, epi, 64)) cfg = k64_of(cfg);
@@ -158,6 +171,7 @@ hipError_t launch_tiled(const qg::Int8GemmArgs& a, int cfg, bool bkm, bool vec, 
             case qg::TILE_128x128_K128: return qg::launch_dma_128x128k128(d, bkm, epi, zp, s);
             case qg::TILE_256x128_W8_K128: return qg::launch_dma_256x128w8k128(d, bkm, epi, zp, s);
             case qg::TILE_256x256_W8_K128: return qg::launch_dma_256x256w8k128(d, bkm, epi, zp, s);
+            case qg::TILE_64x128_K128: return qg::launch_dma_64x128k128(d, bkm, epi, zp, s);
             default: return qg::launch_dma_256x128w8(d, bkm, epi, zp, s);
         }
     }
@@ -574,7 +588,7 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
         e = qg::launch_a8w8_skinny(a, vec, epi, (hipStream_t)stream, &name, skinny_bkm);
         log_dispatch(op, name, 1, M, N, K, splits);
     } else {
-        const int cfg = pick_tile(1, M, N);
+        const int cfg = pick_tile(1, M, N, K);
         // Few output tiles and a long K (128x128 tiles with 128-byte stages):
         // the three-stage kernel, K split across workgroups when the output
         // has at most 128 tiles and a workspace holds the partial sums.
@@ -740,7 +754,7 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
         log_dispatch("matmul_integer", name, 1, a.M, N, K, splits);
         return finish_launch(e, name);
     }
-    const int cfg = pick_tile(a.batch, a.M, N);
+    const int cfg = pick_tile(a.batch, a.M, N, K);
     // Few output tiles and a long K: the three-stage kernel, K split across
     // workgroups (partial tiles and row / column sums in the workspace) when
     // the output has at most 128 tiles and a workspace is given.
@@ -954,7 +968,7 @@ qg_status conv_integer(int64_t N, int64_t C, int64_t H, int64_t W, const void* x
         const bool need_rowsum = a.sb != 0;
         const bool need_colsum = a.ca != 0 || a.a_zp != nullptr;
         const int zp = (need_rowsum ? 1 : 0) | (need_colsum ? 2 : 0);
-        const int cfg = pick_tile(a.batch, a.M, a.N);
+        const int cfg = pick_tile(a.batch, a.M, a.N, a.K);
         e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
         if (e != hipSuccess) return QG_ERR_HIP;
     }

@@ -51,7 +51,8 @@ enum TileCfg {
     TILE_128x128_K128 = 6,     // four waves of 64x64, 128-byte k stages, two stages
     TILE_256x128_W8_K128 = 7,  // eight waves of 64x64, 128-byte k stages, three stages
     TILE_256x256_W8_K128 = 8,  // eight waves of 128x64, 128-byte k stages, two stages
-    NUM_TILE_CFGS = 9
+    TILE_64x128_K128 = 9,      // four waves of 32x64, 128-byte k stages, two stages
+    NUM_TILE_CFGS = 10
 };
 
 // Register-staged kernel, one launcher per tile shape.  bkm: B is [N,K];
@@ -77,6 +78,7 @@ hipError_t launch_dma_128x128k128(const Int8GemmArgs& a, bool bkm, int epi, int 
 hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x128w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+hipError_t launch_dma_64x128k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
 // The split-K workspace starts with a ticket header of fixed size (one int

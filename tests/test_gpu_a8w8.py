@@ -188,7 +188,7 @@ def test_a8w8_repeatable():
 
 
 @pytest.mark.parametrize("stage", [0, 1, 2])
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(10))
 def test_a8w8_every_tile_shape(tile, stage):
     """Every tile configuration, with the output written straight from the
     fragments (stage 0) and through LDS in whole rows (stage 1); ragged M and
@@ -234,10 +234,14 @@ def test_a8w8_k128_stages_partial_last_chunk_and_fallback(tile):
     (3000, 4000, 384, "int8_dma_256x256w8k128"),   # 12 x 16 = 192 tiles, ragged in M and N
     (5120, 4096, 128, "int8_dma_128x128k128"),     # 320: a second round at most 3/8 full
     (2048, 4096, 256, "int8_dma_128x128k128"),     # 128: half a round
+    (256, 1024, 1024, "int8_dma_64x128k128"),      # 16 tiles of 128x128 over K <= 2048: 64x128 tiles
+    (2000, 2032, 2048, "int8_dma_64x128k128"),     # 256 of them, ragged M and N
+    (4096, 2048, 2048, "int8_dma_128x128k128"),    # 512: 128x128 tiles again
+    (256, 2048, 2064, "int8_dma_128x128k128_splitk"),   # K past 2048: the split tiles
 ])
 def test_a8w8_tile_choice_by_tile_count(M, N, K, kernel):
-    """The 256x256 tile is chosen by its tile count; every output of each
-    choice against the oracle."""
+    """The tile is chosen by its count (and, for 64x128 tiles, by K); every
+    output of each choice against the oracle."""
     case(f"a8w8 tile choice M={M} N={N} K={K}")
     A, W, s_a, s_w = si.a8w8_inputs(M, N, K, seed=M + N + K + 3)
     check(A, W, s_a, s_w, expect_kernel=kernel)
@@ -246,6 +250,7 @@ def test_a8w8_tile_choice_by_tile_count(M, N, K, kernel):
 @pytest.mark.parametrize("M,N,K,kernel", [
     (2560, 4096, 256, "int8_dma_256x256w8k128"),
     (5120, 4096, 128, "int8_dma_128x128k128"),
+    (256, 1024, 2048, "int8_dma_64x128k128"),
 ])
 def test_matmul_integer_tile_choice_by_tile_count(M, N, K, kernel):
     """MatMulInteger (uint8 A with a per-row zero point, per-column weight

@@ -36,7 +36,7 @@ def check(acc_in, A, W, s_a, s_w, b_trans=False, expect_kernel=None, acc_dev=Non
 
 
 @pytest.mark.parametrize("stage", [0, 1, 2])
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(10))
 def test_a8w8_acc_every_tile_shape(tile, stage):
     case(f"a8w8_acc tile {tile} stage {stage} 520x704x512 and 300x700x256 b_trans")
     A, W, s_a, s_w = si.a8w8_inputs(520, 704, 512, seed=60 + tile)

@@ -39,7 +39,7 @@ def check(A, W, s_a, s_w, b_trans=False, out_dtype=torch.bfloat16, kernel=SPLITK
     (17, 8192, 8192, False, "bf16"),     # 64 tiles, 4 splits of 2048
     (64, 4096, 8208, False, "f32"),      # 32 tiles, 8 splits; the last holds 1 whole stage + 16 rows
     (128, 1024, 4096, True, "bf16"),     # W as [N,K], 8 tiles, 4 splits
-    (200, 8192, 2048, False, "bf16"),    # 128 tiles, 2 splits, ragged M
+    (200, 8192, 3072, False, "bf16"),    # 128 tiles, 2 splits, ragged M
     (256, 2000, 8192, False, "f32"),     # ragged N
     (33, 8192, 3072, True, "f32"),       # 3 splits of 1024
 ])

@@ -90,7 +90,7 @@ def test_matmul_integer_wraps_mod_2_32():
 
 
 @pytest.mark.parametrize("stage", [0, 1, 2])
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(10))
 def test_matmul_integer_every_tile_shape(tile, stage):
     """Every tile configuration, output straight from the fragments (stage 0)
     or through LDS (stage 1), with ragged M and N edges."""
@@ -117,7 +117,7 @@ def test_matmul_integer_both_kernel_families(family, a_dt, b_dt, za):
 
 
 @pytest.mark.parametrize("a_dt,b_dt", [(np.uint8, np.int8), (np.int8, np.uint8), (np.uint8, np.uint8)])
-@pytest.mark.parametrize("tile", range(9))
+@pytest.mark.parametrize("tile", range(10))
 def test_matmul_integer_row_zero_points_every_tile(tile, a_dt, b_dt):
     """Per-row activation zero points with a shared B (batch folded into M,
     so the row index wraps per batch), per-column b_zp, ragged edges."""

@@ -43,7 +43,7 @@ def check(A, B, za, zb, kernel):
 @pytest.mark.parametrize("M,N,K,a_dt,b_dt,zp", [
     (17, 4096, 8192, np.uint8, np.int8, "column"),    # 32 tiles, 8 splits of 1024
     (100, 2048, 4096, np.int8, np.uint8, "scalar"),   # 16 tiles, 4 splits
-    (256, 1024, 2048, np.uint8, np.uint8, "rows"),    # per-row and per-column zero points, 2 splits
+    (256, 1024, 3072, np.uint8, np.uint8, "rows"),    # per-row and per-column zero points, 3 splits
     (33, 2000, 3072, np.int8, np.int8, "none"),       # ragged N, 3 splits of 1024
     (130, 4096, 4096, np.uint8, np.int8, "rows"),     # ragged M, 64 tiles, 4 splits
 ])
@@ -94,7 +94,7 @@ def test_matmul_integer_split_k_shapes_in_sequence():
     """Calls of different tile and split counts in a row share the binding's
     workspace; its ticket header ends at zero."""
     case("matmul_integer split-K shape sequence")
-    for i, (M, N, K) in enumerate([(64, 4096, 8192), (40, 1024, 4096), (64, 4096, 8192), (130, 2048, 2048)]):
+    for i, (M, N, K) in enumerate([(64, 4096, 8192), (40, 1024, 4096), (64, 4096, 8192), (130, 2048, 3072)]):
         g, A, B = operands(M, N, K, np.uint8, np.int8, seed=710 + i)
         check(A, B, 128, column_zp(g, N, np.int8), SPLITK)
     from quantized_int8_gemm_amd import _binding as b
@@ -102,7 +102,7 @@ def test_matmul_integer_split_k_shapes_in_sequence():
     assert int(ws[:1024].sum().item()) == 0
 
 
-@pytest.mark.parametrize("M,N,K", [(640, 4096, 2048), (300, 8192, 4096)])
+@pytest.mark.parametrize("M,N,K", [(640, 4096, 2176), (300, 8192, 4096)])
 def test_matmul_integer_three_stage_unsplit(M, N, K):
     """129 to 256 output tiles over a long K: the three-stage kernel unsplit."""
     case(f"matmul_integer three-stage unsplit M={M} N={N} K={K}")

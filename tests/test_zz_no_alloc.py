@@ -83,7 +83,8 @@ def test_noalloc_matches_workspace_entry_point(shapes):
         assert noalloc_raw(M, N, K, b._ptr(tA), b._ptr(tW), b._ptr(ta), b._ptr(tw), b._ptr(out), od,
                            stream) == b.QG_OK
         kernel = b.last_kernel()
-        assert kernel == ("a8w8_skinny" if M <= 16 else "int8_dma_128x128k128"), kernel
+        # decode rows, else (K <= 2048, at most 256 tiles of 128 x 128) 64 x 128 tiles
+        assert kernel == ("a8w8_skinny" if M <= 16 else "int8_dma_64x128k128"), kernel
         torch.cuda.synchronize()
         if dt == torch.float32:
             got, want = out.cpu().numpy(), ref_out.cpu().numpy()

@@ -621,8 +621,14 @@ qg_status a8w8_impl(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t ld
             d.splits = splits;
             d.split_steps = splits > 1 ? per : (int)(((K + 127) / 128) * 2);
             d.stage_out = stage_output(cfg, K, epi);
-            name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
-            e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, 0, (hipStream_t)stream);
+            // at most 64 rows: 64x128 tiles, the same tile count (and plan)
+            if (M <= 64) {
+                name = splits > 1 ? "int8_dma_64x128k128_splitk" : "int8_dma_64x128k128x3";
+                e = qg::launch_dma_64x128k128_split(d, b_trans != 0, epi, 0, (hipStream_t)stream);
+            } else {
+                name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
+                e = qg::launch_dma_128x128k128_split(d, b_trans != 0, epi, 0, (hipStream_t)stream);
+            }
         } else {
             e = launch_tiled(a, cfg, b_trans != 0, vec, epi, 0, (hipStream_t)stream, &name);
         }
@@ -775,8 +781,13 @@ qg_status matmul_integer_impl(int64_t batch, int64_t M, int64_t N, int64_t K, co
         d.splits = splits;
         d.split_steps = splits > 1 ? per : (int)(((K + 127) / 128) * 2);
         d.stage_out = stage_output(cfg, K, qg::EPI_I32);
-        name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
-        e = qg::launch_dma_128x128k128_split(d, false, qg::EPI_I32, zp, (hipStream_t)stream);
+        if (a.M <= 64) {   // 64x128 tiles, the same tile count (and plan)
+            name = splits > 1 ? "int8_dma_64x128k128_splitk" : "int8_dma_64x128k128x3";
+            e = qg::launch_dma_64x128k128_split(d, false, qg::EPI_I32, zp, (hipStream_t)stream);
+        } else {
+            name = splits > 1 ? "int8_dma_128x128k128_splitk" : "int8_dma_128x128k128x3";
+            e = qg::launch_dma_128x128k128_split(d, false, qg::EPI_I32, zp, (hipStream_t)stream);
+        }
     } else {
         e = launch_tiled(a, cfg, false, vec, qg::EPI_I32, zp, (hipStream_t)stream, &name);
     }

@@ -79,6 +79,9 @@ hipError_t launch_dma_128x128k128_split(const Int8GemmArgs& a, bool bkm, int epi
 hipError_t launch_dma_256x128w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_256x256w8k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 hipError_t launch_dma_64x128k128(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
+// Three stages of it, split over K when a.splits > 1 (at most 64 rows: the
+// 128x128 split plan's tile count and workspace hold).
+hipError_t launch_dma_64x128k128_split(const Int8GemmArgs& a, bool bkm, int epi, int zp, hipStream_t s);
 
 // Skinny kernel for M <= 16 (A8W8 only, B is [K,N]); splits > 1 needs workspace.
 // The split-K workspace starts with a ticket header of fixed size (one int

@@ -115,7 +115,7 @@ def test_split_and_decode_kernels_graph_replays_match_eager():
         lambda: q.qgemm_a8w8(t["A9"], t["W9t"], t["s_a9"], t["s_w9"], b_trans=True, out=outs[5], workspace=ws),
     ]
     kernels = ["w8a32_skinny", "w8a32_bf16x3_128x128_splitk", "w8a32_input_grad_skinny", "matmul_integer_skinny",
-               "int8_dma_128x128k128_splitk", "a8w8_skinny"]
+               "int8_dma_64x128k128_splitk", "a8w8_skinny"]
     eager = []
     for c, o, k in zip(calls, outs, kernels):
         c()

@@ -141,7 +141,7 @@ def test_matmul_integer_decode_not_taken():
     zb = vals(g, 2048, np.int8)
     st, y = _abi_call(A, B, 128, zb, None, 0)
     assert st == 0
-    assert q.last_kernel() == "int8_dma_128x128k128x3", q.last_kernel()
+    assert q.last_kernel() == "int8_dma_64x128k128x3", q.last_kernel()
     np.testing.assert_array_equal(y.cpu().numpy(), oracle.matmul_integer(A, B, 128, zb))
     g, A, B = operands(8, 2048, 4112, np.uint8, np.int8, seed=831)
     zb = vals(g, 2048, np.int8)

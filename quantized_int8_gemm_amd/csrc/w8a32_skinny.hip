@@ -101,10 +101,19 @@ __device__ __forceinline__ v8bf column8(const u32x4* rows, int j) {
     return __builtin_bit_cast(v8bf, u32x4{pk_hi(f[0], f[1]), pk_hi(f[2], f[3]), pk_hi(f[4], f[5]), pk_hi(f[6], f[7])});
 }
 
-template <bool ZP, bool WT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8a32_skinny_kernel(W8A32Args p) {
-    __shared__ __attribute__((aligned(16))) float red[WAVES][16][TN];
-    __shared__ float s2_red[WAVES][16];
+// WV waves taking steps of KSZ k-rows: the forward runs eight waves of
+// 32-row steps (two waves per SIMD, so one wave's widening and splitting
+// runs beside another's loads and multiplies), the gradient four waves of
+// 64-row steps (its 16-byte loads cover 16 contraction values of a row).
+template <bool ZP, bool WT, int WV = WAVES, int KSZ = KS>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8 ? 2 : 1))) void w8a32_skinny_kernel(W8A32Args p) {
+    constexpr int NTW = 64 * WV;
+    constexpr int RPL = KSZ / 4;    // k-rows per lane per step (forward)
+    constexpr int H = RPL / 8;      // 8-row halves of them
+    static_assert(!WT || (WV == 4 && KSZ == 64), "the gradient's loads take 64-row steps of four waves");
+    static_assert(RPL % 8 == 0 && WV * KSZ == 256, "steps of 512 rows per wave pair");
+    __shared__ __attribute__((aligned(16))) float red[WV][16][TN];
+    __shared__ float s2_red[WV][16];
     __shared__ __attribute__((aligned(16))) float s2_tot[16];
     __shared__ int ticket;
 
@@ -120,24 +129,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     float* Cb = p.C + (int64_t)16 * rb * p.ldc;
     const int unit = rb * (int)gridDim.x + tn;   // this (row block, column tile)'s ticket
 
-    // K range of this split: `per` 64-row steps, a multiple of 2*WAVES.
-    const int per = p.split_k / KS;
+    // K range of this split: `per` steps of KSZ rows, a multiple of 2*WV.
+    const int per = p.split_k / KSZ;
     const int s_begin = split * per;
 
     const int ldw = (int)p.ldw, lda = (int)p.lda;
     const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K))
                                              : make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (uint32_t)(((M - 1) * lda + K) * 4));
-    const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(16 * g * ldw + 16 * c16);
-    const uint32_t a_voff = (uint32_t)((c16 * lda + 16 * g) * 4);
+    const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(RPL * g * ldw + 16 * c16);
+    const uint32_t a_voff = (uint32_t)((c16 * lda + RPL * g) * 4);
 
-    u32x4 wbuf[2][16];
-    u32x4 abuf[2][4];
+    u32x4 wbuf[2][WT ? 16 : RPL];
+    u32x4 abuf[2][RPL / 4];
     // Loads of one step into buffer b; a step past this split's range reads
     // rows that are never multiplied (or zeros past K), so no branch
     // separates the loads.
     auto fetch = [&](int step, int b) {
-        const int k0 = step * KS;
+        const int k0 = step * KSZ;
         if constexpr (WT) {   // W row 16 c16 + j, contraction bytes k0 + 16g ..
             // cached: a step reads half of each 128-byte line, the other half
             // is the next step's (1x8192x8192: 22.3 against 22.6 us; 64
@@ -146,10 +155,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
             for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16(w_rsrc, w_voff + (uint32_t)(j * ldw + k0), 0u);
         } else {   // non-temporal even for several row blocks (M = 64: 37.0 against 43.9 us cached)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
+            for (int r = 0; r < RPL; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) abuf[b][q] = buffer_load16(a_rsrc, a_voff + (uint32_t)((k0 + 4 * q) * 4), 0u);
+        for (int q = 0; q < RPL / 4; ++q) abuf[b][q] = buffer_load16(a_rsrc, a_voff + (uint32_t)((k0 + 4 * q) * 4), 0u);
     };
 
     v4f acc[16];
@@ -158,31 +167,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     float s2 = 0.f;   // this lane's share of S2 for row c16
 
     auto consume = [&](int b, int step) {
-        const int k0 = step * KS + 16 * g;
-        float a[16];
+        const int k0 = step * KSZ + RPL * g;
+        float a[RPL];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < RPL / 4; ++q) {
             a[4 * q] = __uint_as_float(abuf[b][q].x);
             a[4 * q + 1] = __uint_as_float(abuf[b][q].y);
             a[4 * q + 2] = __uint_as_float(abuf[b][q].z);
             a[4 * q + 3] = __uint_as_float(abuf[b][q].w);
         }
-        if (step * KS + KS > K) {   // a step reaching past K: clear those values
+        if (step * KSZ + KSZ > K) {   // a step reaching past K: clear those values
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
+            for (int e = 0; e < RPL; ++e)
                 if (k0 + e >= K) a[e] = 0.f;
         }
         if constexpr (ZP) {
-            s2 += ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])) +
-                  (((a[8] + a[9]) + (a[10] + a[11])) + ((a[12] + a[13]) + (a[14] + a[15])));
+            const float t = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+            if constexpr (H == 2)
+                s2 += t + (((a[8] + a[9]) + (a[10] + a[11])) + ((a[12] + a[13]) + (a[14] + a[15])));
+            else
+                s2 += t;
         }
-        v8bf pa[2][3];
-        split8(a, pa[0][0], pa[0][1], pa[0][2]);
-        split8(a + 8, pa[1][0], pa[1][1], pa[1][2]);
+        v8bf pa[H][3];
+#pragma unroll
+        for (int h = 0; h < H; ++h) split8(a + 8 * h, pa[h][0], pa[h][1], pa[h][2]);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < H; ++h) {
                 const v8bf bw = WT ? half8(wbuf[b][j], h) : column8(&wbuf[b][8 * h], j);
 #pragma unroll
                 for (int pl = 0; pl < 3; ++pl)
@@ -191,27 +203,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
         }
     };
 
-    // This wave's steps: s_begin + wave + WAVES*i, i < n_my (even, the same
+    // This wave's steps: s_begin + wave + WV*i, i < n_my (even, the same
     // for all waves); two in flight, the last pair peeled.
     const int first = s_begin + wave;
-    const int n_my = per / WAVES;
+    const int n_my = per / WV;
     fetch(first, 0);
     __builtin_amdgcn_sched_barrier(0);
-    fetch(first + WAVES, 1);
+    fetch(first + WV, 1);
     __builtin_amdgcn_sched_barrier(0);
     int i = 0;
     for (; i + 2 < n_my; i += 2) {
-        consume(0, first + WAVES * i);
+        consume(0, first + WV * i);
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WAVES * (i + 2), 0);
+        fetch(first + WV * (i + 2), 0);
         __builtin_amdgcn_sched_barrier(0);
-        consume(1, first + WAVES * (i + 1));
+        consume(1, first + WV * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WAVES * (i + 3), 1);
+        fetch(first + WV * (i + 3), 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    consume(0, first + WAVES * i);
-    consume(1, first + WAVES * (i + 1));
+    consume(0, first + WV * i);
+    consume(1, first + WV * (i + 1));
 
     // Register r of block j holds row 4g + r, column 16*c16 + j: four
     // 16-byte chunks per row, placed as in the int8 decode kernel.
@@ -232,14 +244,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
         if (g == 0) s2_red[wave][c16] = s2;
     }
     __syncthreads();
-    if (ZP && tid < 16) s2_tot[tid] = ((s2_red[0][tid] + s2_red[1][tid]) + s2_red[2][tid]) + s2_red[3][tid];
+    if (ZP && tid < 16) {
+        float t = s2_red[0][tid];
+#pragma unroll
+        for (int w = 1; w < WV; ++w) t = t + s2_red[w][tid];
+        s2_tot[tid] = t;
+    }
 
     // Items: (row m < M, group of 4 columns); the waves' tiles in wave order.
     auto tile_sum = [&](int m, int cg) -> v4f {
         const int at = 4 * chunk(cg);
         v4f s = *reinterpret_cast<const v4f*>(&red[0][m][at]);
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) s = s + *reinterpret_cast<const v4f*>(&red[w][m][at]);
+        for (int w = 1; w < WV; ++w) s = s + *reinterpret_cast<const v4f*>(&red[w][m][at]);
         return s;
     };
     const float zp = (float)p.zp;
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
 
     if (S == 1) {
         if constexpr (ZP) __syncthreads();   // s2_tot
-        for (int it = tid; it < items; it += NT) {
+        for (int it = tid; it < items; it += NTW) {
             const int m = it / (TN / 4), cg = it % (TN / 4);
             epilogue(m, n0 + cg * 4, tile_sum(m, cg));
         }
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     char* part = reinterpret_cast<char*>(p.workspace) + SKINNY_TICKET_BYTES + (size_t)unit * S * SLOT;
     const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
     constexpr int COHERENT = 16;   // sc1: device scope
-    for (int it = tid; it < items; it += NT) {
+    for (int it = tid; it < items; it += NTW) {
         const int m = it / (TN / 4), cg = it % (TN / 4);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, tile_sum(m, cg)), p_rsrc,
                                                (uint32_t)(split * SLOT + (m * TN + cg * 4) * 4), 0, COHERENT);
@@ -299,12 +316,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
 
     // Every split's partial, added in split order, SU splits per round with
     // their loads in flight together; loads past split S - 1 read zeros.
-    constexpr int SU = 8, IPT = 16 * (TN / 4) / NT;
+    constexpr int SU = 8, IPT = 16 * (TN / 4) / NTW;
     v4f sum[IPT];
     uint32_t off[IPT];
 #pragma unroll
     for (int q = 0; q < IPT; ++q) {
-        const int it = tid + q * NT;
+        const int it = tid + q * NTW;
         const int m = it / (TN / 4), cg = it % (TN / 4);
         sum[q] = v4f{0.f, 0.f, 0.f, 0.f};
         off[q] = it < items ? (uint32_t)((m * TN + cg * 4) * 4) : 0xFFFFFFF0u;
@@ -344,7 +361,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1))) void w8
     }
 #pragma unroll
     for (int q = 0; q < IPT; ++q) {
-        const int it = tid + q * NT;
+        const int it = tid + q * NTW;
         if (it >= items) continue;
         const int m = it / (TN / 4), cg = it % (TN / 4);
         epilogue(m, n0 + cg * 4, sum[q]);
@@ -568,8 +585,8 @@ hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const
         if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true>), grid, dim3(NT), 0, s, a);
         else hipLaunchKernelGGL((w8a32_skinny_kernel<false, true>), grid, dim3(NT), 0, s, a);
     } else {
-        if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, false>), grid, dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((w8a32_skinny_kernel<false, false>), grid, dim3(NT), 0, s, a);
+        if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, false, 8, 32>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((w8a32_skinny_kernel<false, false, 8, 32>), grid, dim3(512), 0, s, a);
     }
     return hipGetLastError();
 }

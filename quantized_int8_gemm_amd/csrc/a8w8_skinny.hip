@@ -42,10 +42,9 @@
 namespace qg {
 namespace {
 
-constexpr int NT = 256;     // threads (four waves)
 constexpr int TN = 256;     // columns per workgroup
 constexpr int KS = 64;      // k rows per wave step
-constexpr int WAVES = 4;
+constexpr int WAVES = 4;    // the fewest waves of a workgroup: steps per split are a multiple of 2 * WAVES
 
 // In-place 16 x 16 byte transpose: on entry v[r] holds row r (16 bytes); on
 // exit v[c] holds column c (16 bytes, rows 0..15 in order).  Block (q, d) of
@@ -73,18 +72,25 @@ __device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
 
 // MatMulInteger's sums do not fit beside two waves per SIMD; its grid gives
 // one workgroup per CU anyway.
-template <bool VEC, int EPI, bool BKM = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I32 ? 1 : 2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
+// WV waves: eight (two per SIMD, so one wave's transposes run beside
+// another's loads; 8192^2 at M = 1 / 4 / 16: 14.8 / 15.5 / 17.5 -> 14.4 /
+// 15.0 / 16.8 us) when each split spans a multiple of 16 steps, else four;
+// MatMulInteger always four, its sums need the registers of one wave per
+// SIMD.
+template <bool VEC, int EPI, bool BKM = false, int WV = 4>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I32 ? 1 : 2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
     constexpr bool I32 = EPI == EPI_I32;
+    static_assert(!I32 || WV == 4, "MatMulInteger's sums take four waves");
+    constexpr int NTW = 64 * WV;
     // A split's partial: 16 rows of the tile, then (MatMulInteger) a row of
     // column sums and a row whose first 16 entries are the row sums.
     constexpr int SLOT_ROWS = I32 ? 18 : 16;
-    __shared__ __attribute__((aligned(16))) int32_t red[WAVES][16][TN];
+    __shared__ __attribute__((aligned(16))) int32_t red[WV][16][TN];
     __shared__ float ws_tile[I32 ? 1 : TN];
     __shared__ float as_rows[I32 ? 1 : 16];
     // MatMulInteger: per-wave sums, the tile's totals, cb[n] and ca[m]
-    __shared__ __attribute__((aligned(16))) int32_t cs_red[I32 ? WAVES : 1][I32 ? TN : 4];
-    __shared__ int32_t rs_red[I32 ? WAVES : 1][16];
+    __shared__ __attribute__((aligned(16))) int32_t cs_red[I32 ? WV : 1][I32 ? TN : 4];
+    __shared__ int32_t rs_red[I32 ? WV : 1][16];
     __shared__ __attribute__((aligned(16))) int32_t cs_tot[I32 ? TN : 4];
     __shared__ __attribute__((aligned(16))) int32_t rs_tot[16];
     __shared__ int32_t cb_tile[I32 ? TN : 1];
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     const int n0 = tn * TN;
     const int cols = p.N - n0;
 
-    // K range of this split: `per` 64-row steps, a multiple of 2*WAVES.
+    // K range of this split: `per` 64-row steps, a multiple of 2*WV.
     const int per = p.split_steps;
     const int s_begin = split * per;
 
@@ -190,14 +196,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     for (int j = 0; j < (I32 ? 16 : 1); ++j) cs[j] = 0;
     const int nsteps = (p.K + KS - 1) / KS;
 
-    // This wave's steps: s_begin + wave + WAVES*i, i < n_my.  Every split
-    // spans a multiple of 2*WAVES steps (steps past K read as zeros and add
+    // This wave's steps: s_begin + wave + WV*i, i < n_my.  Every split
+    // spans a multiple of 2*WV steps (steps past K read as zeros and add
     // nothing), so n_my is even and the same for all waves, and no branch
     // sits between the loads.  Two steps are in flight; the loop is unrolled
     // by two so both register buffers have fixed homes, and the last pair is
     // peeled so that nothing is fetched past the wave's range.
     const int first = s_begin + wave;
-    const int n_my = per / WAVES;
+    const int n_my = per / WV;
     auto consume = [&](int b, int step) {
         if constexpr (I32) {
             // a step past K multiplies nothing: no flips, A bytes cleared
@@ -230,21 +236,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     // for one buffer never waits for the other buffer's loads.
     fetch(first, 0);
     __builtin_amdgcn_sched_barrier(0);
-    fetch(first + WAVES, 1);
+    fetch(first + WV, 1);
     __builtin_amdgcn_sched_barrier(0);
     int i = 0;
     for (; i + 2 < n_my; i += 2) {
-        consume(0, first + WAVES * i);
+        consume(0, first + WV * i);
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WAVES * (i + 2), 0);
+        fetch(first + WV * (i + 2), 0);
         __builtin_amdgcn_sched_barrier(0);
-        consume(1, first + WAVES * (i + 1));
+        consume(1, first + WV * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WAVES * (i + 3), 1);
+        fetch(first + WV * (i + 3), 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    consume(0, first + WAVES * i);
-    consume(1, first + WAVES * (i + 1));
+    consume(0, first + WV * i);
+    consume(1, first + WV * (i + 1));
 
     // Add the four waves' tiles through LDS.  Register r of MFMA j holds
     // row 4g + r, column 16*c16 + j, so for each r a lane owns 16 consecutive
@@ -286,13 +292,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
         if (tid < TN) {
             uint32_t t = 0u;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) t += (uint32_t)cs_red[w][tid];
+            for (int w = 0; w < WV; ++w) t += (uint32_t)cs_red[w][tid];
             cs_tot[tid] = (int)t;
         }
         if (tid < 16) {
             uint32_t t = 0u;
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) t += (uint32_t)rs_red[w][tid];
+            for (int w = 0; w < WV; ++w) t += (uint32_t)rs_red[w][tid];
             rs_tot[tid] = (int)t;
         }
         __syncthreads();
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
         const int at = 4 * chunk(cg);
         int4 s = *reinterpret_cast<const int4*>(&red[0][m][at]);
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) {
+        for (int w = 1; w < WV; ++w) {
             const int4 v = *reinterpret_cast<const int4*>(&red[w][m][at]);
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     const int items = M * (TN / 4);
 
     if (S == 1) {
-        for (int it = tid; it < items; it += NT) {
+        for (int it = tid; it < items; it += NTW) {
             const int m = it / (TN / 4), cg = it % (TN / 4);
             finish(m, n0 + cg * 4, tile_sum(m, cg));
         }
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     // resource with device-coherent cache policy.
     const __amdgpu_buffer_rsrc_t p_rsrc = make_rsrc(part, (uint32_t)(S * SLOT));
     constexpr int COHERENT = 16;  // sc1: device scope, bypass the XCD-private cache level
-    for (int it = tid; it < items; it += NT) {
+    for (int it = tid; it < items; it += NTW) {
         const int m = it / (TN / 4), cg = it % (TN / 4);
         const int4 s4 = tile_sum(m, cg);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, s4), p_rsrc,
@@ -437,13 +443,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     // Each thread owns up to four (row, column group) items and keeps all of
     // their partial loads in flight at once: SU splits per round, loads past
     // split S - 1 fall outside the buffer range and read as zero.
-    constexpr int SU = 8, IPT = 16 * (TN / 4) / NT;   // items per thread at M = 16
-    static_assert(IPT * NT == 16 * (TN / 4), "whole items");
+    constexpr int SU = 8, IPT = 16 * (TN / 4) / NTW;   // items per thread at M = 16
+    static_assert(IPT * NTW == 16 * (TN / 4), "whole items");
     v4i sum[IPT];
     uint32_t off[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        const int it = tid + i * NT;
+        const int it = tid + i * NTW;
         const int m = it / (TN / 4), cg = it % (TN / 4);
         sum[i] = v4i{0, 0, 0, 0};
         // an item past M reads past the buffer (zeros) and is not stored
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        const int it = tid + i * NT;
+        const int it = tid + i * NTW;
         if (it >= items) continue;
         const int m = it / (TN / 4), cg = it % (TN / 4);
         finish(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w});
@@ -567,6 +573,19 @@ int skinny_splits(int M, int N, int K) {
     return skinny_splits_for(N, K, skinny_split_steps(N, K));
 }
 
+namespace {
+// One A8W8 decode launch with WV waves per workgroup.
+template <bool VEC, int EPI, bool BKM, int WV>
+void launch_waves(const Int8GemmArgs& a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((a8w8_skinny_kernel<VEC, EPI, BKM, WV>), grid, dim3(64 * WV), 0, s, a);
+}
+template <bool VEC, int EPI, bool BKM>
+void launch_a8w8(const Int8GemmArgs& a, dim3 grid, hipStream_t s) {
+    if (a.split_steps % 16 == 0) launch_waves<VEC, EPI, BKM, 8>(a, grid, s);
+    else launch_waves<VEC, EPI, BKM, 4>(a, grid, s);
+}
+}  // namespace
+
 hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStream_t s, const char** name, bool bkm) {
     dim3 grid((a.N + TN - 1) / TN, a.splits > 1 ? a.splits : 1);
     *name = epi == EPI_I32 ? "matmul_integer_skinny" : "a8w8_skinny";
@@ -575,17 +594,17 @@ hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStrea
     if (a.M > 16 || a.batch != 1) return hipErrorInvalidValue;
     if (bkm) {   // A8W8 with W as [N,K]: 16-byte rows, K % 16 == 0
         if (!vec || epi == EPI_I32 || a.K % 16 != 0) return hipErrorInvalidValue;
-        if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32, true>), grid, dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16, true>), grid, dim3(NT), 0, s, a);
+        if (epi == EPI_F32) launch_a8w8<true, EPI_F32, true>(a, grid, s);
+        else launch_a8w8<true, EPI_BF16, true>(a, grid, s);
     } else if (epi == EPI_I32) {   // 16-byte rows, B as [K,N], whole 64-row steps
         if (!vec || a.K % KS != 0 || (a.a_zp != nullptr && a.a_zp_rows < 1)) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_I32>), grid, dim3(NT), 0, s, a);
+        launch_waves<true, EPI_I32, false, 4>(a, grid, s);
     } else if (vec) {
-        if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_F32>), grid, dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_BF16>), grid, dim3(NT), 0, s, a);
+        if (epi == EPI_F32) launch_a8w8<true, EPI_F32, false>(a, grid, s);
+        else launch_a8w8<true, EPI_BF16, false>(a, grid, s);
     } else {
-        if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_skinny_kernel<false, EPI_F32>), grid, dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((a8w8_skinny_kernel<false, EPI_BF16>), grid, dim3(NT), 0, s, a);
+        if (epi == EPI_F32) launch_a8w8<false, EPI_F32, false>(a, grid, s);
+        else launch_a8w8<false, EPI_BF16, false>(a, grid, s);
     }
     return hipGetLastError();
 }

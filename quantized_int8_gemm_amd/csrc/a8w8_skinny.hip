@@ -75,9 +75,11 @@ __device__ __forceinline__ void transpose16x16_inplace(u32x4 v[16]) {
 // WV waves: eight (two per SIMD, so one wave's transposes run beside
 // another's loads; 8192^2 at M = 1 / 4 / 16: 14.8 / 15.5 / 17.5 -> 14.4 /
 // 15.0 / 16.8 us) when each split spans a multiple of 16 steps, else four;
-// MatMulInteger always four, its sums need the registers of one wave per
-// SIMD.
-template <bool VEC, int EPI, bool BKM = false, int WV = 4>
+// MatMulInteger four when it takes the weight's column sums (they need the
+// registers of one wave per SIMD).  CS: MatMulInteger takes the column sums,
+// which only multiply ca[m]; with no activation correction (ca = 0, e.g.
+// uint8 activations at zero point 128) it skips them.
+template <bool VEC, int EPI, bool BKM = false, int WV = 4, bool CS = true>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == EPI_I32 ? 1 : 2))) void a8w8_skinny_kernel(Int8GemmArgs p) {
     constexpr bool I32 = EPI == EPI_I32;
     static_assert(!I32 || WV == 4, "MatMulInteger's sums take four waves");
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[j] = mfma_i8_16x16x64(abuf[b], wbuf[b][j], acc[j]);
-        if constexpr (I32) {
+        if constexpr (I32 && CS) {
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 cs[j] = sum_i8x4(wbuf[b][j].w, sum_i8x4(wbuf[b][j].z, sum_i8x4(wbuf[b][j].y, sum_i8x4(wbuf[b][j].x, cs[j]))));
@@ -273,17 +275,21 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         // wave leaves its sums in LDS
         rs += __shfl_xor(rs, 16);
         rs += __shfl_xor(rs, 32);
+        if constexpr (CS) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            cs[j] += __shfl_xor(cs[j], 16);
-            cs[j] += __shfl_xor(cs[j], 32);
+            for (int j = 0; j < 16; ++j) {
+                cs[j] += __shfl_xor(cs[j], 16);
+                cs[j] += __shfl_xor(cs[j], 32);
+            }
         }
         if (g == 0) {
             rs_red[wave][c16] = rs;
+            if constexpr (CS) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<v4i*>(&cs_red[wave][16 * c16 + 4 * q]) =
-                    v4i{cs[4 * q], cs[4 * q + 1], cs[4 * q + 2], cs[4 * q + 3]};
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4i*>(&cs_red[wave][16 * c16 + 4 * q]) =
+                        v4i{cs[4 * q], cs[4 * q + 1], cs[4 * q + 2], cs[4 * q + 3]};
+            }
         }
     }
     __syncthreads();
@@ -291,9 +297,11 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         // this workgroup's sums over its k range
         if (tid < TN) {
             uint32_t t = 0u;
+            if constexpr (CS) {
 #pragma unroll
-            for (int w = 0; w < WV; ++w) t += (uint32_t)cs_red[w][tid];
-            cs_tot[tid] = (int)t;
+                for (int w = 0; w < WV; ++w) t += (uint32_t)cs_red[w][tid];
+            }
+            cs_tot[tid] = (int)t;   // without CS: zero, and ca = 0 multiplies it
         }
         if (tid < 16) {
             uint32_t t = 0u;
@@ -598,7 +606,8 @@ hipError_t launch_a8w8_skinny(const Int8GemmArgs& a, bool vec, int epi, hipStrea
         else launch_a8w8<true, EPI_BF16, true>(a, grid, s);
     } else if (epi == EPI_I32) {   // 16-byte rows, B as [K,N], whole 64-row steps
         if (!vec || a.K % KS != 0 || (a.a_zp != nullptr && a.a_zp_rows < 1)) return hipErrorInvalidValue;
-        launch_waves<true, EPI_I32, false, 4>(a, grid, s);
+        if (a.ca != 0 || a.a_zp != nullptr) launch_waves<true, EPI_I32, false, 4>(a, grid, s);
+        else hipLaunchKernelGGL((a8w8_skinny_kernel<true, EPI_I32, false, 4, false>), grid, dim3(256), 0, s, a);
     } else if (vec) {
         if (epi == EPI_F32) launch_a8w8<true, EPI_F32, false>(a, grid, s);
         else launch_a8w8<true, EPI_BF16, false>(a, grid, s);

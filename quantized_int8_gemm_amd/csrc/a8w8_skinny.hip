@@ -328,20 +328,23 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
     const bool vec_out = (p.ldo % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.out) & 15) == 0);
     const bool acc_vec = p.acc_in != nullptr && p.ld_acc % 4 == 0 &&
                          (reinterpret_cast<uintptr_t>(p.acc_in) & 15) == 0;
-    auto epilogue = [&](int m, int n, int4 v) {
+    // The accumulator input of row m, columns n .. n+3 (zeros past N).
+    auto load_acc = [&](int m, int n) -> v4i {
+        const int32_t* src = p.acc_in + (int64_t)m * p.ld_acc + n;
+        if (acc_vec && n + 4 <= p.N) return __builtin_bit_cast(v4i, *reinterpret_cast<const int4*>(src));
+        v4i t = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) t[e] = src[e];
+        return t;
+    };
+    // add_acc: the accumulator input is still to be added (the reducing
+    // split folds it into its sum instead).
+    auto epilogue = [&](int m, int n, int4 v, bool add_acc) {
         if (n >= p.N) return;
         int32_t vi[4] = {v.x, v.y, v.z, v.w};
-        if (p.acc_in != nullptr) {   // accumulator input, added before the cast (wrapping)
-            const int32_t* src = p.acc_in + (int64_t)m * p.ld_acc + n;
-            int32_t ai[4] = {0, 0, 0, 0};
-            if (acc_vec && n + 4 <= p.N) {
-                const int4 t = *reinterpret_cast<const int4*>(src);
-                ai[0] = t.x; ai[1] = t.y; ai[2] = t.z; ai[3] = t.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < p.N) ai[e] = src[e];
-            }
+        if (add_acc && p.acc_in != nullptr) {   // accumulator input, added before the cast (wrapping)
+            const v4i ai = load_acc(m, n);
 #pragma unroll
             for (int e = 0; e < 4; ++e) vi[e] = (int32_t)((uint32_t)vi[e] + (uint32_t)ai[e]);
         }
@@ -392,9 +395,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         for (int e = 0; e < 4; ++e)
             if (n + e < p.N) dst[e] = y[e];
     };
-    auto finish = [&](int m, int n, int4 v) {
+    auto finish = [&](int m, int n, int4 v, bool add_acc = true) {
         if constexpr (I32) epilogue_i32(m, n, v);
-        else epilogue(m, n, v);
+        else epilogue(m, n, v, add_acc);
     };
     const int items = M * (TN / 4);
 
@@ -462,6 +465,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         sum[i] = v4i{0, 0, 0, 0};
         // an item past M reads past the buffer (zeros) and is not stored
         off[i] = it < items ? (uint32_t)((m * TN + cg * 4) * 4) : 0xFFFFFFF0u;
+        // the accumulator input starts the sum (wrapping, so the order does
+        // not matter), its loads in flight with the partials'
+        if (!I32 && p.acc_in != nullptr && it < items && n0 + cg * 4 < p.N) sum[i] = load_acc(m, n0 + cg * 4);
     }
     // MatMulInteger: threads below SUM_ITEMS also add one vector of sums
     v4i ssum = v4i{0, 0, 0, 0};
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
         const int it = tid + i * NTW;
         if (it >= items) continue;
         const int m = it / (TN / 4), cg = it % (TN / 4);
-        finish(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w});
+        finish(m, n0 + cg * 4, int4{sum[i].x, sum[i].y, sum[i].z, sum[i].w}, false);
     }
     if (tid == 0) __hip_atomic_store(&tickets[tn], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

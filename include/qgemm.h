@@ -208,7 +208,9 @@ qg_status qgemm_w8a32_input_grad_ws(int64_t M, int64_t N, int64_t K,
  * other shapes run the tiled matrix-core kernel.  With W as [N,K] and
  * N >= 4096 the decode kernel owns whole columns over all of K (no split,
  * the workspace is not touched); otherwise it splits K as described above.
- * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31.
+ * QG_ERR_UNSUPPORTED if an operand's byte span reaches 2^31 (for W as
+ * [N,K], the span of 256 of its rows: the kernels address it a tile of rows
+ * at a time, so the whole weight may be larger).
  */
 qg_status qgemm_a8w8(int64_t M, int64_t N, int64_t K,
                      const int8_t* A, int64_t lda,

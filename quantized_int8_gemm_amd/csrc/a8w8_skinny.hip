@@ -111,7 +111,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(EPI == 
 
     const int ldb = (int)p.ldb, lda = (int)p.lda;
     const int8_t* Wt = BKM ? p.B + (int64_t)n0 * ldb : p.B + n0;
-    const __amdgpu_buffer_rsrc_t w_rsrc = BKM ? make_rsrc(Wt, (uint32_t)((cols - 1) * ldb + p.K))
+    // [N,K]: the tile's own rows only (the whole weight may span 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t w_rsrc = BKM ? make_rsrc(Wt, (uint32_t)(((cols < TN ? cols : TN) - 1) * ldb + p.K))
                                               : make_rsrc(Wt, (uint32_t)((p.K - 1) * ldb + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)((p.M - 1) * lda + p.K));
     const uint32_t w_voff = BKM ? (uint32_t)(16 * c16 * ldb + 16 * g) : (uint32_t)(16 * g * ldb + 16 * c16);

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(SL_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int n0 = blockIdx.x * TN;
     const int cols = p.N - n0;
     const int ldb = (int)p.ldb, lda = (int)p.lda;
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.B + (int64_t)n0 * ldb, (uint32_t)((cols - 1) * ldb + p.K));
+    // the slab's own rows only (a whole [N,K] weight may span 2^31 bytes)
+    const int rows_w = cols < TN ? cols : TN;
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.B + (int64_t)n0 * ldb, (uint32_t)((rows_w - 1) * ldb + p.K));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)((p.M - 1) * lda + p.K));
     const uint32_t w_voff = (uint32_t)(i16 * ldb + 16 * g);
     const uint32_t a_voff = (uint32_t)(i16 * lda + 16 * g);

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
     const int s_begin = split * per;
 
     const int ldw = (int)p.ldw, lda = (int)p.lda;
-    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K))
+    const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)(((cols < TN ? cols : TN) - 1) * ldw + K))
                                              : make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (uint32_t)(((M - 1) * lda + K) * 4));
     const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(RPL * g * ldw + 16 * c16);
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(GS_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int cols = p.N - n0;
     const int M = p.M, K = p.K;
     const int ldw = (int)p.ldw, lda = (int)p.lda;
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)((cols - 1) * ldw + K));
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)(((cols < TS ? cols : TS) - 1) * ldw + K));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.A, (uint32_t)(((M - 1) * lda + K) * 4));
     const uint32_t w_voff = (uint32_t)(i16 * ldw + 16 * g);
     const uint32_t a_voff = (uint32_t)((i16 * lda + 16 * g) * 4);

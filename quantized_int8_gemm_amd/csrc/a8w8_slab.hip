@@ -38,8 +38,9 @@ constexpr int SL_WAVES = 8;
 constexpr int SL_NT = 64 * SL_WAVES;
 
 // TN output columns per workgroup; SK k-bytes per wave step, NB steps in
-// flight per wave.  At most 16 rows (one fragment of A).
-template <int TN, int EPI, int SK, int NB>
+// flight per wave; CONTIG: each wave takes one contiguous range of steps
+// instead of every eighth step.  At most 16 rows (one fragment of A).
+template <int TN, int EPI, int SK, int NB, bool CONTIG>
 __global__ __launch_bounds__(SL_NT) __attribute__((amdgpu_waves_per_eu(2))) void a8w8_slab_kernel(Int8GemmArgs p) {
     constexpr int NF = TN / 16;   // 16-column fragments of the slab
     constexpr int KB = SK / 64;   // 64-byte k-blocks per step
@@ -99,28 +100,28 @@ __global__ __launch_bounds__(SL_NT) __attribute__((amdgpu_waves_per_eu(2))) void
         }
     };
 
-    // This wave's steps: wave + SL_WAVES * i, i < n_my, with n_my a multiple
-    // of NB and the same for every wave (steps past K add nothing), NB in
-    // flight, the loop unrolled by NB so that the register buffers have fixed
-    // homes.
+    // This wave's steps: step_of(i), i < n_my, with n_my a multiple of NB and
+    // the same for every wave (steps past K add nothing), NB in flight, the
+    // loop unrolled by NB so that the register buffers have fixed homes.
     const int n_my = (((nsteps + SL_WAVES - 1) / SL_WAVES) + NB - 1) / NB * NB;
+    auto step_of = [&](int i) { return CONTIG ? wave * n_my + i : wave + SL_WAVES * i; };
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        fetch(wave + SL_WAVES * b, b);
+        fetch(step_of(b), b);
         __builtin_amdgcn_sched_barrier(0);
     }
     int i = 0;
     for (; i + NB < n_my; i += NB) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            consume(b, wave + SL_WAVES * (i + b));
+            consume(b, step_of(i + b));
             __builtin_amdgcn_sched_barrier(0);
-            fetch(wave + SL_WAVES * (i + NB + b), b);
+            fetch(step_of(i + NB + b), b);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) consume(b, wave + SL_WAVES * (i + b));
+    for (int b = 0; b < NB; ++b) consume(b, step_of(i + b));
 
     // The waves' tiles through LDS: register r of fragment c holds row
     // 4g + r, column 16c + i16.
@@ -194,11 +195,11 @@ __global__ __launch_bounds__(SL_NT) __attribute__((amdgpu_waves_per_eu(2))) void
     }
 }
 
-template <int TN, int SK, int NB>
+template <int TN, int SK, int NB, bool CONTIG>
 hipError_t launch_cfg(const Int8GemmArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + TN - 1) / TN), block(SL_NT);
-    if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_slab_kernel<TN, EPI_F32, SK, NB>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((a8w8_slab_kernel<TN, EPI_BF16, SK, NB>), grid, block, 0, s, a);
+    if (epi == EPI_F32) hipLaunchKernelGGL((a8w8_slab_kernel<TN, EPI_F32, SK, NB, CONTIG>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((a8w8_slab_kernel<TN, EPI_BF16, SK, NB, CONTIG>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -214,15 +215,16 @@ bool slab_shape_ok(const Int8GemmArgs& a, int tn) {
            (int64_t)16 * a.lda + a.K + 256 < ((int64_t)1 << 31);
 }
 
-// Steps: a 16-column slab takes 128-byte steps four deep, a 32-column slab
-// 256-byte steps two deep (8 KiB per wave either way; measured fastest of
-// the 16/32-column, 128/256/512-byte, two/three/four-deep forms at
-// N = K = 8192: M = 1 13.9 us, M = 16 16.7 us).
+// Steps: a 16-column slab takes 128-byte steps four deep, each wave one
+// contiguous range of them (13.4 -> 13.1 us at M = 1), a 32-column slab
+// 256-byte steps two deep, every eighth per wave (8 KiB per wave either way;
+// measured fastest of the 16/32-column, 128/256/512-byte, two/three/four-deep
+// forms at N = K = 8192: M = 1 13.9 us, M = 16 16.7 us).
 hipError_t launch_a8w8_slab(const Int8GemmArgs& a, int tn, int epi, hipStream_t s, const char** name) {
     *name = "a8w8_slab";
     if (!slab_shape_ok(a, tn) || (epi != EPI_F32 && epi != EPI_BF16)) return hipErrorInvalidValue;
-    if (tn == 16) return launch_cfg<16, 128, 4>(a, epi, s);
-    return launch_cfg<32, 256, 2>(a, epi, s);
+    if (tn == 16) return launch_cfg<16, 128, 4, true>(a, epi, s);
+    return launch_cfg<32, 256, 2, false>(a, epi, s);
 }
 
 }  // namespace qg

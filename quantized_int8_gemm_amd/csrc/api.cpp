@@ -364,9 +364,9 @@ static bool w8a32_skinny_ok(int64_t M, int64_t N, int64_t K, const void* A, int6
 // The input gradient's slab form (each workgroup owns 32 outputs, i.e. W
 // rows, over the whole contraction; no workspace) for at most 8 rows across
 // at least 8192 outputs.  Graph-timed at N = K = 8192: 17.3 / 17.4 / 18.7 /
-// 20.6 us at M = 1 / 2 / 4 / 8 against 22.7 - 23.4 on the split decode
-// kernel; at 16 rows 25.7 against 24.4 (every workgroup reads and splits all
-// of dC).  QGEMM_FORCE_KERNEL=slab takes it whenever the shape allows.
+// 20.6 us at M = 1 / 2 / 4 / 8 against 20.8 / 21.3 at M = 1 / 4 on the
+// split decode kernel; at 16 rows 25.7 against 23.1 (every workgroup reads
+// and splits all of dC).  QGEMM_FORCE_KERNEL=slab takes it whenever the shape allows.
 static bool w8a32_grad_slab(const qg::W8A32Args& a) {
     if (!w8a32_split() || env_is("QGEMM_FORCE_KERNEL", "tiled") || env_is("QGEMM_FORCE_KERNEL", "skinny")) return false;
     if (!qg::w8a32_grad_slab_ok(a)) return false;

@@ -103,22 +103,33 @@ __device__ __forceinline__ v8bf column8(const u32x4* rows, int j) {
 
 // WV waves taking steps of KSZ k-rows: the forward runs eight waves of
 // 32-row steps (two waves per SIMD, so one wave's widening and splitting
-// runs beside another's loads and multiplies), the gradient four waves of
-// 64-row steps (its 16-byte loads cover 16 contraction values of a row).
+// runs beside another's loads and multiplies).  The gradient takes 64-row
+// steps (its 16-byte loads cover 16 contraction values of a row) with four
+// waves, or with eight as two halves of four: both halves walk the same
+// steps, each over 128 of the tile's 256 outputs (lane c16 then holds rows
+// 128 half + 8 c16 + j, j < 8), which halves a wave's weight registers and
+// again puts two waves on each SIMD; only the first half adds S2.
 template <bool ZP, bool WT, int WV = WAVES, int KSZ = KS>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8 ? 2 : 1))) void w8a32_skinny_kernel(W8A32Args p) {
     constexpr int NTW = 64 * WV;
     constexpr int RPL = KSZ / 4;    // k-rows per lane per step (forward)
     constexpr int H = RPL / 8;      // 8-row halves of them
-    static_assert(!WT || (WV == 4 && KSZ == 64), "the gradient's loads take 64-row steps of four waves");
-    static_assert(RPL % 8 == 0 && WV * KSZ == 256, "steps of 512 rows per wave pair");
-    __shared__ __attribute__((aligned(16))) float red[WV][16][TN];
-    __shared__ float s2_red[WV][16];
+    // The gradient with eight waves: two halves of four, each half covering
+    // 128 of the tile's 256 outputs over the same steps (SW waves share the
+    // steps; JN column blocks of 16 per wave).
+    constexpr bool HALVES = WT && WV == 8;
+    constexpr int SW = HALVES ? 4 : WV;
+    constexpr int JN = HALVES ? 8 : 16;
+    static_assert(!WT || (KSZ == 64 && (WV == 4 || WV == 8)), "the gradient's loads take 64-row steps");
+    static_assert(RPL % 8 == 0 && SW * KSZ == 256, "steps of 512 rows per wave pair");
+    __shared__ __attribute__((aligned(16))) float red[SW][16][TN];
+    __shared__ float s2_red[SW][16];
     __shared__ __attribute__((aligned(16))) float s2_tot[16];
     __shared__ int ticket;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
+    const int half = HALVES ? wave / SW : 0, swave = HALVES ? wave % SW : wave;
     const int tn = blockIdx.x, split = blockIdx.y, S = gridDim.y;
     const int n0 = tn * TN;
     const int cols = p.N - n0;
@@ -137,10 +148,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
     const __amdgpu_buffer_rsrc_t w_rsrc = WT ? make_rsrc(p.W + (int64_t)n0 * ldw, (uint32_t)(((cols < TN ? cols : TN) - 1) * ldw + K))
                                              : make_rsrc(p.W + n0, (uint32_t)((K - 1) * ldw + cols));
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (uint32_t)(((M - 1) * lda + K) * 4));
-    const uint32_t w_voff = WT ? (uint32_t)(16 * c16 * ldw + 16 * g) : (uint32_t)(RPL * g * ldw + 16 * c16);
+    const uint32_t w_voff = WT ? (uint32_t)((128 * half + JN * c16) * ldw + 16 * g) : (uint32_t)(RPL * g * ldw + 16 * c16);
     const uint32_t a_voff = (uint32_t)((c16 * lda + RPL * g) * 4);
 
-    u32x4 wbuf[2][WT ? 16 : RPL];
+    u32x4 wbuf[2][WT ? JN : RPL];
     u32x4 abuf[2][RPL / 4];
     // Loads of one step into buffer b; a step past this split's range reads
     // rows that are never multiplied (or zeros past K), so no branch
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
             // is the next step's (1x8192x8192: 22.3 against 22.6 us; 64
             // rows: 50.3 against 56.0)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) wbuf[b][j] = buffer_load16(w_rsrc, w_voff + (uint32_t)(j * ldw + k0), 0u);
+            for (int j = 0; j < JN; ++j) wbuf[b][j] = buffer_load16(w_rsrc, w_voff + (uint32_t)(j * ldw + k0), 0u);
         } else {   // non-temporal even for several row blocks (M = 64: 37.0 against 43.9 us cached)
 #pragma unroll
             for (int r = 0; r < RPL; ++r) wbuf[b][r] = buffer_load16_nt(w_rsrc, w_voff + (uint32_t)((k0 + r) * ldw));
@@ -161,9 +172,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
         for (int q = 0; q < RPL / 4; ++q) abuf[b][q] = buffer_load16(a_rsrc, a_voff + (uint32_t)((k0 + 4 * q) * 4), 0u);
     };
 
-    v4f acc[16];
+    v4f acc[JN];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JN; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
     float s2 = 0.f;   // this lane's share of S2 for row c16
 
     auto consume = [&](int b, int step) {
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
 #pragma unroll
         for (int h = 0; h < H; ++h) split8(a + 8 * h, pa[h][0], pa[h][1], pa[h][2]);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < JN; ++j) {
 #pragma unroll
             for (int h = 0; h < H; ++h) {
                 const v8bf bw = WT ? half8(wbuf[b][j], h) : column8(&wbuf[b][8 * h], j);
@@ -205,25 +216,25 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
 
     // This wave's steps: s_begin + wave + WV*i, i < n_my (even, the same
     // for all waves); two in flight, the last pair peeled.
-    const int first = s_begin + wave;
-    const int n_my = per / WV;
+    const int first = s_begin + swave;
+    const int n_my = per / SW;
     fetch(first, 0);
     __builtin_amdgcn_sched_barrier(0);
-    fetch(first + WV, 1);
+    fetch(first + SW, 1);
     __builtin_amdgcn_sched_barrier(0);
     int i = 0;
     for (; i + 2 < n_my; i += 2) {
-        consume(0, first + WV * i);
+        consume(0, first + SW * i);
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WV * (i + 2), 0);
+        fetch(first + SW * (i + 2), 0);
         __builtin_amdgcn_sched_barrier(0);
-        consume(1, first + WV * (i + 1));
+        consume(1, first + SW * (i + 1));
         __builtin_amdgcn_sched_barrier(0);
-        fetch(first + WV * (i + 3), 1);
+        fetch(first + SW * (i + 3), 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    consume(0, first + WV * i);
-    consume(1, first + WV * (i + 1));
+    consume(0, first + SW * i);
+    consume(1, first + SW * (i + 1));
 
     // Register r of block j holds row 4g + r, column 16*c16 + j: four
     // 16-byte chunks per row, placed as in the int8 decode kernel.
@@ -232,22 +243,22 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
     for (int r = 0; r < 4; ++r) {
         if (4 * g + r >= M) continue;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < JN / 4; ++q) {
             const v4f v = v4f{acc[4 * q][r], acc[4 * q + 1][r], acc[4 * q + 2][r], acc[4 * q + 3][r]};
-            *reinterpret_cast<v4f*>(&red[wave][4 * g + r][4 * chunk(4 * c16 + q)]) = v;
+            *reinterpret_cast<v4f*>(&red[swave][4 * g + r][4 * chunk(32 * half + (JN / 4) * c16 + q)]) = v;
         }
     }
     if constexpr (ZP) {
         // lane groups held different k: (g0 + g1) + (g2 + g3) in every lane
         s2 += __shfl_xor(s2, 16);
         s2 += __shfl_xor(s2, 32);
-        if (g == 0) s2_red[wave][c16] = s2;
+        if (g == 0 && half == 0) s2_red[swave][c16] = s2;
     }
     __syncthreads();
     if (ZP && tid < 16) {
         float t = s2_red[0][tid];
 #pragma unroll
-        for (int w = 1; w < WV; ++w) t = t + s2_red[w][tid];
+        for (int w = 1; w < SW; ++w) t = t + s2_red[w][tid];
         s2_tot[tid] = t;
     }
 
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV == 8
         const int at = 4 * chunk(cg);
         v4f s = *reinterpret_cast<const v4f*>(&red[0][m][at]);
 #pragma unroll
-        for (int w = 1; w < WV; ++w) s = s + *reinterpret_cast<const v4f*>(&red[w][m][at]);
+        for (int w = 1; w < SW; ++w) s = s + *reinterpret_cast<const v4f*>(&red[w][m][at]);
         return s;
     };
     const float zp = (float)p.zp;
@@ -582,8 +593,16 @@ hipError_t launch_w8a32_skinny(const W8A32Args& a, bool wt, hipStream_t s, const
         (grid.y > 1 && (a.workspace == nullptr || (int)(grid.x * grid.z) > SKINNY_MAX_TICKETS)))
         return hipErrorInvalidValue;
     if (wt) {
-        if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true>), grid, dim3(NT), 0, s, a);
-        else hipLaunchKernelGGL((w8a32_skinny_kernel<false, true>), grid, dim3(NT), 0, s, a);
+        // eight waves for one block of rows (graph-timed at N = K = 8192,
+        // identical bits: M = 1 22.5 -> 20.8 us, M = 16 24.1 -> 23.1), four
+        // for several (M = 40: 49.1 against 51.7 with eight)
+        if (grid.z == 1) {
+            if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true, 8, 64>), grid, dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((w8a32_skinny_kernel<false, true, 8, 64>), grid, dim3(512), 0, s, a);
+        } else {
+            if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, true>), grid, dim3(NT), 0, s, a);
+            else hipLaunchKernelGGL((w8a32_skinny_kernel<false, true>), grid, dim3(NT), 0, s, a);
+        }
     } else {
         if (a.zp != 0) hipLaunchKernelGGL((w8a32_skinny_kernel<true, false, 8, 32>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((w8a32_skinny_kernel<false, false, 8, 32>), grid, dim3(512), 0, s, a);

@@ -589,14 +589,16 @@ def main():
         acc_m = torch.from_numpy(si.randint(g, (m, 8192), -2**20, 2**20, np.int32)).to(dev)
         sets = [(to(A), base_w if r == 0 else base_w.clone(), to(s_a), to(s_w),
                  torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)) for r in range(9)]
-        call = lambda s: q.qgemm_a8w8_acc(acc_m, s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4])
-        ms = time_calls(call, sets, max(steps * 5, 50), warmup * 2, stream)
+        ws = torch.zeros(q.workspace_bytes(q.QG_OP_A8W8, 1, m, 8192, 8192), dtype=torch.uint8, device=dev)
+        call = lambda s: q.qgemm_a8w8_acc(acc_m, s[0], s[1], s[2], s[3], out_dtype=torch.bfloat16, out=s[4],
+                                          workspace=ws)
+        ms, spread = time_graph(call, sets, 36, max(steps // 2, 5), stream, spread=True)
         nbytes = m * 8192 + 8192 * 8192 + 4 * m + 4 * 8192 + 4 * m * 8192 + 2 * m * 8192
         rows["a8w8_acc_decode_m16_8192_bf16"] = {"kernel": q.last_kernel(), "us": ms * 1e3,
                                                  "GB/s": nbytes / (ms * 1e-3) / 1e9,
                                                  "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                                 "per_call": per_call_spread(call, sets, SPREAD_CALLS, stream)}
-        del sets, base_w
+                                                 "timing": "hip_graph", "per_call": spread}
+        del sets, base_w, ws
         A, B, zb = si.matmul_integer_inputs(8, 512, 2048, 2048, seed=303)
         za = to(si.randint(g, (512,), 0, 255, np.uint8))
         tB, tzb = to(B), to(zb)
